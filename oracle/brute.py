@@ -1,0 +1,80 @@
+"""Pure-Python brute force for tiny inputs (test infrastructure only).
+
+These loops restate the definitions element by element with Python floats/ints and
+``math`` functions, without NumPy linear algebra, so that the NumPy oracle can be
+checked against something other than itself on small cases.
+"""
+from __future__ import annotations
+
+import math
+
+__all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row"]
+
+
+def matmul(X, W):
+    """out[i][j] = sum_k X[i][k] * W[k][j], accumulated left to right."""
+    n, kdim, m = len(X), len(W), len(W[0])
+    out = []
+    for i in range(n):
+        row = []
+        for j in range(m):
+            acc = 0
+            for k in range(kdim):
+                acc += X[i][k] * W[k][j]
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+def relu(M):
+    return [[x if x > 0 else 0 for x in row] for row in M]
+
+
+def silu(M):
+    return [[x / (1.0 + math.exp(-x)) for x in row] for row in M]
+
+
+def mlp(X, W_gate, W_up, W_down, kind):
+    if kind == "relu":
+        return matmul(relu(matmul(X, W_gate)), W_down)
+    g, u = silu(matmul(X, W_gate)), matmul(X, W_up)
+    h = [[a * b for a, b in zip(rg, ru)] for rg, ru in zip(g, u)]
+    return matmul(h, W_down)
+
+
+def rope_row(x, pos, theta):
+    """Rotate pairs (x[i], x[i+d/2]) of one vector by pos * theta**(-2i/d)."""
+    d = len(x)
+    half = d // 2
+    out = [0.0] * d
+    for i in range(half):
+        ang = pos * theta ** (-2.0 * i / d)
+        c, s = math.cos(ang), math.sin(ang)
+        out[i] = x[i] * c - x[i + half] * s
+        out[i + half] = x[i + half] * c + x[i] * s
+    return out
+
+
+def attention_head(q, k, v, causal=True):
+    """For each query row t: weights over keys u <= t (all keys if not causal)."""
+    d = len(q[0])
+    out = []
+    for t, qt in enumerate(q):
+        last = t if causal else len(k) - 1
+        scores = []
+        for u in range(last + 1):
+            s = 0.0
+            for c in range(d):
+                s += qt[c] * k[u][c]
+            scores.append(s / math.sqrt(d))
+        m = max(scores)
+        w = [math.exp(s - m) for s in scores]
+        z = sum(w)
+        row = []
+        for c in range(len(v[0])):
+            acc = 0.0
+            for u in range(last + 1):
+                acc += w[u] * v[u][c]
+            row.append(acc / z)
+        out.append(row)
+    return out
