@@ -1,0 +1,209 @@
+/*
+ * libtpshard — one tensor-parallel rank's shard of a Transformer block, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What a rank computes (sources are the pages' titles and sections):
+ *   - a column-parallel linear layer: Y_r = X . W[:, cols_r], X replicated
+ *     ("CUDA tensor parallel computations", 第二类 Column Parallel;
+ *      "张量并行：切分 Transformer 层的分布式训练", 列切分);
+ *   - a row-parallel linear layer whose output is this rank's additive
+ *     contribution to the layer output: P_r = X[:, rows_r] . W[rows_r, :]
+ *     ("CUDA tensor parallel computations", 第三类 Row Parallel; 行切分);
+ *   - the MLP and attention blocks built from the two ("放进 Transformer";
+ *     "Transformer 层的张量并行切分": MLP 块切分, 自注意力块切分);
+ *   - the element-wise sum of partial outputs, i.e. the arithmetic that an
+ *     all-reduce performs (第四类 跨卡通信计算). tp_partial_sum adds buffers that
+ *     all live on the calling GPU; it is not a collective.
+ *
+ * Conventions shared by every call
+ *   - Row-major everywhere. Weights are stored [in, out] (X . W orientation, as in
+ *     both pages' examples). Activations are [T, H] with T = B * S tokens,
+ *     sequence-major.
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or keeps a pointer; scratch space is a caller-owned
+ *     workspace whose size is queried first.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream). Buffers must stay alive until the stream has finished with them.
+ *   - Arguments are validated on the host before any HIP call; on failure the call
+ *     returns a non-OK status, launches nothing and tp_last_error() describes why.
+ *     A failed kernel launch returns TP_ERR_HIP. Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - fp32 path: any positive sizes, 4-byte aligned pointers.
+ *     bf16/fp16 path: 16-byte aligned base pointers; K, N and leading dimensions
+ *     multiples of 8 elements. Tails of T and N inside a tile are masked.
+ *   - Results do not depend on launch timing: repeated calls give bitwise-equal
+ *     outputs (no floating-point atomics).
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+    TP_ERR_BAD_SHAPE = 2,      /* non-positive size, ld < N, uneven head grouping, ... */
+    TP_ERR_BAD_DTYPE = 3,      /* dtype combination not offered by this call */
+    TP_ERR_MISALIGNED = 4,     /* pointer or size breaks the alignment rules above */
+    TP_ERR_WORKSPACE = 5,      /* workspace NULL or smaller than the queried size */
+    TP_ERR_UNSUPPORTED = 6,    /* well-formed but not implemented (e.g. head_dim != 128) */
+    TP_ERR_HIP = 7             /* the HIP runtime reported an error at launch */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1, TP_F16 = 2, TP_FP8_E4M3 = 3 } tp_dtype;
+typedef enum { TP_ACT_NONE = 0, TP_ACT_RELU = 1 } tp_act;
+typedef enum { TP_MLP_RELU = 0, TP_MLP_SWIGLU = 1 } tp_mlp_kind;
+
+/* Per-tensor dequantisation scales for TP_FP8_E4M3 operands (OCP E4M3):
+ * real value = code_value * scale. Only read when in_dt == TP_FP8_E4M3. */
+typedef struct { float x_scale; float w_scale; } tp_fp8_scales;
+
+/*
+ * tp_column_linear — column-parallel rank output Y = act(X . W_shard).
+ *   ("CUDA tensor parallel computations", 第二类 Column Parallel; 第五类 局部逐元素计算
+ *    for the local activation.) Also serves the vocabulary-split output layer
+ *   ("张量并行：切分 Transformer 层的分布式训练", 输入与输出层): logits for this rank's
+ *   vocabulary columns.
+ *   X       [T, K]   in_dt          replicated input
+ *   W_shard [K, N]   in_dt          this rank's columns of the full weight
+ *   Y       [T, ldy] out_dt         row t of the result at Y + t*ldy; ldy >= N lets a
+ *                                   rank write its slice of a full [T, N*tp] buffer
+ *                                   (the concatenation happens in place).
+ *   in_dt/out_dt: (F32, F32) — exact fp32 path; (BF16, BF16|F16|F32);
+ *                 (FP8_E4M3, BF16|F32) with scales q.
+ *   act: TP_ACT_NONE or TP_ACT_RELU (applied in fp32 before the output rounding).
+ */
+tp_status tp_column_linear(const void* X, const void* W_shard, void* Y,
+                           int64_t T, int64_t K, int64_t N, int64_t ldy,
+                           tp_dtype in_dt, tp_dtype out_dt, tp_act act,
+                           const tp_fp8_scales* q, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * tp_row_linear_partial — row-parallel rank contribution P = X_shard . W_shard
+ *   ("CUDA tensor parallel computations", 第三类 Row Parallel): the fp32 partial
+ *   that a sum over ranks (all-reduce) turns into the layer output.
+ *   X_shard [T, K_shard] in_dt      this rank's slice of the input features
+ *   W_shard [K_shard, N] in_dt      this rank's rows of the full weight
+ *   Y_partial [T, N] fp32           overwritten, or += when accumulate != 0
+ *   in_dt: F32 (exact path), BF16, or FP8_E4M3 with scales q.
+ *   workspace: >= tp_linear_workspace_size(T, K_shard, N, in_dt) bytes (both calls).
+ */
+tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float* Y_partial,
+                                int64_t T, int64_t K_shard, int64_t N, tp_dtype in_dt,
+                                int accumulate, const tp_fp8_scales* q, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by tp_column_linear / tp_row_linear_partial for these sizes
+ * (K = the contraction length). Non-zero only for the few-row (decode) regime, T <= 64,
+ * where the contraction is split into chunks whose fp32 partials are summed in chunk
+ * order; when it returns 0, workspace may be NULL.
+ */
+size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt);
+
+/*
+ * tp_mlp_shard — one rank's MLP block: column-split first layer, local activation,
+ *   row-split second layer ("CUDA tensor parallel computations", 放进 Transformer:
+ *   MLP 一扩一收; "张量并行：切分 Transformer 层的分布式训练", MLP 块切分).
+ *   kind TP_MLP_RELU:   P = relu(X . W_gate) . W_down          (W_up must be NULL)
+ *   kind TP_MLP_SWIGLU: P = (SiLU(X . W_gate) * (X . W_up)) . W_down,
+ *                       SiLU(z) = z / (1 + exp(-z)), evaluated in fp32.
+ *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: in_dt (F32 or BF16)
+ *   Y_partial [T, H] fp32 (overwritten).
+ *   h_dt: storage type of the activated intermediate h [T, I_shard], which lives
+ *   only in the workspace: F32 for the F32 path, BF16 for the BF16 path.
+ *   The gate/up pre-activations never leave registers.
+ *   workspace: >= tp_mlp_workspace_size(T, H, I_shard, kind, in_dt, h_dt) bytes,
+ *   16-byte aligned; contents on return are unspecified.
+ */
+tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up,
+                       const void* W_down, float* Y_partial,
+                       int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                       tp_dtype in_dt, tp_dtype h_dt,
+                       void* workspace, size_t ws_bytes, void* stream);
+size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                             tp_dtype in_dt, tp_dtype h_dt);
+
+/*
+ * tp_attn_desc — shapes of one rank's attention shard (all head counts are the
+ * rank's local ones). The rank holds whole heads ("张量并行：切分 Transformer 层的
+ * 分布式训练", 自注意力块切分); query heads share kv heads in groups
+ * ("TensorRT LLM 中的并行策略", 注意力模块): q head j reads kv head
+ * floor(j * n_kv_heads / n_q_heads).
+ *   B, S, H        sequences, tokens per sequence, hidden size (T = B*S rows of X)
+ *   head_dim       must be 128
+ *   rope_theta     rotary base; rotate-half pairs (i, i+64), angle pos*theta^(-2i/128),
+ *                  applied to q and k; pos = index in the sequence (decode: cache_len)
+ *   causal         must be 1 (key position <= query position, within a sequence)
+ *   k_cache, v_cache  decode only (S == 1): [B, n_kv_heads, cache_capacity, 128] in_dt,
+ *                  slots < cache_len hold rotated keys / values; the call writes the
+ *                  new token's rotated key and value at slot cache_len and attends to
+ *                  slots 0..cache_len. NULL for prefill.
+ */
+typedef struct {
+    int64_t B, S, H;
+    int32_t n_q_heads, n_kv_heads, head_dim;
+    float rope_theta;
+    int32_t causal;
+    void* k_cache;
+    void* v_cache;
+    int64_t cache_len, cache_capacity;
+} tp_attn_desc;
+
+/*
+ * tp_attn_shard — one rank's attention block: QKV column projection, rotary
+ *   embedding, per-head causal softmax(q k^T / sqrt(128)) v on the local heads,
+ *   then the O row projection's fp32 partial ("CUDA tensor parallel computations",
+ *   放进 Transformer: QKV / Attention heads / 输出投影).
+ *   X      [B*S, H] in_dt (BF16)
+ *   W_qkv  [H, (hq + 2*hkv)*128]: columns [Q heads | K heads | V heads], 128 each
+ *   W_o    [hq*128, H]
+ *   Y_partial [B*S, H] fp32 (overwritten)
+ *   workspace >= tp_attn_workspace_size(desc, in_dt) bytes, 16-byte aligned.
+ */
+tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float* Y_partial,
+                        const tp_attn_desc* desc, tp_dtype in_dt,
+                        void* workspace, size_t ws_bytes, void* stream);
+size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt);
+
+/*
+ * tp_partial_sum — out = ((P_0 + P_1) + P_2) + ... + P_{k-1}, element-wise, in that
+ *   order, fp32 ("CUDA tensor parallel computations", 第三类 Row Parallel: partial
+ *   contributions are summed; 第四类: the all-reduce result). All buffers are on the
+ *   calling GPU.
+ *   partials: HOST array of k device pointers, each to n_elems floats (16-byte
+ *   aligned). 1 <= k <= 16. out may alias partials[0].
+ */
+tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out,
+                         int64_t n_elems, void* stream);
+
+/* Status text, thread-local detail of this thread's last non-OK status, ABI version. */
+const char* tp_status_string(tp_status st);
+const char* tp_last_error(void);
+int tp_abi_version(void);
+
+/*
+ * Kernel timing for measurement: when enabled, the library brackets every kernel it
+ * launches with a pair of HIP events on the launch stream (the events are created
+ * by the library on first use). tp_profile_read synchronises those events and
+ * returns the summed duration and launch count of the kernels whose name starts
+ * with `prefix` ("" for all). tp_profile_reset discards the recorded pairs.
+ * Off by default; at most 65536 launches are recorded between resets.
+ */
+tp_status tp_profile_enable(int on);
+tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches);
+tp_status tp_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -1,0 +1,266 @@
+"""Python binding of libtpshard (one tensor-parallel rank's shard on an MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libtpshard.so,
+reached through the C ABI declared in include/tpshard.h. Tensors are torch tensors on
+the GPU (PyTorch provides device memory and the current stream). There is no CPU or
+fallback path: if the library is missing, importing the entry points raises.
+
+Names follow the C calls: column_linear, row_linear_partial, mlp_shard, attn_shard,
+partial_sum (+ workspace-size queries and kernel timing).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TpError", "lib", "load", "LIB_PATH", "column_linear", "row_linear_partial", "mlp_shard",
+    "attn_shard", "partial_sum", "linear_workspace_size", "mlp_workspace_size",
+    "attn_workspace_size", "AttnDesc", "profile_enable", "profile_reset", "profile_read",
+    "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
+    "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
+
+TP_F32, TP_BF16, TP_F16, TP_FP8_E4M3 = 0, 1, 2, 3
+TP_ACT_NONE, TP_ACT_RELU = 0, 1
+TP_MLP_RELU, TP_MLP_SWIGLU = 0, 1
+STATUS = {0: "TP_OK", 1: "TP_ERR_NULL_POINTER", 2: "TP_ERR_BAD_SHAPE", 3: "TP_ERR_BAD_DTYPE",
+          4: "TP_ERR_MISALIGNED", 5: "TP_ERR_WORKSPACE", 6: "TP_ERR_UNSUPPORTED", 7: "TP_ERR_HIP"}
+
+EXPORTS = [
+    "tp_column_linear", "tp_row_linear_partial", "tp_linear_workspace_size", "tp_mlp_shard",
+    "tp_mlp_workspace_size", "tp_attn_shard", "tp_attn_workspace_size", "tp_partial_sum",
+    "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
+    "tp_profile_read", "tp_profile_reset",
+]
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("cache_len", ctypes.c_int64), ("cache_capacity", ctypes.c_int64),
+    ]
+
+
+class Fp8Scales(ctypes.Structure):
+    _fields_ = [("x_scale", ctypes.c_float), ("w_scale", ctypes.c_float)]
+
+
+_lib = None
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libtpshard.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"libtpshard.so not built at {path}; run "
+                          "`python -m tensor_transformer_layer_rank_amd.build` first")
+    L = ctypes.CDLL(path)
+    sig = {
+        "tp_column_linear": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
+        "tp_row_linear_partial": ([_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _P, _P, _SZ, _P], _I32),
+        "tp_linear_workspace_size": ([_I64, _I64, _I64, _I32], _SZ),
+        "tp_mlp_shard": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _SZ, _P], _I32),
+        "tp_mlp_workspace_size": ([_I64, _I64, _I64, _I32, _I32, _I32], _SZ),
+        "tp_attn_shard": ([_P, _P, _P, _P, ctypes.POINTER(AttnDesc), _I32, _P, _SZ, _P], _I32),
+        "tp_attn_workspace_size": ([ctypes.POINTER(AttnDesc), _I32], _SZ),
+        "tp_partial_sum": ([ctypes.POINTER(_P), _I32, _P, _I64, _P], _I32),
+        "tp_status_string": ([_I32], ctypes.c_char_p),
+        "tp_last_error": ([], ctypes.c_char_p),
+        "tp_abi_version": ([], ctypes.c_int),
+        "tp_profile_enable": ([ctypes.c_int], _I32),
+        "tp_profile_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
+        "tp_profile_reset": ([], _I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = L
+    return L
+
+
+def lib() -> ctypes.CDLL:
+    return load()
+
+
+def _check(st: int):
+    if st != 0:
+        raise TpError(st, lib().tp_last_error().decode())
+
+
+# --- tensor helpers -------------------------------------------------------------------------
+
+def _dt(t) -> int:
+    import torch
+    m = {torch.float32: TP_F32, torch.bfloat16: TP_BF16, torch.float16: TP_F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libtpshard takes GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("libtpshard takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes}")
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+# --- entry points (same names as the C calls) --------------------------------------------------
+
+def linear_workspace_size(T: int, K: int, N: int, in_dt: int) -> int:
+    return int(lib().tp_linear_workspace_size(T, K, N, in_dt))
+
+
+def column_linear(X, W, Y=None, act: int = TP_ACT_NONE, out_dtype=None, ldy: int | None = None,
+                  workspace=None, stream=None):
+    """Y = act(X @ W) for this rank's column shard W [K, N]; returns Y ([T, ldy] if given)."""
+    import torch
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [*, {K}] but W is [{K2}, *]")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=out_dtype or X.dtype, device=X.device)
+    ldy = ldy if ldy is not None else Y.shape[-1]
+    ws, wsb = _workspace(linear_workspace_size(T, K, N, _dt(X)), X.device, workspace)
+    _check(lib().tp_column_linear(_ptr(X), _ptr(W), ctypes.c_void_p(Y.data_ptr()), T, K, N, ldy,
+                                  _dt(X), _dt(Y), act, None, _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def row_linear_partial(X, W, Y=None, accumulate: bool = False, workspace=None, stream=None):
+    """fp32 partial X_shard @ W_shard [K_shard, N] of a row-parallel layer."""
+    import torch
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [*, {K}] but W is [{K2}, *]")
+    if Y is None:
+        Y = torch.empty((T, N), dtype=torch.float32, device=X.device)
+    ws, wsb = _workspace(linear_workspace_size(T, K, N, _dt(X)), X.device, workspace)
+    _check(lib().tp_row_linear_partial(_ptr(X), _ptr(W), _ptr(Y), T, K, N, _dt(X), int(accumulate),
+                                       None, _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def mlp_workspace_size(T: int, H: int, I: int, kind: int, in_dt: int, h_dt: int | None = None) -> int:
+    h_dt = in_dt if h_dt is None else h_dt
+    return int(lib().tp_mlp_workspace_size(T, H, I, kind, in_dt, h_dt))
+
+
+def mlp_shard(X, W_gate, W_up, W_down, Y=None, kind: int = TP_MLP_SWIGLU, workspace=None, stream=None):
+    """fp32 partial of this rank's MLP block (ReLU form: W_up=None)."""
+    import torch
+    T, H = X.shape
+    I = W_gate.shape[1]
+    if Y is None:
+        Y = torch.empty((T, H), dtype=torch.float32, device=X.device)
+    dt = _dt(X)
+    ws, wsb = _workspace(mlp_workspace_size(T, H, I, kind, dt), X.device, workspace)
+    _check(lib().tp_mlp_shard(_ptr(X), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Y), T, H, I,
+                              kind, dt, dt, _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def _desc(B, S, H, hq, hkv, theta=10000.0, k_cache=None, v_cache=None, cache_len=0, head_dim=128):
+    d = AttnDesc()
+    d.B, d.S, d.H = B, S, H
+    d.n_q_heads, d.n_kv_heads, d.head_dim = hq, hkv, head_dim
+    d.rope_theta, d.causal = theta, 1
+    d.k_cache = k_cache.data_ptr() if k_cache is not None else None
+    d.v_cache = v_cache.data_ptr() if v_cache is not None else None
+    d.cache_len = cache_len
+    d.cache_capacity = k_cache.shape[2] if k_cache is not None else 0
+    return d
+
+
+def attn_workspace_size(B, S, H, hq, hkv, theta=10000.0, k_cache=None, v_cache=None, cache_len=0) -> int:
+    d = _desc(B, S, H, hq, hkv, theta, k_cache, v_cache, cache_len)
+    return int(lib().tp_attn_workspace_size(ctypes.byref(d), TP_BF16))
+
+
+def attn_shard(X, W_qkv, W_o, B: int, S: int, hq: int, hkv: int, theta: float = 10000.0,
+               k_cache=None, v_cache=None, cache_len: int = 0, Y=None, workspace=None, stream=None):
+    """fp32 partial of this rank's attention block (prefill, or decode when a cache is given)."""
+    import torch
+    T, H = X.shape
+    if Y is None:
+        Y = torch.empty((T, H), dtype=torch.float32, device=X.device)
+    for c in (k_cache, v_cache):
+        if c is not None and not c.is_contiguous():
+            raise ValueError("caches must be contiguous")
+    d = _desc(B, S, H, hq, hkv, theta, k_cache, v_cache, cache_len)
+    nb = int(lib().tp_attn_workspace_size(ctypes.byref(d), _dt(X)))
+    ws, wsb = _workspace(max(nb, 1), X.device, workspace)
+    _check(lib().tp_attn_shard(_ptr(X), _ptr(W_qkv), _ptr(W_o), _ptr(Y), ctypes.byref(d), _dt(X),
+                               _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def partial_sum(partials, out=None, stream=None):
+    """((P0 + P1) + P2) + ... for fp32 GPU tensors of equal size."""
+    import torch
+    k = len(partials)
+    n = partials[0].numel()
+    if out is None:
+        out = torch.empty_like(partials[0])
+    arr = (ctypes.c_void_p * k)(*[p.data_ptr() for p in partials])
+    for p in partials:
+        _ptr(p)
+    _check(lib().tp_partial_sum(arr, k, _ptr(out), n, _stream(stream)))
+    return out
+
+
+# --- kernel timing ------------------------------------------------------------------------------
+
+def profile_enable(on: bool = True):
+    _check(lib().tp_profile_enable(int(on)))
+
+
+def profile_reset():
+    _check(lib().tp_profile_reset())
+
+
+def profile_read(prefix: str = ""):
+    """(total milliseconds, launch count) of recorded kernels whose name starts with prefix."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().tp_profile_read(prefix.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,468 @@
+// C-ABI front end of libtpshard: host-side validation, workspace carving and dispatch
+// to the gfx950 kernels. Every check runs before the first HIP call, so a rejected call
+// launches nothing. The public contract is documented in include/tpshard.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tp_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tp_status fail(tp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+tp_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return TP_OK;
+    return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr size_t WS_ALIGN = 256;
+constexpr int64_t SKINNY_MAX_T = 64;   // rows at or below which the decode (weight-streaming) kernels run
+
+// carve consecutive 256-byte aligned sub-buffers out of a workspace
+struct Carver {
+    unsigned char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<unsigned char*>(b)) {}
+    void* take(size_t bytes) {
+        void* p = base ? base + off : nullptr;
+        off += round_up(bytes, WS_ALIGN);
+        return p;
+    }
+};
+
+// ---- kernel timing ------------------------------------------------------------------------
+struct ProfRec {
+    std::string name;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_used = 0;
+std::vector<ProfRec> g_recs;
+thread_local bool t_pending = false;
+thread_local std::string t_pending_name;
+thread_local hipEvent_t t_pending_start;
+constexpr size_t PROF_MAX = 65536;
+
+hipEvent_t pool_event() {
+    if (g_pool_used == g_pool.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_pool.push_back(e);
+    }
+    return g_pool[g_pool_used++];
+}
+
+}  // namespace
+
+namespace tpk {
+
+void prof_begin(const char* name, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    t_pending = false;
+    if (!g_prof_on || g_recs.size() >= PROF_MAX) return;
+    hipEvent_t a = pool_event();
+    if (!a) return;
+    if (hipEventRecord(a, s) != hipSuccess) return;
+    t_pending = true;
+    t_pending_name = name;
+    t_pending_start = a;
+}
+
+void prof_end(hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!t_pending) return;
+    t_pending = false;
+    hipEvent_t b = pool_event();
+    if (!b) return;
+    if (hipEventRecord(b, s) != hipSuccess) return;
+    g_recs.push_back(ProfRec{t_pending_name, t_pending_start, b});
+}
+
+}  // namespace tpk
+
+extern "C" {
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+const char* tp_status_string(tp_status st) {
+    switch (st) {
+        case TP_OK: return "TP_OK";
+        case TP_ERR_NULL_POINTER: return "TP_ERR_NULL_POINTER";
+        case TP_ERR_BAD_SHAPE: return "TP_ERR_BAD_SHAPE";
+        case TP_ERR_BAD_DTYPE: return "TP_ERR_BAD_DTYPE";
+        case TP_ERR_MISALIGNED: return "TP_ERR_MISALIGNED";
+        case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+        case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED";
+        case TP_ERR_HIP: return "TP_ERR_HIP";
+    }
+    return "TP_ERR_UNKNOWN";
+}
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+tp_status tp_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = on != 0;
+    return TP_OK;
+}
+
+tp_status tp_profile_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_recs.clear();
+    g_pool_used = 0;
+    return TP_OK;
+}
+
+tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches) {
+    if (!prefix || !total_ms || !launches) return fail(TP_ERR_NULL_POINTER, "tp_profile_read: NULL argument");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    double tot = 0.0;
+    int64_t n = 0;
+    const size_t plen = strlen(prefix);
+    for (const ProfRec& r : g_recs) {
+        if (r.name.compare(0, plen, prefix) != 0) continue;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e != hipSuccess) return from_hip(e, "tp_profile_read");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) return from_hip(e, "tp_profile_read");
+        tot += ms;
+        ++n;
+    }
+    *total_ms = tot;
+    *launches = n;
+    return TP_OK;
+}
+
+// ---- linear layers ----------------------------------------------------------------------
+
+size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt) {
+    if (in_dt != TP_BF16 || T <= 0 || T > SKINNY_MAX_T || K <= 0 || N <= 0) return 0;
+    return round_up(tpk::skinny_partials_bytes(T, N, K), WS_ALIGN);
+}
+
+static tp_status check_bf16_gemm(const char* fn, const void* X, const void* W, const void* Y,
+                                 int64_t K, int64_t N, int64_t ldy) {
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: bf16 path needs 16-byte aligned X, W and Y", fn);
+    if (K % 8 || N % 8 || ldy % 8)
+        return fail(TP_ERR_MISALIGNED, "%s: bf16 path needs K, N and ldy multiples of 8 (K=%lld N=%lld ldy=%lld)",
+                    fn, (long long)K, (long long)N, (long long)ldy);
+    return TP_OK;
+}
+
+tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t T, int64_t K,
+                           int64_t N, int64_t ldy, tp_dtype in_dt, tp_dtype out_dt, tp_act act,
+                           const tp_fp8_scales* q, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    (void)q;
+    if (!X || !W_shard || !Y) return fail(TP_ERR_NULL_POINTER, "tp_column_linear: X, W_shard and Y must be non-NULL");
+    if (T <= 0 || K <= 0 || N <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: sizes must be positive (T=%lld K=%lld N=%lld)",
+                    (long long)T, (long long)K, (long long)N);
+    if (ldy < N) return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
+    if (act != TP_ACT_NONE && act != TP_ACT_RELU) return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: unknown activation %d", (int)act);
+    hipStream_t s = as_stream(stream);
+    if (in_dt == TP_F32) {
+        if (out_dt != TP_F32) return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: fp32 input needs fp32 output");
+        if (!aligned(X, 4) || !aligned(W_shard, 4) || !aligned(Y, 4))
+            return fail(TP_ERR_MISALIGNED, "tp_column_linear: fp32 pointers must be 4-byte aligned");
+        return from_hip(tpk::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W_shard),
+                                      static_cast<float*>(Y), T, N, K, K, N, ldy, act == TP_ACT_RELU, 0, s),
+                        "tp_column_linear");
+    }
+    if (in_dt == TP_FP8_E4M3) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp8 operands are not implemented yet");
+    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: input dtype %d not offered", (int)in_dt);
+    if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
+        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: bf16 input needs bf16, fp16 or fp32 output");
+    tp_status st = check_bf16_gemm("tp_column_linear", X, W_shard, Y, K, N, ldy);
+    if (st != TP_OK) return st;
+    const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
+    if (T <= SKINNY_MAX_T) {
+        if (out_dt == TP_F16) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp16 output is not offered for T <= %d", (int)SKINNY_MAX_T);
+        const size_t need = tp_linear_workspace_size(T, K, N, in_dt);
+        if (!workspace || ws_bytes < need)
+            return fail(TP_ERR_WORKSPACE, "tp_column_linear: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+        if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_column_linear: workspace must be 16-byte aligned");
+        int splits = 0;
+        hipError_t e = tpk::skinny_gemm_partials(X, W_shard, static_cast<float*>(workspace), T, N, K, K, &splits, s);
+        if (e != hipSuccess) return from_hip(e, "tp_column_linear");
+        const int rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
+        if (rk < 0) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: ReLU with fp32 output is not offered for T <= %d", (int)SKINNY_MAX_T);
+        return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(workspace), splits, T, N, Y, ldy, rk, s),
+                        "tp_column_linear");
+    }
+    return from_hip(tpk::gemm_bf16_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU, s),
+                    "tp_column_linear");
+}
+
+tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float* Y_partial,
+                                int64_t T, int64_t K_shard, int64_t N, tp_dtype in_dt,
+                                int accumulate, const tp_fp8_scales* q, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    (void)q;
+    if (!X_shard || !W_shard || !Y_partial)
+        return fail(TP_ERR_NULL_POINTER, "tp_row_linear_partial: X_shard, W_shard and Y_partial must be non-NULL");
+    if (T <= 0 || K_shard <= 0 || N <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "tp_row_linear_partial: sizes must be positive (T=%lld K=%lld N=%lld)",
+                    (long long)T, (long long)K_shard, (long long)N);
+    hipStream_t s = as_stream(stream);
+    if (in_dt == TP_F32) {
+        if (!aligned(X_shard, 4) || !aligned(W_shard, 4) || !aligned(Y_partial, 4))
+            return fail(TP_ERR_MISALIGNED, "tp_row_linear_partial: fp32 pointers must be 4-byte aligned");
+        return from_hip(tpk::gemm_f32(static_cast<const float*>(X_shard), static_cast<const float*>(W_shard),
+                                      Y_partial, T, N, K_shard, K_shard, N, N, 0, accumulate != 0, s),
+                        "tp_row_linear_partial");
+    }
+    if (in_dt == TP_FP8_E4M3) return fail(TP_ERR_UNSUPPORTED, "tp_row_linear_partial: fp8 operands are not implemented yet");
+    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_row_linear_partial: input dtype %d not offered", (int)in_dt);
+    tp_status st = check_bf16_gemm("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, N);
+    if (st != TP_OK) return st;
+    if (T <= SKINNY_MAX_T) {
+        const size_t need = tp_linear_workspace_size(T, K_shard, N, in_dt);
+        if (!workspace || ws_bytes < need)
+            return fail(TP_ERR_WORKSPACE, "tp_row_linear_partial: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+        if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_row_linear_partial: workspace must be 16-byte aligned");
+        int splits = 0;
+        hipError_t e = tpk::skinny_gemm_partials(X_shard, W_shard, static_cast<float*>(workspace), T, N, K_shard, K_shard, &splits, s);
+        if (e != hipSuccess) return from_hip(e, "tp_row_linear_partial");
+        return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(workspace), splits, T, N, Y_partial, N,
+                                                 accumulate ? 1 : 0, s),
+                        "tp_row_linear_partial");
+    }
+    return from_hip(tpk::gemm_bf16_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
+                                         accumulate ? 3 : 2, 0, s),
+                    "tp_row_linear_partial");
+}
+
+// ---- MLP shard ------------------------------------------------------------------------------
+
+size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                             tp_dtype in_dt, tp_dtype h_dt) {
+    (void)kind;
+    if (T <= 0 || H <= 0 || I_shard <= 0) return 0;
+    if (in_dt == TP_F32) return round_up((size_t)(T * I_shard) * 4, WS_ALIGN);
+    if (in_dt != TP_BF16 || h_dt != TP_BF16) return 0;
+    size_t bytes = round_up((size_t)(T * I_shard) * 2, WS_ALIGN);   // h
+    if (T <= SKINNY_MAX_T) {
+        const size_t first = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu_partials_bytes(T, I_shard, H)
+                                                   : tpk::skinny_partials_bytes(T, I_shard, H);
+        const size_t second = tpk::skinny_partials_bytes(T, H, I_shard);
+        bytes += round_up(first > second ? first : second, WS_ALIGN);
+    }
+    return bytes;
+}
+
+tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, const void* W_down,
+                       float* Y_partial, int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                       tp_dtype in_dt, tp_dtype h_dt, void* workspace, size_t ws_bytes,
+                       void* stream) {
+    if (!X || !W_gate || !W_down || !Y_partial)
+        return fail(TP_ERR_NULL_POINTER, "tp_mlp_shard: X, W_gate, W_down and Y_partial must be non-NULL");
+    if (kind != TP_MLP_RELU && kind != TP_MLP_SWIGLU) return fail(TP_ERR_BAD_SHAPE, "tp_mlp_shard: unknown kind %d", (int)kind);
+    if (kind == TP_MLP_SWIGLU && !W_up) return fail(TP_ERR_NULL_POINTER, "tp_mlp_shard: SwiGLU needs W_up");
+    if (kind == TP_MLP_RELU && W_up) return fail(TP_ERR_BAD_SHAPE, "tp_mlp_shard: the ReLU form takes no W_up");
+    if (T <= 0 || H <= 0 || I_shard <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "tp_mlp_shard: sizes must be positive (T=%lld H=%lld I=%lld)",
+                    (long long)T, (long long)H, (long long)I_shard);
+    if (in_dt == TP_F32 && h_dt != TP_F32) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: fp32 input keeps h in fp32");
+    if (in_dt == TP_BF16 && h_dt != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: bf16 input keeps h in bf16");
+    if (in_dt != TP_F32 && in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: input dtype %d not offered", (int)in_dt);
+    if (in_dt == TP_F32 && kind == TP_MLP_SWIGLU) return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: the fp32 path offers the ReLU form");
+    const size_t need = tp_mlp_workspace_size(T, H, I_shard, kind, in_dt, h_dt);
+    if (!workspace || ws_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "tp_mlp_shard: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: workspace must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    if (in_dt == TP_F32) {
+        if (!aligned(X, 4) || !aligned(W_gate, 4) || !aligned(W_down, 4) || !aligned(Y_partial, 4))
+            return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: fp32 pointers must be 4-byte aligned");
+        float* h = static_cast<float*>(workspace);
+        hipError_t e = tpk::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W_gate), h, T, I_shard,
+                                     H, H, I_shard, I_shard, 1, 0, s);
+        if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
+        return from_hip(tpk::gemm_f32(h, static_cast<const float*>(W_down), Y_partial, T, H, I_shard, I_shard, H, H,
+                                      0, 0, s),
+                        "tp_mlp_shard");
+    }
+    if (!aligned(X, 16) || !aligned(W_gate, 16) || (W_up && !aligned(W_up, 16)) || !aligned(W_down, 16) ||
+        !aligned(Y_partial, 16))
+        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs 16-byte aligned pointers");
+    if (H % 8 || I_shard % 8)
+        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs H and I_shard multiples of 8");
+    Carver c(workspace);
+    void* h = c.take((size_t)(T * I_shard) * 2);
+    if (T <= SKINNY_MAX_T) {
+        float* part = static_cast<float*>(c.take(0));
+        hipError_t e;
+        if (kind == TP_MLP_SWIGLU) {
+            e = tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I_shard, H, s);
+        } else {
+            int splits = 0;
+            e = tpk::skinny_gemm_partials(X, W_gate, part, T, I_shard, H, H, &splits, s);
+            if (e == hipSuccess) e = tpk::skinny_reduce_store(part, splits, T, I_shard, h, I_shard, 3, s);
+        }
+        if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
+        int splits = 0;
+        e = tpk::skinny_gemm_partials(h, W_down, part, T, H, I_shard, I_shard, &splits, s);
+        if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
+        return from_hip(tpk::skinny_reduce_store(part, splits, T, H, Y_partial, H, 0, s), "tp_mlp_shard");
+    }
+    hipError_t e;
+    if (kind == TP_MLP_SWIGLU)
+        e = tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I_shard, H, s);
+    else
+        e = tpk::gemm_bf16_store(X, W_gate, h, T, I_shard, H, H, I_shard, I_shard, 0, 1, s);
+    if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
+    return from_hip(tpk::gemm_bf16_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0, s),
+                    "tp_mlp_shard");
+}
+
+// ---- attention shard --------------------------------------------------------------------------
+
+static tp_status check_attn_desc(const tp_attn_desc* d, bool* decode) {
+    if (!d) return fail(TP_ERR_NULL_POINTER, "tp_attn_shard: desc is NULL");
+    if (d->B <= 0 || d->S <= 0 || d->H <= 0 || d->n_q_heads <= 0 || d->n_kv_heads <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "tp_attn_shard: B, S, H and head counts must be positive");
+    if (d->head_dim != 128) return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: head_dim %d (only 128 is offered)", (int)d->head_dim);
+    if (d->n_q_heads % d->n_kv_heads)
+        return fail(TP_ERR_BAD_SHAPE, "tp_attn_shard: %d query heads do not group evenly over %d kv heads",
+                    (int)d->n_q_heads, (int)d->n_kv_heads);
+    if (d->causal != 1) return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: only causal attention is offered");
+    if (!(d->rope_theta > 0.0f)) return fail(TP_ERR_BAD_SHAPE, "tp_attn_shard: rope_theta must be positive");
+    if (d->H % 8) return fail(TP_ERR_MISALIGNED, "tp_attn_shard: H must be a multiple of 8");
+    const bool has_cache = d->k_cache || d->v_cache;
+    if (has_cache) {
+        if (!d->k_cache || !d->v_cache) return fail(TP_ERR_NULL_POINTER, "tp_attn_shard: k_cache and v_cache go together");
+        if (d->S != 1) return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: a KV cache is offered for S == 1 (decode) only");
+        if (d->cache_len < 0 || d->cache_len >= d->cache_capacity)
+            return fail(TP_ERR_BAD_SHAPE, "tp_attn_shard: need 0 <= cache_len (%lld) < cache_capacity (%lld)",
+                        (long long)d->cache_len, (long long)d->cache_capacity);
+        if (d->B > SKINNY_MAX_T) return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: decode offers at most %d sequences", (int)SKINNY_MAX_T);
+        if (!aligned(d->k_cache, 16) || !aligned(d->v_cache, 16))
+            return fail(TP_ERR_MISALIGNED, "tp_attn_shard: caches must be 16-byte aligned");
+    } else if (d->S % 8) {
+        return fail(TP_ERR_MISALIGNED, "tp_attn_shard: prefill needs S to be a multiple of 8 (S=%lld)", (long long)d->S);
+    }
+    *decode = has_cache;
+    return TP_OK;
+}
+
+static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, void** k,
+                      void** vt, void** rope, void** att, void** part, void** qbuf, void** scratch) {
+    Carver c(base);
+    const int64_t hq = d->n_q_heads, hkv = d->n_kv_heads;
+    const int64_t nqkv = (hq + 2 * hkv) * 128;
+    if (!decode) {
+        const int64_t T = d->B * d->S;
+        *rope = c.take((size_t)d->S * 64 * sizeof(float2));
+        *q = c.take((size_t)(T * hq * 128) * 2);
+        *k = c.take((size_t)(T * hkv * 128) * 2);
+        *vt = c.take((size_t)(T * hkv * 128) * 2);
+        *att = c.take((size_t)(T * hq * 128) * 2);
+        return c.off;
+    }
+    const int64_t B = d->B, L = d->cache_len + 1;
+    const size_t p1 = tpk::skinny_partials_bytes(B, nqkv, d->H);
+    const size_t p2 = tpk::skinny_partials_bytes(B, d->H, hq * 128);
+    *part = c.take(p1 > p2 ? p1 : p2);
+    *qbuf = c.take((size_t)(B * hq * 128) * 4);
+    *scratch = c.take(tpk::decode_attn_scratch_bytes(B, (int)hq, L));
+    *att = c.take((size_t)(B * hq * 128) * 2);
+    return c.off;
+}
+
+size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt) {
+    if (in_dt != TP_BF16) return 0;
+    bool decode = false;
+    if (check_attn_desc(desc, &decode) != TP_OK) return 0;
+    void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
+    return attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+}
+
+tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float* Y_partial,
+                        const tp_attn_desc* desc, tp_dtype in_dt, void* workspace,
+                        size_t ws_bytes, void* stream) {
+    if (!X || !W_qkv || !W_o || !Y_partial)
+        return fail(TP_ERR_NULL_POINTER, "tp_attn_shard: X, W_qkv, W_o and Y_partial must be non-NULL");
+    bool decode = false;
+    tp_status st = check_attn_desc(desc, &decode);
+    if (st != TP_OK) return st;
+    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_attn_shard: the attention shard takes bf16 inputs");
+    if (!aligned(X, 16) || !aligned(W_qkv, 16) || !aligned(W_o, 16) || !aligned(Y_partial, 16))
+        return fail(TP_ERR_MISALIGNED, "tp_attn_shard: X, W_qkv, W_o and Y_partial must be 16-byte aligned");
+    void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
+    const size_t need = attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+    if (!workspace || ws_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "tp_attn_shard: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+    if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_attn_shard: workspace must be 16-byte aligned");
+    attn_ws(desc, decode, workspace, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+    hipStream_t s = as_stream(stream);
+    const int hq = desc->n_q_heads, hkv = desc->n_kv_heads;
+    const int64_t H = desc->H, dq = (int64_t)hq * 128;
+    if (!decode) {
+        const int64_t T = desc->B * desc->S;
+        hipError_t e = tpk::rope_table(static_cast<float2*>(rope), 0, desc->S, desc->rope_theta, s);
+        if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+        tpk::QKVOut o{q, k, vt, static_cast<const float2*>(rope), desc->B, desc->S, hq, hkv};
+        e = tpk::gemm_bf16_qkv_rope(X, W_qkv, H, o, s);
+        if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+        e = tpk::flash_attn_fwd(q, k, vt, att, desc->B, desc->S, hq, hkv, s);
+        if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+        return from_hip(tpk::gemm_bf16_store(att, W_o, Y_partial, T, H, dq, dq, H, H, 2, 0, s), "tp_attn_shard");
+    }
+    const int64_t B = desc->B, nqkv = (int64_t)(hq + 2 * hkv) * 128;
+    int splits = 0;
+    hipError_t e = tpk::skinny_gemm_partials(X, W_qkv, static_cast<float*>(part), B, nqkv, H, H, &splits, s);
+    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+    e = tpk::skinny_reduce_qkv_decode(static_cast<const float*>(part), splits, B, hq, hkv, desc->cache_len,
+                                      desc->rope_theta, static_cast<float*>(qbuf), desc->k_cache, desc->v_cache,
+                                      desc->cache_capacity, s);
+    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+    e = tpk::decode_attn(static_cast<const float*>(qbuf), desc->k_cache, desc->v_cache, B, hq, hkv,
+                         desc->cache_len + 1, desc->cache_capacity, static_cast<float*>(scratch), att, s);
+    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+    e = tpk::skinny_gemm_partials(att, W_o, static_cast<float*>(part), B, H, dq, dq, &splits, s);
+    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
+    return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(part), splits, B, H, Y_partial, H, 0, s),
+                    "tp_attn_shard");
+}
+
+// ---- merges ------------------------------------------------------------------------------------
+
+tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out, int64_t n_elems,
+                         void* stream) {
+    if (!partials || !out) return fail(TP_ERR_NULL_POINTER, "tp_partial_sum: partials and out must be non-NULL");
+    if (k < 1 || k > 16) return fail(TP_ERR_BAD_SHAPE, "tp_partial_sum: k=%d outside 1..16", (int)k);
+    if (n_elems <= 0) return fail(TP_ERR_BAD_SHAPE, "tp_partial_sum: n_elems must be positive");
+    if (!aligned(out, 16)) return fail(TP_ERR_MISALIGNED, "tp_partial_sum: out must be 16-byte aligned");
+    for (int i = 0; i < k; ++i) {
+        if (!partials[i]) return fail(TP_ERR_NULL_POINTER, "tp_partial_sum: partials[%d] is NULL", i);
+        if (!aligned(partials[i], 16)) return fail(TP_ERR_MISALIGNED, "tp_partial_sum: partials[%d] must be 16-byte aligned", i);
+    }
+    return from_hip(tpk::partial_sum(partials, k, out, n_elems, as_stream(stream)), "tp_partial_sum");
+}
+
+}  // extern "C"

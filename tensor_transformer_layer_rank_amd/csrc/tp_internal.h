@@ -1,0 +1,83 @@
+// Internal declarations shared by the C-ABI front end (api.cpp) and the gfx950 kernels.
+// Not part of the public interface (include/tpshard.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tpshard.h"
+
+namespace tpk {
+
+// ---- kernel timing hook (implemented in api.cpp) --------------------------------
+// Every launcher brackets its kernel with prof_begin/prof_end; both are no-ops
+// unless tp_profile_enable(1) was called.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+struct ProfScope {
+    hipStream_t s;
+    ProfScope(const char* name, hipStream_t st) : s(st) { prof_begin(name, st); }
+    ~ProfScope() { prof_end(s); }
+};
+
+// ---- exact fp32 path ---------------------------------------------------------------
+// C[M, N] (ldc) = act(A[M, K] (lda) . B[K, N] (ldb)); accumulate: C += A.B.
+hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb, int64_t ldc, int relu, int accumulate,
+                    hipStream_t s);
+
+// ---- bf16 MFMA path -----------------------------------------------------------------
+// out_kind for gemm_bf16_store: 0 = bf16, 1 = fp16, 2 = fp32 (overwrite), 3 = fp32 (+=)
+hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                           int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
+                           int relu, hipStream_t s);
+// h[M, N] (bf16, ld = N) = SiLU(A . Bg) * (A . Bu)
+hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
+                            int64_t N, int64_t K, hipStream_t s);
+
+// QKV projection of a prefill with rotary embedding and head-major scatter.
+struct QKVOut {
+    void* q;        // fp16 [B, hq, S, 128]
+    void* k;        // fp16 [B, hkv, S, 128]
+    void* vt;       // fp16 [B, hkv, 128, S]   (values stored transposed)
+    const float2* rope;   // [S, 64] (cos, sin)
+    int64_t B, S;
+    int hq, hkv;
+};
+hipError_t gemm_bf16_qkv_rope(const void* X, const void* Wqkv, int64_t H, const QKVOut& o,
+                              hipStream_t s);
+// rotary table [npos, 64] of (cos, sin) of (pos0 + p) * theta^(-2i/128), computed in fp64
+hipError_t rope_table(float2* table, int64_t pos0, int64_t npos, float theta, hipStream_t s);
+
+// causal flash attention over the head-major fp16 q/k/vt; out bf16 [B*S, hq*128]
+hipError_t flash_attn_fwd(const void* q, const void* k, const void* vt, void* out, int64_t B,
+                          int64_t S, int hq, int hkv, hipStream_t s);
+
+// ---- decode (skinny M) path ------------------------------------------------------------
+// split-K skinny GEMM partials: part[split][M, N] fp32 = A[M, K-chunk] . B[K-chunk, N]
+size_t skinny_partials_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t skinny_gemm_partials(const void* A, const void* B, float* part, int64_t M, int64_t N,
+                                int64_t K, int64_t lda, int* splits_out, hipStream_t s);
+// reduce partials into: 0 = fp32 out (ld), 1 = fp32 += , 2 = bf16 out, 3 = bf16 relu
+hipError_t skinny_reduce_store(const float* part, int splits, int64_t M, int64_t N, void* C,
+                               int64_t ldc, int kind, hipStream_t s);
+// gate/up in one dual skinny launch + SiLU(gate)*up reduce into h bf16 [M, I]
+size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H);
+hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
+                         int64_t M, int64_t I, int64_t H, hipStream_t s);
+// reduce QKV partials, rotate q/k at position pos, append k/v to the caches, q to qbuf (fp32)
+hipError_t skinny_reduce_qkv_decode(const float* part, int splits, int64_t B, int hq, int hkv,
+                                    int64_t pos, float theta, float* qbuf, void* k_cache,
+                                    void* v_cache, int64_t cap, hipStream_t s);
+// split-KV decode attention: out bf16 [B, hq*128]; scratch for per-split (m, l, o)
+size_t decode_attn_scratch_bytes(int64_t B, int hq, int64_t L);
+hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache, int64_t B,
+                       int hq, int hkv, int64_t L, int64_t cap, float* scratch, void* out,
+                       hipStream_t s);
+
+// ---- merges -------------------------------------------------------------------------------
+hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s);
+
+}  // namespace tpk

@@ -1,0 +1,56 @@
+"""Helpers shared by the test modules (no arithmetic of the method lives here)."""
+import numpy as np
+
+REL_F_TOL = 5e-3     # relative Frobenius error bound for bf16 inputs with fp32 accumulation
+MAX_ABS_TOL = 3e-2   # max-abs error bound for the same
+
+
+def rel_fro(got, ref) -> float:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_abs(got, ref) -> float:
+    return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))))
+
+
+OUT_ROUNDING = {"f32": 0.0, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def assert_close_bf16(got, ref, what="", out="f32"):
+    """relF <= 5e-3 and max-abs <= 3e-2 (fp32 outputs).
+
+    For outputs stored in bf16/fp16 the rounding of the stored value itself (half an
+    ulp: 2^-8 resp. 2^-11 of |ref|) is added to the max-abs bound.
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rf = rel_fro(got, ref)
+    err = np.abs(got - ref) - OUT_ROUNDING[out] * np.abs(ref)
+    ma = float(np.max(err))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert rf <= REL_F_TOL and ma <= MAX_ABS_TOL, f"{what}: relF={rf:.3e} max-abs={ma:.3e}"
+    return rf, ma
+
+
+def dev(a, dtype="bf16"):
+    """numpy float32 -> contiguous GPU tensor (bf16 values are exact: inputs are bf16-rounded)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    elif dtype == "f16":
+        t = t.to(torch.float16)
+    return t.cuda()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def sample_rows(T: int, n: int, seed: int = 0):
+    """First, last and random rows (sorted, unique)."""
+    rng = np.random.default_rng(seed)
+    rows = set([0, T - 1]) | set(rng.integers(0, T, size=n).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,156 @@
+"""Host-only checks of the C ABI (no GPU needed; no call reaches a kernel).
+
+* libtpshard.so loads and exports every function include/tpshard.h declares.
+* Every validation error path returns its status before any HIP call: the pointers
+  passed here are fake (never dereferenced) and no stream is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_transformer_layer_rank_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return tp.load()
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("tp_column_linear", "tp_row_linear_partial", "tp_mlp_shard", "tp_attn_shard", "tp_partial_sum"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in _declared():
+        assert hasattr(L, n), f"{n} declared in tpshard.h but not exported"
+    assert set(_declared()) <= set(tp.EXPORTS)
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.tp_abi_version() == 1
+    for code, name in tp.STATUS.items():
+        assert L.tp_status_string(code).decode() == name
+
+
+FAKE = ctypes.c_void_p(0x1000)         # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x1002)     # misaligned
+
+
+def _st(x):
+    return tp.STATUS[x]
+
+
+def test_column_linear_validation(L):
+    f = L.tp_column_linear
+    assert _st(f(None, FAKE, FAKE, 4, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
+    assert "non-NULL" in L.tp_last_error().decode()
+    assert _st(f(FAKE, FAKE, FAKE, 0, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 4, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 7, None, None, 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 12, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE_ODD, FAKE, FAKE, 100, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_F32, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_FP8_E4M3, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_UNSUPPORTED"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, 9, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
+    # decode-size bf16 needs a workspace
+    assert _st(f(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_WORKSPACE"
+
+
+def test_linear_workspace_sizes(L):
+    assert L.tp_linear_workspace_size(4096, 4096, 4096, tp.TP_BF16) == 0
+    assert L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_BF16) > 32 * 16000 * 4
+    assert L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_F32) == 0
+
+
+def test_row_linear_validation(L):
+    f = L.tp_row_linear_partial
+    assert _st(f(FAKE, None, FAKE, 4, 8, 8, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE, FAKE, FAKE, 4, -8, 8, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 10, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
+
+
+def test_mlp_validation(L):
+    f = L.tp_mlp_shard
+    ws = L.tp_mlp_workspace_size(512, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16)
+    assert ws >= 512 * 128 * 2
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 512, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16, FAKE, ws, None]
+    bad = list(args); bad[2] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"            # SwiGLU without W_up
+    bad = list(args); bad[8] = tp.TP_MLP_RELU
+    assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"               # ReLU form with a W_up
+    bad = list(args); bad[12] = ws - 1
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
+    bad = list(args); bad[11] = None
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
+    bad = list(args); bad[10] = tp.TP_F16
+    assert _st(f(*bad)) == "TP_ERR_UNSUPPORTED"
+    bad = list(args); bad[7] = 100
+    bws = L.tp_mlp_workspace_size(512, 256, 100, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16)
+    bad[12] = bws
+    assert _st(f(*bad)) == "TP_ERR_MISALIGNED"              # I_shard not a multiple of 8
+    bad = list(args); bad[5] = 0
+    assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"
+
+
+def _desc(**kw):
+    d = tp.AttnDesc()
+    d.B, d.S, d.H, d.n_q_heads, d.n_kv_heads, d.head_dim = 2, 64, 256, 4, 2, 128
+    d.rope_theta, d.causal = 10000.0, 1
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_attn_validation(L):
+    f = L.tp_attn_shard
+    def st(d, ws=1 << 30):
+        return _st(f(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), tp.TP_BF16, FAKE, ws, None))
+    assert st(_desc(head_dim=64)) == "TP_ERR_UNSUPPORTED"
+    assert st(_desc(n_q_heads=3)) == "TP_ERR_BAD_SHAPE"
+    assert st(_desc(causal=0)) == "TP_ERR_UNSUPPORTED"
+    assert st(_desc(S=60)) == "TP_ERR_MISALIGNED"
+    assert st(_desc(k_cache=0x1000)) == "TP_ERR_NULL_POINTER"
+    assert st(_desc(S=1, k_cache=0x1000, v_cache=0x2000, cache_len=8, cache_capacity=8)) == "TP_ERR_BAD_SHAPE"
+    assert st(_desc(S=4, k_cache=0x1000, v_cache=0x2000, cache_len=2, cache_capacity=8)) == "TP_ERR_UNSUPPORTED"
+    assert st(_desc(), ws=16) == "TP_ERR_WORKSPACE"
+    assert _st(f(FAKE, FAKE, FAKE, FAKE, None, tp.TP_BF16, FAKE, 16, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc()), tp.TP_F32, FAKE, 1 << 30, None)) == "TP_ERR_BAD_DTYPE"
+    d = _desc()
+    need = L.tp_attn_workspace_size(ctypes.byref(d), tp.TP_BF16)
+    T = 2 * 64
+    assert need >= T * (4 + 2 + 2 + 4) * 128 * 2          # q, k, vt, attention output
+    dd = _desc(S=1, k_cache=0x1000, v_cache=0x2000, cache_len=100, cache_capacity=128)
+    assert L.tp_attn_workspace_size(ctypes.byref(dd), tp.TP_BF16) > 0
+
+
+def test_partial_sum_validation(L):
+    f = L.tp_partial_sum
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert _st(f(arr, 0, FAKE, 8, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(arr, 17, FAKE, 8, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(arr, 2, FAKE, 0, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(None, 2, FAKE, 8, None)) == "TP_ERR_NULL_POINTER"
+    arr2 = (ctypes.c_void_p * 2)(0x1000, None)
+    assert _st(f(arr2, 2, FAKE, 8, None)) == "TP_ERR_NULL_POINTER"
+    arr3 = (ctypes.c_void_p * 2)(0x1000, 0x2004)
+    assert _st(f(arr3, 2, FAKE, 8, None)) == "TP_ERR_MISALIGNED"
+
+
+def test_profile_api_without_launches(L):
+    assert L.tp_profile_reset() == 0
+    ms, n = tp.profile_read("")
+    assert ms == 0.0 and n == 0

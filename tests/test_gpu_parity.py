@@ -1,0 +1,388 @@
+"""GPU parity of every libtpshard call against the fp64 oracle (through the C ABI).
+
+Bar: bit-exact on integer-valued fp32; relative Frobenius error <= 5e-3 and max-abs
+error <= 3e-2 for bf16 inputs with fp32 accumulation. Outputs are pre-filled with NaN so
+that an unwritten tile fails.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wl
+from tests._util import assert_close_bf16, dev, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def tp():
+    import tensor_transformer_layer_rank_amd as tp
+    tp.load()
+    return tp
+
+
+def _nan(shape, dtype):
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+# ---------------------------------------------------------------- exact fp32 path
+
+def test_worked_example_on_gpu(tp):
+    import torch
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    X = dev(np.array(g["X"], np.float32), "f32")
+    W = np.array(g["W"], np.float32)
+    full = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+    for r in range(2):   # each rank writes its columns of the full buffer (ldy = 4)
+        Wr = dev(np.ascontiguousarray(W[:, 2 * r:2 * r + 2]), "f32")
+        tp.column_linear(X, Wr, Y=full[:, 2 * r:], ldy=4)
+    torch.cuda.synchronize()
+    assert host(full).tolist() == g["column"]["concat"]
+    parts = []
+    for r, key in enumerate(("X0", "X1")):
+        Xr = dev(np.array(g["row"][key], np.float32), "f32")
+        Wr = dev(np.array(g["row"]["W%d" % r], np.float32), "f32")
+        parts.append(tp.row_linear_partial(Xr, Wr))
+    torch.cuda.synchronize()
+    assert host(parts[0]).tolist() == g["row"]["Y0"]
+    assert host(parts[1]).tolist() == g["row"]["Y1"]
+    assert host(tp.partial_sum(parts)).tolist() == g["row"]["sum"]
+
+
+def test_config0_two_ranks_bit_exact(tp):
+    import torch
+    inp = wl.mlp_relu_tp2(0)
+    X = dev(inp.X, "f32")
+    parts_gpu, parts_ref = [], []
+    for r in range(2):
+        W1 = O.column_shard(inp.W_gate, r, 2)
+        W2 = O.row_shard(inp.W_down, r, 2)
+        H = tp.column_linear(X, dev(W1, "f32"), act=tp.TP_ACT_RELU)
+        P = tp.row_linear_partial(H, dev(W2, "f32"))
+        parts_gpu.append(P)
+        parts_ref.append(O.mlp_relu_shard(inp.X, W1, W2))
+        # the same rank partial through the fused MLP call
+        P2 = tp.mlp_shard(X, dev(W1, "f32"), None, dev(W2, "f32"), kind=tp.TP_MLP_RELU)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(P2), parts_ref[-1])
+    Y = tp.partial_sum(parts_gpu)
+    torch.cuda.synchronize()
+    for r in range(2):
+        assert np.array_equal(host(parts_gpu[r]), parts_ref[r])
+    assert np.array_equal(host(Y), O.partial_sum(parts_ref))
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 1, 1), (70, 33, 130), (129, 200, 65)])
+def test_fp32_linear_ragged_exact(tp, T, K, N):
+    import torch
+    rng = np.random.default_rng(T + K + N)
+    X = wl.int_matrix(rng, (T, K))
+    W = wl.int_matrix(rng, (K, N))
+    Y = tp.column_linear(dev(X, "f32"), dev(W, "f32"))
+    P = tp.row_linear_partial(dev(X, "f32"), dev(W, "f32"))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Y), O.linear(X, W))
+    assert np.array_equal(host(P), O.linear(X, W))
+
+
+@pytest.mark.parametrize("k,n", [(1, 5), (2, 64), (3, 1027), (8, 4096 * 33 + 3)])
+def test_partial_sum_order_and_tails(tp, k, n):
+    import torch
+    rng = np.random.default_rng(k * n)
+    parts = [rng.standard_normal(n).astype(np.float32) for _ in range(k)]
+    out = tp.partial_sum([dev(p, "f32") for p in parts])
+    torch.cuda.synchronize()
+    ref = parts[0].copy()
+    for p in parts[1:]:
+        ref = ref + p        # fp32, left to right: the order the call documents
+    assert np.array_equal(host(out), ref)
+
+
+def test_partial_sum_accumulate_in_place(tp):
+    import torch
+    a = dev(np.arange(12, dtype=np.float32), "f32")
+    b = dev(np.ones(12, np.float32), "f32")
+    tp.partial_sum([a, b], out=a)
+    torch.cuda.synchronize()
+    assert host(a).tolist() == (np.arange(12) + 1.0).tolist()
+
+
+# ---------------------------------------------------------------- bf16 linear layers
+
+@pytest.mark.parametrize("T,K,N", [(300, 256, 200), (513, 520, 264), (256, 64, 256), (65, 4096, 384)])
+@pytest.mark.parametrize("out", ["bf16", "f32", "f16"])
+def test_column_linear_bf16(tp, T, K, N, out):
+    import torch
+    rng = np.random.default_rng(T * 7 + N)
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[out]
+    Y = tp.column_linear(dev(X), dev(W), Y=_nan((T, N), dt))
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.linear(X, W), f"column {T}x{K}x{N} -> {out}", out=out)
+
+
+def test_column_linear_relu_and_ldy(tp):
+    import torch
+    rng = np.random.default_rng(3)
+    T, K, N, tpn = 200, 128, 96, 3
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N * tpn)) * 0.05).astype(np.float32))
+    full = _nan((T, N * tpn), torch.float32)
+    for r in range(tpn):
+        tp.column_linear(dev(X), dev(np.ascontiguousarray(O.column_shard(W, r, tpn))),
+                         Y=full[:, r * N:], ldy=N * tpn, act=tp.TP_ACT_RELU)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(full), O.relu(O.linear(X, W)), "relu + ldy concat")
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 264, 136), (64, 2048, 4096), (1, 128, 64), (33, 520, 200)])
+def test_row_linear_partial_bf16(tp, T, K, N):
+    import torch
+    rng = np.random.default_rng(T + 11 * K)
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    P = tp.row_linear_partial(dev(X), dev(W), Y=_nan((T, N), torch.float32))
+    torch.cuda.synchronize()
+    ref = O.linear(X, W)
+    assert_close_bf16(host(P), ref, f"row partial {T}x{K}x{N}")
+    tp.row_linear_partial(dev(X), dev(W), Y=P, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(P), 2 * ref, "row partial accumulate")
+
+
+def test_row_partials_sum_to_unsharded_layer(tp):
+    import torch
+    rng = np.random.default_rng(5)
+    T, K, N, tpn = 260, 512, 136, 4
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    parts = [tp.row_linear_partial(dev(np.ascontiguousarray(O.column_shard(X, r, tpn))),
+                                   dev(np.ascontiguousarray(O.row_shard(W, r, tpn)))) for r in range(tpn)]
+    Y = tp.partial_sum(parts)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.linear(X, W), "sum of row partials")
+
+
+# ---------------------------------------------------------------- MLP shard
+
+@pytest.mark.parametrize("T,H,I", [(300, 256, 200), (520, 512, 264), (32, 512, 136), (7, 256, 64)])
+def test_mlp_swiglu_small(tp, T, H, I):
+    import torch
+    inp = wl.random_mlp(T + H + I, T, H, I)
+    Y = tp.mlp_shard(dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down),
+                     Y=_nan((T, H), torch.float32))
+    torch.cuda.synchronize()
+    ref = O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down)
+    assert_close_bf16(host(Y), ref, f"mlp {T}x{H}x{I}")
+
+
+def test_mlp_relu_bf16(tp):
+    import torch
+    rng = np.random.default_rng(9)
+    T, H, I = 280, 256, 192
+    X = wl.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    W1 = wl.bf16_round((rng.standard_normal((H, I)) * 0.05).astype(np.float32))
+    W2 = wl.bf16_round((rng.standard_normal((I, H)) * 0.05).astype(np.float32))
+    Y = tp.mlp_shard(dev(X), dev(W1), None, dev(W2), kind=tp.TP_MLP_RELU)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.mlp_relu_shard(X, W1, W2), "relu mlp bf16")
+
+
+def test_mlp_shards_sum_to_unsharded_mlp(tp):
+    import torch
+    inp = wl.random_mlp(17, 200, 256, 512)
+    tpn = 4
+    parts = []
+    for r in range(tpn):
+        parts.append(tp.mlp_shard(dev(inp.X), dev(np.ascontiguousarray(O.column_shard(inp.W_gate, r, tpn))),
+                                  dev(np.ascontiguousarray(O.column_shard(inp.W_up, r, tpn))),
+                                  dev(np.ascontiguousarray(O.row_shard(inp.W_down, r, tpn)))))
+    Y = tp.partial_sum(parts)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.mlp_full(inp.X, inp.W_gate, inp.W_up, inp.W_down, "swiglu"), "sum of mlp shards")
+
+
+def test_mlp7b_tp4_full_size_sampled(tp):
+    """LLaMA-7B MLP shard at TP=4 (X[4096,4096], gate/up [4096,2752], down [2752,4096])."""
+    import torch
+    inp = wl.mlp7b_tp4()
+    Xd, Wg, Wu, Wd = dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down)
+    Y = tp.mlp_shard(Xd, Wg, Wu, Wd, Y=_nan((4096, 4096), torch.float32))
+    Y2 = tp.mlp_shard(Xd, Wg, Wu, Wd)
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.all(np.isfinite(y))
+    assert np.array_equal(y, host(Y2)), "two launches differ bitwise"
+    rows = sample_rows(4096, 48, seed=1)
+    ref = O.mlp_swiglu_shard(inp.X[rows], inp.W_gate, inp.W_up, inp.W_down)
+    assert_close_bf16(y[rows], ref, "mlp7b_tp4 sampled rows")
+
+
+# ---------------------------------------------------------------- attention shard
+
+@pytest.mark.parametrize("B,S,hq,hkv,H", [(2, 136, 4, 4, 256), (1, 200, 4, 2, 128), (3, 64, 8, 1, 256), (1, 8, 2, 2, 128)])
+def test_attn_prefill_small(tp, B, S, hq, hkv, H):
+    import torch
+    inp = wl.random_attn(B * 100 + S, B, S, H, hq, hkv)
+    Y = tp.attn_shard(dev(inp.X), dev(inp.W_qkv), dev(inp.W_o), B, S, hq, hkv,
+                      Y=_nan((B * S, H), torch.float32))
+    torch.cuda.synchronize()
+    ref = O.attn_shard(inp.X, inp.W_qkv, inp.W_o, B, S, hq, hkv, 128, inp.theta)
+    assert_close_bf16(host(Y), ref, f"attn B{B} S{S} hq{hq} hkv{hkv}")
+
+
+def test_attn_shards_sum_to_full_block(tp):
+    import torch
+    rng = np.random.default_rng(23)
+    B, S, H, nh, nkv, d, tpn = 2, 72, 256, 4, 2, 128, 2
+    X = wl.bf16_round(rng.standard_normal((B * S, H)).astype(np.float32))
+    Wq, Wk, Wv = (wl.bf16_round((rng.standard_normal((H, n * d)) * 0.05).astype(np.float32))
+                  for n in (nh, nkv, nkv))
+    Wo = wl.bf16_round((rng.standard_normal((nh * d, H)) * 0.05).astype(np.float32))
+    parts = []
+    for r in range(tpn):
+        Wqkv, Wo_r, hq, hkv = O.attn_shard_weights(Wq, Wk, Wv, Wo, nh, nkv, d, r, tpn)
+        parts.append(tp.attn_shard(dev(X), dev(np.ascontiguousarray(Wqkv)), dev(np.ascontiguousarray(Wo_r)),
+                                   B, S, hq, hkv))
+    Y = tp.partial_sum(parts)
+    torch.cuda.synchronize()
+    ref = O.full_attention_block(X, Wq, Wk, Wv, Wo, B, S, nh, nkv, d, 10000.0)
+    assert_close_bf16(host(Y), ref, "sum of attention shards")
+
+
+def _attn_full_size(tp, inp, nsamp, seed):
+    import torch
+    T = inp.B * inp.S
+    Xd = dev(inp.X)
+    Y = tp.attn_shard(Xd, dev(inp.W_qkv), dev(inp.W_o), inp.B, inp.S, inp.hq, inp.hkv,
+                      Y=_nan((T, inp.H), torch.float32))
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(seed)
+    # one or two sequences, late positions (long causal prefixes) plus the first rows
+    rows = [0, 1, inp.S - 1]
+    b = int(rng.integers(0, inp.B))
+    rows += sorted(set((b * inp.S + rng.integers(inp.S // 2, inp.S, size=nsamp)).tolist()))
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    ref = O.attn_shard_rows(inp.X, inp.W_qkv, inp.W_o, inp.B, inp.S, inp.hq, inp.hkv, inp.d,
+                            inp.theta, rows)
+    assert_close_bf16(y[rows], ref, inp.name + " sampled rows")
+    return Xd, y
+
+
+def test_attn7b_tp4_full_size_sampled(tp):
+    """LLaMA-7B attention shard at TP=4: B=4, S=2048, 8 local heads, causal, RoPE 1e4."""
+    _attn_full_size(tp, wl.attn7b_tp4(), 12, 2)
+
+
+def test_layer70b_tp8_full_size_sampled(tp):
+    """70B GQA layer shard at TP=8: attention (8 q heads, 1 kv head) and MLP on the same X."""
+    import torch
+    inp = wl.layer70b_tp8()
+    Xd, _ = _attn_full_size(tp, inp, 8, 3)
+    m = inp.mlp
+    Y = tp.mlp_shard(Xd, dev(m.W_gate), dev(m.W_up), dev(m.W_down), Y=_nan((8192, 8192), torch.float32))
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.all(np.isfinite(y))
+    rows = sample_rows(8192, 24, seed=3)
+    ref = O.mlp_swiglu_shard(m.X[rows], m.W_gate, m.W_up, m.W_down)
+    assert_close_bf16(y[rows], ref, "layer70b_tp8 mlp sampled rows")
+
+
+# ---------------------------------------------------------------- decode step
+
+def _decode(tp, inp):
+    import torch
+    kc, vc = dev(inp.k_cache), dev(inp.v_cache)
+    Y = tp.attn_shard(dev(inp.X), dev(inp.W_qkv), dev(inp.W_o), inp.B, 1, inp.hq, inp.hkv,
+                      inp.theta, k_cache=kc, v_cache=vc, cache_len=inp.cache_len,
+                      Y=_nan((inp.B, inp.H), torch.float32))
+    torch.cuda.synchronize()
+    return host(Y), host(kc), host(vc)
+
+
+@pytest.mark.parametrize("B,H,hq,hkv,L,cap", [(4, 256, 2, 2, 37, 40), (3, 512, 4, 1, 300, 301), (32, 256, 2, 2, 1, 8)])
+def test_decode_attn_small(tp, B, H, hq, hkv, L, cap):
+    inp = wl.random_decode(B + L, B, H, hq, hkv, 64, 64, L, cap)
+    y, kc, vc = _decode(tp, inp)
+    ref, knew, vnew = O.decode_attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.k_cache, inp.v_cache,
+                                          inp.cache_len, inp.hq, inp.hkv, inp.d, inp.theta)
+    assert_close_bf16(y, ref, "decode attention")
+    assert_close_bf16(kc[:, :, L], knew, "appended keys", out="bf16")
+    assert_close_bf16(vc[:, :, L], vnew, "appended values", out="bf16")
+    assert np.array_equal(kc[:, :, :L], inp.k_cache[:, :, :L]), "cache prefix modified"
+
+
+def test_decode7b_tp2_full_size(tp):
+    """7B decode step at TP=2: 32 sequences, 16 heads, 1024 cached tokens; MLP and LM head."""
+    import torch
+    inp = wl.decode7b_tp2()
+    y, kc, vc = _decode(tp, inp)
+    ref, knew, vnew = O.decode_attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.k_cache, inp.v_cache,
+                                          inp.cache_len, inp.hq, inp.hkv, inp.d, inp.theta)
+    assert_close_bf16(y, ref, "decode attention partial")
+    assert_close_bf16(kc[:, :, inp.cache_len], knew, "appended keys", out="bf16")
+    Xd = dev(inp.X)
+    Ym = tp.mlp_shard(Xd, dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down), Y=_nan((32, 4096), torch.float32))
+    logits = tp.column_linear(Xd, dev(inp.W_lm), Y=_nan((32, 16000), torch.float32))
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Ym), O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down), "decode mlp")
+    assert_close_bf16(host(logits), O.lm_head_shard(inp.X, inp.W_lm), "vocab-parallel logits")
+
+
+def test_decode_matches_prefill_last_row(tp):
+    """Decode at position p with the prefill's own keys/values in the cache = prefill row p."""
+    import torch
+    B, S, H, hq, hkv = 2, 48, 256, 2, 1
+    inp = wl.random_attn(31, B, S, H, hq, hkv)
+    p = S - 1
+    pre = O.attn_shard(inp.X, inp.W_qkv, inp.W_o, B, S, hq, hkv, 128, inp.theta)
+    QKV = O.linear(inp.X, inp.W_qkv)
+    kc = np.zeros((B, hkv, S, 128), np.float32)
+    vc = np.zeros_like(kc)
+    for b in range(B):
+        for g in range(hkv):
+            kk = QKV[b * S:b * S + p, (hq + g) * 128:(hq + g + 1) * 128]
+            kc[b, g, :p] = wl.bf16_round(O.apply_rope(kk, np.arange(p), inp.theta).astype(np.float32))
+            vc[b, g, :p] = wl.bf16_round(QKV[b * S:b * S + p, (hq + hkv + g) * 128:(hq + hkv + g + 1) * 128]
+                                         .astype(np.float32))
+    kd, vd = dev(kc), dev(vc)
+    Xl = np.ascontiguousarray(inp.X[p::S])
+    Y = tp.attn_shard(dev(Xl), dev(inp.W_qkv), dev(inp.W_o), B, 1, hq, hkv, inp.theta,
+                      k_cache=kd, v_cache=vd, cache_len=p)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), pre[p::S], "decode vs prefill last row")
+
+
+# ---------------------------------------------------------------- repeatability
+
+def test_repeated_launches_bitwise_equal(tp):
+    import torch
+    inp = wl.random_attn(41, 2, 256, 512, 4, 2, I=264)
+    Xd, Wq, Wo = dev(inp.X), dev(inp.W_qkv), dev(inp.W_o)
+    a = host(tp.attn_shard(Xd, Wq, Wo, 2, 256, 4, 2))
+    b = host(tp.attn_shard(Xd, Wq, Wo, 2, 256, 4, 2))
+    m = inp.mlp
+    c = host(tp.mlp_shard(Xd, dev(m.W_gate), dev(m.W_up), dev(m.W_down)))
+    d = host(tp.mlp_shard(Xd, dev(m.W_gate), dev(m.W_up), dev(m.W_down)))
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b) and np.array_equal(c, d)
+
+
+def test_error_is_raised_not_launched(tp):
+    import torch
+    X = dev(np.zeros((4, 12), np.float32))   # K = 12 is not a multiple of 8 on the bf16 path
+    W = dev(np.zeros((12, 16), np.float32))
+    with pytest.raises(tp.TpError) as ei:
+        tp.column_linear(X, W)
+    assert ei.value.name == "TP_ERR_MISALIGNED"
+    torch.cuda.synchronize()
