@@ -1,0 +1,278 @@
+"""Throughput of one tensor-parallel rank's shard on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra]
+
+Headline: the LLaMA-7B MLP shard at TP=4 (X[4096,4096] bf16, gate/up [4096,2752],
+down [2752,4096], fp32 partial out) — one step = one tp_mlp_shard call (fused
+SiLU(gate)*up GEMM + down GEMM). `value` is shard TFLOP/s (2*M*K*N per GEMM, 277.03
+GFLOP per step). Alongside: the 7B TP=2 decode step (attention shard over a 1024-token
+KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compulsory HBM
+bytes. Inputs are seeded synthetic tensors already resident in HBM. With --extra the
+attention shard (B=4, S=2048) and the 70B GQA layer shard are timed too.
+
+Prints ONE JSON line. Per-kernel durations come from HIP events that libtpshard records
+around each launch on the launch stream while the timed steps run.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense MFMA)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--extra", action="store_true", help="also time the attention and 70B layer shards")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
+    return ap.parse_args()
+
+
+def timed(step, warmup: int, steps: int):
+    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    tp.profile_reset()
+    tp.profile_enable(True)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    tp.profile_enable(False)
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_avg(prefix: str):
+    import tensor_transformer_layer_rank_amd as tp
+    ms, n = tp.profile_read(prefix)
+    return (ms / n if n else None), n
+
+
+def mlp_bench(args):
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.mlp7b_tp4()
+    T, H, I = inp.T, inp.H, inp.I
+    X, Wg, Wu, Wd = dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down)
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.mlp_shard(X, Wg, Wu, Wd, Y=Y, workspace=ws)
+
+    ms = timed(step, args.warmup, args.steps)
+    gu_ms, gu_n = kernel_avg("gemm_bf16_swiglu")
+    dn_ms, dn_n = kernel_avg("gemm_bf16_f32out")
+    flops_gu = 2.0 * T * H * I * 2
+    flops_dn = 2.0 * T * I * H
+    flops = flops_gu + flops_dn
+    res = {
+        "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "flops_per_step": flops,
+        "kernels": {
+            "gemm_bf16_swiglu": {"avg_us": gu_ms * 1e3, "launches": gu_n,
+                                 "tflops": flops_gu / (gu_ms * 1e-3) / 1e12},
+            "gemm_bf16_f32out(down)": {"avg_us": dn_ms * 1e3, "launches": dn_n,
+                                       "tflops": flops_dn / (dn_ms * 1e-3) / 1e12},
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "gemm_bf16_swiglu",
+            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+    }
+    return res, inp
+
+
+def decode_bench(args):
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.decode7b_tp2()
+    B, H, hq, hkv, L = inp.B, inp.H, inp.hq, inp.hkv, inp.cache_len + 1
+    X = dev(inp.X)
+    Wqkv, Wo, Wg, Wu, Wd, Wlm = (dev(w) for w in (inp.W_qkv, inp.W_o, inp.W_gate, inp.W_up, inp.W_down, inp.W_lm))
+    kc, vc = dev(inp.k_cache), dev(inp.v_cache)
+    I, V = inp.W_gate.shape[1], inp.W_lm.shape[1]
+    Ya = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    Ym = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
+    ws_a = torch.empty(tp.attn_workspace_size(B, 1, H, hq, hkv, inp.theta, kc, vc, inp.cache_len),
+                       dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(tp.mlp_workspace_size(B, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+    ws_l = torch.empty(tp.linear_workspace_size(B, H, V, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.attn_shard(X, Wqkv, Wo, B, 1, hq, hkv, inp.theta, k_cache=kc, v_cache=vc,
+                      cache_len=inp.cache_len, Y=Ya, workspace=ws_a)
+        tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
+        tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
+
+    ms = timed(step, args.warmup, args.steps)
+    d = 128
+    w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
+    kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
+    new_kv = 2 * 2 * B * hkv * d                       # the new key/value written (and read back)
+    act = 2 * B * H + 4 * (2 * B * H + B * V)          # X in; two fp32 partials and the logits out
+    total = w_bytes + kv_bytes + 2 * new_kv + act
+    att_ms, att_n = kernel_avg("decode_attn")
+    sk_ms, sk_n = kernel_avg("skinny_gemm")
+    return {
+        "ms_per_step": ms,
+        "bytes_per_step": total,
+        "gbs": total / (ms * 1e-3) / 1e9,
+        "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
+                    "skinny_gemm*(avg_us)": sk_ms * 1e3 if sk_ms else None,
+                    "skinny_gemm*(launches/step)": sk_n / max(args.steps, 1)},
+        "workload": "decode7b_tp2: B=32 one token each, 16 local heads (MHA), KV cache 1024 tokens, "
+                    "H=4096, I_shard=5504, LM head [4096,16000]",
+    }
+
+
+def attn_bench(args, name):
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.WORKLOADS[name]()
+    B, S, H, hq, hkv = inp.B, inp.S, inp.H, inp.hq, inp.hkv
+    X, Wqkv, Wo = dev(inp.X), dev(inp.W_qkv), dev(inp.W_o)
+    T = B * S
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.attn_workspace_size(B, S, H, hq, hkv, inp.theta), dtype=torch.uint8, device="cuda")
+    mlp = None
+    if inp.mlp is not None:
+        m = inp.mlp
+        I = m.W_gate.shape[1]
+        mlp = (dev(m.W_gate), dev(m.W_up), dev(m.W_down),
+               torch.empty((T, H), dtype=torch.float32, device="cuda"),
+               torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda"))
+
+    def step():
+        tp.attn_shard(X, Wqkv, Wo, B, S, hq, hkv, inp.theta, Y=Y, workspace=ws)
+        if mlp:
+            tp.mlp_shard(X, mlp[0], mlp[1], mlp[2], Y=mlp[3], workspace=mlp[4])
+
+    ms = timed(step, max(2, args.warmup // 2), max(5, args.steps // 2))
+    d = 128
+    f_qkv = 2.0 * T * H * (hq + 2 * hkv) * d
+    f_att = 2.0 * 2 * d * B * hq * S * (S + 1) / 2      # causal triangle only: QK^T and PV
+    f_o = 2.0 * T * hq * d * H
+    f_mlp = 0.0
+    if inp.mlp is not None:
+        I = inp.mlp.W_gate.shape[1]
+        f_mlp = 2.0 * T * H * I * 3
+    flops = f_qkv + f_att + f_o + f_mlp
+    fa_ms, _ = kernel_avg("flash_attn_fwd")
+    q_ms, _ = kernel_avg("gemm_bf16_qkv_rope")
+    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "flash_attn_tflops": f_att / (fa_ms * 1e-3) / 1e12 if fa_ms else None,
+            "qkv_rope_tflops": f_qkv / (q_ms * 1e-3) / 1e12 if q_ms else None}
+
+
+def cpu_baseline(inp, target_s: float):
+    """The fp64 oracle on a row sample of the same MLP shard, on this host's cores."""
+    import numpy as np
+    import oracle as O
+    rows0 = 32
+    t0 = time.perf_counter()
+    O.mlp_swiglu_shard(inp.X[:rows0], inp.W_gate, inp.W_up, inp.W_down)
+    t_small = time.perf_counter() - t0
+    rows = int(min(inp.T, max(rows0, rows0 * target_s / max(t_small, 1e-3))))
+    rows = max(rows0, rows - rows % 32)
+    t0 = time.perf_counter()
+    O.mlp_swiglu_shard(inp.X[:rows], inp.W_gate, inp.W_up, inp.W_down)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * inp.H * inp.I * 3
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on rows 0..{rows - 1} of the 4096-row MLP shard "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.2f} s)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU: one rank's shard; "
+                                   "run with --gpus 1 (multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    tp.load()
+    mlp, inp = mlp_bench(args)
+    dec = decode_bench(args)
+    extra = {}
+    if args.extra:
+        extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
+        extra["layer70b_tp8"] = attn_bench(args, "layer70b_tp8")
+    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds)
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": "shard TFLOP/s (+% bf16 MFMA peak) for 7B TP=4 MLP; decode GB/s (%HBM)",
+        "value": round(mlp["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mlp["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, bf16-rounded)",
+        "config": {"workload": "mlp7b_tp4: LLaMA-7B MLP shard at TP=4, X[4096,4096] (B=8,S=512), "
+                               "gate/up [4096,2752], down [2752,4096], fp32 partial out",
+                   "frac_bf16_peak": round(mlp["tflops"] / PEAK_BF16_TFLOPS, 4),
+                   "decode_gbs": round(dec["gbs"], 1),
+                   "decode_frac_hbm": round(dec["frac_hbm"], 4),
+                   "decode_ms_per_step": round(dec["ms_per_step"], 5)},
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in mlp["roofline"].items()},
+        "cpu_baseline": cpu and {k: v for k, v in cpu.items() if k != "seconds"},
+        "kernels": mlp["kernels"],
+        "decode": dec,
+        "extra": extra or None,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", None)},
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

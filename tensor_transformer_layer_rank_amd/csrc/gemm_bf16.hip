@@ -10,15 +10,21 @@
 //     and V^T (自注意力块切分: each rank holds whole heads).
 //
 // Tile: 256 x 256 outputs per workgroup (gate/up: 256 rows x 128 h columns, i.e. 128
-// gate + 128 up accumulator columns), K step 64, 512 threads = 8 wave64s laid out 4 (M)
-// x 2 (N); each wave owns 64 x 128 outputs = 2 x 4 MFMA 32x32 blocks (128 fp32
-// accumulators per lane).
-// Staging: 128-bit global loads into registers one K step ahead; the weight block
-// [K, N] (N contiguous in memory) is transposed in registers (v_perm) so that LDS holds
-// both operands K-contiguous, which is what the MFMA operand layout wants (each lane
-// supplies 8 consecutive k of one row/column). LDS is double buffered (2 x 64 KB) with an
-// XOR swizzle of the 16-byte chunks so that the ds_read_b128 of 8 consecutive rows hit
-// distinct banks.
+// gate + 128 up accumulator columns), 256 threads = 4 wave64s laid out 2 (M) x 2 (N), one
+// per SIMD; each wave owns 128 x 128 outputs = 4 x 4 MFMA 32x32 blocks (256 fp32
+// accumulators per lane, held in the accumulation registers).
+// Staging: K steps of 32 go global -> LDS directly (global_load_lds_dwordx4, no register
+// staging) into a ring of 4 LDS stages, so three K steps of loads are in flight while the
+// MFMAs consume the fourth. One barrier per K step, placed between its two 16-deep
+// slices: it publishes the next stage and releases the oldest one for refilling, so the
+// next stage's first operand fragments are read before the step ends.
+// LDS layouts: the activation tile is kept [m][k] with 80-byte rows and read with
+// ds_read_b128; the weight tile is kept in its memory order [k][n] with 576-byte rows and
+// read with the gfx950 transposing load ds_read_b64_tr_b16, which hands each lane 4
+// consecutive k of one column (two of them make the 8-k MFMA operand). The row paddings
+// make both reads free of LDS bank conflicts; the DMA writes skip the pad granules.
+// Tiles are ordered so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
+// works on a compact block of 4 row tiles x n column tiles, which keeps its L2 hit rate up.
 #include "tp_internal.h"
 
 namespace tpk {
@@ -27,18 +33,22 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
-constexpr int A_BYTES = BM * BK * 2;
-constexpr int B_BYTES = BN * BK * 2;
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, NSTAGE = 4;
+constexpr int A_STRIDE = BK * 2 + 16;     // 80 B per activation row (64 data + 16 pad)
+constexpr int B_STRIDE = BN * 2 + 64;     // 576 B per weight row (512 data + 64 pad)
+constexpr int A_GRAN = A_STRIDE / 16;     // 5 granules of 16 B per activation row
+constexpr int B_GRAN = B_STRIDE / 16;     // 36 granules per weight row
+constexpr int A_BYTES = BM * A_STRIDE;    // 20480
+constexpr int B_BYTES = BK * B_STRIDE;    // 18432
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-
-// byte offset of 16-byte chunk `chunk` (0..7) of row `row` in a [rows][64] bf16 tile
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * 128 + ((chunk ^ ((row + (row >> 3)) & 7)) << 4);
-}
+constexpr int A_PER_WAVE = BM * A_GRAN / 4;   // 320 granules = 5 DMA instructions
+constexpr int B_PER_WAVE = BK * B_GRAN / 4;   // 288 granules (5 instructions, the last partial)
+constexpr int DMA_A = 5, DMA_B = 5;
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -54,99 +64,199 @@ struct GemmGeom {
     int64_t M, N, K, lda, ldb;
 };
 
-struct TileRegs {
-    u32x4 a[4];
-    u32x4 b[4];
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane source offsets of one wave's share of a stage (fixed for the whole K loop; only
+// the K offset moves), in elements relative to the tile's base pointers. Wave w fills
+// activation rows 64w..64w+63 (5 DMA instructions of 64 granules) and weight rows
+// 8w..8w+7 (288 granules: 4 instructions plus a fifth that starts 32 granules early and
+// rewrites identical data). Every lane of every instruction loads an in-bounds address, so
+// each wave issues exactly DMA_A + DMA_B loads per stage and vmcnt counts stay exact:
+// pad granules, rows past M and columns past N fetch a harmless valid address (row 0 /
+// column n0), and granules past K fetch K chunk 0 and are zeroed after they land.
+struct DmaPlan {
+    int32_t a_off[DMA_A];   // row * lda + 8 * chunk  (pad granules: chunk 0)
+    int64_t b_off[DMA_B];   // k row * ldb + column, relative to the first weight (dual: the
+                            // second weight's granules carry the pointer difference)
 };
 
+// geometry of granule i of this wave (recomputed only on the K-tail path)
+__device__ __forceinline__ void a_granule(int wave, int i, int lane, int& row, int& c) {
+    const int G = wave * A_PER_WAVE + i * 64 + lane;
+    row = G / A_GRAN;
+    c = G % A_GRAN;
+}
+__device__ __forceinline__ int b_granule_base(int i) { return i < 4 ? i * 64 : B_PER_WAVE - 64; }
+__device__ __forceinline__ void b_granule(int wave, int i, int lane, int& row, int& c) {
+    const int G = wave * B_PER_WAVE + b_granule_base(i) + lane;
+    row = G / B_GRAN;
+    c = G % B_GRAN;
+}
+
 template <bool DUAL>
-__device__ __forceinline__ void load_tile(TileRegs& t, const GemmGeom& g, int64_t m0, int64_t n0,
-                                          int64_t k0, int tid) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NTHR;
-        const int row = q >> 3, c = q & 7;
-        const int64_t gm = m0 + row, gk = k0 + c * 8;
-        if (gm < g.M && gk < g.K)
-            t.a[p] = *reinterpret_cast<const u32x4*>(g.A + gm * g.lda + gk);
-        else
-            t.a[p] = u32x4{0u, 0u, 0u, 0u};
+__device__ __forceinline__ int64_t b_offset(const GemmGeom& g, int64_t n0, int row, int c) {
+    int64_t col = n0, extra = 0;
+    if (c < 32) {
+        if (DUAL) {
+            col = n0 + (int64_t)(c & 15) * 8;
+            if (c >= 16) extra = g.B2 - g.B1;
+        } else {
+            col = n0 + (int64_t)c * 8;
+        }
+        if (col >= g.N) {
+            col = n0;
+            extra = 0;
+        }
     }
-    const int cg = tid & 31, rg = tid >> 5;
-    const uint16_t* Bp;
-    int64_t gn;
-    if (DUAL) {
-        Bp = (cg < 16) ? g.B1 : g.B2;
-        gn = n0 + (int64_t)(cg & 15) * 8;
-    } else {
-        Bp = g.B1;
-        gn = n0 + (int64_t)cg * 8;
+    return extra + (int64_t)row * g.ldb + col;
+}
+
+template <bool DUAL>
+__device__ __forceinline__ void make_plan(DmaPlan& p, const GemmGeom& g, int64_t m0, int64_t n0,
+                                          int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < DMA_A; ++i) {
+        int row, c;
+        a_granule(wave, i, lane, row, c);
+        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + 8 * (c < 4 ? c : 0));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gk = k0 + rg * 4 + i;
-        if (gk < g.K && gn < g.N)
-            t.b[i] = *reinterpret_cast<const u32x4*>(Bp + gk * g.ldb + gn);
-        else
-            t.b[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < DMA_B; ++i) {
+        int row, c;
+        b_granule(wave, i, lane, row, c);
+        p.b_off[i] = b_offset<DUAL>(g, n0, row, c);
     }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& t, unsigned char* stage, int tid) {
-    unsigned char* As = stage;
-    unsigned char* Bs = stage + A_BYTES;
+// One 16-byte global -> LDS transfer per lane; the lanes of a wave fill 64 consecutive
+// granules starting at dst (wave-uniform). Written as a volatile asm statement with no
+// register outputs: the compiler then neither reorders it against other memory accesses
+// nor adds its own vmcnt waits before LDS reads (it cannot tell which stage a DMA writes),
+// and the kernel keeps the exact per-stage vmcnt accounting itself.
+__device__ __forceinline__ void dma16(const uint16_t* src, unsigned char* dst) {
+    const unsigned lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)(dst)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// Issue this wave's DMA_A + DMA_B loads for the K step starting at k0 into `stage`.
+template <bool DUAL>
+__device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan& p, const GemmGeom& g,
+                                            const uint16_t* a_base, int64_t m0, int64_t n0, int64_t k0,
+                                            int wave, int lane) {
+    unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
+    unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
+    if (k0 + BK <= g.K) {
+        const uint16_t* a_k = a_base + k0;
+        const uint16_t* b_k = g.B1 + k0 * g.ldb;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NTHR;
-        *reinterpret_cast<u32x4*>(As + lds_off(q >> 3, q & 7)) = t.a[p];
+        for (int i = 0; i < DMA_A; ++i)
+            dma16(a_k + p.a_off[i], a_dst + i * 1024);
+#pragma unroll
+        for (int i = 0; i < DMA_B; ++i)
+            dma16(b_k + p.b_off[i], b_dst + b_granule_base(i) * 16);
+        return;
     }
-    // this thread holds rows 4*rg..4*rg+3 (k) x columns 8*cg..8*cg+7 (n) of the weight
-    // block; column c becomes 4 consecutive k of LDS row n = 8*cg + c.
-    const int cg = tid & 31, rg = tid >> 5;
-    const int kc = rg >> 1, half = rg & 1;
+    // partial final step: granules past K fetch K chunk 0 / row 0 (zeroed once landed)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const unsigned sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 v;
-        v.x = __builtin_amdgcn_perm(t.b[1][c >> 1], t.b[0][c >> 1], sel);
-        v.y = __builtin_amdgcn_perm(t.b[3][c >> 1], t.b[2][c >> 1], sel);
-        const int n = cg * 8 + c;
-        *reinterpret_cast<u32x2*>(Bs + lds_off(n, kc) + half * 8) = v;
+    for (int i = 0; i < DMA_A; ++i) {
+        int row, c;
+        a_granule(wave, i, lane, row, c);
+        if (c >= 4 || k0 + 8 * c >= g.K) c = 0;
+        if (m0 + row >= g.M) row = 0;
+        dma16(a_base + k0 + (int64_t)row * g.lda + 8 * c, a_dst + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < DMA_B; ++i) {
+        int row, c;
+        b_granule(wave, i, lane, row, c);
+        if (k0 + row >= g.K) row = 0;
+        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL>(g, n0, row, c), b_dst + b_granule_base(i) * 16);
     }
 }
 
-// LDS column (row of the transposed weight tile) of the j-th 32-wide block of wave wn
+// After a partial final K step has landed: zero this wave's granules that lie past K.
+__device__ __forceinline__ void zero_tail(unsigned char* stage, const GemmGeom& g, int64_t k0,
+                                          int wave, int lane) {
+    unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
+#pragma unroll
+    for (int i = 0; i < DMA_A; ++i) {
+        int row, c;
+        a_granule(wave, i, lane, row, c);
+        if (c < 4 && k0 + 8 * c >= g.K)
+            *reinterpret_cast<u32x4*>(a_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
+#pragma unroll
+    for (int i = 0; i < DMA_B; ++i) {
+        int row, c;
+        b_granule(wave, i, lane, row, c);
+        if (k0 + row >= g.K)
+            *reinterpret_cast<u32x4*>(b_dst + b_granule_base(i) * 16 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// wait until at most n DMA instructions of this wave are outstanding (vmcnt(n))
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// LDS column of the j-th 32-wide block of wave wn
 template <bool DUAL>
-__device__ __forceinline__ int b_row_of(int j, int wn) {
+__device__ __forceinline__ int b_col_of(int j, int wn) {
     if (DUAL) return (j < 2) ? (wn * 64 + j * 32) : (128 + wn * 64 + (j - 2) * 32);
     return wn * 128 + j * 32;
 }
 
+// 8 consecutive k (rows ks*16 + 8*(lane/32) ..) of column col0 + lane%32 of the weight tile:
+// two transposing reads, each giving 4 k of one column to every lane of a 16-lane group.
+__device__ __forceinline__ bf16x8 read_b_frag(const unsigned char* Bs, int ks, int col0, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = ks * 16 + 8 * (g >> 1) + (r >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
+    const lds_u8* base = (const lds_u8*)(Bs) + row * B_STRIDE + col * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * B_STRIDE));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+}
+
+struct Frags {
+    bf16x8 a[4];
+    bf16x8 b[4];
+};
+
+// Pieces of the operand fragments of 16-deep K slice ks for wave (wm, wn), so that they can
+// be interleaved one by one with MFMAs: piece 0..3 = activation block i (ds_read_b128),
+// piece 4..7 = weight block j (two ds_read_b64_tr_b16).
 template <bool DUAL>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[2][4], const unsigned char* stage,
-                                              int wm, int wn, int lane) {
-    const unsigned char* As = stage;
-    const unsigned char* Bs = stage + A_BYTES;
-    const int r32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int chunk = ks * 2 + hi;
-        bf16x8 a[2], b[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            a[i] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(As + lds_off(wm * 64 + i * 32 + r32, chunk)));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(Bs + lds_off(b_row_of<DUAL>(j, wn) + r32, chunk)));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+__device__ __forceinline__ void read_piece(Frags& f, int piece, const unsigned char* stage, int ks,
+                                           int wm, int wn, int lane) {
+    if (piece < 4) {
+        const int r32 = lane & 31, hi = lane >> 5;
+        f.a[piece] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(stage + (wm * 128 + piece * 32 + r32) * A_STRIDE +
+                                                    (ks * 2 + hi) * 16));
+    } else {
+        f.b[piece - 4] = read_b_frag(stage + A_BYTES, ks, b_col_of<DUAL>(piece - 4, wn), lane);
     }
 }
+
+template <bool DUAL>
+__device__ __forceinline__ void read_frags(Frags& f, const unsigned char* stage, int ks, int wm,
+                                           int wn, int lane) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) read_piece<DUAL>(f, q, stage, ks, wm, wn, lane);
+}
+
+__device__ __forceinline__ void mfma1(f32x16 (&acc)[4][4], const Frags& f, int n) {
+    const int i = n >> 2, j = n & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+#define TP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // row of accumulator register r of block i for a lane in half `hi` (MFMA 32x32 layout)
 __device__ __forceinline__ int acc_row(int i, int r, int hi) {
@@ -160,7 +270,7 @@ template <int KIND, bool RELU>
 struct EpiStore {
     void* C;
     int64_t ldc, M, N;
-    __device__ void operator()(f32x16 (&acc)[2][4], int64_t m0, int64_t n0, int wm, int wn,
+    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
                                int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -168,10 +278,10 @@ struct EpiStore {
             const int64_t col = n0 + wn * 128 + j * 32 + r32;
             if (col >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 64 + acc_row(i, r, hi);
+                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                     if (row >= M) continue;
                     float v = acc[i][j][r];
                     if (RELU) v = v > 0.0f ? v : 0.0f;
@@ -188,7 +298,7 @@ struct EpiStore {
 struct EpiSwiGLU {
     uint16_t* h;   // [M, N] bf16
     int64_t M, N;
-    __device__ void operator()(f32x16 (&acc)[2][4], int64_t m0, int64_t n0, int wm, int wn,
+    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
                                int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
@@ -196,10 +306,10 @@ struct EpiSwiGLU {
             const int64_t col = n0 + wn * 64 + j * 32 + r32;
             if (col >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 64 + acc_row(i, r, hi);
+                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                     if (row >= M) continue;
                     const float gte = acc[i][j][r], up = acc[i][j + 2][r];
                     const float silu = gte / (1.0f + __expf(-gte));
@@ -212,7 +322,7 @@ struct EpiSwiGLU {
 struct EpiQKV {
     QKVOut o;
     int64_t M;   // B*S
-    __device__ void operator()(f32x16 (&acc)[2][4], int64_t m0, int64_t n0, int wm, int wn,
+    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
                                int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
         const int head = (int)((n0 + wn * 128) >> 7);   // one wave = one head of 128 columns
@@ -225,10 +335,10 @@ struct EpiQKV {
             const int nh = is_q ? o.hq : o.hkv;
             uint16_t* dst = static_cast<uint16_t*>(is_q ? o.q : o.k);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 64 + acc_row(i, r, hi);
+                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                     if (row >= M) continue;
                     const int64_t b = row / S, s = row - b * S;
                     uint16_t* out = dst + ((b * nh + hh) * S + s) * 128;
@@ -245,10 +355,10 @@ struct EpiQKV {
             const int hv = head - o.hq - o.hkv;
             uint16_t* vt = static_cast<uint16_t*>(o.vt);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 64 + acc_row(i, r, hi);
+                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                     if (row >= M) continue;
                     const int64_t b = row / S, s = row - b * S;
 #pragma unroll
@@ -261,56 +371,144 @@ struct EpiQKV {
     }
 };
 
+// Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8). Give XCD x
+// a contiguous range of logical tiles, ordered in groups of 4 row tiles (row fastest), so
+// the tiles resident on one XCD share 4 activation row blocks and few weight column blocks.
+__device__ __forceinline__ void map_tile(int bid, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int x = bid & 7, idx = bid >> 3, q = G >> 3, rem = G & 7;
+    const int L = x * q + (x < rem ? x : rem) + idx;
+    constexpr int GM = 4;
+    const int group = L / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = (tiles_m - first_m < GM) ? tiles_m - first_m : GM;
+    const int r = L - group * GM * tiles_n;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+__device__ __forceinline__ bool k0_full(const GemmGeom& g, int64_t k0) { return k0 + BK <= g.K; }
+
+// Wait until this wave's DMA for a stage has landed while `pending` later stages (0..3) may
+// still be in flight, zero its granules past K if it is the partial final step, then
+// barrier: after it the stage is readable by every wave.
+__device__ __forceinline__ void publish(unsigned char* stage, int pending, const GemmGeom& g,
+                                        int64_t k0, int wave, int lane) {
+    constexpr int GRP = DMA_A + DMA_B;
+    if (pending >= 3) wait_vm<3 * GRP>();
+    else if (pending == 2) wait_vm<2 * GRP>();
+    else if (pending == 1) wait_vm<GRP>();
+    else wait_vm<0>();
+    if (k0 + BK > g.K) {
+        wait_vm<0>();
+        zero_tail(stage, g, k0, wave, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS traffic done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K step kt on stage `cur` (slice-0 fragments already in f0). The instruction order is
+// pinned: slice-0 MFMAs alternate with the reads of slice 1 (into f1); then stage kt+1 is
+// published (wait + barrier), after which `cur` is free; slice-1 MFMAs then alternate with
+// the reads of stage kt+1's slice 0 (into f0) and with this wave's DMA refilling `cur` with
+// step kt+4. The MFMA pipe thus always has queued work while loads are issued.
+template <bool DUAL>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                       unsigned char* cur, unsigned char* nxt, int kt, int nk,
+                                       const DmaPlan& p, const GemmGeom& g, const uint16_t* a_base,
+                                       int64_t m0, int64_t n0, int wm, int wn, int wave, int lane) {
+    TP_FENCE();
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        mfma1(acc, f0, n);
+        if (n < 8) read_piece<DUAL>(f1, n, cur, 1, wm, wn, lane);
+        TP_FENCE();
+    }
+    const bool has_next = kt + 1 < nk;
+    const bool refill = kt + 4 < nk;
+    if (has_next) {
+        // stages issued after kt+1 and still allowed in flight: kt+2, kt+3
+        const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
+        publish(nxt, pending, g, (int64_t)(kt + 1) * BK, wave, lane);
+    }
+    TP_FENCE();
+    // full refill steps interleave their DMA with the MFMAs; a partial final step takes
+    // the general path up front
+    const bool inline_dma = refill && k0_full(g, (int64_t)(kt + 4) * BK);
+    if (refill && !inline_dma) issue_stage<DUAL>(cur, p, g, a_base, m0, n0, (int64_t)(kt + 4) * BK, wave, lane);
+    const uint16_t* a_k = a_base + (int64_t)(kt + 4) * BK;
+    const uint16_t* b_k = g.B1 + (int64_t)(kt + 4) * BK * g.ldb;
+    unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
+    unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        mfma1(acc, f1, n);
+        if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
+        if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
+        if (inline_dma && n >= 11 && n < 11 + DMA_B) dma16(b_k + p.b_off[n - 11], b_dst + b_granule_base(n - 11) * 16);
+        TP_FENCE();
+    }
+}
+
 template <bool DUAL, class Epi>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi, int tiles_m) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;
-    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi, int tiles_m,
+                                                            int tiles_n) {
+    __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE_BYTES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    map_tile((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * (DUAL ? BN / 2 : BN);
+    const uint16_t* a_base = g.A + m0 * g.lda;
 
-    f32x16 acc[2][4];
+    DmaPlan p;
+    make_plan<DUAL>(p, g, m0, n0, wave, lane);
+
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = (int)((g.K + BK - 1) / BK);
-    TileRegs t;
-    load_tile<DUAL>(t, g, m0, n0, 0, tid);
-    store_tile(t, smem, tid);
-    __syncthreads();
+    // prologue: steps 0..3 in flight, publish step 0
+    issue_stage<DUAL>(st0, p, g, a_base, m0, n0, 0, wave, lane);
+    if (nk > 1) issue_stage<DUAL>(st1, p, g, a_base, m0, n0, BK, wave, lane);
+    if (nk > 2) issue_stage<DUAL>(st2, p, g, a_base, m0, n0, 2 * BK, wave, lane);
+    if (nk > 3) issue_stage<DUAL>(st3, p, g, a_base, m0, n0, 3 * BK, wave, lane);
+    publish(st0, (nk - 1 < 3) ? nk - 1 : 3, g, 0, wave, lane);
+
+    Frags f0, f1;
+    read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
+    unsigned char* sa = st0;   // stage of step kt; sb, sc, sd hold steps kt+1, kt+2, kt+3
+    unsigned char* sb = st1;
+    unsigned char* sc = st2;
+    unsigned char* sd = st3;
     for (int kt = 0; kt < nk; ++kt) {
-        unsigned char* cur = smem + (kt & 1) * STAGE_BYTES;
-        unsigned char* nxt = smem + ((kt + 1) & 1) * STAGE_BYTES;
-        const bool more = kt + 1 < nk;
-        if (more) load_tile<DUAL>(t, g, m0, n0, (int64_t)(kt + 1) * BK, tid);
-        compute_stage<DUAL>(acc, cur, wm, wn, lane);
-        if (more) store_tile(t, nxt, tid);
-        __syncthreads();
+        k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, p, g, a_base, m0, n0, wm, wn, wave, lane);
+        unsigned char* t = sa;
+        sa = sb;
+        sb = sc;
+        sc = sd;
+        sd = t;
     }
     epi(acc, m0, n0, wm, wn, lane);
 }
 
 template <bool DUAL, class Epi>
 hipError_t launch(const GemmGeom& g, const Epi& epi, hipStream_t s, const char* name) {
-    static bool attr_done[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 64 && !attr_done[dev]) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_bf16_kernel<DUAL, Epi>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_done[dev] = true;
-    }
     const int64_t tiles_m = (g.M + BM - 1) / BM;
     const int64_t tiles_n = (g.N + (DUAL ? BN / 2 : BN) - 1) / (DUAL ? BN / 2 : BN);
     ProfScope ps(name, s);
-    gemm_bf16_kernel<DUAL, Epi><<<(unsigned)(tiles_m * tiles_n), NTHR, LDS_BYTES, s>>>(g, epi, (int)tiles_m);
+    gemm_bf16_kernel<DUAL, Epi><<<(unsigned)(tiles_m * tiles_n), NTHR, 0, s>>>(g, epi, (int)tiles_m,
+                                                                              (int)tiles_n);
     return hipGetLastError();
 }
 
