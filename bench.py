@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--extra", action="store_true", help="also time the attention and 70B layer shards")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="after timing, run a plain 256 MiB device copy (3 times): the reference that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
     return ap.parse_args()
 
 
@@ -101,7 +104,7 @@ def mlp_bench(args):
             "bound": "mfma", "kernel": "gemm_bf16_swiglu",
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": recorded_traffic("gemm_bf16_swiglu"),
         },
     }
     return res, inp
@@ -196,6 +199,31 @@ def attn_bench(args, name):
             "qkv_rope_tflops": f_qkv / (q_ms * 1e-3) / 1e12 if q_ms else None}
 
 
+def traffic_probe():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    import torch
+    a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it was taken on
+    the current kernel source (profiles/traffic.json records the source file's hash)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return rec["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, target_s: float):
     """The fp64 oracle on a row sample of the same MLP shard, on this host's cores."""
     import numpy as np
@@ -242,6 +270,8 @@ def main():
     if args.extra:
         extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
         extra["layer70b_tp8"] = attn_bench(args, "layer70b_tp8")
+    if args.traffic_probe:
+        traffic_probe()
     cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
     out = {
