@@ -110,6 +110,30 @@ def mlp_bench(args):
     return res, inp
 
 
+def graph_timed(step, warmup: int, steps: int):
+    """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def decode_bench(args):
     import torch
     import tensor_transformer_layer_rank_amd as tp
@@ -135,7 +159,8 @@ def decode_bench(args):
         tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
         tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
 
-    ms = timed(step, args.warmup, args.steps)
+    ms_eager = timed(step, args.warmup, args.steps)       # per-kernel HIP-event timing
+    ms = graph_timed(step, args.warmup, args.steps)       # the step as one HIP graph
     d = 128
     w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
     kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
@@ -146,6 +171,8 @@ def decode_bench(args):
     sk_ms, sk_n = kernel_avg("skinny_gemm")
     return {
         "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "graph": True,
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
         "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
