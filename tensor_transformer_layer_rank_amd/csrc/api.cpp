@@ -206,12 +206,9 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
         if (!workspace || ws_bytes < need)
             return fail(TP_ERR_WORKSPACE, "tp_column_linear: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
         if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_column_linear: workspace must be 16-byte aligned");
-        int splits = 0;
-        hipError_t e = tpk::skinny_gemm_partials(X, W_shard, static_cast<float*>(workspace), T, N, K, K, &splits, s);
-        if (e != hipSuccess) return from_hip(e, "tp_column_linear");
         const int rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
         if (rk < 0) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: ReLU with fp32 output is not offered for T <= %d", (int)SKINNY_MAX_T);
-        return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(workspace), splits, T, N, Y, ldy, rk, s),
+        return from_hip(tpk::skinny_linear(X, W_shard, static_cast<float*>(workspace), T, N, K, K, Y, ldy, rk, s),
                         "tp_column_linear");
     }
     return from_hip(tpk::gemm_bf16_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU, s),
@@ -245,11 +242,8 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
         if (!workspace || ws_bytes < need)
             return fail(TP_ERR_WORKSPACE, "tp_row_linear_partial: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
         if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_row_linear_partial: workspace must be 16-byte aligned");
-        int splits = 0;
-        hipError_t e = tpk::skinny_gemm_partials(X_shard, W_shard, static_cast<float*>(workspace), T, N, K_shard, K_shard, &splits, s);
-        if (e != hipSuccess) return from_hip(e, "tp_row_linear_partial");
-        return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(workspace), splits, T, N, Y_partial, N,
-                                                 accumulate ? 1 : 0, s),
+        return from_hip(tpk::skinny_linear(X_shard, W_shard, static_cast<float*>(workspace), T, N, K_shard, K_shard,
+                                           Y_partial, N, accumulate ? 1 : 0, s),
                         "tp_row_linear_partial");
     }
     return from_hip(tpk::gemm_bf16_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
@@ -317,18 +311,13 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
     if (T <= SKINNY_MAX_T) {
         float* part = static_cast<float*>(c.take(0));
         hipError_t e;
-        if (kind == TP_MLP_SWIGLU) {
+        if (kind == TP_MLP_SWIGLU)
             e = tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I_shard, H, s);
-        } else {
-            int splits = 0;
-            e = tpk::skinny_gemm_partials(X, W_gate, part, T, I_shard, H, H, &splits, s);
-            if (e == hipSuccess) e = tpk::skinny_reduce_store(part, splits, T, I_shard, h, I_shard, 3, s);
-        }
+        else
+            e = tpk::skinny_linear(X, W_gate, part, T, I_shard, H, H, h, I_shard, 3, s);
         if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
-        int splits = 0;
-        e = tpk::skinny_gemm_partials(h, W_down, part, T, H, I_shard, I_shard, &splits, s);
-        if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
-        return from_hip(tpk::skinny_reduce_store(part, splits, T, H, Y_partial, H, 0, s), "tp_mlp_shard");
+        return from_hip(tpk::skinny_linear(h, W_down, part, T, H, I_shard, I_shard, Y_partial, H, 0, s),
+                        "tp_mlp_shard");
     }
     hipError_t e;
     if (kind == TP_MLP_SWIGLU)
@@ -433,20 +422,15 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
         if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
         return from_hip(tpk::gemm_bf16_store(att, W_o, Y_partial, T, H, dq, dq, H, H, 2, 0, s), "tp_attn_shard");
     }
-    const int64_t B = desc->B, nqkv = (int64_t)(hq + 2 * hkv) * 128;
-    int splits = 0;
-    hipError_t e = tpk::skinny_gemm_partials(X, W_qkv, static_cast<float*>(part), B, nqkv, H, H, &splits, s);
-    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
-    e = tpk::skinny_reduce_qkv_decode(static_cast<const float*>(part), splits, B, hq, hkv, desc->cache_len,
-                                      desc->rope_theta, static_cast<float*>(qbuf), desc->k_cache, desc->v_cache,
-                                      desc->cache_capacity, s);
+    const int64_t B = desc->B;
+    hipError_t e = tpk::skinny_qkv_decode(X, W_qkv, static_cast<float*>(part), B, H, hq, hkv, desc->cache_len,
+                                          desc->rope_theta, static_cast<float*>(qbuf), desc->k_cache,
+                                          desc->v_cache, desc->cache_capacity, s);
     if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
     e = tpk::decode_attn(static_cast<const float*>(qbuf), desc->k_cache, desc->v_cache, B, hq, hkv,
                          desc->cache_len + 1, desc->cache_capacity, static_cast<float*>(scratch), att, s);
     if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
-    e = tpk::skinny_gemm_partials(att, W_o, static_cast<float*>(part), B, H, dq, dq, &splits, s);
-    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
-    return from_hip(tpk::skinny_reduce_store(static_cast<const float*>(part), splits, B, H, Y_partial, H, 0, s),
+    return from_hip(tpk::skinny_linear(att, W_o, static_cast<float*>(part), B, H, dq, dq, Y_partial, H, 0, s),
                     "tp_attn_shard");
 }
 

@@ -1,24 +1,31 @@
 // Decode-step (one new token per sequence, M <= 64 rows) kernels of a rank's shard.
 // The work is bound by streaming the weight shards and the KV cache from HBM once.
 //
-//   skinny_gemm_kernel   split-K GEMM A[M, K] . W[K, N] for small M: each wave streams a
-//                        32 (k) x 128 (n) block of W per step with 128-bit loads (every byte
-//                        of the weight read exactly once), transposes it in registers and
-//                        feeds v_mfma_f32_16x16x32_bf16 with the activations as the A operand.
-//                        The 4 waves of a workgroup take interleaved steps of one K chunk and
-//                        are summed in LDS in a fixed order; chunks go to a partial buffer.
-//   reduce kernels       sum the K-chunk partials in chunk order and apply the layer's
-//                        epilogue: plain fp32/bf16 store (O and down partials, vocabulary-
-//                        split logits), SiLU(gate)*up, or QKV: rotary embedding at the
-//                        cache position, key/value append into the cache, q kept in fp32.
-//   decode_attn_kernel   split-KV attention of one query over cache slots 0..L-1
-//                        (16-lane groups read one 256-byte key row each), then a combine
-//                        kernel merges the per-split (max, sum, output) triples.
+//   skinny_kernel        split-K GEMM A[M, K] . W[K, N] for small M. A workgroup owns a
+//                        128-column strip and one K chunk; its 4 waves take interleaved 32-row
+//                        steps, each streaming a 32 x 128 weight block with 128-bit loads
+//                        (every weight byte read once, the next step's block already in
+//                        flight), transposing it in registers (v_perm) and feeding
+//                        v_mfma_f32_16x16x32_bf16 with the activations as the A operand. The
+//                        waves are summed in LDS in a fixed order and the chunk's fp32 partial
+//                        is written to a partial buffer.
+//   reduce kernels       sum the chunk partials in chunk order and apply the layer's
+//                        epilogue: fp32/bf16 store (O and down partials, vocabulary-split
+//                        logits), SiLU(gate)*up, or QKV: rotary embedding at the cache
+//                        position, key and value appended to the cache, q kept in fp32.
+//   decode_attn_kernel   split-KV attention of one query over cache slots 0..L-1 (16-lane
+//                        groups read one 256-byte key row each; the value rows are fetched
+//                        while the scores are formed); decode_combine_kernel merges the
+//                        per-split (max, sum, output) triples.
+//
+// Partial sums across workgroups go through HBM-resident buffers and a separate kernel:
+// a device-scope fence per workgroup (L2 write-back and invalidate on this GPU) costs far
+// more than the extra launch.
 //
 // Sources: the column/row split of "CUDA tensor parallel computations" (第二类, 第三类), the
-// attention shard of "放进 Transformer", and the KV cache kept per rank in
-// "TensorRT LLM 中的并行策略" (注意力模块). The vocabulary-split output layer is from
-// "张量并行：切分 Transformer 层的分布式训练" (输入与输出层).
+// attention shard of its section 放进 Transformer, the per-rank KV cache of "TensorRT LLM
+// 中的并行策略" (注意力模块), and the vocabulary-split output layer of "张量并行：切分
+// Transformer 层的分布式训练" (输入与输出层).
 #include "tp_internal.h"
 
 namespace tpk {
@@ -40,7 +47,7 @@ SkinnyPlan plan_skinny(int64_t N, int64_t K, int nb) {
     p.strips_per_b = (N + STRIP - 1) / STRIP;
     p.strips = p.strips_per_b * nb;
     p.ncols = p.strips * STRIP;
-    int64_t target = (768 + p.strips - 1) / p.strips;   // aim for ~768 workgroups
+    int64_t target = (1024 + p.strips - 1) / p.strips;   // aim for ~1024 workgroups
     if (target < 1) target = 1;
     int64_t kchunk = (K + target - 1) / target;
     kchunk = ((kchunk + 4 * STEP - 1) / (4 * STEP)) * (4 * STEP);   // whole steps for all 4 waves
@@ -56,24 +63,73 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+struct SkinnyArgs {
+    const uint16_t* A;
+    int64_t lda;
+    const uint16_t* B1;
+    const uint16_t* B2;      // second weight of the dual (gate/up) form
+    int64_t M, N, K, kchunk, strips_per_b, ncols;
+    int splits;
+    float* part;             // [splits][M][ncols]
+};
+
 template <int MB>
-__global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __restrict__ A,
-                                                          int64_t lda,
-                                                          const uint16_t* __restrict__ B1,
-                                                          const uint16_t* __restrict__ B2,
-                                                          int64_t M, int64_t N, int64_t K,
-                                                          int64_t kchunk, int64_t strips_per_b,
-                                                          int64_t ncols, float* __restrict__ part) {
-    __shared__ f32x4 red[4][MB * 16][STRIP / 4];
+struct StepRegs {
+    u32x4 w[8];
+    bf16x8 a[MB];
+};
+
+// Loads of one 32-row step: `wp` points at this lane's 8-column group in weight row kr
+// (kr = k0 + 8 * grp), `ap` at this lane's activation rows, column kr.
+template <int MB>
+__device__ __forceinline__ void load_step(StepRegs<MB>& s, const uint16_t* wp, const uint16_t* ap,
+                                          int64_t ldw, int64_t lda, int64_t kr, int64_t kend,
+                                          bool col_ok, uint32_t m_ok) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        s.w[i] = (kr + i < kend && col_ok) ? *reinterpret_cast<const u32x4*>(wp + i * ldw)
+                                           : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        s.a[mb] = ((m_ok >> mb) & 1u) && kr < kend
+                      ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ap + mb * 16 * lda))
+                      : bf16x8{};
+}
+
+// acc[mb][t][r] += A[m = mb*16 + 4*grp + r][kr..] . W[kr..][col + t]: the 8 x 8 block of
+// weights a lane loaded (rows kr..kr+7, columns col..col+7) is transposed so that column t
+// becomes the 8-k operand of MFMA t.
+template <int MB>
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>& s) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const unsigned sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 bt;
+        bt.x = __builtin_amdgcn_perm(s.w[1][t >> 1], s.w[0][t >> 1], sel);
+        bt.y = __builtin_amdgcn_perm(s.w[3][t >> 1], s.w[2][t >> 1], sel);
+        bt.z = __builtin_amdgcn_perm(s.w[5][t >> 1], s.w[4][t >> 1], sel);
+        bt.w = __builtin_amdgcn_perm(s.w[7][t >> 1], s.w[6][t >> 1], sel);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bt);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.a[mb], b, acc[mb][t], 0, 0, 0);
+    }
+}
+
+template <int MB>
+__global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs g) {
+    __shared__ f32x4 red[2][MB * 16][STRIP / 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, l16 = lane & 15;
     const int64_t strip = blockIdx.x, split = blockIdx.y;
-    const uint16_t* Bp = (strip < strips_per_b) ? B1 : B2;
-    const int64_t c0 = (strip % strips_per_b) * STRIP;
+    const bool second = strip >= g.strips_per_b;
+    const uint16_t* Bp = second ? g.B2 : g.B1;
+    const int64_t cgroup = strip % g.strips_per_b;
+    const int64_t c0 = cgroup * STRIP;
     const int64_t col = c0 + 8 * l16;
-    const int64_t kbeg = split * kchunk;
-    const int64_t kend = (kbeg + kchunk < K) ? kbeg + kchunk : K;
-    const bool col_ok = col < N;
+    const bool col_ok = col < g.N;
+    const int64_t kbeg = split * g.kchunk;
+    const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
 
     f32x4 acc[MB][8];
 #pragma unroll
@@ -81,59 +137,68 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __rest
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[mb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t k0 = kbeg + wave * STEP; k0 < kend; k0 += 4 * STEP) {
-        u32x4 w[8];
-        const int64_t kr = k0 + 8 * grp;
+    // waves take steps wave, wave+4, ...; two register sets keep the next step in flight
+    uint32_t m_ok = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t row = kr + i;
-            w[i] = (row < kend && col_ok) ? *reinterpret_cast<const u32x4*>(Bp + row * N + col)
-                                          : u32x4{0u, 0u, 0u, 0u};
-        }
-        bf16x8 a[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int64_t m = mb * 16 + l16;
-            a[mb] = (m < M && kr < kend)
-                        ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(A + m * lda + kr))
-                        : bf16x8{};
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const unsigned sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 bt;
-            bt.x = __builtin_amdgcn_perm(w[1][t >> 1], w[0][t >> 1], sel);
-            bt.y = __builtin_amdgcn_perm(w[3][t >> 1], w[2][t >> 1], sel);
-            bt.z = __builtin_amdgcn_perm(w[5][t >> 1], w[4][t >> 1], sel);
-            bt.w = __builtin_amdgcn_perm(w[7][t >> 1], w[6][t >> 1], sel);
-            const bf16x8 b = __builtin_bit_cast(bf16x8, bt);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][t], 0, 0, 0);
-        }
+    for (int mb = 0; mb < MB; ++mb) m_ok |= (mb * 16 + l16 < g.M) ? (1u << mb) : 0u;
+    const int64_t kfirst = kbeg + wave * STEP + 8 * grp;
+    const uint16_t* wp = Bp + kfirst * g.N + col;          // advances 4 steps at a time
+    const uint16_t* ap = g.A + (int64_t)l16 * g.lda + kfirst;
+    const int64_t wstep = 4 * STEP * g.N, astep = 4 * STEP;
+    StepRegs<MB> s0, s1;
+    int64_t kr = kfirst;
+    if (kr - 8 * grp < kend) load_step<MB>(s0, wp, ap, g.N, g.lda, kr, kend, col_ok, m_ok);
+    for (; kr - 8 * grp < kend; kr += 8 * STEP) {
+        const bool h1 = kr + 4 * STEP - 8 * grp < kend;
+        if (h1) load_step<MB>(s1, wp + wstep, ap + astep, g.N, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
+        mma_step<MB>(acc, s0);
+        const bool h2 = kr + 8 * STEP - 8 * grp < kend;
+        if (h2) load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, g.N, g.lda, kr + 8 * STEP, kend, col_ok, m_ok);
+        if (h1) mma_step<MB>(acc, s1);
+        wp += 2 * wstep;
+        ap += 2 * astep;
     }
-    // acc[mb][t][r] = C[m = mb*16 + 4*grp + r][col = c0 + 8*l16 + t]
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mb * 16 + 4 * grp + r;
-            red[wave][m][2 * l16] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
-            red[wave][m][2 * l16 + 1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
-        }
+
+    // waves 2,3 -> LDS, added by waves 0,1; wave 1 -> LDS, added by wave 0 (fixed order)
+    // acc[mb][t][r] = C[m = mb*16 + 4*grp + r][c0 + 8*l16 + t]
+#define TP_RED_STORE(SLOT)                                                                          \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) _Pragma("unroll") for (int r = 0; r < 4; ++r) { \
+        const int m = mb * 16 + 4 * grp + r;                                                        \
+        red[SLOT][m][2 * l16] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};  \
+        red[SLOT][m][2 * l16 + 1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]}; \
+    }
+#define TP_RED_ADD(SLOT)                                                                            \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) _Pragma("unroll") for (int r = 0; r < 4; ++r) { \
+        const int m = mb * 16 + 4 * grp + r;                                                        \
+        const f32x4 u = red[SLOT][m][2 * l16], v = red[SLOT][m][2 * l16 + 1];                       \
+        acc[mb][0][r] += u.x; acc[mb][1][r] += u.y; acc[mb][2][r] += u.z; acc[mb][3][r] += u.w;     \
+        acc[mb][4][r] += v.x; acc[mb][5][r] += v.y; acc[mb][6][r] += v.z; acc[mb][7][r] += v.w;     \
+    }
+    if (wave >= 2) TP_RED_STORE(wave - 2)
     __syncthreads();
-    for (int idx = tid; idx < MB * 16 * (STRIP / 4); idx += 256) {
-        const int m = idx / (STRIP / 4), c4 = idx % (STRIP / 4);
-        if (m >= M) continue;
-        f32x4 s = red[0][m][c4];
-        s += red[1][m][c4];
-        s += red[2][m][c4];
-        s += red[3][m][c4];
-        *reinterpret_cast<f32x4*>(part + (split * M + m) * ncols + strip * STRIP + 4 * c4) = s;
+    if (wave < 2) TP_RED_ADD(wave)
+    __syncthreads();
+    if (wave == 1) TP_RED_STORE(0)
+    __syncthreads();
+    if (wave == 0) {
+        TP_RED_ADD(0)
+        float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = mb * 16 + 4 * grp + r;
+                if (m >= g.M) continue;
+                f32x4* o = reinterpret_cast<f32x4*>(dst + m * g.ncols + 8 * l16);
+                o[0] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+                o[1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+            }
     }
+#undef TP_RED_STORE
+#undef TP_RED_ADD
 }
 
-// out[m][n] = sum over splits (in order) of part[s][m][n]
+// out[m][n] = sum over chunks (in order) of part[s][m][n]
 __device__ __forceinline__ float sum_splits(const float* part, int splits, int64_t M,
                                             int64_t ncols, int64_t m, int64_t c) {
     float v = part[m * ncols + c];
@@ -141,8 +206,10 @@ __device__ __forceinline__ float sum_splits(const float* part, int splits, int64
     return v;
 }
 
-__global__ void reduce_store_kernel(const float* __restrict__ part, int splits, int64_t M,
-                                    int64_t N, int64_t ncols, void* C, int64_t ldc, int kind) {
+// kind: 0 fp32 store, 1 fp32 +=, 2 bf16, 3 bf16 ReLU
+__global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restrict__ part, int splits,
+                                                           int64_t M, int64_t N, int64_t ncols, void* C,
+                                                           int64_t ldc, int kind) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= M * N) return;
     const int64_t m = idx / N, n = idx - m * N;
@@ -154,34 +221,36 @@ __global__ void reduce_store_kernel(const float* __restrict__ part, int splits, 
     else static_cast<uint16_t*>(C)[off] = f32_to_bf16(v > 0.f ? v : 0.f);
 }
 
-__global__ void reduce_swiglu_kernel(const float* __restrict__ part, int splits, int64_t M,
-                                     int64_t I, int64_t ncols, int64_t up_off,
-                                     uint16_t* __restrict__ h) {
+__global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t M, int64_t I, int64_t ncols,
+                                                            int64_t up_off, uint16_t* __restrict__ h) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= M * I) return;
     const int64_t m = idx / I, c = idx - m * I;
-    const float g = sum_splits(part, splits, M, ncols, m, c);
-    const float u = sum_splits(part, splits, M, ncols, m, up_off + c);
-    h[idx] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+    const float gt = sum_splits(part, splits, M, ncols, m, c);
+    const float up = sum_splits(part, splits, M, ncols, m, up_off + c);
+    h[idx] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
 }
 
-// one thread per (sequence, head, i < 64); heads 0..hq-1 are q, then hkv k heads, then v
-__global__ void reduce_qkv_decode_kernel(const float* __restrict__ part, int splits, int64_t B,
-                                         int hq, int hkv, int64_t ncols, int64_t pos, double theta,
-                                         float* __restrict__ qbuf, uint16_t* __restrict__ kc,
-                                         uint16_t* __restrict__ vc, int64_t cap) {
+// one thread per (sequence, head, i < 64): heads 0..hq-1 are q, then hkv k heads, then hkv v
+// heads; q and k pairs (i, i+64) are rotated by pos * theta^(-2i/128), formed in fp64
+__global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict__ part, int splits,
+                                                         int64_t B, int hq, int hkv, int64_t ncols,
+                                                         int64_t pos, double theta,
+                                                         float* __restrict__ qbuf,
+                                                         uint16_t* __restrict__ kc,
+                                                         uint16_t* __restrict__ vc, int64_t cap) {
     const int nh = hq + 2 * hkv;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= B * nh * 64) return;
-    const int i = (int)(idx % 64);
-    const int head = (int)((idx / 64) % nh);
+    const int i = (int)(idx & 63);
+    const int head = (int)((idx >> 6) % nh);
     const int64_t b = idx / (64 * nh);
     const int64_t c = (int64_t)head * 128 + i;
     const float x1 = sum_splits(part, splits, B, ncols, b, c);
     const float x2 = sum_splits(part, splits, B, ncols, b, c + 64);
     if (head >= hq + hkv) {
-        const int g = head - hq - hkv;
-        uint16_t* dst = vc + ((b * hkv + g) * cap + pos) * 128;
+        uint16_t* dst = vc + ((b * hkv + (head - hq - hkv)) * cap + pos) * 128;
         dst[i] = f32_to_bf16(x1);
         dst[i + 64] = f32_to_bf16(x2);
         return;
@@ -194,8 +263,7 @@ __global__ void reduce_qkv_decode_kernel(const float* __restrict__ part, int spl
         dst[i] = y1;
         dst[i + 64] = y2;
     } else {
-        const int g = head - hq;
-        uint16_t* dst = kc + ((b * hkv + g) * cap + pos) * 128;
+        uint16_t* dst = kc + ((b * hkv + (head - hq)) * cap + pos) * 128;
         dst[i] = f32_to_bf16(y1);
         dst[i + 64] = f32_to_bf16(y2);
     }
@@ -218,7 +286,8 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
     return ((sh[0] + sh[1]) + sh[2]) + sh[3];
 }
 
-// grid (nsplit, hq, B); scratch[b][h][split][130] = (max in log2 units, sum, o[128])
+// grid (nsplit, hq, B). scratch[b][h][split][130] = (max in log2 units, sum, o[128])
+template <int VPRE>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restrict__ q,
                                                           const uint16_t* __restrict__ kc,
                                                           const uint16_t* __restrict__ vc,
@@ -242,6 +311,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
     for (int e = 0; e < 8; ++e) qv[e] = qp[e] * scale;
     const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
+    // the first VPRE value rows of this group are fetched together with the keys
+    u32x4 vpre[VPRE];
+#pragma unroll
+    for (int e = 0; e < VPRE; ++e) {
+        const int j = grp + 16 * e;
+        vpre[e] = (j < n) ? *reinterpret_cast<const u32x4*>(vb + (kbeg + j) * 128) : u32x4{0u, 0u, 0u, 0u};
+    }
     for (int j = grp; j < n; j += 16) {
         const u32x4 kk = *reinterpret_cast<const u32x4*>(kb + (kbeg + j) * 128);
         float s = qv[0] * bf16_lo(kk.x) + qv[1] * bf16_hi(kk.x);
@@ -266,9 +342,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
     }
     sm = block_sum(sm, sh);   // its barriers also publish sc[]
     float acc[8] = {};
-    for (int j = grp; j < n; j += 16) {
-        const float p = sc[j];
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vb + (kbeg + j) * 128);
+    auto pv = [&](float p, const u32x4& vv) {
         acc[0] += p * bf16_lo(vv.x);
         acc[1] += p * bf16_hi(vv.x);
         acc[2] += p * bf16_lo(vv.y);
@@ -277,7 +351,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
         acc[5] += p * bf16_hi(vv.z);
         acc[6] += p * bf16_lo(vv.w);
         acc[7] += p * bf16_hi(vv.w);
+    };
+#pragma unroll
+    for (int e = 0; e < VPRE; ++e) {
+        const int j = grp + 16 * e;
+        if (j < n) pv(sc[j], vpre[e]);
     }
+    for (int j = grp + 16 * VPRE; j < n; j += 16)
+        pv(sc[j], *reinterpret_cast<const u32x4*>(vb + (kbeg + j) * 128));
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[grp][8 * l16 + e] = acc[e];
     __syncthreads();
@@ -321,78 +402,82 @@ int64_t decode_chunk(int64_t L, int* nsplit_out) {
     return chunk;
 }
 
+hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name) {
+    a.kchunk = p.kchunk;
+    a.strips_per_b = p.strips_per_b;
+    a.ncols = p.ncols;
+    a.splits = (int)p.splits;
+    dim3 grid((unsigned)p.strips, (unsigned)p.splits);
+    ProfScope ps(name, s);
+    if (a.M <= 32)
+        skinny_kernel<2><<<grid, 256, 0, s>>>(a);
+    else
+        skinny_kernel<4><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+SkinnyArgs skinny_args(const void* A, const void* B1, const void* B2, float* part, int64_t M,
+                       int64_t N, int64_t K, int64_t lda) {
+    SkinnyArgs a{};
+    a.A = static_cast<const uint16_t*>(A);
+    a.lda = lda;
+    a.B1 = static_cast<const uint16_t*>(B1);
+    a.B2 = static_cast<const uint16_t*>(B2 ? B2 : B1);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.part = part;
+    return a;
+}
+
 }  // namespace
 
 size_t skinny_partials_bytes(int64_t M, int64_t N, int64_t K) {
     const SkinnyPlan p = plan_skinny(N, K, 1);
     return (size_t)(p.splits * M * p.ncols) * sizeof(float);
 }
-
-// B2 != nullptr: dual form; columns [0, ncols/2) come from B, [ncols/2, ncols) from B2
-static hipError_t skinny_launch(const void* A, const void* B, const void* B2, float* part,
-                                int64_t M, int64_t N, int64_t K, int64_t lda, int* splits_out,
-                                int64_t* ncols_out, hipStream_t s, const char* name) {
-    const SkinnyPlan p = plan_skinny(N, K, B2 ? 2 : 1);
-    *splits_out = (int)p.splits;
-    *ncols_out = p.ncols;
-    dim3 grid((unsigned)p.strips, (unsigned)p.splits);
-    const uint16_t* a = static_cast<const uint16_t*>(A);
-    const uint16_t* b1 = static_cast<const uint16_t*>(B);
-    const uint16_t* b2 = static_cast<const uint16_t*>(B2 ? B2 : B);
-    ProfScope ps(name, s);
-    if (M <= 32)
-        skinny_gemm_kernel<2><<<grid, 256, 0, s>>>(a, lda, b1, b2, M, N, K, p.kchunk,
-                                                   p.strips_per_b, p.ncols, part);
-    else
-        skinny_gemm_kernel<4><<<grid, 256, 0, s>>>(a, lda, b1, b2, M, N, K, p.kchunk,
-                                                   p.strips_per_b, p.ncols, part);
-    return hipGetLastError();
-}
-
-hipError_t skinny_gemm_partials(const void* A, const void* B, float* part, int64_t M, int64_t N,
-                                int64_t K, int64_t lda, int* splits_out, hipStream_t s) {
-    int64_t ncols;
-    return skinny_launch(A, B, nullptr, part, M, N, K, lda, splits_out, &ncols, s, "skinny_gemm");
-}
-
-hipError_t skinny_reduce_store(const float* part, int splits, int64_t M, int64_t N, void* C,
-                               int64_t ldc, int kind, hipStream_t s) {
-    const SkinnyPlan p = plan_skinny(N, 1, 1);
-    const int64_t n = M * N;
-    ProfScope ps("skinny_reduce", s);
-    reduce_store_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, splits, M, N, p.ncols,
-                                                                    C, ldc, kind);
-    return hipGetLastError();
-}
-
-// dual gate/up in one skinny launch, then SiLU(gate) * up into h
-hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
-                         int64_t M, int64_t I, int64_t H, hipStream_t s) {
-    int splits;
-    int64_t ncols;
-    hipError_t e = skinny_launch(X, Wg, Wu, part, M, I, H, H, &splits, &ncols, s, "skinny_gemm_gateup");
-    if (e != hipSuccess) return e;
-    const int64_t n = M * I;
-    ProfScope ps("skinny_reduce_swiglu", s);
-    reduce_swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        part, splits, M, I, ncols, ncols / 2, static_cast<uint16_t*>(h));
-    return hipGetLastError();
-}
-
 size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H) {
     const SkinnyPlan p = plan_skinny(I, H, 2);
     return (size_t)(p.splits * M * p.ncols) * sizeof(float);
 }
 
-hipError_t skinny_reduce_qkv_decode(const float* part, int splits, int64_t B, int hq, int hkv,
-                                    int64_t pos, float theta, float* qbuf, void* k_cache,
-                                    void* v_cache, int64_t cap, hipStream_t s) {
+hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s) {
+    SkinnyArgs a = skinny_args(A, B, nullptr, part, M, N, K, lda);
+    const SkinnyPlan p = plan_skinny(N, K, 1);
+    hipError_t e = skinny_run(a, p, s, "skinny_gemm");
+    if (e != hipSuccess) return e;
+    const int64_t n = M * N;
+    ProfScope ps("skinny_reduce", s);
+    reduce_store_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, (int)p.splits, M, N, p.ncols, C, ldc, kind);
+    return hipGetLastError();
+}
+
+hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
+                         int64_t M, int64_t I, int64_t H, hipStream_t s) {
+    SkinnyArgs a = skinny_args(X, Wg, Wu, part, M, I, H, H);
+    const SkinnyPlan p = plan_skinny(I, H, 2);
+    hipError_t e = skinny_run(a, p, s, "skinny_gemm_gateup");
+    if (e != hipSuccess) return e;
+    const int64_t n = M * I;
+    ProfScope ps("skinny_reduce_swiglu", s);
+    reduce_swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, (int)p.splits, M, I, p.ncols,
+                                                                     p.ncols / 2, static_cast<uint16_t*>(h));
+    return hipGetLastError();
+}
+
+hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H,
+                             int hq, int hkv, int64_t pos, float theta, float* qbuf, void* k_cache,
+                             void* v_cache, int64_t cap, hipStream_t s) {
     const int64_t N = (int64_t)(hq + 2 * hkv) * 128;
-    const SkinnyPlan p = plan_skinny(N, 1, 1);
+    SkinnyArgs a = skinny_args(X, Wqkv, nullptr, part, B, N, H, H);
+    const SkinnyPlan p = plan_skinny(N, H, 1);
+    hipError_t e = skinny_run(a, p, s, "skinny_gemm_qkv");
+    if (e != hipSuccess) return e;
     const int64_t n = B * (hq + 2 * hkv) * 64;
     ProfScope ps("skinny_reduce_qkv", s);
-    reduce_qkv_decode_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        part, splits, B, hq, hkv, p.ncols, pos, (double)theta, qbuf,
+    reduce_qkv_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+        part, (int)p.splits, B, hq, hkv, p.ncols, pos, (double)theta, qbuf,
         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), cap);
     return hipGetLastError();
 }
@@ -410,9 +495,10 @@ hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache,
     const int64_t chunk = decode_chunk(L, &nsplit);
     {
         ProfScope ps("decode_attn", s);
-        decode_attn_kernel<<<dim3((unsigned)nsplit, (unsigned)hq, (unsigned)B), 256, 0, s>>>(
-            q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), hq,
-            hkv, L, cap, chunk, scratch);
+        dim3 grid((unsigned)nsplit, (unsigned)hq, (unsigned)B);
+        const uint16_t* k = static_cast<const uint16_t*>(k_cache);
+        const uint16_t* v = static_cast<const uint16_t*>(v_cache);
+        decode_attn_kernel<4><<<grid, 256, 0, s>>>(q, k, v, hq, hkv, L, cap, chunk, scratch);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

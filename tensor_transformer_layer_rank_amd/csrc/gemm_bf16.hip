@@ -18,11 +18,13 @@
 // MFMAs consume the fourth. One barrier per K step, placed between its two 16-deep
 // slices: it publishes the next stage and releases the oldest one for refilling, so the
 // next stage's first operand fragments are read before the step ends.
-// LDS layouts: the activation tile is kept [m][k] with 80-byte rows and read with
-// ds_read_b128; the weight tile is kept in its memory order [k][n] with 576-byte rows and
-// read with the gfx950 transposing load ds_read_b64_tr_b16, which hands each lane 4
-// consecutive k of one column (two of them make the 8-k MFMA operand). The row paddings
-// make both reads free of LDS bank conflicts; the DMA writes skip the pad granules.
+// LDS layouts: the activation tile is kept [m][k] (64-byte rows) and read with
+// ds_read_b128; the weight tile is kept in its memory order [k][n] (512-byte rows) and read
+// with the gfx950 transposing load ds_read_b64_tr_b16, which hands each lane 4 consecutive k
+// of one column (two of them make the 8-k MFMA operand). The 16-byte granules of a row are
+// XOR-permuted (activation: chunk ^ ((row >> 2) & 3); weight: granule ^ 4 * (k & 3)), which
+// makes both reads free of LDS bank conflicts (measured); the DMA applies the permutation by
+// choosing which source granule each lane fetches.
 // Tiles are ordered so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
 // works on a compact block of 4 row tiles x n column tiles, which keeps its L2 hit rate up.
 #include "tp_internal.h"
@@ -39,16 +41,19 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, NSTAGE = 4;
-constexpr int A_STRIDE = BK * 2 + 16;     // 80 B per activation row (64 data + 16 pad)
-constexpr int B_STRIDE = BN * 2 + 64;     // 576 B per weight row (512 data + 64 pad)
-constexpr int A_GRAN = A_STRIDE / 16;     // 5 granules of 16 B per activation row
-constexpr int B_GRAN = B_STRIDE / 16;     // 36 granules per weight row
-constexpr int A_BYTES = BM * A_STRIDE;    // 20480
-constexpr int B_BYTES = BK * B_STRIDE;    // 18432
+constexpr int A_STRIDE = BK * 2;          // 64 B per activation row
+constexpr int B_STRIDE = BN * 2;          // 512 B per weight row (k)
+constexpr int A_BYTES = BM * A_STRIDE;    // 16384
+constexpr int B_BYTES = BK * B_STRIDE;    // 16384
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int A_PER_WAVE = BM * A_GRAN / 4;   // 320 granules = 5 DMA instructions
-constexpr int B_PER_WAVE = BK * B_GRAN / 4;   // 288 granules (5 instructions, the last partial)
-constexpr int DMA_A = 5, DMA_B = 5;
+constexpr int A_PER_WAVE = BM * 4 / 4;    // 256 granules of 16 B = 4 DMA instructions
+constexpr int B_PER_WAVE = BK * 32 / 4;   // 256 granules
+constexpr int DMA_A = 4, DMA_B = 4;
+
+// byte offset of logical 16-byte chunk c (0..3) of activation row r
+__device__ __forceinline__ int a_lds(int r, int c) { return r * A_STRIDE + ((c ^ ((r >> 2) & 3)) << 4); }
+// byte offset of logical 16-byte granule g (0..31) of weight row k
+__device__ __forceinline__ int b_lds(int k, int g) { return k * B_STRIDE + ((g ^ (4 * (k & 3))) << 4); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -74,39 +79,45 @@ typedef __attribute__((address_space(3))) void lds_void;
 // each wave issues exactly DMA_A + DMA_B loads per stage and vmcnt counts stay exact:
 // pad granules, rows past M and columns past N fetch a harmless valid address (row 0 /
 // column n0), and granules past K fetch K chunk 0 and are zeroed after they land.
+// Per-lane source offsets of one wave's share of a stage (fixed for the whole K loop; only
+// the K offset moves), in elements relative to the tile's base pointers. Wave w fills
+// activation rows 64w..64w+63 and weight rows 8w..8w+7, 4 DMA instructions of 64
+// granules each; LDS granule G holds the logical granule that the XOR permutation maps to
+// it. Every lane of every instruction loads an in-bounds address, so each wave issues
+// exactly DMA_A + DMA_B loads per stage and vmcnt counts stay exact: rows past M and
+// columns past N fetch a harmless valid address (row 0 / column n0), and granules past K
+// fetch K chunk 0 and are zeroed after they land.
 struct DmaPlan {
-    int32_t a_off[DMA_A];   // row * lda + 8 * chunk  (pad granules: chunk 0)
+    int32_t a_off[DMA_A];   // row * lda + 8 * chunk
     int64_t b_off[DMA_B];   // k row * ldb + column, relative to the first weight (dual: the
                             // second weight's granules carry the pointer difference)
 };
 
-// geometry of granule i of this wave (recomputed only on the K-tail path)
+// geometry of LDS granule i*64+lane of this wave: activation row and logical chunk
 __device__ __forceinline__ void a_granule(int wave, int i, int lane, int& row, int& c) {
     const int G = wave * A_PER_WAVE + i * 64 + lane;
-    row = G / A_GRAN;
-    c = G % A_GRAN;
+    row = G >> 2;
+    c = (G & 3) ^ ((row >> 2) & 3);
 }
-__device__ __forceinline__ int b_granule_base(int i) { return i < 4 ? i * 64 : B_PER_WAVE - 64; }
-__device__ __forceinline__ void b_granule(int wave, int i, int lane, int& row, int& c) {
-    const int G = wave * B_PER_WAVE + b_granule_base(i) + lane;
-    row = G / B_GRAN;
-    c = G % B_GRAN;
+// weight k row and logical granule
+__device__ __forceinline__ void b_granule(int wave, int i, int lane, int& row, int& g) {
+    const int G = wave * B_PER_WAVE + i * 64 + lane;
+    row = G >> 5;
+    g = (G & 31) ^ (4 * (row & 3));
 }
 
 template <bool DUAL>
-__device__ __forceinline__ int64_t b_offset(const GemmGeom& g, int64_t n0, int row, int c) {
-    int64_t col = n0, extra = 0;
-    if (c < 32) {
-        if (DUAL) {
-            col = n0 + (int64_t)(c & 15) * 8;
-            if (c >= 16) extra = g.B2 - g.B1;
-        } else {
-            col = n0 + (int64_t)c * 8;
-        }
-        if (col >= g.N) {
-            col = n0;
-            extra = 0;
-        }
+__device__ __forceinline__ int64_t b_offset(const GemmGeom& g, int64_t n0, int row, int gr) {
+    int64_t col, extra = 0;
+    if (DUAL) {
+        col = n0 + (int64_t)(gr & 15) * 8;
+        if (gr >= 16) extra = g.B2 - g.B1;
+    } else {
+        col = n0 + (int64_t)gr * 8;
+    }
+    if (col >= g.N) {
+        col = n0;
+        extra = 0;
     }
     return extra + (int64_t)row * g.ldb + col;
 }
@@ -118,13 +129,13 @@ __device__ __forceinline__ void make_plan(DmaPlan& p, const GemmGeom& g, int64_t
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + 8 * (c < 4 ? c : 0));
+        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + 8 * c);
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
-        int row, c;
-        b_granule(wave, i, lane, row, c);
-        p.b_off[i] = b_offset<DUAL>(g, n0, row, c);
+        int row, gr;
+        b_granule(wave, i, lane, row, gr);
+        p.b_off[i] = b_offset<DUAL>(g, n0, row, gr);
     }
 }
 
@@ -150,11 +161,9 @@ __device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan&
         const uint16_t* a_k = a_base + k0;
         const uint16_t* b_k = g.B1 + k0 * g.ldb;
 #pragma unroll
-        for (int i = 0; i < DMA_A; ++i)
-            dma16(a_k + p.a_off[i], a_dst + i * 1024);
+        for (int i = 0; i < DMA_A; ++i) dma16(a_k + p.a_off[i], a_dst + i * 1024);
 #pragma unroll
-        for (int i = 0; i < DMA_B; ++i)
-            dma16(b_k + p.b_off[i], b_dst + b_granule_base(i) * 16);
+        for (int i = 0; i < DMA_B; ++i) dma16(b_k + p.b_off[i], b_dst + i * 1024);
         return;
     }
     // partial final step: granules past K fetch K chunk 0 / row 0 (zeroed once landed)
@@ -162,16 +171,16 @@ __device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan&
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        if (c >= 4 || k0 + 8 * c >= g.K) c = 0;
+        if (k0 + 8 * c >= g.K) c = 0;
         if (m0 + row >= g.M) row = 0;
         dma16(a_base + k0 + (int64_t)row * g.lda + 8 * c, a_dst + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
-        int row, c;
-        b_granule(wave, i, lane, row, c);
+        int row, gr;
+        b_granule(wave, i, lane, row, gr);
         if (k0 + row >= g.K) row = 0;
-        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL>(g, n0, row, c), b_dst + b_granule_base(i) * 16);
+        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL>(g, n0, row, gr), b_dst + i * 1024);
     }
 }
 
@@ -183,16 +192,16 @@ __device__ __forceinline__ void zero_tail(unsigned char* stage, const GemmGeom& 
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        if (c < 4 && k0 + 8 * c >= g.K)
+        if (k0 + 8 * c >= g.K)
             *reinterpret_cast<u32x4*>(a_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
     unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
-        int row, c;
-        b_granule(wave, i, lane, row, c);
+        int row, gr;
+        b_granule(wave, i, lane, row, gr);
         if (k0 + row >= g.K)
-            *reinterpret_cast<u32x4*>(b_dst + b_granule_base(i) * 16 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(b_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -216,7 +225,9 @@ __device__ __forceinline__ bf16x8 read_b_frag(const unsigned char* Bs, int ks, i
     const int g = lane >> 4, r = lane & 15;
     const int row = ks * 16 + 8 * (g >> 1) + (r >> 2);
     const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
-    const lds_u8* base = (const lds_u8*)(Bs) + row * B_STRIDE + col * 2;
+    const int gr = col >> 3, within = (col & 7) * 2;
+    // rows row and row+4 have the same (row & 3), hence the same permutation
+    const lds_u8* base = (const lds_u8*)(Bs) + b_lds(row, gr) + within;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * B_STRIDE));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -237,8 +248,7 @@ __device__ __forceinline__ void read_piece(Frags& f, int piece, const unsigned c
     if (piece < 4) {
         const int r32 = lane & 31, hi = lane >> 5;
         f.a[piece] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(stage + (wm * 128 + piece * 32 + r32) * A_STRIDE +
-                                                    (ks * 2 + hi) * 16));
+            bf16x8, *reinterpret_cast<const u32x4*>(stage + a_lds(wm * 128 + piece * 32 + r32, ks * 2 + hi)));
     } else {
         f.b[piece - 4] = read_b_frag(stage + A_BYTES, ks, b_col_of<DUAL>(piece - 4, wn), lane);
     }
@@ -445,7 +455,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
         mfma1(acc, f1, n);
         if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
         if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
-        if (inline_dma && n >= 11 && n < 11 + DMA_B) dma16(b_k + p.b_off[n - 11], b_dst + b_granule_base(n - 11) * 16);
+        if (inline_dma && n >= 10 && n < 10 + DMA_B) dma16(b_k + p.b_off[n - 10], b_dst + (n - 10) * 1024);
         TP_FENCE();
     }
 }

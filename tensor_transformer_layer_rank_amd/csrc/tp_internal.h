@@ -56,21 +56,21 @@ hipError_t flash_attn_fwd(const void* q, const void* k, const void* vt, void* ou
                           int64_t S, int hq, int hkv, hipStream_t s);
 
 // ---- decode (skinny M) path ------------------------------------------------------------
-// split-K skinny GEMM partials: part[split][M, N] fp32 = A[M, K-chunk] . B[K-chunk, N]
+// Split-K GEMMs for M <= 64 rows: chunk partials go to `part`, then a reduce kernel sums them
+// in chunk order and applies the epilogue.
 size_t skinny_partials_bytes(int64_t M, int64_t N, int64_t K);
-hipError_t skinny_gemm_partials(const void* A, const void* B, float* part, int64_t M, int64_t N,
-                                int64_t K, int64_t lda, int* splits_out, hipStream_t s);
-// reduce partials into: 0 = fp32 out (ld), 1 = fp32 += , 2 = bf16 out, 3 = bf16 relu
-hipError_t skinny_reduce_store(const float* part, int splits, int64_t M, int64_t N, void* C,
-                               int64_t ldc, int kind, hipStream_t s);
-// gate/up in one dual skinny launch + SiLU(gate)*up reduce into h bf16 [M, I]
 size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H);
+// kind: 0 = fp32 store (ldc), 1 = fp32 +=, 2 = bf16 store, 3 = bf16 ReLU
+hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s);
+// h bf16 [M, I] = SiLU(X . Wg) * (X . Wu)
 hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
                          int64_t M, int64_t I, int64_t H, hipStream_t s);
-// reduce QKV partials, rotate q/k at position pos, append k/v to the caches, q to qbuf (fp32)
-hipError_t skinny_reduce_qkv_decode(const float* part, int splits, int64_t B, int hq, int hkv,
-                                    int64_t pos, float theta, float* qbuf, void* k_cache,
-                                    void* v_cache, int64_t cap, hipStream_t s);
+// QKV of one decode step: q (rotated, fp32) to qbuf [B, hq, 128]; rotated k and v appended to the
+// caches at slot pos
+hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H,
+                             int hq, int hkv, int64_t pos, float theta, float* qbuf, void* k_cache,
+                             void* v_cache, int64_t cap, hipStream_t s);
 // split-KV decode attention: out bf16 [B, hq*128]; scratch for per-split (m, l, o)
 size_t decode_attn_scratch_bytes(int64_t B, int hq, int64_t L);
 hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache, int64_t B,
