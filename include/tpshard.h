@@ -103,9 +103,12 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
 
 /*
  * Workspace bytes needed by tp_column_linear / tp_row_linear_partial for these sizes
- * (K = the contraction length). Non-zero only for the few-row (decode) regime, T <= 64,
- * where the contraction is split into chunks whose fp32 partials are summed in chunk
- * order; when it returns 0, workspace may be NULL.
+ * (K = the contraction length), on the current device. Two cases use it, both fp32
+ * partials summed in a fixed order (results are run-to-run identical):
+ *   - the few-row (decode) regime, T <= 64: the contraction is split into chunks;
+ *   - larger bf16 products whose 256x256 output tiles do not fill whole rounds of the
+ *     device's compute units: the tiles past the last full round are split along K.
+ * When it returns 0, workspace may be NULL.
  */
 size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt);
 

@@ -159,8 +159,17 @@ tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launche
 // ---- linear layers ----------------------------------------------------------------------
 
 size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt) {
-    if (in_dt != TP_BF16 || T <= 0 || T > SKINNY_MAX_T || K <= 0 || N <= 0) return 0;
+    if (in_dt != TP_BF16 || T <= 0 || K <= 0 || N <= 0) return 0;
+    if (T > SKINNY_MAX_T) return round_up(tpk::gemm_bf16_split_bytes(T, N, K, 0), WS_ALIGN);
     return round_up(tpk::skinny_partials_bytes(T, N, K), WS_ALIGN);
+}
+
+static tp_status check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return TP_OK;
+    if (!ws || ws_bytes < need)
+        return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
+    if (!aligned(ws, 16)) return fail(TP_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+    return TP_OK;
 }
 
 static tp_status check_bf16_gemm(const char* fn, const void* X, const void* W, const void* Y,
@@ -200,18 +209,18 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
     tp_status st = check_bf16_gemm("tp_column_linear", X, W_shard, Y, K, N, ldy);
     if (st != TP_OK) return st;
     const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
+    if (T <= SKINNY_MAX_T && out_dt == TP_F16)
+        return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp16 output is not offered for T <= %d", (int)SKINNY_MAX_T);
+    st = check_ws("tp_column_linear", workspace, ws_bytes, tp_linear_workspace_size(T, K, N, in_dt));
+    if (st != TP_OK) return st;
     if (T <= SKINNY_MAX_T) {
-        if (out_dt == TP_F16) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp16 output is not offered for T <= %d", (int)SKINNY_MAX_T);
-        const size_t need = tp_linear_workspace_size(T, K, N, in_dt);
-        if (!workspace || ws_bytes < need)
-            return fail(TP_ERR_WORKSPACE, "tp_column_linear: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
-        if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_column_linear: workspace must be 16-byte aligned");
         const int rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
         if (rk < 0) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: ReLU with fp32 output is not offered for T <= %d", (int)SKINNY_MAX_T);
         return from_hip(tpk::skinny_linear(X, W_shard, static_cast<float*>(workspace), T, N, K, K, Y, ldy, rk, s),
                         "tp_column_linear");
     }
-    return from_hip(tpk::gemm_bf16_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU, s),
+    return from_hip(tpk::gemm_bf16_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU,
+                                         workspace, ws_bytes, s),
                     "tp_column_linear");
 }
 
@@ -237,17 +246,15 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
     if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_row_linear_partial: input dtype %d not offered", (int)in_dt);
     tp_status st = check_bf16_gemm("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, N);
     if (st != TP_OK) return st;
+    st = check_ws("tp_row_linear_partial", workspace, ws_bytes, tp_linear_workspace_size(T, K_shard, N, in_dt));
+    if (st != TP_OK) return st;
     if (T <= SKINNY_MAX_T) {
-        const size_t need = tp_linear_workspace_size(T, K_shard, N, in_dt);
-        if (!workspace || ws_bytes < need)
-            return fail(TP_ERR_WORKSPACE, "tp_row_linear_partial: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
-        if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_row_linear_partial: workspace must be 16-byte aligned");
         return from_hip(tpk::skinny_linear(X_shard, W_shard, static_cast<float*>(workspace), T, N, K_shard, K_shard,
                                            Y_partial, N, accumulate ? 1 : 0, s),
                         "tp_row_linear_partial");
     }
     return from_hip(tpk::gemm_bf16_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
-                                         accumulate ? 3 : 2, 0, s),
+                                         accumulate ? 3 : 2, 0, workspace, ws_bytes, s),
                     "tp_row_linear_partial");
 }
 
@@ -264,6 +271,10 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
         const size_t first = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu_partials_bytes(T, I_shard, H)
                                                    : tpk::skinny_partials_bytes(T, I_shard, H);
         const size_t second = tpk::skinny_partials_bytes(T, H, I_shard);
+        bytes += round_up(first > second ? first : second, WS_ALIGN);
+    } else {
+        const size_t first = tpk::gemm_bf16_split_bytes(T, I_shard, H, kind == TP_MLP_SWIGLU ? 1 : 0);
+        const size_t second = tpk::gemm_bf16_split_bytes(T, H, I_shard, 0);
         bytes += round_up(first > second ? first : second, WS_ALIGN);
     }
     return bytes;
@@ -319,13 +330,16 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
         return from_hip(tpk::skinny_linear(h, W_down, part, T, H, I_shard, I_shard, Y_partial, H, 0, s),
                         "tp_mlp_shard");
     }
+    void* split = c.take(0);
+    const size_t split_bytes = need - c.off;
     hipError_t e;
     if (kind == TP_MLP_SWIGLU)
-        e = tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I_shard, H, s);
+        e = tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I_shard, H, split, split_bytes, s);
     else
-        e = tpk::gemm_bf16_store(X, W_gate, h, T, I_shard, H, H, I_shard, I_shard, 0, 1, s);
+        e = tpk::gemm_bf16_store(X, W_gate, h, T, I_shard, H, H, I_shard, I_shard, 0, 1, split, split_bytes, s);
     if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
-    return from_hip(tpk::gemm_bf16_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0, s),
+    return from_hip(tpk::gemm_bf16_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0, split,
+                                         split_bytes, s),
                     "tp_mlp_shard");
 }
 
@@ -360,7 +374,8 @@ static tp_status check_attn_desc(const tp_attn_desc* d, bool* decode) {
 }
 
 static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, void** k,
-                      void** vt, void** rope, void** att, void** part, void** qbuf, void** scratch) {
+                      void** vt, void** rope, void** att, void** part, void** qbuf, void** scratch,
+                      size_t* split_bytes) {
     Carver c(base);
     const int64_t hq = d->n_q_heads, hkv = d->n_kv_heads;
     const int64_t nqkv = (hq + 2 * hkv) * 128;
@@ -371,12 +386,17 @@ static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, 
         *k = c.take((size_t)(T * hkv * 128) * 2);
         *vt = c.take((size_t)(T * hkv * 128) * 2);
         *att = c.take((size_t)(T * hq * 128) * 2);
+        const size_t s1 = tpk::gemm_bf16_split_bytes(T, nqkv, d->H, 0);
+        const size_t s2 = tpk::gemm_bf16_split_bytes(T, d->H, hq * 128, 0);
+        *split_bytes = s1 > s2 ? s1 : s2;
+        *part = c.take(*split_bytes);
         return c.off;
     }
     const int64_t B = d->B, L = d->cache_len + 1;
     const size_t p1 = tpk::skinny_partials_bytes(B, nqkv, d->H);
     const size_t p2 = tpk::skinny_partials_bytes(B, d->H, hq * 128);
-    *part = c.take(p1 > p2 ? p1 : p2);
+    *split_bytes = p1 > p2 ? p1 : p2;
+    *part = c.take(*split_bytes);
     *qbuf = c.take((size_t)(B * hq * 128) * 4);
     *scratch = c.take(tpk::decode_attn_scratch_bytes(B, (int)hq, L));
     *att = c.take((size_t)(B * hq * 128) * 2);
@@ -388,7 +408,8 @@ size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt) {
     bool decode = false;
     if (check_attn_desc(desc, &decode) != TP_OK) return 0;
     void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
-    return attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+    size_t split_bytes = 0;
+    return attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
 }
 
 tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float* Y_partial,
@@ -403,11 +424,12 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
     if (!aligned(X, 16) || !aligned(W_qkv, 16) || !aligned(W_o, 16) || !aligned(Y_partial, 16))
         return fail(TP_ERR_MISALIGNED, "tp_attn_shard: X, W_qkv, W_o and Y_partial must be 16-byte aligned");
     void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
-    const size_t need = attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+    size_t split_bytes = 0;
+    const size_t need = attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
     if (!workspace || ws_bytes < need)
         return fail(TP_ERR_WORKSPACE, "tp_attn_shard: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_attn_shard: workspace must be 16-byte aligned");
-    attn_ws(desc, decode, workspace, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch);
+    attn_ws(desc, decode, workspace, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
     hipStream_t s = as_stream(stream);
     const int hq = desc->n_q_heads, hkv = desc->n_kv_heads;
     const int64_t H = desc->H, dq = (int64_t)hq * 128;
@@ -416,11 +438,12 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
         hipError_t e = tpk::rope_table(static_cast<float2*>(rope), 0, desc->S, desc->rope_theta, s);
         if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
         tpk::QKVOut o{q, k, vt, static_cast<const float2*>(rope), desc->B, desc->S, hq, hkv};
-        e = tpk::gemm_bf16_qkv_rope(X, W_qkv, H, o, s);
+        e = tpk::gemm_bf16_qkv_rope(X, W_qkv, H, o, part, split_bytes, s);
         if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
         e = tpk::flash_attn_fwd(q, k, vt, att, desc->B, desc->S, hq, hkv, s);
         if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
-        return from_hip(tpk::gemm_bf16_store(att, W_o, Y_partial, T, H, dq, dq, H, H, 2, 0, s), "tp_attn_shard");
+        return from_hip(tpk::gemm_bf16_store(att, W_o, Y_partial, T, H, dq, dq, H, H, 2, 0, part, split_bytes, s),
+                        "tp_attn_shard");
     }
     const int64_t B = desc->B;
     hipError_t e = tpk::skinny_qkv_decode(X, W_qkv, static_cast<float*>(part), B, H, hq, hkv, desc->cache_len,

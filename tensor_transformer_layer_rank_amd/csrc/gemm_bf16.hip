@@ -280,27 +280,26 @@ template <int KIND, bool RELU>
 struct EpiStore {
     void* C;
     int64_t ldc, M, N;
-    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
-                               int lane) const {
+    // accumulator row block i (acc[i][0..3]) of wave (wm, wn)
+    __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
+                         int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t col = n0 + wn * 128 + j * 32 + r32;
             if (col >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                    if (row >= M) continue;
-                    float v = acc[i][j][r];
-                    if (RELU) v = v > 0.0f ? v : 0.0f;
-                    const int64_t off = row * ldc + col;
-                    if (KIND == 0) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v);
-                    else if (KIND == 1) static_cast<uint16_t*>(C)[off] = f32_to_f16(v);
-                    else if (KIND == 2) static_cast<float*>(C)[off] = v;
-                    else static_cast<float*>(C)[off] += v;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
+                if (row >= M) continue;
+                float v = a[j][r];
+                if (RELU) v = v > 0.0f ? v : 0.0f;
+                const int64_t off = row * ldc + col;
+                if (KIND == 0) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v);
+                else if (KIND == 1) static_cast<uint16_t*>(C)[off] = f32_to_f16(v);
+                else if (KIND == 2) static_cast<float*>(C)[off] = v;
+                else static_cast<float*>(C)[off] += v;
+            }
         }
     }
 };
@@ -308,23 +307,22 @@ struct EpiStore {
 struct EpiSwiGLU {
     uint16_t* h;   // [M, N] bf16
     int64_t M, N;
-    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
-                               int lane) const {
+    // acc[i][0..1] hold gate columns, acc[i][2..3] the matching up columns
+    __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
+                         int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t col = n0 + wn * 64 + j * 32 + r32;
             if (col >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                    if (row >= M) continue;
-                    const float gte = acc[i][j][r], up = acc[i][j + 2][r];
-                    const float silu = gte / (1.0f + __expf(-gte));
-                    h[row * N + col] = f32_to_bf16(silu * up);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
+                if (row >= M) continue;
+                const float gte = a[j][r], up = a[j + 2][r];
+                const float silu = gte / (1.0f + __expf(-gte));
+                h[row * N + col] = f32_to_bf16(silu * up);
+            }
         }
     }
 };
@@ -332,8 +330,8 @@ struct EpiSwiGLU {
 struct EpiQKV {
     QKVOut o;
     int64_t M;   // B*S
-    __device__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm, int wn,
-                               int lane) const {
+    __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
+                         int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
         const int head = (int)((n0 + wn * 128) >> 7);   // one wave = one head of 128 columns
         const int n_heads = o.hq + 2 * o.hkv;
@@ -345,48 +343,48 @@ struct EpiQKV {
             const int nh = is_q ? o.hq : o.hkv;
             uint16_t* dst = static_cast<uint16_t*>(is_q ? o.q : o.k);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
+                if (row >= M) continue;
+                const int64_t b = row / S, s = row - b * S;
+                uint16_t* out = dst + ((b * nh + hh) * S + s) * 128;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                    if (row >= M) continue;
-                    const int64_t b = row / S, s = row - b * S;
-                    uint16_t* out = dst + ((b * nh + hh) * S + s) * 128;
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int c = j * 32 + r32;               // pair (c, c + 64)
-                        const float2 cs = o.rope[s * 64 + c];
-                        const float x1 = acc[i][j][r], x2 = acc[i][j + 2][r];
-                        out[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
-                        out[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
-                    }
+                for (int j = 0; j < 2; ++j) {
+                    const int c = j * 32 + r32;               // pair (c, c + 64)
+                    const float2 cs = o.rope[s * 64 + c];
+                    const float x1 = a[j][r], x2 = a[j + 2][r];
+                    out[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
+                    out[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
                 }
+            }
         } else {
             const int hv = head - o.hq - o.hkv;
             uint16_t* vt = static_cast<uint16_t*>(o.vt);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
+                if (row >= M) continue;
+                const int64_t b = row / S, s = row - b * S;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                    if (row >= M) continue;
-                    const int64_t b = row / S, s = row - b * S;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int d = j * 32 + r32;
-                        vt[((b * o.hkv + hv) * 128 + d) * S + s] = f32_to_f16(acc[i][j][r]);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int d = j * 32 + r32;
+                    vt[((b * o.hkv + hv) * 128 + d) * S + s] = f32_to_f16(a[j][r]);
                 }
+            }
         }
     }
 };
 
-// Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8). Give XCD x
-// a contiguous range of logical tiles, ordered in groups of 4 row tiles (row fastest), so
-// the tiles resident on one XCD share 4 activation row blocks and few weight column blocks.
-__device__ __forceinline__ void map_tile(int bid, int G, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int x = bid & 7, idx = bid >> 3, q = G >> 3, rem = G & 7;
-    const int L = x * q + (x < rem ? x : rem) + idx;
+// the whole 128x128 accumulator of one wave through an epilogue
+template <class Epi>
+__device__ __forceinline__ void run_epilogue(const Epi& epi, f32x16 (&acc)[4][4], int64_t m0,
+                                             int64_t n0, int wm, int wn, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) epi.rows(acc[i], i, m0, n0, wm, wn, lane);
+}
+
+// Logical tile L -> (row tile, column tile): groups of 4 row tiles, row fastest.
+__device__ __forceinline__ void tile_of(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
     constexpr int GM = 4;
     const int group = L / (GM * tiles_n);
     const int first_m = group * GM;
@@ -394,6 +392,14 @@ __device__ __forceinline__ void map_tile(int bid, int G, int tiles_m, int tiles_
     const int r = L - group * GM * tiles_n;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8). Give XCD x a
+// contiguous range of the first G logical tiles, so the tiles resident on one XCD share 4
+// activation row blocks and few weight column blocks.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    const int x = bid & 7, idx = bid >> 3, q = G >> 3, rem = G & 7;
+    return x * q + (x < rem ? x : rem) + idx;
 }
 
 __device__ __forceinline__ bool k0_full(const GemmGeom& g, int64_t k0) { return k0 + BK <= g.K; }
@@ -425,8 +431,9 @@ __device__ __forceinline__ void publish(unsigned char* stage, int pending, const
 template <bool DUAL>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                        unsigned char* cur, unsigned char* nxt, int kt, int nk,
-                                       const DmaPlan& p, const GemmGeom& g, const uint16_t* a_base,
-                                       int64_t m0, int64_t n0, int wm, int wn, int wave, int lane) {
+                                       int64_t kbase, const DmaPlan& p, const GemmGeom& g,
+                                       const uint16_t* a_base, int64_t m0, int64_t n0, int wm, int wn,
+                                       int wave, int lane) {
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -439,15 +446,16 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     if (has_next) {
         // stages issued after kt+1 and still allowed in flight: kt+2, kt+3
         const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
-        publish(nxt, pending, g, (int64_t)(kt + 1) * BK, wave, lane);
+        publish(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
     // full refill steps interleave their DMA with the MFMAs; a partial final step takes
     // the general path up front
-    const bool inline_dma = refill && k0_full(g, (int64_t)(kt + 4) * BK);
-    if (refill && !inline_dma) issue_stage<DUAL>(cur, p, g, a_base, m0, n0, (int64_t)(kt + 4) * BK, wave, lane);
-    const uint16_t* a_k = a_base + (int64_t)(kt + 4) * BK;
-    const uint16_t* b_k = g.B1 + (int64_t)(kt + 4) * BK * g.ldb;
+    const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
+    const bool inline_dma = refill && k0_full(g, k_ref);
+    if (refill && !inline_dma) issue_stage<DUAL>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
+    const uint16_t* a_k = a_base + k_ref;
+    const uint16_t* b_k = g.B1 + k_ref * g.ldb;
     unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
     unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
@@ -460,9 +468,18 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     }
 }
 
+// Tail split: the first g_full tiles (one full round of the machine, or more) run whole;
+// each of the remaining tiles is cut into `pieces` K ranges of piece_steps K steps, one
+// workgroup each, whose accumulators go to `part` in register order; gemm_fixup_kernel then
+// sums a tile's pieces in piece order and runs the epilogue.
+struct SplitArgs {
+    int g_full, pieces, piece_steps;
+    float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
+};
+
 template <bool DUAL, class Epi>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi, int tiles_m,
-                                                            int tiles_n) {
+                                                            int tiles_n, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
@@ -470,11 +487,27 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi,
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
+    const int bid = (int)blockIdx.x;
+    int L, q = -1;
+    if (bid < sp.g_full) {
+        L = xcd_remap(bid, sp.g_full);
+    } else {
+        q = bid - sp.g_full;
+        L = sp.g_full + q / sp.pieces;
+    }
     int tm, tn;
-    map_tile((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_of(L, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * (DUAL ? BN / 2 : BN);
     const uint16_t* a_base = g.A + m0 * g.lda;
+    const int nk_total = (int)((g.K + BK - 1) / BK);
+    int64_t kbase = 0;
+    int nk = nk_total;
+    if (q >= 0) {
+        const int first = (q % sp.pieces) * sp.piece_steps;
+        kbase = (int64_t)first * BK;
+        nk = (nk_total - first < sp.piece_steps) ? nk_total - first : sp.piece_steps;
+    }
 
     DmaPlan p;
     make_plan<DUAL>(p, g, m0, n0, wave, lane);
@@ -487,38 +520,133 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (int)((g.K + BK - 1) / BK);
-    // prologue: steps 0..3 in flight, publish step 0
-    issue_stage<DUAL>(st0, p, g, a_base, m0, n0, 0, wave, lane);
-    if (nk > 1) issue_stage<DUAL>(st1, p, g, a_base, m0, n0, BK, wave, lane);
-    if (nk > 2) issue_stage<DUAL>(st2, p, g, a_base, m0, n0, 2 * BK, wave, lane);
-    if (nk > 3) issue_stage<DUAL>(st3, p, g, a_base, m0, n0, 3 * BK, wave, lane);
-    publish(st0, (nk - 1 < 3) ? nk - 1 : 3, g, 0, wave, lane);
+    if (nk > 0) {
+        // prologue: steps 0..3 in flight, publish step 0
+        issue_stage<DUAL>(st0, p, g, a_base, m0, n0, kbase, wave, lane);
+        if (nk > 1) issue_stage<DUAL>(st1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
+        if (nk > 2) issue_stage<DUAL>(st2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
+        if (nk > 3) issue_stage<DUAL>(st3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
+        publish(st0, (nk - 1 < 3) ? nk - 1 : 3, g, kbase, wave, lane);
 
-    Frags f0, f1;
-    read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
-    unsigned char* sa = st0;   // stage of step kt; sb, sc, sd hold steps kt+1, kt+2, kt+3
-    unsigned char* sb = st1;
-    unsigned char* sc = st2;
-    unsigned char* sd = st3;
-    for (int kt = 0; kt < nk; ++kt) {
-        k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, p, g, a_base, m0, n0, wm, wn, wave, lane);
-        unsigned char* t = sa;
-        sa = sb;
-        sb = sc;
-        sc = sd;
-        sd = t;
+        Frags f0, f1;
+        read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
+        unsigned char* sa = st0;   // stage of step kt; sb, sc, sd hold steps kt+1, kt+2, kt+3
+        unsigned char* sb = st1;
+        unsigned char* sc = st2;
+        unsigned char* sd = st3;
+        for (int kt = 0; kt < nk; ++kt) {
+            k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+            unsigned char* t = sa;
+            sa = sb;
+            sb = sc;
+            sc = sd;
+            sd = t;
+        }
     }
-    epi(acc, m0, n0, wm, wn, lane);
+    if (q < 0) {
+        run_epilogue(epi, acc, m0, n0, wm, wn, lane);
+        return;
+    }
+    float* dst = sp.part + ((int64_t)q * 4 + wave) * (256 * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[((i * 4 + j) * 16 + r) * 64] = acc[i][j][r];
 }
 
+// One wave per (split tile, wave of the tile, accumulator row block i): sum the tile's
+// pieces in piece order, then that row block's epilogue. 16 single-wave workgroups per tile
+// keep the partial reads spread over the machine.
 template <bool DUAL, class Epi>
-hipError_t launch(const GemmGeom& g, const Epi& epi, hipStream_t s, const char* name) {
-    const int64_t tiles_m = (g.M + BM - 1) / BM;
-    const int64_t tiles_n = (g.N + (DUAL ? BN / 2 : BN) - 1) / (DUAL ? BN / 2 : BN);
-    ProfScope ps(name, s);
-    gemm_bf16_kernel<DUAL, Epi><<<(unsigned)(tiles_m * tiles_n), NTHR, 0, s>>>(g, epi, (int)tiles_m,
-                                                                              (int)tiles_n);
+__global__ __launch_bounds__(64) void gemm_fixup_kernel(Epi epi, int tiles_m, int tiles_n,
+                                                        SplitArgs sp) {
+    const int lane = threadIdx.x;
+    const int t = (int)blockIdx.x >> 4, wave = ((int)blockIdx.x >> 2) & 3, i = (int)blockIdx.x & 3;
+    const int wm = wave & 1, wn = wave >> 1;
+    int tm, tn;
+    tile_of(sp.g_full + t, tiles_m, tiles_n, tm, tn);
+    f32x16 a[4];
+    const float* src = sp.part + ((int64_t)t * sp.pieces * 4 + wave) * (256 * 64) + i * (64 * 64) + lane;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[j][r] = src[(j * 16 + r) * 64];
+    for (int pc = 1; pc < sp.pieces; ++pc) {
+        const float* s2 = src + (int64_t)pc * 4 * (256 * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[j][r] += s2[(j * 16 + r) * 64];
+    }
+    epi.rows(a, i, (int64_t)tm * BM, (int64_t)tn * (DUAL ? BN / 2 : BN), wm, wn, lane);
+}
+
+int cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// How a grid of G tiles (nk K steps each) is cut: full tiles for whole rounds of the machine,
+// the rest split into pieces so that the last round is filled.
+SplitArgs plan_split(int64_t G, int nk, int n_cu) {
+    SplitArgs sp{(int)G, 1, nk, nullptr};
+    if (G <= n_cu) return sp;
+    const int64_t full = (G / n_cu) * n_cu;
+    const int64_t tail = G - full;
+    if (tail == 0) return sp;
+    int pieces = (int)(n_cu / tail);
+    if (pieces > 4) pieces = 4;
+    if (pieces < 2 || nk < 2 * pieces) return sp;
+    sp.g_full = (int)full;
+    sp.pieces = pieces;
+    sp.piece_steps = (nk + pieces - 1) / pieces;
+    return sp;
+}
+
+template <bool DUAL>
+void tiles_of(const GemmGeom& g, int64_t& tiles_m, int64_t& tiles_n) {
+    tiles_m = (g.M + BM - 1) / BM;
+    tiles_n = (g.N + (DUAL ? BN / 2 : BN) - 1) / (DUAL ? BN / 2 : BN);
+}
+
+template <bool DUAL>
+size_t split_bytes(const GemmGeom& g) {
+    int64_t tm, tn;
+    tiles_of<DUAL>(g, tm, tn);
+    const SplitArgs sp = plan_split(tm * tn, (int)((g.K + BK - 1) / BK), cu_count());
+    if (sp.pieces < 2) return 0;
+    return (size_t)(tm * tn - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
+}
+
+// ws may be NULL (or too small): the tiles then all run whole
+template <bool DUAL, class Epi>
+hipError_t launch(const GemmGeom& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
+                  const char* name) {
+    int64_t tiles_m, tiles_n;
+    tiles_of<DUAL>(g, tiles_m, tiles_n);
+    const int64_t G = tiles_m * tiles_n;
+    SplitArgs sp = plan_split(G, (int)((g.K + BK - 1) / BK), cu_count());
+    const size_t need = sp.pieces >= 2 ? (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float) : 0;
+    if (sp.pieces >= 2 && (!ws || ws_bytes < need)) sp = SplitArgs{(int)G, 1, (int)((g.K + BK - 1) / BK), nullptr};
+    sp.part = static_cast<float*>(ws);
+    const int64_t blocks = sp.pieces >= 2 ? sp.g_full + (G - sp.g_full) * sp.pieces : G;
+    {
+        ProfScope ps(name, s);
+        gemm_bf16_kernel<DUAL, Epi><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || sp.pieces < 2) return e;
+    }
+    ProfScope ps(DUAL ? "fixup_swiglu" : "fixup_gemm", s);
+    gemm_fixup_kernel<DUAL, Epi><<<(unsigned)((G - sp.g_full) * 16), 64, 0, s>>>(epi, (int)tiles_m, (int)tiles_n, sp);
     return hipGetLastError();
 }
 
@@ -534,14 +662,19 @@ __global__ void rope_table_kernel(float2* t, int64_t pos0, int64_t npos, double 
 
 }  // namespace
 
+size_t gemm_bf16_split_bytes(int64_t M, int64_t N, int64_t K, int dual) {
+    GemmGeom g{nullptr, nullptr, nullptr, M, N, K, K, N};
+    return dual ? split_bytes<true>(g) : split_bytes<false>(g);
+}
+
 hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
-                           int relu, hipStream_t s) {
+                           int relu, void* ws, size_t ws_bytes, hipStream_t s) {
     GemmGeom g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), nullptr,
                M, N, K, lda, ldb};
 #define TP_STORE_CASE(KIND, RELU)                                                   \
     if (out_kind == KIND && (relu != 0) == RELU)                                    \
-        return launch<false>(g, EpiStore<KIND, RELU>{C, ldc, M, N}, s,              \
+        return launch<false>(g, EpiStore<KIND, RELU>{C, ldc, M, N}, ws, ws_bytes, s, \
                              KIND >= 2 ? "gemm_bf16_f32out" : "gemm_bf16_store");
     TP_STORE_CASE(0, false)
     TP_STORE_CASE(0, true)
@@ -555,18 +688,18 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
 }
 
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
-                            int64_t N, int64_t K, hipStream_t s) {
+                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
     GemmGeom g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg),
                static_cast<const uint16_t*>(Bu), M, N, K, K, N};
-    return launch<true>(g, EpiSwiGLU{static_cast<uint16_t*>(h), M, N}, s, "gemm_bf16_swiglu");
+    return launch<true>(g, EpiSwiGLU{static_cast<uint16_t*>(h), M, N}, ws, ws_bytes, s, "gemm_bf16_swiglu");
 }
 
 hipError_t gemm_bf16_qkv_rope(const void* X, const void* Wqkv, int64_t H, const QKVOut& o,
-                              hipStream_t s) {
+                              void* ws, size_t ws_bytes, hipStream_t s) {
     const int64_t M = o.B * o.S, N = (int64_t)(o.hq + 2 * o.hkv) * 128;
     GemmGeom g{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wqkv), nullptr,
                M, N, H, H, N};
-    return launch<false>(g, EpiQKV{o, M}, s, "gemm_bf16_qkv_rope");
+    return launch<false>(g, EpiQKV{o, M}, ws, ws_bytes, s, "gemm_bf16_qkv_rope");
 }
 
 hipError_t rope_table(float2* table, int64_t pos0, int64_t npos, float theta, hipStream_t s) {

@@ -29,13 +29,17 @@ hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t
                     hipStream_t s);
 
 // ---- bf16 MFMA path -----------------------------------------------------------------
+// Workspace that lets the tiles past the last full round of the machine be split along K
+// (0 when the grid needs no split). Every call below accepts ws = NULL / too small: the
+// tiles then all run whole.
+size_t gemm_bf16_split_bytes(int64_t M, int64_t N, int64_t K, int dual);
 // out_kind for gemm_bf16_store: 0 = bf16, 1 = fp16, 2 = fp32 (overwrite), 3 = fp32 (+=)
 hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
-                           int relu, hipStream_t s);
+                           int relu, void* ws, size_t ws_bytes, hipStream_t s);
 // h[M, N] (bf16, ld = N) = SiLU(A . Bg) * (A . Bu)
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
-                            int64_t N, int64_t K, hipStream_t s);
+                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 
 // QKV projection of a prefill with rotary embedding and head-major scatter.
 struct QKVOut {
@@ -47,7 +51,7 @@ struct QKVOut {
     int hq, hkv;
 };
 hipError_t gemm_bf16_qkv_rope(const void* X, const void* Wqkv, int64_t H, const QKVOut& o,
-                              hipStream_t s);
+                              void* ws, size_t ws_bytes, hipStream_t s);
 // rotary table [npos, 64] of (cos, sin) of (pos0 + p) * theta^(-2i/128), computed in fp64
 hipError_t rope_table(float2* table, int64_t pos0, int64_t npos, float theta, hipStream_t s);
 

@@ -170,6 +170,55 @@ def test_row_partials_sum_to_unsharded_layer(tp):
     assert_close_bf16(host(Y), O.linear(X, W), "sum of row partials")
 
 
+# Grids past one round of the 256 compute units: the tiles after the last full round are
+# cut along K into 4 (272 tiles), 3 (336 tiles) or 2 (352 tiles) pieces whose fp32 partials
+# a fix-up pass sums; ragged M, N and K so that the last piece holds the K tail.
+@pytest.mark.parametrize("T,K,N,out", [(4200, 296, 4096, "bf16"), (5376, 200, 4096, "f32"),
+                                       (5632, 136, 4096, "bf16"), (4100, 1000, 4000, "f32")])
+def test_column_linear_tail_split(tp, T, K, N, out):
+    import torch
+    rng = np.random.default_rng(T + K)
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    assert tp.linear_workspace_size(T, K, N, tp.TP_BF16) > 0, "expected a split grid"
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[out]
+    Y = tp.column_linear(dev(X), dev(W), Y=_nan((T, N), dt))
+    Y2 = tp.column_linear(dev(X), dev(W), out_dtype=dt)
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.array_equal(y, host(Y2)), "split launches differ bitwise"
+    assert_close_bf16(y, O.linear(X, W), f"split column {T}x{K}x{N}", out=out)
+
+
+def test_row_linear_partial_tail_split_accumulate(tp):
+    import torch
+    rng = np.random.default_rng(77)
+    T, K, N = 4100, 1000, 4000
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    P = tp.row_linear_partial(dev(X), dev(W), Y=_nan((T, N), torch.float32))
+    tp.row_linear_partial(dev(X), dev(W), Y=P, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(P), 2 * O.linear(X, W), "split row partial accumulate")
+
+
+@pytest.mark.parametrize("kind", ["swiglu", "relu"])
+def test_mlp_tail_split(tp, kind):
+    import torch
+    T, H, I = 4200, 296, 2048
+    inp = wl.random_mlp(41, T, H, I)
+    if kind == "swiglu":
+        Y = tp.mlp_shard(dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down),
+                         Y=_nan((T, H), torch.float32))
+        ref = O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down)
+    else:
+        Y = tp.mlp_shard(dev(inp.X), dev(inp.W_gate), None, dev(inp.W_down), kind=tp.TP_MLP_RELU,
+                         Y=_nan((T, H), torch.float32))
+        ref = O.mlp_relu_shard(inp.X, inp.W_gate, inp.W_down)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), ref, f"split mlp {kind}")
+
+
 # ---------------------------------------------------------------- MLP shard
 
 @pytest.mark.parametrize("T,H,I", [(300, 256, 200), (520, 512, 264), (32, 512, 136), (7, 256, 64)])
