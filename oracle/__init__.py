@@ -18,11 +18,18 @@ Every function is the plain definition of what a rank computes, in float64 NumPy
   切分"), the vocabulary-split output layer ("输入与输出层").
 * "TensorRT LLM 中的并行策略", "注意力模块": heads split evenly; KV shared by
   grouped query heads.
+* ``fp8_ref``: the same layers on OCP E4M3 operands with per-tensor scales (the pages
+  name no number format; the format's own definition is restated there).
 
 Parity status per function (pins live in ``tests/test_oracle_pins.py``):
-all functions are pinned except the rotary-embedding *convention* (rotate-half
+all functions are pinned (the E4M3 table and rounding against torch's float8_e4m3fn
+conversion and a bit-by-bit construction; the fp8 layers against pure-Python loops)
+except the rotary-embedding *convention* (rotate-half
 pairs (i, i+d/2), frequency theta^(-2i/d)), which the pages never state: its
 closed-form properties are pinned, the choice of convention is "parity unpinned".
 """
 from .tp_ref import *  # noqa: F401,F403
-from .tp_ref import __all__  # noqa: F401
+from .fp8_ref import *  # noqa: F401,F403
+from . import tp_ref as _tp, fp8_ref as _f8
+
+__all__ = list(_tp.__all__) + list(_f8.__all__)

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import math
 
-__all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row"]
+__all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row", "e4m3_to_float", "fp8_matmul"]
 
 
 def matmul(X, W):
@@ -78,3 +78,26 @@ def attention_head(q, k, v, causal=True):
             row.append(acc / z)
         out.append(row)
     return out
+
+
+def e4m3_to_float(code):
+    """Value of an OCP E4M3 code, built bit by bit: the 3 mantissa bits are the binary
+    fraction after the leading 1 (0 for exponent field 0), scaled by 2^(field - 7)
+    (2^-6 for field 0); field 15 with mantissa 7 is NaN."""
+    code &= 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    field = (code >> 3) & 0xF
+    bits = [(code >> 2) & 1, (code >> 1) & 1, code & 1]
+    if field == 15 and bits == [1, 1, 1]:
+        return float("nan")
+    frac = sum(b * 0.5 ** (i + 1) for i, b in enumerate(bits))
+    lead = 1.0 if field else 0.0
+    power = field - 7 if field else -6
+    return sign * (lead + frac) * 2.0 ** power
+
+
+def fp8_matmul(Xc, x_scale, Wc, w_scale):
+    """Element by element: sum_k value(X[i][k]) * value(W[k][j]), times both scales."""
+    X = [[e4m3_to_float(c) for c in row] for row in Xc]
+    W = [[e4m3_to_float(c) for c in row] for row in Wc]
+    return [[v * x_scale * w_scale for v in row] for row in matmul(X, W)]

@@ -402,3 +402,121 @@ def test_softmax_is_shift_invariant_at_large_scores():
     p = O.softmax_rows(np.array([[1000.0, 1001.0]]))
     s = 1.0 / (1.0 + math.exp(-1.0))
     np.testing.assert_allclose(p[0], [1.0 - s, s], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- fp8 (OCP E4M3) operands
+
+def test_e4m3_table_matches_library_and_brute_force():
+    """All 256 codes: the oracle's table equals torch's float8_e4m3fn decoding and the
+    bit-by-bit construction (NaN exactly at 0x7F and 0xFF)."""
+    import torch
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t = O.e4m3_table()
+    bf = np.array([brute.e4m3_to_float(c) for c in range(256)])
+    assert np.array_equal(np.isnan(t), np.isnan(lib)) and np.array_equal(np.isnan(t), np.isnan(bf))
+    assert np.flatnonzero(np.isnan(t)).tolist() == [0x7F, 0xFF]
+    ok = ~np.isnan(t)
+    assert np.array_equal(t[ok], lib[ok]) and np.array_equal(t[ok], bf[ok])
+
+
+def test_e4m3_closed_forms():
+    t = O.e4m3_table()
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0          # largest finite
+    assert t[0x08] == 2.0 ** -6                            # smallest normal
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9   # subnormals
+    assert t[0x38] == 1.0 and t[0xC0] == -2.0 and t[0x00] == 0.0
+    assert np.signbit(t[0x80]) and t[0x80] == 0.0
+    assert np.all(np.diff(t[:0x7F]) > 0)                   # positive codes are ordered
+
+
+def test_e4m3_quantize_matches_library_in_range():
+    """Round-to-nearest-even against torch's conversion, over values inside +-448."""
+    import torch
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(100000) * np.exp2(rng.integers(-12, 9, 100000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_quantize(x), lib)
+
+
+def test_e4m3_quantize_ties_saturation_and_specials():
+    q = O.e4m3_quantize
+    # exact midpoints go to the even mantissa
+    assert q([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10]).tolist() == [0x38, 0x3A, 0x00, 0x02]
+    assert q([448.0, 449.0, 500.0, 1e30, -1e30]).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    assert q([float("nan"), -0.0, 0.0]).tolist() == [0x7F, 0x80, 0x00]
+    # every finite code round-trips
+    t = O.e4m3_table()
+    codes = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    assert np.array_equal(q(t[codes]), codes)
+
+
+def test_e4m3_quantize_is_nearest():
+    """|value(q(x)) - x| is no larger than the distance to either neighbouring code."""
+    rng = np.random.default_rng(9)
+    x = rng.uniform(-448, 448, 20000) * np.exp2(rng.integers(-14, 0, 20000))
+    v = O.e4m3_decode(O.e4m3_quantize(x))
+    pos = O.e4m3_table()[:0x7F]
+    a = np.abs(x)
+    best = np.min(np.abs(pos[None, :] - a[:, None]), axis=1)
+    assert np.array_equal(np.abs(np.abs(v) - a), best)
+    assert np.array_equal(np.signbit(v), np.signbit(x))
+
+
+def test_fp8_linear_matches_brute_force():
+    rng = np.random.default_rng(10)
+    Xc = rng.integers(0, 256, (3, 7)).astype(np.uint8)
+    Wc = rng.integers(0, 256, (7, 5)).astype(np.uint8)
+    Xc[Xc & 0x7F == 0x7F] = 0x12            # keep NaN codes out
+    Wc[Wc & 0x7F == 0x7F] = 0x33
+    got = O.fp8_linear(Xc, 0.5, Wc, 0.25)
+    ref = brute.fp8_matmul(Xc.tolist(), 0.5, Wc.tolist(), 0.25)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_integer_codes_are_exact():
+    """Small integers are exact E4M3 values, so an fp8 layer on them is an integer product."""
+    rng = np.random.default_rng(11)
+    X = wl.int_matrix(rng, (9, 16))
+    W = wl.int_matrix(rng, (16, 12))
+    Xc, Wc = O.e4m3_quantize(X), O.e4m3_quantize(W)
+    assert np.array_equal(O.e4m3_decode(Xc), X)
+    assert np.array_equal(O.fp8_column_linear(Xc, 1.0, Wc, 1.0, "relu"), np.maximum(X.astype(np.float64) @ W, 0))
+    assert np.array_equal(O.fp8_row_linear_partial(Xc, 2.0, Wc, 0.5), X.astype(np.float64) @ W)
+
+
+def test_fp8_mlp_against_brute_force_and_h_codes():
+    inp = wl.random_mlp_fp8(12, 4, 32, 8, h_scale=0.125)
+    got = O.fp8_mlp_shard(inp.X, inp.x_scale, inp.W_gate, inp.wg_scale, inp.W_up, inp.wu_scale,
+                          inp.W_down, inp.wd_scale, inp.h_scale)
+    g = brute.fp8_matmul(inp.X.tolist(), inp.x_scale, inp.W_gate.tolist(), inp.wg_scale)
+    u = brute.fp8_matmul(inp.X.tolist(), inp.x_scale, inp.W_up.tolist(), inp.wu_scale)
+    h = [[a * b for a, b in zip(rg, ru)] for rg, ru in zip(brute.silu(g), u)]
+    # h / h_scale in fp32, then the nearest code by exhaustive search (ties: even code)
+    finite = [(c, brute.e4m3_to_float(c)) for c in range(256) if not math.isnan(brute.e4m3_to_float(c))]
+    hc = []
+    for row in h:
+        out = []
+        for v in row:
+            q = float(np.float32(np.float32(v) / np.float32(inp.h_scale)))
+            q = max(-448.0, min(448.0, q))
+            best = min(finite, key=lambda cv: (abs(cv[1] - q), cv[0] & 1, cv[0] if q >= 0 else -cv[0]))
+            out.append(best[0])
+        hc.append(out)
+    ref = brute.fp8_matmul(hc, inp.h_scale, inp.W_down.tolist(), inp.wd_scale)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-12, atol=1e-12)
+    # relu form: h = relu(X W1)
+    got_r = O.fp8_mlp_shard(inp.X, inp.x_scale, inp.W_gate, inp.wg_scale, None, 1.0,
+                            inp.W_down, inp.wd_scale, inp.h_scale, kind="relu")
+    hr = O.fp8_quantize_h(np.maximum(np.array(g), 0), inp.h_scale)
+    np.testing.assert_allclose(got_r, O.fp8_linear(hr, inp.h_scale, inp.W_down, inp.wd_scale), rtol=1e-12)
+
+
+def test_fp8_workload_codes_and_scales():
+    inp = wl.random_mlp_fp8(13, 64, 128, 96)
+    for codes, scale in ((inp.X, inp.x_scale), (inp.W_gate, inp.wg_scale), (inp.W_down, inp.wd_scale)):
+        assert codes.dtype == np.uint8
+        v = O.e4m3_decode(codes)
+        assert np.all(np.isfinite(v)) and np.max(np.abs(v)) <= 448.0
+        assert np.max(np.abs(v)) >= 400.0            # scale = amax / 448 uses the range
+        assert scale > 0

@@ -20,6 +20,10 @@ the order the fields are listed):
 * ``decode7b_tp2``  (seed 4): X[32,4096]; Wqkv [4096, 3*2048], Wo [2048,4096],
   Wg, Wu [4096,5504], Wd [5504,4096], Wlm [4096,16000]; K and V caches
   [32,16,1025,128] whose first 1024 positions are N(0,1) (post-rotation keys). bf16.
+* ``mlp7b_tp4_fp8`` (seed 5): the shapes and distributions of ``mlp7b_tp4`` stored as
+  OCP E4M3 codes: each tensor is drawn in fp32, given the per-tensor scale
+  amax / 448 (fp32), and each draw / scale is rounded to the nearest E4M3 value
+  (ties to even). The intermediate h of the MLP gets the static scale 1/8.
 
 "N(0, 0.02)" is read as standard deviation 0.02.
 """
@@ -33,6 +37,7 @@ __all__ = [
     "bf16_round", "bf16_bits", "bits_to_f32", "MLPInputs", "AttnInputs", "DecodeInputs",
     "mlp_relu_tp2", "mlp7b_tp4", "attn7b_tp4", "layer70b_tp8", "decode7b_tp2",
     "random_mlp", "random_attn", "random_decode", "int_matrix", "WORKLOADS",
+    "e4m3_codes", "FP8MLPInputs", "random_mlp_fp8", "mlp7b_tp4_fp8",
 ]
 
 
@@ -56,6 +61,32 @@ def bits_to_f32(b: np.ndarray) -> np.ndarray:
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """float32 array whose values are exactly the bf16 (RNE) roundings of ``x``."""
     return bits_to_f32(bf16_bits(x))
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no
+    infinities): nearest value, ties to even, magnitudes past 448 saturated; uint8 codes.
+
+    Input preparation for fp8 workloads: each value is rounded once to the grid of its
+    binade (spacing 2^(e-3) for |x| in [2^e, 2^(e+1)), e >= -6; spacing 2^-9 below 2^-6).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.exp2(e - 3)
+    r = np.round(a / step) * step            # numpy rounds halves to even
+    r = np.minimum(r, 448.0)
+    # fields of the rounded magnitude
+    with np.errstate(divide="ignore"):
+        er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    exp_field = np.where(normal, er + 7, 0)
+    man_field = np.where(normal, r / np.exp2(er) * 8 - 8, r * 2.0 ** 9)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(man_field).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return code.astype(np.uint8)
 
 
 def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
@@ -214,10 +245,58 @@ def decode7b_tp2(seed: int = 4) -> DecodeInputs:
     return random_decode(seed, 32, 4096, 16, 16, 5504, 16000, 1024, 1025, name="decode7b_tp2")
 
 
+@dataclass
+class FP8MLPInputs:
+    """An MLP shard whose X and weights are E4M3 codes (uint8) with fp32 per-tensor scales."""
+    name: str
+    X: np.ndarray                  # [T, H] uint8
+    x_scale: float
+    W_gate: np.ndarray             # [H, I] uint8
+    wg_scale: float
+    W_up: np.ndarray               # [H, I] uint8
+    wu_scale: float
+    W_down: np.ndarray             # [I, H] uint8
+    wd_scale: float
+    h_scale: float                 # static scale of the intermediate h
+
+    @property
+    def T(self): return self.X.shape[0]
+
+    @property
+    def H(self): return self.X.shape[1]
+
+    @property
+    def I(self): return self.W_gate.shape[1]
+
+
+def _fp8_tensor(rng: np.random.Generator, shape, std: float):
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    scale = np.float32(np.max(np.abs(a)) / np.float32(448.0))
+    return e4m3_codes(a / scale), float(scale)
+
+
+def random_mlp_fp8(seed: int, T: int, H: int, I: int, name: str = "mlp_fp8",
+                   h_scale: float = 0.125) -> FP8MLPInputs:
+    rng = np.random.default_rng(seed)
+    X, xs = _fp8_tensor(rng, (T, H), 1.0)
+    Wg, gs = _fp8_tensor(rng, (H, I), 0.02)
+    Wu, us = _fp8_tensor(rng, (H, I), 0.02)
+    Wd, ds = _fp8_tensor(rng, (I, H), 0.02)
+    return FP8MLPInputs(name, X, xs, Wg, gs, Wu, us, Wd, ds, h_scale)
+
+
+def mlp7b_tp4_fp8(seed: int = 5) -> FP8MLPInputs:
+    """mlp7b_tp4's shapes as E4M3 codes: X[4096,4096], gate/up [4096,2752], down [2752,4096]."""
+    return random_mlp_fp8(seed, 4096, 4096, 2752, "mlp7b_tp4_fp8")
+
+
 WORKLOADS = {
     "mlp_relu_tp2": mlp_relu_tp2,
     "mlp7b_tp4": mlp7b_tp4,
     "attn7b_tp4": attn7b_tp4,
     "layer70b_tp8": layer70b_tp8,
     "decode7b_tp2": decode7b_tp2,
+    "mlp7b_tp4_fp8": mlp7b_tp4_fp8,
 }
