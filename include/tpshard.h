@@ -31,6 +31,9 @@
  *   - fp32 path: any positive sizes, 4-byte aligned pointers.
  *     bf16/fp16 path: 16-byte aligned base pointers; K, N and leading dimensions
  *     multiples of 8 elements. Tails of T and N inside a tile are masked.
+ *     fp8 path (TP_FP8_E4M3, OCP E4M3 codes, one byte each, with fp32 per-tensor
+ *     scales): 16-byte aligned base pointers; K and N multiples of 16. The pages
+ *     name no number format; E4M3 is an extension of the same layers.
  *   - Results do not depend on launch timing: repeated calls give bitwise-equal
  *     outputs (no floating-point atomics).
  */
@@ -61,8 +64,10 @@ typedef enum { TP_F32 = 0, TP_BF16 = 1, TP_F16 = 2, TP_FP8_E4M3 = 3 } tp_dtype;
 typedef enum { TP_ACT_NONE = 0, TP_ACT_RELU = 1 } tp_act;
 typedef enum { TP_MLP_RELU = 0, TP_MLP_SWIGLU = 1 } tp_mlp_kind;
 
-/* Per-tensor dequantisation scales for TP_FP8_E4M3 operands (OCP E4M3):
- * real value = code_value * scale. Only read when in_dt == TP_FP8_E4M3. */
+/* Per-tensor dequantisation scales for TP_FP8_E4M3 operands (OCP E4M3: sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest
+ * magnitude 448): real value = code_value * scale. Required (non-NULL) when
+ * in_dt == TP_FP8_E4M3, ignored otherwise. */
 typedef struct { float x_scale; float w_scale; } tp_fp8_scales;
 
 /*
@@ -77,7 +82,9 @@ typedef struct { float x_scale; float w_scale; } tp_fp8_scales;
  *                                   rank write its slice of a full [T, N*tp] buffer
  *                                   (the concatenation happens in place).
  *   in_dt/out_dt: (F32, F32) — exact fp32 path; (BF16, BF16|F16|F32);
- *                 (FP8_E4M3, BF16|F32) with scales q.
+ *                 (FP8_E4M3, BF16|F16|F32) with scales q: Y = act(x_scale * w_scale *
+ *                 (codes(X) . codes(W))), accumulated in fp32.
+ *   workspace: >= tp_linear_workspace_size(T, K, N, in_dt) bytes.
  *   act: TP_ACT_NONE or TP_ACT_RELU (applied in fp32 before the output rounding).
  */
 tp_status tp_column_linear(const void* X, const void* W_shard, void* Y,
@@ -93,7 +100,8 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y,
  *   X_shard [T, K_shard] in_dt      this rank's slice of the input features
  *   W_shard [K_shard, N] in_dt      this rank's rows of the full weight
  *   Y_partial [T, N] fp32           overwritten, or += when accumulate != 0
- *   in_dt: F32 (exact path), BF16, or FP8_E4M3 with scales q.
+ *   in_dt: F32 (exact path), BF16, or FP8_E4M3 with scales q (P = x_scale * w_scale *
+ *          (codes(X_shard) . codes(W_shard)), fp32 accumulation).
  *   workspace: >= tp_linear_workspace_size(T, K_shard, N, in_dt) bytes (both calls).
  */
 tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float* Y_partial,
@@ -134,6 +142,29 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up,
                        void* workspace, size_t ws_bytes, void* stream);
 size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
                              tp_dtype in_dt, tp_dtype h_dt);
+
+/*
+ * tp_mlp_shard_fp8 — tp_mlp_shard on OCP E4M3 operands with per-tensor scales. The
+ *   activated intermediate h is itself stored as E4M3 codes with the static scale
+ *   h_scale (the down projection's input must be fp8 too):
+ *     g = x_scale*wg_scale * (X . W_gate),  u = x_scale*wu_scale * (X . W_up)   (fp32)
+ *     h = SiLU(g) * u   (TP_MLP_SWIGLU)   or   relu(g)   (TP_MLP_RELU, W_up NULL)
+ *     code(h) = nearest E4M3 value to h / h_scale (fp32 division; ties to even;
+ *               magnitudes past 448 saturate to +-448)
+ *     P = h_scale*wd_scale * (code(h) . W_down)   fp32, overwritten
+ *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: E4M3 codes.
+ *   Requires H and I_shard multiples of 16 and 16-byte aligned pointers.
+ *   workspace >= tp_mlp_fp8_workspace_size(T, H, I_shard, kind) bytes, 16-byte aligned.
+ */
+typedef struct {
+    float x_scale, w_gate_scale, w_up_scale, w_down_scale, h_scale;
+} tp_fp8_mlp_scales;
+tp_status tp_mlp_shard_fp8(const void* X, const void* W_gate, const void* W_up,
+                           const void* W_down, float* Y_partial,
+                           int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                           const tp_fp8_mlp_scales* q,
+                           void* workspace, size_t ws_bytes, void* stream);
+size_t tp_mlp_fp8_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind);
 
 /*
  * tp_attn_desc — shapes of one rank's attention shard (all head counts are the

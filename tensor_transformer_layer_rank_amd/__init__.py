@@ -16,7 +16,8 @@ import os
 __all__ = [
     "TpError", "lib", "load", "LIB_PATH", "column_linear", "row_linear_partial", "mlp_shard",
     "attn_shard", "partial_sum", "linear_workspace_size", "mlp_workspace_size",
-    "attn_workspace_size", "AttnDesc", "profile_enable", "profile_reset", "profile_read",
+    "attn_workspace_size", "mlp_shard_fp8", "mlp_fp8_workspace_size", "AttnDesc",
+    "profile_enable", "profile_reset", "profile_read",
     "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
     "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
 ]
@@ -33,7 +34,7 @@ EXPORTS = [
     "tp_column_linear", "tp_row_linear_partial", "tp_linear_workspace_size", "tp_mlp_shard",
     "tp_mlp_workspace_size", "tp_attn_shard", "tp_attn_workspace_size", "tp_partial_sum",
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
-    "tp_profile_read", "tp_profile_reset",
+    "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
 ]
 
 
@@ -56,6 +57,12 @@ class AttnDesc(ctypes.Structure):
 
 class Fp8Scales(ctypes.Structure):
     _fields_ = [("x_scale", ctypes.c_float), ("w_scale", ctypes.c_float)]
+
+
+class Fp8MlpScales(ctypes.Structure):
+    _fields_ = [("x_scale", ctypes.c_float), ("w_gate_scale", ctypes.c_float),
+                ("w_up_scale", ctypes.c_float), ("w_down_scale", ctypes.c_float),
+                ("h_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -87,6 +94,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tp_profile_enable": ([ctypes.c_int], _I32),
         "tp_profile_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I32),
         "tp_profile_reset": ([], _I32),
+        "tp_mlp_shard_fp8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(Fp8MlpScales),
+                              _P, _SZ, _P], _I32),
+        "tp_mlp_fp8_workspace_size": ([_I64, _I64, _I64, _I32], _SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -108,8 +118,10 @@ def _check(st: int):
 # --- tensor helpers -------------------------------------------------------------------------
 
 def _dt(t) -> int:
+    """tp_dtype of a tensor; uint8 and float8_e4m3fn tensors hold OCP E4M3 codes."""
     import torch
-    m = {torch.float32: TP_F32, torch.bfloat16: TP_BF16, torch.float16: TP_F16}
+    m = {torch.float32: TP_F32, torch.bfloat16: TP_BF16, torch.float16: TP_F16,
+         torch.uint8: TP_FP8_E4M3, torch.float8_e4m3fn: TP_FP8_E4M3}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -148,25 +160,38 @@ def linear_workspace_size(T: int, K: int, N: int, in_dt: int) -> int:
     return int(lib().tp_linear_workspace_size(T, K, N, in_dt))
 
 
+def _scales(X, scales):
+    """Fp8Scales for E4M3 operands (scales = (x_scale, w_scale)), else None."""
+    if _dt(X) != TP_FP8_E4M3:
+        return None
+    if scales is None:
+        raise ValueError("fp8 operands need scales=(x_scale, w_scale)")
+    return ctypes.byref(Fp8Scales(float(scales[0]), float(scales[1])))
+
+
 def column_linear(X, W, Y=None, act: int = TP_ACT_NONE, out_dtype=None, ldy: int | None = None,
-                  workspace=None, stream=None):
-    """Y = act(X @ W) for this rank's column shard W [K, N]; returns Y ([T, ldy] if given)."""
+                  scales=None, workspace=None, stream=None):
+    """Y = act(X @ W) for this rank's column shard W [K, N]; returns Y ([T, ldy] if given).
+    E4M3 operands (uint8 codes) take scales=(x_scale, w_scale); their output defaults to bf16."""
     import torch
     T, K = X.shape
     K2, N = W.shape
     if K2 != K:
         raise ValueError(f"X is [*, {K}] but W is [{K2}, *]")
     if Y is None:
-        Y = torch.empty((T, N), dtype=out_dtype or X.dtype, device=X.device)
+        default = torch.bfloat16 if _dt(X) == TP_FP8_E4M3 else X.dtype
+        Y = torch.empty((T, N), dtype=out_dtype or default, device=X.device)
     ldy = ldy if ldy is not None else Y.shape[-1]
+    q = _scales(X, scales)
     ws, wsb = _workspace(linear_workspace_size(T, K, N, _dt(X)), X.device, workspace)
     _check(lib().tp_column_linear(_ptr(X), _ptr(W), ctypes.c_void_p(Y.data_ptr()), T, K, N, ldy,
-                                  _dt(X), _dt(Y), act, None, _ptr(ws), wsb, _stream(stream)))
+                                  _dt(X), _dt(Y), act, q, _ptr(ws), wsb, _stream(stream)))
     return Y
 
 
-def row_linear_partial(X, W, Y=None, accumulate: bool = False, workspace=None, stream=None):
-    """fp32 partial X_shard @ W_shard [K_shard, N] of a row-parallel layer."""
+def row_linear_partial(X, W, Y=None, accumulate: bool = False, scales=None, workspace=None, stream=None):
+    """fp32 partial X_shard @ W_shard [K_shard, N] of a row-parallel layer (E4M3 operands:
+    scales=(x_scale, w_scale))."""
     import torch
     T, K = X.shape
     K2, N = W.shape
@@ -174,9 +199,10 @@ def row_linear_partial(X, W, Y=None, accumulate: bool = False, workspace=None, s
         raise ValueError(f"X is [*, {K}] but W is [{K2}, *]")
     if Y is None:
         Y = torch.empty((T, N), dtype=torch.float32, device=X.device)
+    q = _scales(X, scales)
     ws, wsb = _workspace(linear_workspace_size(T, K, N, _dt(X)), X.device, workspace)
     _check(lib().tp_row_linear_partial(_ptr(X), _ptr(W), _ptr(Y), T, K, N, _dt(X), int(accumulate),
-                                       None, _ptr(ws), wsb, _stream(stream)))
+                                       q, _ptr(ws), wsb, _stream(stream)))
     return Y
 
 
@@ -196,6 +222,26 @@ def mlp_shard(X, W_gate, W_up, W_down, Y=None, kind: int = TP_MLP_SWIGLU, worksp
     ws, wsb = _workspace(mlp_workspace_size(T, H, I, kind, dt), X.device, workspace)
     _check(lib().tp_mlp_shard(_ptr(X), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Y), T, H, I,
                               kind, dt, dt, _ptr(ws), wsb, _stream(stream)))
+    return Y
+
+
+def mlp_fp8_workspace_size(T: int, H: int, I: int, kind: int) -> int:
+    return int(lib().tp_mlp_fp8_workspace_size(T, H, I, kind))
+
+
+def mlp_shard_fp8(X, W_gate, W_up, W_down, scales, Y=None, kind: int = TP_MLP_SWIGLU, workspace=None,
+                  stream=None):
+    """fp32 partial of this rank's MLP block on E4M3 codes (uint8 tensors).
+    scales = (x_scale, w_gate_scale, w_up_scale, w_down_scale, h_scale)."""
+    import torch
+    T, H = X.shape
+    I = W_gate.shape[1]
+    if Y is None:
+        Y = torch.empty((T, H), dtype=torch.float32, device=X.device)
+    q = Fp8MlpScales(*[float(v) for v in scales])
+    ws, wsb = _workspace(mlp_fp8_workspace_size(T, H, I, kind), X.device, workspace)
+    _check(lib().tp_mlp_shard_fp8(_ptr(X), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Y), T, H, I,
+                                  kind, ctypes.byref(q), _ptr(ws), wsb, _stream(stream)))
     return Y
 
 

@@ -159,7 +159,9 @@ tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launche
 // ---- linear layers ----------------------------------------------------------------------
 
 size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt) {
-    if (in_dt != TP_BF16 || T <= 0 || K <= 0 || N <= 0) return 0;
+    if (T <= 0 || K <= 0 || N <= 0) return 0;
+    if (in_dt == TP_FP8_E4M3) return round_up(tpk::gemm_f8_split_bytes(T, N, K, 0), WS_ALIGN);
+    if (in_dt != TP_BF16) return 0;
     if (T > SKINNY_MAX_T) return round_up(tpk::gemm_bf16_split_bytes(T, N, K, 0), WS_ALIGN);
     return round_up(tpk::skinny_partials_bytes(T, N, K), WS_ALIGN);
 }
@@ -169,6 +171,20 @@ static tp_status check_ws(const char* fn, const void* ws, size_t ws_bytes, size_
     if (!ws || ws_bytes < need)
         return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
     if (!aligned(ws, 16)) return fail(TP_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+    return TP_OK;
+}
+
+static tp_status check_f8(const char* fn, const void* X, const void* W, const void* Y,
+                          int64_t K, int64_t N, const tp_fp8_scales* q) {
+    if (!q) return fail(TP_ERR_NULL_POINTER, "%s: fp8 operands need their scales (q is NULL)", fn);
+    if (!(q->x_scale > 0.0f) || !(q->w_scale > 0.0f))
+        return fail(TP_ERR_BAD_SHAPE, "%s: fp8 scales must be positive (x %g, w %g)", fn, (double)q->x_scale,
+                    (double)q->w_scale);
+    if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs 16-byte aligned X, W and Y", fn);
+    if (K % 16 || N % 16)
+        return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs K and N multiples of 16 (K=%lld N=%lld)", fn,
+                    (long long)K, (long long)N);
     return TP_OK;
 }
 
@@ -202,7 +218,19 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
                                       static_cast<float*>(Y), T, N, K, K, N, ldy, act == TP_ACT_RELU, 0, s),
                         "tp_column_linear");
     }
-    if (in_dt == TP_FP8_E4M3) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp8 operands are not implemented yet");
+    if (in_dt == TP_FP8_E4M3) {
+        if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
+            return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: fp8 input needs bf16, fp16 or fp32 output");
+        tp_status st = check_f8("tp_column_linear", X, W_shard, Y, K, N, q);
+        if (st != TP_OK) return st;
+        if (ldy % 8) return fail(TP_ERR_MISALIGNED, "tp_column_linear: ldy must be a multiple of 8");
+        st = check_ws("tp_column_linear", workspace, ws_bytes, tp_linear_workspace_size(T, K, N, in_dt));
+        if (st != TP_OK) return st;
+        const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
+        return from_hip(tpk::gemm_f8_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU,
+                                           q->x_scale * q->w_scale, 1.0f, workspace, ws_bytes, s),
+                        "tp_column_linear");
+    }
     if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: input dtype %d not offered", (int)in_dt);
     if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
         return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: bf16 input needs bf16, fp16 or fp32 output");
@@ -242,7 +270,16 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
                                       Y_partial, T, N, K_shard, K_shard, N, N, 0, accumulate != 0, s),
                         "tp_row_linear_partial");
     }
-    if (in_dt == TP_FP8_E4M3) return fail(TP_ERR_UNSUPPORTED, "tp_row_linear_partial: fp8 operands are not implemented yet");
+    if (in_dt == TP_FP8_E4M3) {
+        tp_status st = check_f8("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, q);
+        if (st != TP_OK) return st;
+        st = check_ws("tp_row_linear_partial", workspace, ws_bytes, tp_linear_workspace_size(T, K_shard, N, in_dt));
+        if (st != TP_OK) return st;
+        return from_hip(tpk::gemm_f8_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
+                                           accumulate ? 3 : 2, 0, q->x_scale * q->w_scale, 1.0f, workspace,
+                                           ws_bytes, s),
+                        "tp_row_linear_partial");
+    }
     if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_row_linear_partial: input dtype %d not offered", (int)in_dt);
     tp_status st = check_bf16_gemm("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, N);
     if (st != TP_OK) return st;
@@ -341,6 +378,55 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
     return from_hip(tpk::gemm_bf16_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0, split,
                                          split_bytes, s),
                     "tp_mlp_shard");
+}
+
+size_t tp_mlp_fp8_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind) {
+    if (T <= 0 || H <= 0 || I_shard <= 0) return 0;
+    const size_t first = tpk::gemm_f8_split_bytes(T, I_shard, H, kind == TP_MLP_SWIGLU ? 1 : 0);
+    const size_t second = tpk::gemm_f8_split_bytes(T, H, I_shard, 0);
+    return round_up((size_t)(T * I_shard), WS_ALIGN) + round_up(first > second ? first : second, WS_ALIGN);
+}
+
+tp_status tp_mlp_shard_fp8(const void* X, const void* W_gate, const void* W_up, const void* W_down,
+                           float* Y_partial, int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
+                           const tp_fp8_mlp_scales* q, void* workspace, size_t ws_bytes, void* stream) {
+    const char* fn = "tp_mlp_shard_fp8";
+    if (!X || !W_gate || !W_down || !Y_partial)
+        return fail(TP_ERR_NULL_POINTER, "%s: X, W_gate, W_down and Y_partial must be non-NULL", fn);
+    if (!q) return fail(TP_ERR_NULL_POINTER, "%s: scales q must be non-NULL", fn);
+    if (kind != TP_MLP_RELU && kind != TP_MLP_SWIGLU) return fail(TP_ERR_BAD_SHAPE, "%s: unknown kind %d", fn, (int)kind);
+    if (kind == TP_MLP_SWIGLU && !W_up) return fail(TP_ERR_NULL_POINTER, "%s: SwiGLU needs W_up", fn);
+    if (kind == TP_MLP_RELU && W_up) return fail(TP_ERR_BAD_SHAPE, "%s: the ReLU form takes no W_up", fn);
+    if (T <= 0 || H <= 0 || I_shard <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "%s: sizes must be positive (T=%lld H=%lld I=%lld)", fn, (long long)T,
+                    (long long)H, (long long)I_shard);
+    const bool up = kind == TP_MLP_SWIGLU;
+    if (!(q->x_scale > 0.0f) || !(q->w_gate_scale > 0.0f) || !(q->w_down_scale > 0.0f) || !(q->h_scale > 0.0f) ||
+        (up && !(q->w_up_scale > 0.0f)))
+        return fail(TP_ERR_BAD_SHAPE, "%s: scales must be positive", fn);
+    if (!aligned(X, 16) || !aligned(W_gate, 16) || (W_up && !aligned(W_up, 16)) || !aligned(W_down, 16) ||
+        !aligned(Y_partial, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs 16-byte aligned pointers", fn);
+    if (H % 16 || I_shard % 16) return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs H and I_shard multiples of 16", fn);
+    const size_t need = tp_mlp_fp8_workspace_size(T, H, I_shard, kind);
+    tp_status st = check_ws(fn, workspace, ws_bytes, need);
+    if (st != TP_OK) return st;
+    hipStream_t s = as_stream(stream);
+    Carver c(workspace);
+    void* h = c.take((size_t)(T * I_shard));
+    void* split = c.take(0);
+    const size_t split_bytes = need - c.off;
+    hipError_t e;
+    if (up)
+        e = tpk::gemm_f8_swiglu(X, W_gate, W_up, h, T, I_shard, H, q->x_scale * q->w_gate_scale,
+                                q->x_scale * q->w_up_scale, q->h_scale, split, split_bytes, s);
+    else
+        e = tpk::gemm_f8_store(X, W_gate, h, T, I_shard, H, H, I_shard, I_shard, 4, 1,
+                               q->x_scale * q->w_gate_scale, q->h_scale, split, split_bytes, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    return from_hip(tpk::gemm_f8_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0,
+                                       q->h_scale * q->w_down_scale, 1.0f, split, split_bytes, s),
+                    fn);
 }
 
 // ---- attention shard --------------------------------------------------------------------------

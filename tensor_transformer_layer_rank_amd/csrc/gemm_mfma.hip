@@ -1,5 +1,6 @@
-// bf16 MFMA GEMM tiles for gfx950 (v_mfma_f32_32x32x16_bf16), used by every prefill-size
-// linear layer of a rank's shard:
+// MFMA GEMM tiles for gfx950, used by every prefill-size linear layer of a rank's shard,
+// on bf16 operands (v_mfma_f32_32x32x16_bf16) or on OCP E4M3 fp8 operands with per-tensor
+// scales (v_mfma_f32_32x32x64_f8f6f4):
 //   - column-parallel output, optional ReLU, bf16/fp16/fp32 store with a leading dimension
 //     ("CUDA tensor parallel computations", 第二类 Column Parallel; 第五类 for the activation);
 //   - row-parallel fp32 partial, overwrite or += (第三类 Row Parallel);
@@ -13,18 +14,20 @@
 // gate + 128 up accumulator columns), 256 threads = 4 wave64s laid out 2 (M) x 2 (N), one
 // per SIMD; each wave owns 128 x 128 outputs = 4 x 4 MFMA 32x32 blocks (256 fp32
 // accumulators per lane, held in the accumulation registers).
-// Staging: K steps of 32 go global -> LDS directly (global_load_lds_dwordx4, no register
-// staging) into a ring of 4 LDS stages, so three K steps of loads are in flight while the
-// MFMAs consume the fourth. One barrier per K step, placed between its two 16-deep
-// slices: it publishes the next stage and releases the oldest one for refilling, so the
-// next stage's first operand fragments are read before the step ends.
+// Staging: K steps (32 bf16 or 64 fp8 = 64 bytes of each activation row) go global -> LDS
+// directly (global_load_lds_dwordx4, no register staging) into a ring of 4 LDS stages of
+// 32 KB, so three K steps of loads are in flight while the MFMAs consume the fourth. One
+// barrier per K step, placed inside the step: it publishes the next stage and releases the
+// oldest one for refilling, so the next stage's first operand fragments are read while the
+// current step's MFMAs still run.
 // LDS layouts: the activation tile is kept [m][k] (64-byte rows) and read with
-// ds_read_b128; the weight tile is kept in its memory order [k][n] (512-byte rows) and read
-// with the gfx950 transposing load ds_read_b64_tr_b16, which hands each lane 4 consecutive k
-// of one column (two of them make the 8-k MFMA operand). The 16-byte granules of a row are
-// XOR-permuted (activation: chunk ^ ((row >> 2) & 3); weight: granule ^ 4 * (k & 3)), which
-// makes both reads free of LDS bank conflicts (measured); the DMA applies the permutation by
-// choosing which source granule each lane fetches.
+// ds_read_b128; the weight tile is kept in its memory order [k][n] (512-byte rows for bf16,
+// 256 for fp8) and read with the gfx950 transposing loads ds_read_b64_tr_b16 / _b8, which
+// hand each lane 4 (bf16) or 8 (fp8) consecutive k of one column. The 16-byte granules of a
+// row are XOR-permuted (activation: chunk ^ ((row >> 2) & 3); bf16 weight: granule ^
+// 4 * (k & 3); fp8 weight: granule ^ 2 * (k & 7)), which makes every read free of LDS bank
+// conflicts; the DMA applies the permutation by choosing which source granule each lane
+// fetches.
 // Tiles are ordered so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
 // works on a compact block of 4 row tiles x n column tiles, which keeps its L2 hit rate up.
 #include "tp_internal.h"
@@ -33,27 +36,48 @@ namespace tpk {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, NSTAGE = 4;
-constexpr int A_STRIDE = BK * 2;          // 64 B per activation row
-constexpr int B_STRIDE = BN * 2;          // 512 B per weight row (k)
+constexpr int BM = 256, BN = 256, NTHR = 256, NSTAGE = 4;
+constexpr int A_STRIDE = 64;              // bytes per activation row (one K step)
 constexpr int A_BYTES = BM * A_STRIDE;    // 16384
-constexpr int B_BYTES = BK * B_STRIDE;    // 16384
+constexpr int B_BYTES = 16384;            // one K step of the weight tile
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int A_PER_WAVE = BM * 4 / 4;    // 256 granules of 16 B = 4 DMA instructions
-constexpr int B_PER_WAVE = BK * 32 / 4;   // 256 granules
+constexpr int B_PER_WAVE = B_BYTES / 16 / 4;
 constexpr int DMA_A = 4, DMA_B = 4;
+
+// Operand format: element type, K per step, elements per 16-byte granule, weight row bytes
+template <bool F8>
+struct Fmt;
+template <>
+struct Fmt<false> {   // bf16
+    typedef uint16_t E;
+    static constexpr int BK = 32, EPG = 8, B_STRIDE = 512, GPR = 32;
+    __device__ static int swz(int k) { return 4 * (k & 3); }
+};
+template <>
+struct Fmt<true> {    // OCP E4M3
+    typedef uint8_t E;
+    static constexpr int BK = 64, EPG = 16, B_STRIDE = 256, GPR = 16;
+    __device__ static int swz(int k) { return 2 * (k & 7); }
+};
 
 // byte offset of logical 16-byte chunk c (0..3) of activation row r
 __device__ __forceinline__ int a_lds(int r, int c) { return r * A_STRIDE + ((c ^ ((r >> 2) & 3)) << 4); }
-// byte offset of logical 16-byte granule g (0..31) of weight row k
-__device__ __forceinline__ int b_lds(int k, int g) { return k * B_STRIDE + ((g ^ (4 * (k & 3))) << 4); }
+// byte offset of logical 16-byte granule g of weight row k
+template <bool F8>
+__device__ __forceinline__ int b_lds(int k, int g) {
+    return k * Fmt<F8>::B_STRIDE + ((g ^ Fmt<F8>::swz(k)) << 4);
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -61,34 +85,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
+// OCP E4M3 code of f: nearest value, ties to even (the conversion instruction), with
+// magnitudes past 448 saturated first (the instruction alone would give NaN); NaN stays NaN
+__device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
+    f = f > 448.0f ? 448.0f : (f < -448.0f ? -448.0f : f);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xFF);
+}
 
-struct GemmGeom {
-    const uint16_t* A;    // [M, K] row-major, lda
-    const uint16_t* B1;   // [K, N] row-major, ldb
-    const uint16_t* B2;   // second weight of the dual (gate/up) form, else unused
+template <bool F8>
+struct Geom {
+    typedef typename Fmt<F8>::E E;
+    const E* A;    // [M, K] row-major, lda
+    const E* B1;   // [K, N] row-major, ldb
+    const E* B2;   // second weight of the dual (gate/up) form, else unused
     int64_t M, N, K, lda, ldb;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Per-lane source offsets of one wave's share of a stage (fixed for the whole K loop; only
 // the K offset moves), in elements relative to the tile's base pointers. Wave w fills
-// activation rows 64w..64w+63 (5 DMA instructions of 64 granules) and weight rows
-// 8w..8w+7 (288 granules: 4 instructions plus a fifth that starts 32 granules early and
-// rewrites identical data). Every lane of every instruction loads an in-bounds address, so
-// each wave issues exactly DMA_A + DMA_B loads per stage and vmcnt counts stay exact:
-// pad granules, rows past M and columns past N fetch a harmless valid address (row 0 /
-// column n0), and granules past K fetch K chunk 0 and are zeroed after they land.
-// Per-lane source offsets of one wave's share of a stage (fixed for the whole K loop; only
-// the K offset moves), in elements relative to the tile's base pointers. Wave w fills
-// activation rows 64w..64w+63 and weight rows 8w..8w+7, 4 DMA instructions of 64
+// activation rows 64w..64w+63 and a quarter of the weight rows, 4 DMA instructions of 64
 // granules each; LDS granule G holds the logical granule that the XOR permutation maps to
 // it. Every lane of every instruction loads an in-bounds address, so each wave issues
 // exactly DMA_A + DMA_B loads per stage and vmcnt counts stay exact: rows past M and
 // columns past N fetch a harmless valid address (row 0 / column n0), and granules past K
 // fetch K chunk 0 and are zeroed after they land.
 struct DmaPlan {
-    int32_t a_off[DMA_A];   // row * lda + 8 * chunk
+    int32_t a_off[DMA_A];   // row * lda + EPG * chunk
     int64_t b_off[DMA_B];   // k row * ldb + column, relative to the first weight (dual: the
                             // second weight's granules carry the pointer difference)
 };
@@ -100,20 +122,22 @@ __device__ __forceinline__ void a_granule(int wave, int i, int lane, int& row, i
     c = (G & 3) ^ ((row >> 2) & 3);
 }
 // weight k row and logical granule
+template <bool F8>
 __device__ __forceinline__ void b_granule(int wave, int i, int lane, int& row, int& g) {
     const int G = wave * B_PER_WAVE + i * 64 + lane;
-    row = G >> 5;
-    g = (G & 31) ^ (4 * (row & 3));
+    row = G / Fmt<F8>::GPR;
+    g = (G % Fmt<F8>::GPR) ^ Fmt<F8>::swz(row);
 }
 
-template <bool DUAL>
-__device__ __forceinline__ int64_t b_offset(const GemmGeom& g, int64_t n0, int row, int gr) {
+template <bool DUAL, bool F8>
+__device__ __forceinline__ int64_t b_offset(const Geom<F8>& g, int64_t n0, int row, int gr) {
+    constexpr int HALF = Fmt<F8>::GPR / 2, EPG = Fmt<F8>::EPG;
     int64_t col, extra = 0;
     if (DUAL) {
-        col = n0 + (int64_t)(gr & 15) * 8;
-        if (gr >= 16) extra = g.B2 - g.B1;
+        col = n0 + (int64_t)(gr % HALF) * EPG;
+        if (gr >= HALF) extra = g.B2 - g.B1;
     } else {
-        col = n0 + (int64_t)gr * 8;
+        col = n0 + (int64_t)gr * EPG;
     }
     if (col >= g.N) {
         col = n0;
@@ -122,20 +146,20 @@ __device__ __forceinline__ int64_t b_offset(const GemmGeom& g, int64_t n0, int r
     return extra + (int64_t)row * g.ldb + col;
 }
 
-template <bool DUAL>
-__device__ __forceinline__ void make_plan(DmaPlan& p, const GemmGeom& g, int64_t m0, int64_t n0,
+template <bool DUAL, bool F8>
+__device__ __forceinline__ void make_plan(DmaPlan& p, const Geom<F8>& g, int64_t m0, int64_t n0,
                                           int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + 8 * c);
+        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + Fmt<F8>::EPG * c);
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule(wave, i, lane, row, gr);
-        p.b_off[i] = b_offset<DUAL>(g, n0, row, gr);
+        b_granule<F8>(wave, i, lane, row, gr);
+        p.b_off[i] = b_offset<DUAL, F8>(g, n0, row, gr);
     }
 }
 
@@ -144,22 +168,23 @@ __device__ __forceinline__ void make_plan(DmaPlan& p, const GemmGeom& g, int64_t
 // register outputs: the compiler then neither reorders it against other memory accesses
 // nor adds its own vmcnt waits before LDS reads (it cannot tell which stage a DMA writes),
 // and the kernel keeps the exact per-stage vmcnt accounting itself.
-__device__ __forceinline__ void dma16(const uint16_t* src, unsigned char* dst) {
+__device__ __forceinline__ void dma16(const void* src, unsigned char* dst) {
     const unsigned lds = __builtin_amdgcn_readfirstlane(
         (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)(dst)));
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
 }
 
 // Issue this wave's DMA_A + DMA_B loads for the K step starting at k0 into `stage`.
-template <bool DUAL>
-__device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan& p, const GemmGeom& g,
-                                            const uint16_t* a_base, int64_t m0, int64_t n0, int64_t k0,
-                                            int wave, int lane) {
+template <bool DUAL, bool F8>
+__device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan& p, const Geom<F8>& g,
+                                            const typename Fmt<F8>::E* a_base, int64_t m0, int64_t n0,
+                                            int64_t k0, int wave, int lane) {
+    constexpr int BK = Fmt<F8>::BK, EPG = Fmt<F8>::EPG;
     unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
     unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
     if (k0 + BK <= g.K) {
-        const uint16_t* a_k = a_base + k0;
-        const uint16_t* b_k = g.B1 + k0 * g.ldb;
+        const auto* a_k = a_base + k0;
+        const auto* b_k = g.B1 + k0 * g.ldb;
 #pragma unroll
         for (int i = 0; i < DMA_A; ++i) dma16(a_k + p.a_off[i], a_dst + i * 1024);
 #pragma unroll
@@ -171,35 +196,36 @@ __device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan&
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        if (k0 + 8 * c >= g.K) c = 0;
+        if (k0 + EPG * c >= g.K) c = 0;
         if (m0 + row >= g.M) row = 0;
-        dma16(a_base + k0 + (int64_t)row * g.lda + 8 * c, a_dst + i * 1024);
+        dma16(a_base + k0 + (int64_t)row * g.lda + EPG * c, a_dst + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule(wave, i, lane, row, gr);
+        b_granule<F8>(wave, i, lane, row, gr);
         if (k0 + row >= g.K) row = 0;
-        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL>(g, n0, row, gr), b_dst + i * 1024);
+        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL, F8>(g, n0, row, gr), b_dst + i * 1024);
     }
 }
 
 // After a partial final K step has landed: zero this wave's granules that lie past K.
-__device__ __forceinline__ void zero_tail(unsigned char* stage, const GemmGeom& g, int64_t k0,
+template <bool F8>
+__device__ __forceinline__ void zero_tail(unsigned char* stage, const Geom<F8>& g, int64_t k0,
                                           int wave, int lane) {
     unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
         a_granule(wave, i, lane, row, c);
-        if (k0 + 8 * c >= g.K)
+        if (k0 + Fmt<F8>::EPG * c >= g.K)
             *reinterpret_cast<u32x4*>(a_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
     unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule(wave, i, lane, row, gr);
+        b_granule<F8>(wave, i, lane, row, gr);
         if (k0 + row >= g.K)
             *reinterpret_cast<u32x4*>(b_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
@@ -219,6 +245,8 @@ __device__ __forceinline__ int b_col_of(int j, int wn) {
     return wn * 128 + j * 32;
 }
 
+// ---- bf16 operand fragments ---------------------------------------------------------
+
 // 8 consecutive k (rows ks*16 + 8*(lane/32) ..) of column col0 + lane%32 of the weight tile:
 // two transposing reads, each giving 4 k of one column to every lane of a 16-lane group.
 __device__ __forceinline__ bf16x8 read_b_frag(const unsigned char* Bs, int ks, int col0, int lane) {
@@ -227,9 +255,9 @@ __device__ __forceinline__ bf16x8 read_b_frag(const unsigned char* Bs, int ks, i
     const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
     const int gr = col >> 3, within = (col & 7) * 2;
     // rows row and row+4 have the same (row & 3), hence the same permutation
-    const lds_u8* base = (const lds_u8*)(Bs) + b_lds(row, gr) + within;
+    const lds_u8* base = (const lds_u8*)(Bs) + b_lds<false>(row, gr) + within;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * B_STRIDE));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * 512));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
 }
@@ -266,6 +294,45 @@ __device__ __forceinline__ void mfma1(f32x16 (&acc)[4][4], const Frags& f, int n
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// ---- fp8 operand fragments ----------------------------------------------------------
+// The 32x32x64 fp8 MFMA takes 32 bytes per lane of each operand: lane l holds row (A) or
+// column (B) l % 32 at k = 32 * (l / 32) + 0..31, byte b at k offset b (the same k order for
+// both operands, which is all the product needs).
+
+// half `part` (16 bytes: k = 32*(lane/32) + 16*part ..) of activation block i
+__device__ __forceinline__ u32x4 read_a8_half(const unsigned char* stage, int i, int part, int wm,
+                                              int lane) {
+    const int r32 = lane & 31, hi = lane >> 5;
+    return *reinterpret_cast<const u32x4*>(stage + a_lds(wm * 128 + i * 32 + r32, 2 * hi + part));
+}
+
+// quarter t (8 bytes: k = 32*(lane/32) + 8t .. +7) of weight block column col0 + lane%32:
+// one transposing read; lane r of a 16-lane group addresses row k0 + r/2, 8 columns from
+// 8*(r%2), and lane i receives column i of those 8 rows.
+__device__ __forceinline__ i32x2 read_b8_quarter(const unsigned char* Bs, int t, int col0, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = 32 * (g >> 1) + 8 * t + (r >> 1);
+    const int col = col0 + 16 * (g & 1) + 8 * (r & 1);
+    const lds_u8* p = (const lds_u8*)(Bs) + b_lds<true>(row, col >> 4) + (col & 15);
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+}
+
+__device__ __forceinline__ void set_a8(i32x8& v, int part, u32x4 x) {
+    v[4 * part + 0] = (int)x.x;
+    v[4 * part + 1] = (int)x.y;
+    v[4 * part + 2] = (int)x.z;
+    v[4 * part + 3] = (int)x.w;
+}
+__device__ __forceinline__ void set_b8(i32x8& v, int t, i32x2 x) {
+    v[2 * t + 0] = x.x;
+    v[2 * t + 1] = x.y;
+}
+
+__device__ __forceinline__ void mfma8(f32x16& acc, const i32x8& a, const i32x8& b) {
+    // format 0 = E4M3 for both operands; zero scale operands select the unscaled instruction
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+}
+
 #define TP_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // row of accumulator register r of block i for a lane in half `hi` (MFMA 32x32 layout)
@@ -275,11 +342,14 @@ __device__ __forceinline__ int acc_row(int i, int r, int hi) {
 
 // ---- epilogues ----------------------------------------------------------------------
 
-// KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=
+// KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=, 4 OCP E4M3 code of v / out_div.
+// Every accumulator is first multiplied by `scale` (the product of the per-tensor operand
+// scales of fp8 operands; 1 for bf16).
 template <int KIND, bool RELU>
 struct EpiStore {
     void* C;
     int64_t ldc, M, N;
+    float scale, out_div;
     // accumulator row block i (acc[i][0..3]) of wave (wm, wn)
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
                          int lane) const {
@@ -292,21 +362,26 @@ struct EpiStore {
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                 if (row >= M) continue;
-                float v = a[j][r];
+                float v = a[j][r] * scale;
                 if (RELU) v = v > 0.0f ? v : 0.0f;
                 const int64_t off = row * ldc + col;
                 if (KIND == 0) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v);
                 else if (KIND == 1) static_cast<uint16_t*>(C)[off] = f32_to_f16(v);
                 else if (KIND == 2) static_cast<float*>(C)[off] = v;
-                else static_cast<float*>(C)[off] += v;
+                else if (KIND == 3) static_cast<float*>(C)[off] += v;
+                else static_cast<uint8_t*>(C)[off] = f32_to_e4m3(v / out_div);
             }
         }
     }
 };
 
+// h = SiLU(gate * gs) * (up * us); stored as bf16 (H8 = false) or as the E4M3 code of
+// h / h_scale (H8 = true).
+template <bool H8>
 struct EpiSwiGLU {
-    uint16_t* h;   // [M, N] bf16
+    void* h;   // [M, N]
     int64_t M, N;
+    float gs, us, h_scale;
     // acc[i][0..1] hold gate columns, acc[i][2..3] the matching up columns
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
                          int lane) const {
@@ -319,9 +394,10 @@ struct EpiSwiGLU {
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                 if (row >= M) continue;
-                const float gte = a[j][r], up = a[j + 2][r];
+                const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
                 const float silu = gte / (1.0f + __expf(-gte));
-                h[row * N + col] = f32_to_bf16(silu * up);
+                if (H8) static_cast<uint8_t*>(h)[row * N + col] = f32_to_e4m3(silu * up / h_scale);
+                else static_cast<uint16_t*>(h)[row * N + col] = f32_to_bf16(silu * up);
             }
         }
     }
@@ -402,38 +478,42 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
     return x * q + (x < rem ? x : rem) + idx;
 }
 
-__device__ __forceinline__ bool k0_full(const GemmGeom& g, int64_t k0) { return k0 + BK <= g.K; }
+template <bool F8>
+__device__ __forceinline__ bool k0_full(const Geom<F8>& g, int64_t k0) { return k0 + Fmt<F8>::BK <= g.K; }
 
 // Wait until this wave's DMA for a stage has landed while `pending` later stages (0..3) may
 // still be in flight, zero its granules past K if it is the partial final step, then
 // barrier: after it the stage is readable by every wave.
-__device__ __forceinline__ void publish(unsigned char* stage, int pending, const GemmGeom& g,
+template <bool F8>
+__device__ __forceinline__ void publish(unsigned char* stage, int pending, const Geom<F8>& g,
                                         int64_t k0, int wave, int lane) {
     constexpr int GRP = DMA_A + DMA_B;
     if (pending >= 3) wait_vm<3 * GRP>();
     else if (pending == 2) wait_vm<2 * GRP>();
     else if (pending == 1) wait_vm<GRP>();
     else wait_vm<0>();
-    if (k0 + BK > g.K) {
+    if (k0 + Fmt<F8>::BK > g.K) {
         wait_vm<0>();
-        zero_tail(stage, g, k0, wave, lane);
+        zero_tail<F8>(stage, g, k0, wave, lane);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS traffic done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One K step kt on stage `cur` (slice-0 fragments already in f0). The instruction order is
-// pinned: slice-0 MFMAs alternate with the reads of slice 1 (into f1); then stage kt+1 is
-// published (wait + barrier), after which `cur` is free; slice-1 MFMAs then alternate with
-// the reads of stage kt+1's slice 0 (into f0) and with this wave's DMA refilling `cur` with
-// step kt+4. The MFMA pipe thus always has queued work while loads are issued.
+// One bf16 K step kt on stage `cur` (slice-0 fragments already in f0). The instruction
+// order is pinned: slice-0 MFMAs alternate with the reads of slice 1 (into f1); then stage
+// kt+1 is published (wait + barrier), after which `cur` is free; slice-1 MFMAs then
+// alternate with the reads of stage kt+1's slice 0 (into f0) and with this wave's DMA
+// refilling `cur` with step kt+4. The MFMA pipe thus always has queued work while loads
+// are issued.
 template <bool DUAL>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                        unsigned char* cur, unsigned char* nxt, int kt, int nk,
-                                       int64_t kbase, const DmaPlan& p, const GemmGeom& g,
+                                       int64_t kbase, const DmaPlan& p, const Geom<false>& g,
                                        const uint16_t* a_base, int64_t m0, int64_t n0, int wm, int wn,
                                        int wave, int lane) {
+    constexpr int BK = Fmt<false>::BK;
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -446,14 +526,14 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     if (has_next) {
         // stages issued after kt+1 and still allowed in flight: kt+2, kt+3
         const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
-        publish(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
+        publish<false>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
     // full refill steps interleave their DMA with the MFMAs; a partial final step takes
     // the general path up front
     const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
-    const bool inline_dma = refill && k0_full(g, k_ref);
-    if (refill && !inline_dma) issue_stage<DUAL>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
+    const bool inline_dma = refill && k0_full<false>(g, k_ref);
+    if (refill && !inline_dma) issue_stage<DUAL, false>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
     const uint16_t* a_k = a_base + k_ref;
     const uint16_t* b_k = g.B1 + k_ref * g.ldb;
     unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
@@ -462,6 +542,61 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     for (int n = 0; n < 16; ++n) {
         mfma1(acc, f1, n);
         if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
+        if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
+        if (inline_dma && n >= 10 && n < 10 + DMA_B) dma16(b_k + p.b_off[n - 10], b_dst + (n - 10) * 1024);
+        TP_FENCE();
+    }
+}
+
+// One fp8 K step kt (64 deep) on stage `cur`: 16 MFMAs in row-block order (n -> block
+// (n/4, n%4)). On entry a[0..2] and bc[0..3] hold the step's fragments; a[3] is read during
+// the first four MFMAs. The barrier that publishes stage kt+1 (and frees `cur`) follows
+// them; the remaining twelve MFMAs then alternate with the reads of stage kt+1 — its weight
+// fragments into bn (the other weight buffer), its activation block i into a[i] as soon as
+// the last MFMA of row block i has been issued — and with the DMA refilling `cur` with
+// step kt+4.
+template <bool DUAL>
+__device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i32x8 (&bc)[4],
+                                          i32x8 (&bn)[4], unsigned char* cur, unsigned char* nxt,
+                                          int kt, int nk, int64_t kbase, const DmaPlan& p,
+                                          const Geom<true>& g, const uint8_t* a_base, int64_t m0,
+                                          int64_t n0, int wm, int wn, int wave, int lane) {
+    constexpr int BK = Fmt<true>::BK;
+    TP_FENCE();
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        mfma8(acc[0][n], a[0], bc[n]);
+        if (n < 2) set_a8(a[3], n, read_a8_half(cur, 3, n, wm, lane));
+        TP_FENCE();
+    }
+    const bool has_next = kt + 1 < nk;
+    const bool refill = kt + 4 < nk;
+    if (has_next) {
+        const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
+        publish<true>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
+    }
+    TP_FENCE();
+    const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
+    const bool inline_dma = refill && k0_full<true>(g, k_ref);
+    if (refill && !inline_dma) issue_stage<DUAL, true>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
+    const uint8_t* a_k = a_base + k_ref;
+    const uint8_t* b_k = g.B1 + k_ref * g.ldb;
+    unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
+    unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
+    const unsigned char* nb = nxt + A_BYTES;
+#pragma unroll
+    for (int n = 4; n < 16; ++n) {
+        mfma8(acc[n >> 2][n & 3], a[n >> 2], bc[n & 3]);
+        if (has_next) {
+            if (n < 12) {   // weight block (n-4)/2, quarters 2*((n-4)%2) and +1
+                const int j = (n - 4) >> 1, t0 = 2 * ((n - 4) & 1);
+                set_b8(bn[j], t0, read_b8_quarter(nb, t0, b_col_of<DUAL>(j, wn), lane));
+                set_b8(bn[j], t0 + 1, read_b8_quarter(nb, t0 + 1, b_col_of<DUAL>(j, wn), lane));
+            }
+            if (n == 4 || n == 5) set_a8(a[0], n - 4, read_a8_half(nxt, 0, n - 4, wm, lane));
+            if (n == 8 || n == 9) set_a8(a[1], n - 8, read_a8_half(nxt, 1, n - 8, wm, lane));
+            if (n == 12 || n == 13) set_a8(a[2], n - 12, read_a8_half(nxt, 2, n - 12, wm, lane));
+        }
         if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
         if (inline_dma && n >= 10 && n < 10 + DMA_B) dma16(b_k + p.b_off[n - 10], b_dst + (n - 10) * 1024);
         TP_FENCE();
@@ -477,9 +612,10 @@ struct SplitArgs {
     float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
 };
 
-template <bool DUAL, class Epi>
-__global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi, int tiles_m,
+template <bool F8, bool DUAL, class Epi>
+__global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
                                                             int tiles_n, SplitArgs sp) {
+    constexpr int BK = Fmt<F8>::BK;
     __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
@@ -499,7 +635,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi,
     tile_of(L, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * (DUAL ? BN / 2 : BN);
-    const uint16_t* a_base = g.A + m0 * g.lda;
+    const auto* a_base = g.A + m0 * g.lda;
     const int nk_total = (int)((g.K + BK - 1) / BK);
     int64_t kbase = 0;
     int nk = nk_total;
@@ -510,7 +646,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi,
     }
 
     DmaPlan p;
-    make_plan<DUAL>(p, g, m0, n0, wave, lane);
+    make_plan<DUAL, F8>(p, g, m0, n0, wave, lane);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -522,25 +658,50 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmGeom g, Epi epi,
 
     if (nk > 0) {
         // prologue: steps 0..3 in flight, publish step 0
-        issue_stage<DUAL>(st0, p, g, a_base, m0, n0, kbase, wave, lane);
-        if (nk > 1) issue_stage<DUAL>(st1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
-        if (nk > 2) issue_stage<DUAL>(st2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
-        if (nk > 3) issue_stage<DUAL>(st3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
-        publish(st0, (nk - 1 < 3) ? nk - 1 : 3, g, kbase, wave, lane);
+        issue_stage<DUAL, F8>(st0, p, g, a_base, m0, n0, kbase, wave, lane);
+        if (nk > 1) issue_stage<DUAL, F8>(st1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
+        if (nk > 2) issue_stage<DUAL, F8>(st2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
+        if (nk > 3) issue_stage<DUAL, F8>(st3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
+        publish<F8>(st0, (nk - 1 < 3) ? nk - 1 : 3, g, kbase, wave, lane);
 
-        Frags f0, f1;
-        read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
         unsigned char* sa = st0;   // stage of step kt; sb, sc, sd hold steps kt+1, kt+2, kt+3
         unsigned char* sb = st1;
         unsigned char* sc = st2;
         unsigned char* sd = st3;
-        for (int kt = 0; kt < nk; ++kt) {
-            k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-            unsigned char* t = sa;
-            sa = sb;
-            sb = sc;
-            sc = sd;
-            sd = t;
+        if constexpr (!F8) {
+            Frags f0, f1;
+            read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
+            for (int kt = 0; kt < nk; ++kt) {
+                k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                unsigned char* t = sa;
+                sa = sb;
+                sb = sc;
+                sc = sd;
+                sd = t;
+            }
+        } else {
+            i32x8 a[4], b0[4], b1[4];
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int part = 0; part < 2; ++part) set_a8(a[i], part, read_a8_half(st0, i, part, wm, lane));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) set_b8(b0[j], t, read_b8_quarter(st0 + A_BYTES, t, b_col_of<DUAL>(j, wn), lane));
+            // one step per iteration; the next step's weight fragments move into b0 at its
+            // end (32 register moves that overlap the last MFMAs; two inlined steps with
+            // swapped buffers instead would exceed the register file)
+            for (int kt = 0; kt < nk; ++kt) {
+                k_step_f8<DUAL>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                unsigned char* t = sa;
+                sa = sb;
+                sb = sc;
+                sc = sd;
+                sd = t;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b0[j] = b1[j];
+            }
         }
     }
     if (q < 0) {
@@ -613,35 +774,37 @@ SplitArgs plan_split(int64_t G, int nk, int n_cu) {
 }
 
 template <bool DUAL>
-void tiles_of(const GemmGeom& g, int64_t& tiles_m, int64_t& tiles_n) {
-    tiles_m = (g.M + BM - 1) / BM;
-    tiles_n = (g.N + (DUAL ? BN / 2 : BN) - 1) / (DUAL ? BN / 2 : BN);
+void tiles_of(int64_t M, int64_t N, int64_t& tiles_m, int64_t& tiles_n) {
+    tiles_m = (M + BM - 1) / BM;
+    tiles_n = (N + (DUAL ? BN / 2 : BN) - 1) / (DUAL ? BN / 2 : BN);
 }
 
-template <bool DUAL>
-size_t split_bytes(const GemmGeom& g) {
+size_t split_bytes_of(int64_t M, int64_t N, int64_t K, bool dual, int bk) {
     int64_t tm, tn;
-    tiles_of<DUAL>(g, tm, tn);
-    const SplitArgs sp = plan_split(tm * tn, (int)((g.K + BK - 1) / BK), cu_count());
+    if (dual) tiles_of<true>(M, N, tm, tn);
+    else tiles_of<false>(M, N, tm, tn);
+    const SplitArgs sp = plan_split(tm * tn, (int)((K + bk - 1) / bk), cu_count());
     if (sp.pieces < 2) return 0;
     return (size_t)(tm * tn - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
 }
 
 // ws may be NULL (or too small): the tiles then all run whole
-template <bool DUAL, class Epi>
-hipError_t launch(const GemmGeom& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
+template <bool F8, bool DUAL, class Epi>
+hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
                   const char* name) {
+    constexpr int BK = Fmt<F8>::BK;
     int64_t tiles_m, tiles_n;
-    tiles_of<DUAL>(g, tiles_m, tiles_n);
+    tiles_of<DUAL>(g.M, g.N, tiles_m, tiles_n);
     const int64_t G = tiles_m * tiles_n;
-    SplitArgs sp = plan_split(G, (int)((g.K + BK - 1) / BK), cu_count());
+    const int nk = (int)((g.K + BK - 1) / BK);
+    SplitArgs sp = plan_split(G, nk, cu_count());
     const size_t need = sp.pieces >= 2 ? (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float) : 0;
-    if (sp.pieces >= 2 && (!ws || ws_bytes < need)) sp = SplitArgs{(int)G, 1, (int)((g.K + BK - 1) / BK), nullptr};
+    if (sp.pieces >= 2 && (!ws || ws_bytes < need)) sp = SplitArgs{(int)G, 1, nk, nullptr};
     sp.part = static_cast<float*>(ws);
     const int64_t blocks = sp.pieces >= 2 ? sp.g_full + (G - sp.g_full) * sp.pieces : G;
     {
         ProfScope ps(name, s);
-        gemm_bf16_kernel<DUAL, Epi><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp);
+        gemm_mfma_kernel<F8, DUAL, Epi><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || sp.pieces < 2) return e;
     }
@@ -663,19 +826,22 @@ __global__ void rope_table_kernel(float2* t, int64_t pos0, int64_t npos, double 
 }  // namespace
 
 size_t gemm_bf16_split_bytes(int64_t M, int64_t N, int64_t K, int dual) {
-    GemmGeom g{nullptr, nullptr, nullptr, M, N, K, K, N};
-    return dual ? split_bytes<true>(g) : split_bytes<false>(g);
+    return split_bytes_of(M, N, K, dual != 0, Fmt<false>::BK);
+}
+
+size_t gemm_f8_split_bytes(int64_t M, int64_t N, int64_t K, int dual) {
+    return split_bytes_of(M, N, K, dual != 0, Fmt<true>::BK);
 }
 
 hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
                            int relu, void* ws, size_t ws_bytes, hipStream_t s) {
-    GemmGeom g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), nullptr,
-               M, N, K, lda, ldb};
-#define TP_STORE_CASE(KIND, RELU)                                                   \
-    if (out_kind == KIND && (relu != 0) == RELU)                                    \
-        return launch<false>(g, EpiStore<KIND, RELU>{C, ldc, M, N}, ws, ws_bytes, s, \
-                             KIND >= 2 ? "gemm_bf16_f32out" : "gemm_bf16_store");
+    Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), nullptr,
+                  M, N, K, lda, ldb};
+#define TP_STORE_CASE(KIND, RELU)                                                                   \
+    if (out_kind == KIND && (relu != 0) == RELU)                                                    \
+        return launch<false, false>(g, EpiStore<KIND, RELU>{C, ldc, M, N, 1.0f, 1.0f}, ws, ws_bytes, s, \
+                                    KIND >= 2 ? "gemm_bf16_f32out" : "gemm_bf16_store");
     TP_STORE_CASE(0, false)
     TP_STORE_CASE(0, true)
     TP_STORE_CASE(1, false)
@@ -687,19 +853,50 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
     return hipErrorInvalidValue;
 }
 
+hipError_t gemm_f8_store(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, int out_kind, int relu, float scale,
+                         float out_div, void* ws, size_t ws_bytes, hipStream_t s) {
+    Geom<true> g{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), nullptr,
+                 M, N, K, lda, ldb};
+#define TP_STORE_CASE(KIND, RELU)                                                                     \
+    if (out_kind == KIND && (relu != 0) == RELU)                                                      \
+        return launch<true, false>(g, EpiStore<KIND, RELU>{C, ldc, M, N, scale, out_div}, ws, ws_bytes, s, \
+                                   KIND == 2 || KIND == 3 ? "gemm_f8_f32out" : "gemm_f8_store");
+    TP_STORE_CASE(0, false)
+    TP_STORE_CASE(0, true)
+    TP_STORE_CASE(1, false)
+    TP_STORE_CASE(1, true)
+    TP_STORE_CASE(2, false)
+    TP_STORE_CASE(2, true)
+    TP_STORE_CASE(3, false)
+    TP_STORE_CASE(4, true)
+#undef TP_STORE_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
                             int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
-    GemmGeom g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg),
-               static_cast<const uint16_t*>(Bu), M, N, K, K, N};
-    return launch<true>(g, EpiSwiGLU{static_cast<uint16_t*>(h), M, N}, ws, ws_bytes, s, "gemm_bf16_swiglu");
+    Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg),
+                  static_cast<const uint16_t*>(Bu), M, N, K, K, N};
+    return launch<false, true>(g, EpiSwiGLU<false>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
+                               "gemm_bf16_swiglu");
+}
+
+hipError_t gemm_f8_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
+                          int64_t N, int64_t K, float gate_scale, float up_scale, float h_scale,
+                          void* ws, size_t ws_bytes, hipStream_t s) {
+    Geom<true> g{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(Bg),
+                 static_cast<const uint8_t*>(Bu), M, N, K, K, N};
+    return launch<true, true>(g, EpiSwiGLU<true>{h, M, N, gate_scale, up_scale, h_scale}, ws, ws_bytes, s,
+                              "gemm_f8_swiglu");
 }
 
 hipError_t gemm_bf16_qkv_rope(const void* X, const void* Wqkv, int64_t H, const QKVOut& o,
                               void* ws, size_t ws_bytes, hipStream_t s) {
     const int64_t M = o.B * o.S, N = (int64_t)(o.hq + 2 * o.hkv) * 128;
-    GemmGeom g{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wqkv), nullptr,
-               M, N, H, H, N};
-    return launch<false>(g, EpiQKV{o, M}, ws, ws_bytes, s, "gemm_bf16_qkv_rope");
+    Geom<false> g{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wqkv), nullptr,
+                  M, N, H, H, N};
+    return launch<false, false>(g, EpiQKV{o, M}, ws, ws_bytes, s, "gemm_bf16_qkv_rope");
 }
 
 hipError_t rope_table(float2* table, int64_t pos0, int64_t npos, float theta, hipStream_t s) {

@@ -41,6 +41,18 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
                             int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 
+// ---- fp8 (OCP E4M3) MFMA path: operands are uint8 codes; every accumulator is scaled ----
+size_t gemm_f8_split_bytes(int64_t M, int64_t N, int64_t K, int dual);
+// C = act(scale * A . B); out_kind 0 bf16, 1 fp16, 2 fp32, 3 fp32 +=, 4 E4M3 code of
+// relu(scale * A . B) / out_div (relu must be 1 for kind 4)
+hipError_t gemm_f8_store(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                         int64_t lda, int64_t ldb, int64_t ldc, int out_kind, int relu, float scale,
+                         float out_div, void* ws, size_t ws_bytes, hipStream_t s);
+// h[M, N] (E4M3 codes, ld = N) = code(SiLU(gate_scale * A . Bg) * (up_scale * A . Bu) / h_scale)
+hipError_t gemm_f8_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
+                          int64_t N, int64_t K, float gate_scale, float up_scale, float h_scale,
+                          void* ws, size_t ws_bytes, hipStream_t s);
+
 // QKV projection of a prefill with rotary embedding and head-major scatter.
 struct QKVOut {
     void* q;        // fp16 [B, hq, S, 128]

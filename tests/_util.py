@@ -54,3 +54,9 @@ def sample_rows(T: int, n: int, seed: int = 0):
     rng = np.random.default_rng(seed)
     rows = set([0, T - 1]) | set(rng.integers(0, T, size=n).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def dev_codes(a):
+    """numpy uint8 codes (E4M3) -> contiguous GPU uint8 tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()

@@ -63,10 +63,55 @@ def test_column_linear_validation(L):
     assert _st(f(FAKE, FAKE, FAKE, 4, 12, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
     assert _st(f(FAKE_ODD, FAKE, FAKE, 100, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
     assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_F32, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
-    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_FP8_E4M3, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_UNSUPPORTED"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, tp.TP_FP8_E4M3, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
     assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, 9, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
     # decode-size bf16 needs a workspace
     assert _st(f(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_BF16, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_WORKSPACE"
+
+
+def test_fp8_linear_validation(L):
+    q = ctypes.byref(tp.Fp8Scales(0.5, 0.25))
+    col, row = L.tp_column_linear, L.tp_row_linear_partial
+    ok = [FAKE, FAKE, FAKE, 64, 32, 32, 32, tp.TP_FP8_E4M3, tp.TP_BF16, 0, q, None, 0, None]
+    bad = list(ok); bad[10] = ctypes.byref(tp.Fp8Scales(0.0, 1.0))
+    assert _st(col(*bad)) == "TP_ERR_BAD_SHAPE"                      # non-positive scale
+    bad = list(ok); bad[4] = 24
+    assert _st(col(*bad)) == "TP_ERR_MISALIGNED"                     # K not a multiple of 16
+    bad = list(ok); bad[5] = 40; bad[6] = 40
+    assert _st(col(*bad)) == "TP_ERR_MISALIGNED"                     # N not a multiple of 16
+    bad = list(ok); bad[0] = FAKE_ODD
+    assert _st(col(*bad)) == "TP_ERR_MISALIGNED"
+    bad = list(ok); bad[8] = tp.TP_FP8_E4M3
+    assert _st(col(*bad)) == "TP_ERR_BAD_DTYPE"                      # no fp8 output
+    assert _st(row(FAKE, FAKE, FAKE, 64, 32, 32, tp.TP_FP8_E4M3, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(row(FAKE, FAKE, FAKE, 64, 40, 32, tp.TP_FP8_E4M3, 0, q, None, 0, None)) == "TP_ERR_MISALIGNED"
+    # a grid past one round of the device needs the split workspace (256 compute units assumed
+    # when no device is visible)
+    need = L.tp_linear_workspace_size(4200, 512, 4096, tp.TP_FP8_E4M3)
+    assert need > 0
+    assert _st(row(FAKE, FAKE, FAKE, 4200, 512, 4096, tp.TP_FP8_E4M3, 0, q, None, 0, None)) == "TP_ERR_WORKSPACE"
+
+
+def test_fp8_mlp_validation(L):
+    f = L.tp_mlp_shard_fp8
+    q = tp.Fp8MlpScales(0.01, 0.001, 0.001, 0.001, 0.125)
+    ws = L.tp_mlp_fp8_workspace_size(512, 256, 128, tp.TP_MLP_SWIGLU)
+    assert ws >= 512 * 128
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 512, 256, 128, tp.TP_MLP_SWIGLU, ctypes.byref(q), FAKE, ws, None]
+    bad = list(args); bad[9] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"
+    bad = list(args); bad[2] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"                     # SwiGLU without W_up
+    bad = list(args); bad[8] = tp.TP_MLP_RELU
+    assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"                        # ReLU form with a W_up
+    bad = list(args); bad[9] = ctypes.byref(tp.Fp8MlpScales(0.01, 0.001, 0.001, 0.001, 0.0))
+    assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"                        # h_scale must be positive
+    bad = list(args); bad[7] = 136
+    assert _st(f(*bad)) == "TP_ERR_MISALIGNED"                       # I_shard not a multiple of 16
+    bad = list(args); bad[11] = ws - 1
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
+    bad = list(args); bad[10] = None
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
 
 
 def test_linear_workspace_sizes(L):
