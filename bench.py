@@ -7,7 +7,8 @@ down [2752,4096], fp32 partial out) — one step = one tp_mlp_shard call (fused
 SiLU(gate)*up GEMM + down GEMM). `value` is shard TFLOP/s (2*M*K*N per GEMM, 277.03
 GFLOP per step). Alongside: the 7B TP=2 decode step (attention shard over a 1024-token
 KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compulsory HBM
-bytes. Inputs are seeded synthetic tensors already resident in HBM. With --extra the
+bytes, and the same MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8) against the fp8
+MFMA peak. Inputs are seeded synthetic tensors already resident in HBM. With --extra the
 attention shard (B=4, S=2048) and the 70B GQA layer shard are timed too.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events that libtpshard records
@@ -26,14 +27,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense MFMA)
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 flop/clk/CU (dense MFMA)
 PEAK_HBM_GBS = 8000.0
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--extra", action="store_true", help="also time the attention and 70B layer shards")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
@@ -86,7 +88,12 @@ def mlp_bench(args):
 
     ms = timed(step, args.warmup, args.steps)
     gu_ms, gu_n = kernel_avg("gemm_bf16_swiglu")
+    fx_ms, fx_n = kernel_avg("fixup_swiglu")
     dn_ms, dn_n = kernel_avg("gemm_bf16_f32out")
+    # the tail-split fix-up pass belongs to the gate/up GEMM: count its time per launch
+    gu_main_ms = gu_ms
+    if fx_n:
+        gu_ms = gu_ms + fx_ms * fx_n / gu_n
     flops_gu = 2.0 * T * H * I * 2
     flops_dn = 2.0 * T * I * H
     flops = flops_gu + flops_dn
@@ -96,6 +103,8 @@ def mlp_bench(args):
         "flops_per_step": flops,
         "kernels": {
             "gemm_bf16_swiglu": {"avg_us": gu_ms * 1e3, "launches": gu_n,
+                                 "main_avg_us": gu_main_ms * 1e3,
+                                 "fixup_avg_us": (fx_ms * 1e3) if fx_n else 0.0,
                                  "tflops": flops_gu / (gu_ms * 1e-3) / 1e12},
             "gemm_bf16_f32out(down)": {"avg_us": dn_ms * 1e3, "launches": dn_n,
                                        "tflops": flops_dn / (dn_ms * 1e-3) / 1e12},
@@ -108,6 +117,45 @@ def mlp_bench(args):
         },
     }
     return res, inp
+
+
+def fp8_mlp_bench(args):
+    """The same MLP shard on OCP E4M3 codes with per-tensor scales (tp_mlp_shard_fp8)."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev_codes
+    inp = wl.mlp7b_tp4_fp8()
+    T, H, I = inp.T, inp.H, inp.I
+    X, Wg, Wu, Wd = (dev_codes(a) for a in (inp.X, inp.W_gate, inp.W_up, inp.W_down))
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.mlp_fp8_workspace_size(T, H, I, tp.TP_MLP_SWIGLU), dtype=torch.uint8, device="cuda")
+    scales = (inp.x_scale, inp.wg_scale, inp.wu_scale, inp.wd_scale, inp.h_scale)
+
+    def step():
+        tp.mlp_shard_fp8(X, Wg, Wu, Wd, scales, Y=Y, workspace=ws)
+
+    ms = timed(step, args.warmup, args.steps)
+    gu_ms, gu_n = kernel_avg("gemm_f8_swiglu")
+    fx_ms, fx_n = kernel_avg("fixup_swiglu")
+    dn_ms, _ = kernel_avg("gemm_f8_f32out")
+    if fx_n:
+        gu_ms = gu_ms + fx_ms * fx_n / gu_n
+    flops_gu = 2.0 * T * H * I * 2
+    flops_dn = 2.0 * T * I * H
+    tf = (flops_gu + flops_dn) / (ms * 1e-3) / 1e12
+    return {
+        "workload": "mlp7b_tp4_fp8: the mlp7b_tp4 shapes as OCP E4M3 codes, per-tensor fp32 scales, "
+                    "h re-encoded to E4M3 with a static scale",
+        "ms_per_step": ms,
+        "tflops": tf,
+        "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+        "kernels": {"gemm_f8_swiglu(+fixup)": {"avg_us": gu_ms * 1e3, "tflops": flops_gu / (gu_ms * 1e-3) / 1e12},
+                    "gemm_f8_f32out(down)": {"avg_us": dn_ms * 1e3, "tflops": flops_dn / (dn_ms * 1e-3) / 1e12}},
+        "roofline": {"bound": "mfma", "kernel": "gemm_f8_swiglu", "achieved": flops_gu / (gu_ms * 1e-3) / 1e12,
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
+    }
 
 
 def graph_timed(step, warmup: int, steps: int):
@@ -293,6 +341,7 @@ def main():
     tp.load()
     mlp, inp = mlp_bench(args)
     dec = decode_bench(args)
+    fp8 = fp8_mlp_bench(args)
     extra = {}
     if args.extra:
         extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
@@ -324,6 +373,7 @@ def main():
         "cpu_baseline": cpu and {k: v for k, v in cpu.items() if k != "seconds"},
         "kernels": mlp["kernels"],
         "decode": dec,
+        "fp8_mlp": fp8,
         "extra": extra or None,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},
