@@ -154,7 +154,8 @@ def fp8_mlp_bench(args):
                     "gemm_f8_f32out(down)": {"avg_us": dn_ms * 1e3, "tflops": flops_dn / (dn_ms * 1e-3) / 1e12}},
         "roofline": {"bound": "mfma", "kernel": "gemm_f8_swiglu", "achieved": flops_gu / (gu_ms * 1e-3) / 1e12,
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
+                     "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                     "traffic": recorded_traffic("gemm_f8_swiglu")},
     }
 
 
