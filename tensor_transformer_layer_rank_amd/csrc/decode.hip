@@ -26,6 +26,8 @@
 // attention shard of its section 放进 Transformer, the per-rank KV cache of "TensorRT LLM
 // 中的并行策略" (注意力模块), and the vocabulary-split output layer of "张量并行：切分
 // Transformer 层的分布式训练" (输入与输出层).
+#include <cmath>
+
 #include "tp_internal.h"
 
 namespace tpk {
@@ -76,24 +78,35 @@ struct SkinnyArgs {
 template <int MB>
 struct StepRegs {
     u32x4 w[8];
-    bf16x8 a[MB];
+    u32x4 a[MB];
+    bool k_ok;   // this lane's 8 k rows lie inside the chunk (else its activations count as 0)
 };
 
 // Loads of one 32-row step: `wp` points at this lane's 8-column group in weight row kr
-// (kr = k0 + 8 * grp), `ap` at this lane's activation rows, column kr.
+// (kr = k0 + 8 * grp), `ap` at this lane's activation rows, column kr. Every load is issued
+// unconditionally, from an always-valid stand-in address (wsafe / asafe) where the element
+// lies outside the matrix, and no loaded value is touched here: branch-free loads whose
+// results are first used by the step's MFMAs let the compiler count outstanding loads
+// exactly, so a step waits only for its own loads while the next step's are in flight.
+// Outside elements cannot leak into stored results: columns past N and tokens past M only
+// feed accumulators that are never stored, and rows past the chunk are cancelled by zeroing
+// the activations (k_ok) when the MFMAs consume them. K chunks and K are multiples of 8, so
+// a lane's 8 rows are all inside or all outside.
 template <int MB>
 __device__ __forceinline__ void load_step(StepRegs<MB>& s, const uint16_t* wp, const uint16_t* ap,
+                                          const uint16_t* wsafe, const uint16_t* asafe,
                                           int64_t ldw, int64_t lda, int64_t kr, int64_t kend,
                                           bool col_ok, uint32_t m_ok) {
+    s.k_ok = kr < kend;
+    const bool w_ok = s.k_ok && col_ok;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        s.w[i] = (kr + i < kend && col_ok) ? *reinterpret_cast<const u32x4*>(wp + i * ldw)
-                                           : u32x4{0u, 0u, 0u, 0u};
+        s.w[i] = *reinterpret_cast<const u32x4*>(w_ok ? wp + i * ldw : wsafe);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        s.a[mb] = ((m_ok >> mb) & 1u) && kr < kend
-                      ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ap + mb * 16 * lda))
-                      : bf16x8{};
+    for (int mb = 0; mb < MB; ++mb) {
+        const bool ok = ((m_ok >> mb) & 1u) && s.k_ok;
+        s.a[mb] = *reinterpret_cast<const u32x4*>(ok ? ap + mb * 16 * lda : asafe);
+    }
 }
 
 // acc[mb][t][r] += A[m = mb*16 + 4*grp + r][kr..] . W[kr..][col + t]: the 8 x 8 block of
@@ -101,6 +114,10 @@ __device__ __forceinline__ void load_step(StepRegs<MB>& s, const uint16_t* wp, c
 // becomes the 8-k operand of MFMA t.
 template <int MB>
 __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>& s) {
+    bf16x8 a[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        a[mb] = __builtin_bit_cast(bf16x8, s.k_ok ? s.a[mb] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const unsigned sel = (t & 1) ? 0x07060302u : 0x05040100u;
@@ -112,7 +129,7 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>
         const bf16x8 b = __builtin_bit_cast(bf16x8, bt);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-            acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.a[mb], b, acc[mb][t], 0, 0, 0);
+            acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][t], 0, 0, 0);
     }
 }
 
@@ -145,16 +162,25 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
     const uint16_t* wp = Bp + kfirst * g.N + col;          // advances 4 steps at a time
     const uint16_t* ap = g.A + (int64_t)l16 * g.lda + kfirst;
     const int64_t wstep = 4 * STEP * g.N, astep = 4 * STEP;
+    // in-bounds stand-ins: row kbeg of this lane's column group (or of the strip's first
+    // group), and token row 0 at column kbeg
+    const uint16_t* wsafe = Bp + kbeg * g.N + (col_ok ? col : c0);
+    const uint16_t* asafe = g.A + kbeg;
     StepRegs<MB> s0, s1;
     int64_t kr = kfirst;
-    if (kr - 8 * grp < kend) load_step<MB>(s0, wp, ap, g.N, g.lda, kr, kend, col_ok, m_ok);
+    if (kr - 8 * grp < kend) load_step<MB>(s0, wp, ap, wsafe, asafe, g.N, g.lda, kr, kend, col_ok, m_ok);
     for (; kr - 8 * grp < kend; kr += 8 * STEP) {
-        const bool h1 = kr + 4 * STEP - 8 * grp < kend;
-        if (h1) load_step<MB>(s1, wp + wstep, ap + astep, g.N, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
+        // the next two steps are loaded whether or not they exist (see load_step); the
+        // scheduling barriers keep each step's loads issued before the previous step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        load_step<MB>(s1, wp + wstep, ap + astep, wsafe, asafe, g.N, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
+        __builtin_amdgcn_sched_barrier(0);
         mma_step<MB>(acc, s0);
-        const bool h2 = kr + 8 * STEP - 8 * grp < kend;
-        if (h2) load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, g.N, g.lda, kr + 8 * STEP, kend, col_ok, m_ok);
-        if (h1) mma_step<MB>(acc, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, wsafe, asafe, g.N, g.lda, kr + 8 * STEP, kend, col_ok,
+                      m_ok);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kr + 4 * STEP - 8 * grp < kend) mma_step<MB>(acc, s1);
         wp += 2 * wstep;
         ap += 2 * astep;
     }
@@ -232,11 +258,17 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
     h[idx] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
 }
 
+// cos / sin of the 64 rotary angles pos * theta^(-2i/128) of one position (formed in fp64
+// on the host and passed by value)
+struct RopeRow {
+    float c[64], s[64];
+};
+
 // one thread per (sequence, head, i < 64): heads 0..hq-1 are q, then hkv k heads, then hkv v
-// heads; q and k pairs (i, i+64) are rotated by pos * theta^(-2i/128), formed in fp64
+// heads; q and k pairs (i, i+64) are rotated by the angle of pair i
 __global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict__ part, int splits,
                                                          int64_t B, int hq, int hkv, int64_t ncols,
-                                                         int64_t pos, double theta,
+                                                         int64_t pos, RopeRow rope,
                                                          float* __restrict__ qbuf,
                                                          uint16_t* __restrict__ kc,
                                                          uint16_t* __restrict__ vc, int64_t cap) {
@@ -255,8 +287,7 @@ __global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict
         dst[i + 64] = f32_to_bf16(x2);
         return;
     }
-    const double ang = (double)pos * pow(theta, -2.0 * (double)i / 128.0);
-    const float cs = (float)cos(ang), sn = (float)sin(ang);
+    const float cs = rope.c[i], sn = rope.s[i];
     const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
     if (head < hq) {
         float* dst = qbuf + (b * hq + head) * 128;
@@ -475,9 +506,15 @@ hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64
     hipError_t e = skinny_run(a, p, s, "skinny_gemm_qkv");
     if (e != hipSuccess) return e;
     const int64_t n = B * (hq + 2 * hkv) * 64;
+    RopeRow rope;
+    for (int i = 0; i < 64; ++i) {
+        const double ang = (double)pos * std::pow((double)theta, -2.0 * (double)i / 128.0);
+        rope.c[i] = (float)std::cos(ang);
+        rope.s[i] = (float)std::sin(ang);
+    }
     ProfScope ps("skinny_reduce_qkv", s);
     reduce_qkv_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        part, (int)p.splits, B, hq, hkv, p.ncols, pos, (double)theta, qbuf,
+        part, (int)p.splits, B, hq, hkv, p.ncols, pos, rope, qbuf,
         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), cap);
     return hipGetLastError();
 }
