@@ -10,14 +10,18 @@
 // [B*S, hq*128], token-major, head h in columns h*128 .. h*128+127 (the rows of this rank's
 // O shard).
 //
-// Work split: one workgroup = 4 wave64s = 128 consecutive queries of one (sequence, head);
-// each wave owns 32 queries. Keys are visited in blocks of 64 up to the causal diagonal,
-// double-buffered in LDS. The scores are formed transposed, S^T = K Q^T
-// (v_mfma_f32_32x32x16_f16, keys = rows), so each lane holds 32 of the 64 scores of ONE
-// query: the online-softmax max and sum need only the lane's own registers plus one
-// exchange with the lane 32 apart. P^T stays in registers as the B operand of
+// Work split: one workgroup = 8 wave64s = 128 consecutive queries of one (sequence, head),
+// one workgroup per compute unit (2 waves per SIMD). Keys are visited in blocks of 64 up to
+// the causal diagonal, double-buffered in LDS; wave (slab, half) owns 32 queries and the 32
+// keys `half` of every block, and the two halves of a slab are merged once at the end (max,
+// sum and output of two online softmaxes). The grid (4 sequences x 8 heads x 16 query blocks
+// = 512 for S = 2048) is twice the number of compute units and is dealt heaviest (longest
+// causal prefix) first, so a unit that finishes a short block early takes the next longest:
+// the causal triangle balances out across two rounds. The scores are formed transposed,
+// S^T = K Q^T (v_mfma_f32_32x32x16_f16, keys = rows), so each lane holds 16 of the 32
+// scores of ONE query: the online-softmax max and sum need only the lane's own registers
+// plus one exchange with the lane 32 apart. P^T stays in registers as the B operand of
 // O^T += V^T P^T. Exponentials use exp2 with log2(e)/sqrt(128) folded into the scale.
-// Query blocks are scheduled heaviest (longest causal prefix) first.
 #include "tp_internal.h"
 
 namespace tpk {
@@ -28,14 +32,18 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int QB = 128;          // queries per workgroup
+constexpr int NWAVE = 8;         // 4 query slabs x 2 key halves
+constexpr int NT = NWAVE * 64;
 constexpr int KB = 64;           // keys per block
 constexpr int K_TILE = KB * 256; // 64 keys x 128 dims x 2 B
 constexpr int V_TILE = 128 * KB * 2;
 constexpr int STAGE = K_TILE + V_TILE;
 
-// K tile: row = key (0..63), 16 chunks of 16 B per row
+// K tile: row = key (0..63), 16 chunks of 16 B per row; the chunk index is XOR-permuted
+// by the row's low 4 bits, so the 16 rows that a quarter-wave reads (one chunk each) hit 16
+// different 16-byte bank groups
 __device__ __forceinline__ int k_off(int row, int chunk) {
-    return row * 256 + ((chunk ^ (row & 7)) << 4);
+    return row * 256 + ((chunk ^ (row & 15)) << 4);
 }
 // V^T tile: row = dim (0..127), 8 chunks of 16 B (8 keys) per row
 __device__ __forceinline__ int v_off(int row, int chunk) {
@@ -43,31 +51,31 @@ __device__ __forceinline__ int v_off(int row, int chunk) {
 }
 
 struct KVRegs {
-    u32x4 k[4];
-    u32x4 v[4];
+    u32x4 k[2];
+    u32x4 v[2];
 };
 
-// K: 64 rows x 16 chunks = 1024 chunks, 4 per thread.
-// V^T: 128 rows x 4 groups of 16 keys, 2 groups per thread (two 16-byte chunks each).
+// K: 64 rows x 16 chunks = 1024 chunks, 2 per thread.
+// V^T: 128 rows x 4 groups of 16 keys, 1 group per thread (two 16-byte chunks).
+// Keys past S are fetched from the last valid row / chunk instead (branch-free loads): their
+// scores are masked to -inf, so their probabilities are exactly 0 and the finite stand-in
+// values contribute nothing. S is a multiple of 8, so an 8-key chunk is wholly in or out.
 __device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* kp, const uint16_t* vp,
                                         int64_t S, int64_t key0, int tid) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * 256;
-        const int row = q >> 4, c = q & 15;
-        const int64_t key = key0 + row;
-        r.k[p] = (key < S) ? *reinterpret_cast<const u32x4*>(kp + key * 128 + c * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const int u = tid + p * 256;
-        const int d = u >> 2, grp = u & 3;
+        const int q = tid + p * NT;
+        const int row = q >> 4, c = q & 15;
+        const int64_t key = (key0 + row < S) ? key0 + row : S - 1;
+        r.k[p] = *reinterpret_cast<const u32x4*>(kp + key * 128 + c * 8);
+    }
+    {
+        const int d = tid >> 2, grp = tid & 3;
         const int64_t key = key0 + grp * 16;
-        const uint16_t* src = vp + (int64_t)d * S + key;
-        r.v[2 * p] = (key < S) ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-        r.v[2 * p + 1] = (key + 8 < S) ? *reinterpret_cast<const u32x4*>(src + 8)
-                                       : u32x4{0u, 0u, 0u, 0u};
+        const int64_t k_lo = (key < S) ? key : S - 8;
+        const int64_t k_hi = (key + 8 < S) ? key + 8 : S - 8;
+        r.v[0] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_lo);
+        r.v[1] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_hi);
     }
 }
 
@@ -75,30 +83,32 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* kp, const uin
 // the MFMA lane half `hi` reads the 8 keys its P^T registers hold with one 16-byte load.
 __device__ __forceinline__ void store_kv(const KVRegs& r, unsigned char* st, int tid) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * 256;
+    for (int p = 0; p < 2; ++p) {
+        const int q = tid + p * NT;
         *reinterpret_cast<u32x4*>(st + k_off(q >> 4, q & 15)) = r.k[p];
     }
     unsigned char* vs = st + K_TILE;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int u = tid + p * 256;
-        const int d = u >> 2, grp = u & 3;
-        const u32x4 a = r.v[2 * p], b = r.v[2 * p + 1];
+    {
+        const int d = tid >> 2, grp = tid & 3;
+        const u32x4 a = r.v[0], b = r.v[1];
         *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp)) = u32x4{a.x, a.y, b.x, b.y};
         *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp + 1)) = u32x4{a.z, a.w, b.z, b.w};
     }
 }
 
-__global__ __launch_bounds__(256, 2) void flash_attn_kernel(const uint16_t* __restrict__ q,
+constexpr int XCH_FLOATS = 66 * 64;   // (m, l, o[64 registers]) of one wave
+constexpr int LDS_BYTES = (2 * STAGE > 4 * XCH_FLOATS * 4) ? 2 * STAGE : 4 * XCH_FLOATS * 4;
+
+__global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ vt,
                                                             uint16_t* __restrict__ out,
                                                             int64_t S, int hq, int hkv, int B,
                                                             int nqb) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r32 = lane & 31, hi = lane >> 5;
+    const int slab = wave & 3, kh = wave >> 2;    // 32-query slab, 32-key half of each block
     const int bh_count = B * hq;
     const int qb = nqb - 1 - (int)(blockIdx.x / bh_count);   // heaviest first
     const int bh = (int)(blockIdx.x % bh_count);
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(const uint16_t* __re
     const uint16_t* kp = k + ((int64_t)(b * hkv + g) * S) * 128;
     const uint16_t* vp = vt + ((int64_t)(b * hkv + g) * 128) * S;
 
-    const int64_t q0 = (int64_t)qb * QB + wave * 32;   // first query of this wave
+    const int64_t q0 = (int64_t)qb * QB + slab * 32;   // first query of this wave
     const int64_t qrow = q0 + r32;                      // this lane's query
     f16x8 qf[8];
 #pragma unroll
@@ -129,84 +139,109 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(const uint16_t* __re
     if (kend > S) kend = S;
     const int nkb = (int)((kend + KB - 1) / KB);
 
-    KVRegs regs;
-    load_kv(regs, kp, vp, S, 0, tid);
-    store_kv(regs, lds, tid);
+    // K/V of block kb+1 are in registers (ra) while block kb is computed; block kb+2 is
+    // requested (rb) before block kb's MFMAs, so every load has a whole block to land
+    KVRegs ra, rb;
+    load_kv(ra, kp, vp, S, 0, tid);
+    store_kv(ra, lds, tid);
+    if (nkb > 1) load_kv(ra, kp, vp, S, KB, tid);
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
         const unsigned char* cur = lds + (kb & 1) * STAGE;
         unsigned char* nxt = lds + ((kb + 1) & 1) * STAGE;
-        const bool more = kb + 1 < nkb;
-        if (more) load_kv(regs, kp, vp, S, (int64_t)(kb + 1) * KB, tid);
-        const int64_t key0 = (int64_t)kb * KB;
-        if (key0 <= q0 + 31 && q0 < S) {   // some key of the block is visible to this wave
-            f32x16 st[2];
+        if (kb + 2 < nkb) load_kv(rb, kp, vp, S, (int64_t)(kb + 2) * KB, tid);
+        const int64_t key0 = (int64_t)kb * KB + kh * 32;   // this wave's 32 keys
+        if (key0 <= q0 + 31 && q0 < S && key0 < S) {       // some key visible to the slab
+            // two independent accumulation chains (even / odd 16-dim slices)
+            f32x16 sa, sb;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
-#pragma unroll
-                for (int dk = 0; dk < 8; ++dk) {
-                    const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(t * 32 + r32, dk * 2 + hi)));
-                    st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[dk], st[t], 0, 0, 0);
-                }
+            for (int r = 0; r < 16; ++r) {
+                sa[r] = 0.0f;
+                sb[r] = 0.0f;
             }
-            // scale, mask, block max over this query's 64 scores
-            const bool diag = key0 + KB - 1 > q0;   // block reaches past some query of the wave
-            float mblk = -__builtin_inff();
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int dk = 0; dk < 8; dk += 2) {
+                const f16x8 a0 = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + hi)));
+                const f16x8 a1 = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + 2 + hi)));
+                sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[dk], sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[dk + 1], sb, 0, 0, 0);
+            }
+            f32x16 st;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] = sa[r] + sb[r];
+            // mask (keys past the query or past S), block max of the raw scores
+            const bool diag = key0 + 31 > q0 || key0 + 32 > S;
+            if (diag) {
+                const int64_t lim64 = ((qrow < S - 1) ? qrow : S - 1) - key0;   // last visible key offset
+                const int lim = (int)(lim64 < -1 ? -1 : lim64);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float sv = st[t][r] * scale;
-                    if (diag) {
-                        const int64_t key = key0 + t * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (key > qrow || key >= S) sv = -__builtin_inff();
-                    }
-                    st[t][r] = sv;
-                    mblk = fmaxf(mblk, sv);
+                    const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
+                    st[r] = (kr > lim) ? -__builtin_inff() : st[r];
                 }
-            mblk = fmaxf(mblk, __shfl_xor(mblk, 32));
+            }
+            float mblk = st[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mblk = fmaxf(mblk, st[r]);
+            mblk = fmaxf(mblk, __shfl_xor(mblk, 32)) * scale;   // scale > 0 keeps the order
             const float m_new = fmaxf(m_run, mblk);
             const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             float lsum = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(st[t][r] - m_use);
-                    st[t][r] = p;
-                    lsum += p;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], scale, -m_use));
+                st[r] = p;
+                lsum += p;
+            }
             lsum += __shfl_xor(lsum, 32);
             l_run = l_run * alpha + lsum;
             m_run = m_new;
+            // the running max rarely moves once a few blocks are in: skip the rescale of the
+            // accumulators when no query of the wave needs it (alpha == 1 exactly)
+            if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            // O^T += V^T P^T over 4 sub-blocks of 16 keys
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            }
+            // O^T += V^T P^T over this wave's two sub-blocks of 16 keys
             const unsigned char* vs = cur + K_TILE;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 2; ++ks) {
                 f16x8 pb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pb[e] = (_Float16)st[ks >> 1][8 * (ks & 1) + e];
+                for (int e = 0; e < 8; ++e) pb[e] = (_Float16)st[8 * ks + e];
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(vs + v_off(dt * 32 + r32, ks * 2 + hi)));
+                        f16x8, *reinterpret_cast<const u32x4*>(vs + v_off(dt * 32 + r32, (2 * kh + ks) * 2 + hi)));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[dt], 0, 0, 0);
                 }
             }
         }
-        if (more) store_kv(regs, nxt, tid);
+        if (kb + 1 < nkb) store_kv(ra, nxt, tid);
+        ra = rb;
         __syncthreads();
     }
-    if (qrow >= S) return;
-    const float inv = 1.0f / l_run;
+    // merge the two key halves of each slab: the kh = 1 wave hands (m, l, o) to the kh = 0 wave
+    float* xch = reinterpret_cast<float*>(lds) + slab * XCH_FLOATS;
+    if (kh == 1) {
+        xch[lane] = m_run;
+        xch[64 + lane] = l_run;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xch[128 + (dt * 16 + r) * 64 + lane] = o[dt][r];
+    }
+    __syncthreads();
+    if (kh == 1 || qrow >= S) return;
+    const float m1 = xch[lane], l1 = xch[64 + lane];
+    const float mm = fmaxf(m_run, m1);          // finite: key 0 is visible to every query
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    const float inv = 1.0f / (l_run * a0 + l1 * a1);
     const int64_t ld = (int64_t)hq * 128;
     uint16_t* op = out + ((int64_t)b * S + qrow) * ld + (int64_t)h * 128;
 #pragma unroll
@@ -216,8 +251,11 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(const uint16_t* __re
             const int d0 = dt * 32 + 8 * rq + 4 * hi;
             unsigned short w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(o[dt][4 * rq + e] * inv));
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rq + e;
+                const float v = (o[dt][r] * a0 + xch[128 + (dt * 16 + r) * 64 + lane] * a1) * inv;
+                w[e] = __builtin_bit_cast(unsigned short, static_cast<__bf16>(v));
+            }
             const uint2 packed = make_uint2((unsigned)w[0] | ((unsigned)w[1] << 16),
                                             (unsigned)w[2] | ((unsigned)w[3] << 16));
             *reinterpret_cast<uint2*>(op + d0) = packed;
@@ -231,7 +269,7 @@ hipError_t flash_attn_fwd(const void* q, const void* k, const void* vt, void* ou
     const int nqb = (int)((S + QB - 1) / QB);
     const int64_t blocks = (int64_t)nqb * B * hq;
     ProfScope ps("flash_attn_fwd", s);
-    flash_attn_kernel<<<(unsigned)blocks, 256, 0, s>>>(
+    flash_attn_kernel<<<(unsigned)blocks, NT, 0, s>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
         static_cast<const uint16_t*>(vt), static_cast<uint16_t*>(out), S, hq, hkv, (int)B, nqb);
     return hipGetLastError();
