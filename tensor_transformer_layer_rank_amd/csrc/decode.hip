@@ -13,10 +13,9 @@
 //                        epilogue: fp32/bf16 store (O and down partials, vocabulary-split
 //                        logits), SiLU(gate)*up, or QKV: rotary embedding at the cache
 //                        position, key and value appended to the cache, q kept in fp32.
-//   decode_attn_kernel   split-KV attention of one query over cache slots 0..L-1 (16-lane
-//                        groups read one 256-byte key row each; the value rows are fetched
-//                        while the scores are formed); decode_combine_kernel merges the
-//                        per-split (max, sum, output) triples.
+//   decode_attn_kernel   attention of one query over cache slots 0..L-1 in a single pass:
+//                        16-lane groups stream 256-byte key and value rows with an online
+//                        softmax each, merged in LDS at the end.
 //
 // Partial sums across workgroups go through HBM-resident buffers and a separate kernel:
 // a device-scope fence per workgroup (L2 write-back and invalidate on this GPU) costs far
@@ -49,7 +48,7 @@ SkinnyPlan plan_skinny(int64_t N, int64_t K, int nb) {
     p.strips_per_b = (N + STRIP - 1) / STRIP;
     p.strips = p.strips_per_b * nb;
     p.ncols = p.strips * STRIP;
-    int64_t target = (1024 + p.strips - 1) / p.strips;   // aim for ~1024 workgroups
+    int64_t target = (256 + p.strips - 1) / p.strips;   // aim for ~256 workgroups (one round)
     if (target < 1) target = 1;
     int64_t kchunk = (K + target - 1) / target;
     kchunk = ((kchunk + 4 * STEP - 1) / (4 * STEP)) * (4 * STEP);   // whole steps for all 4 waves
@@ -300,41 +299,24 @@ __global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict
     }
 }
 
-constexpr int CHUNK_MAX = 1024;
+// Decode attention, one workgroup per (sequence, q head), one pass over the cache: the 16
+// lane groups (16 lanes x 8 dims = one 256-byte key or value row per group) take keys
+// grp, grp+16, ... four at a time (eight 16-byte loads per lane in flight), each group
+// keeping its own online softmax (running max in log2 units, sum, 128-dim output); the 16
+// groups are merged in LDS at the end and the normalised row is written as bf16.
+constexpr int DU = 4;   // keys per group per iteration
 
-__device__ __forceinline__ float block_max(float v, float* sh) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return ((sh[0] + sh[1]) + sh[2]) + sh[3];
-}
-
-// grid (nsplit, hq, B). scratch[b][h][split][130] = (max in log2 units, sum, o[128])
-template <int VPRE>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restrict__ q,
                                                           const uint16_t* __restrict__ kc,
                                                           const uint16_t* __restrict__ vc,
                                                           int hq, int hkv, int64_t L, int64_t cap,
-                                                          int64_t chunk, float* __restrict__ scratch) {
-    __shared__ float sc[CHUNK_MAX];
-    __shared__ float red[16][128];
-    __shared__ float sh[4];
+                                                          uint16_t* __restrict__ out) {
+    __shared__ float red_o[16][128];
+    __shared__ float red_m[16], red_l[16];
     const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
-    const int split = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int nsplit = gridDim.x;
+    const int h = blockIdx.x;
+    const int64_t b = blockIdx.y;
     const int g = (h * hkv) / hq;
-    const int64_t kbeg = (int64_t)split * chunk;
-    const int64_t kend = (kbeg + chunk < L) ? kbeg + chunk : L;
-    const int n = (int)(kend - kbeg);
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     float qv[8];
     const float* qp = q + (b * hq + h) * 128 + 8 * l16;
@@ -342,95 +324,80 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
     for (int e = 0; e < 8; ++e) qv[e] = qp[e] * scale;
     const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
-    // the first VPRE value rows of this group are fetched together with the keys
-    u32x4 vpre[VPRE];
+    float m = -__builtin_inff(), l = 0.f, acc[8] = {};
+    for (int64_t j0 = grp; j0 < L; j0 += 16 * DU) {
+        // keys past L are read from row L-1 (branch-free) and masked below
+        u32x4 kk[DU], vv[DU];
 #pragma unroll
-    for (int e = 0; e < VPRE; ++e) {
-        const int j = grp + 16 * e;
-        vpre[e] = (j < n) ? *reinterpret_cast<const u32x4*>(vb + (kbeg + j) * 128) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < DU; ++u) {
+            const int64_t j = j0 + 16 * u;
+            const int64_t jj = j < L ? j : L - 1;
+            kk[u] = *reinterpret_cast<const u32x4*>(kb + jj * 128);
+            vv[u] = *reinterpret_cast<const u32x4*>(vb + jj * 128);
+        }
+        float sc[DU];
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+            float s = qv[0] * bf16_lo(kk[u].x) + qv[1] * bf16_hi(kk[u].x);
+            s += qv[2] * bf16_lo(kk[u].y) + qv[3] * bf16_hi(kk[u].y);
+            s += qv[4] * bf16_lo(kk[u].z) + qv[5] * bf16_hi(kk[u].z);
+            s += qv[6] * bf16_lo(kk[u].w) + qv[7] * bf16_hi(kk[u].w);
+            sc[u] = s;
+        }
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+            sc[u] += __shfl_xor(sc[u], 8);
+            sc[u] += __shfl_xor(sc[u], 4);
+            sc[u] += __shfl_xor(sc[u], 2);
+            sc[u] += __shfl_xor(sc[u], 1);
+            if (j0 + 16 * u >= L) sc[u] = -__builtin_inff();
+        }
+        float mc = sc[0];
+#pragma unroll
+        for (int u = 1; u < DU; ++u) mc = fmaxf(mc, sc[u]);
+        const float m_new = fmaxf(m, mc);                    // finite: key j0 < L is real
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        float p[DU], ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+            p[u] = __builtin_amdgcn_exp2f(sc[u] - m_new);
+            ps += p[u];
+        }
+        l = l * alpha + ps;
+        m = m_new;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+            acc[0] += p[u] * bf16_lo(vv[u].x);
+            acc[1] += p[u] * bf16_hi(vv[u].x);
+            acc[2] += p[u] * bf16_lo(vv[u].y);
+            acc[3] += p[u] * bf16_hi(vv[u].y);
+            acc[4] += p[u] * bf16_lo(vv[u].z);
+            acc[5] += p[u] * bf16_hi(vv[u].z);
+            acc[6] += p[u] * bf16_lo(vv[u].w);
+            acc[7] += p[u] * bf16_hi(vv[u].w);
+        }
     }
-    for (int j = grp; j < n; j += 16) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(kb + (kbeg + j) * 128);
-        float s = qv[0] * bf16_lo(kk.x) + qv[1] * bf16_hi(kk.x);
-        s += qv[2] * bf16_lo(kk.y) + qv[3] * bf16_hi(kk.y);
-        s += qv[4] * bf16_lo(kk.z) + qv[5] * bf16_hi(kk.z);
-        s += qv[6] * bf16_lo(kk.w) + qv[7] * bf16_hi(kk.w);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        if (l16 == 0) sc[j] = s;
+    // merge the 16 groups (a group without keys has m = -inf and weight 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[grp][8 * l16 + e] = acc[e];
+    if (l16 == 0) {
+        red_m[grp] = m;
+        red_l[grp] = l;
     }
     __syncthreads();
-    float mx = -__builtin_inff();
-    for (int j = tid; j < n; j += 256) mx = fmaxf(mx, sc[j]);
-    mx = block_max(mx, sh);
-    float sm = 0.f;
-    for (int j = tid; j < n; j += 256) {
-        const float p = __builtin_amdgcn_exp2f(sc[j] - mx);
-        sc[j] = p;
-        sm += p;
-    }
-    sm = block_sum(sm, sh);   // its barriers also publish sc[]
-    float acc[8] = {};
-    auto pv = [&](float p, const u32x4& vv) {
-        acc[0] += p * bf16_lo(vv.x);
-        acc[1] += p * bf16_hi(vv.x);
-        acc[2] += p * bf16_lo(vv.y);
-        acc[3] += p * bf16_hi(vv.y);
-        acc[4] += p * bf16_lo(vv.z);
-        acc[5] += p * bf16_hi(vv.z);
-        acc[6] += p * bf16_lo(vv.w);
-        acc[7] += p * bf16_hi(vv.w);
-    };
-#pragma unroll
-    for (int e = 0; e < VPRE; ++e) {
-        const int j = grp + 16 * e;
-        if (j < n) pv(sc[j], vpre[e]);
-    }
-    for (int j = grp + 16 * VPRE; j < n; j += 16)
-        pv(sc[j], *reinterpret_cast<const u32x4*>(vb + (kbeg + j) * 128));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[grp][8 * l16 + e] = acc[e];
-    __syncthreads();
-    float* dst = scratch + (((b * hq + h) * nsplit) + split) * 130;
     if (tid < 128) {
-        float o = red[0][tid];
-        for (int r = 1; r < 16; ++r) o += red[r][tid];
-        dst[2 + tid] = o;
+        float M = red_m[0];
+        for (int r = 1; r < 16; ++r) M = fmaxf(M, red_m[r]);
+        float num = 0.f, den = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            const float w = __builtin_amdgcn_exp2f(red_m[r] - M);
+            num += w * red_o[r][tid];
+            den += w * red_l[r];
+        }
+        out[(b * hq + h) * 128 + tid] = f32_to_bf16(num / den);
     }
-    if (tid == 0) {
-        dst[0] = mx;
-        dst[1] = sm;
-    }
-}
-
-// grid (hq, B), 128 threads: merge the splits of one (sequence, head) into bf16 output
-__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ scratch,
-                                                             int nsplit, int hq,
-                                                             uint16_t* __restrict__ out) {
-    const int h = blockIdx.x, d = threadIdx.x;
-    const int64_t b = blockIdx.y;
-    const float* src = scratch + ((b * hq + h) * nsplit) * 130;
-    float M = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, src[s * 130]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float w = __builtin_amdgcn_exp2f(src[s * 130] - M);
-        num += w * src[s * 130 + 2 + d];
-        den += w * src[s * 130 + 1];
-    }
-    out[(b * hq + h) * 128 + d] = f32_to_bf16(num / den);
-}
-
-int64_t decode_chunk(int64_t L, int* nsplit_out) {
-    int64_t nsplit = 8;
-    int64_t chunk = (L + nsplit - 1) / nsplit;
-    chunk = ((chunk + 15) / 16) * 16;
-    if (chunk > CHUNK_MAX) chunk = CHUNK_MAX;
-    if (chunk < 16) chunk = 16;
-    *nsplit_out = (int)((L + chunk - 1) / chunk);
-    return chunk;
 }
 
 hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name) {
@@ -520,28 +487,20 @@ hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64
 }
 
 size_t decode_attn_scratch_bytes(int64_t B, int hq, int64_t L) {
-    int nsplit;
-    decode_chunk(L, &nsplit);
-    return (size_t)(B * hq * nsplit * 130) * sizeof(float);
+    (void)B;
+    (void)hq;
+    (void)L;
+    return 0;   // one pass, no per-split partials
 }
 
 hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache, int64_t B,
                        int hq, int hkv, int64_t L, int64_t cap, float* scratch, void* out,
                        hipStream_t s) {
-    int nsplit;
-    const int64_t chunk = decode_chunk(L, &nsplit);
-    {
-        ProfScope ps("decode_attn", s);
-        dim3 grid((unsigned)nsplit, (unsigned)hq, (unsigned)B);
-        const uint16_t* k = static_cast<const uint16_t*>(k_cache);
-        const uint16_t* v = static_cast<const uint16_t*>(v_cache);
-        decode_attn_kernel<4><<<grid, 256, 0, s>>>(q, k, v, hq, hkv, L, cap, chunk, scratch);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    ProfScope ps("decode_combine", s);
-    decode_combine_kernel<<<dim3((unsigned)hq, (unsigned)B), 128, 0, s>>>(scratch, nsplit, hq,
-                                                                        static_cast<uint16_t*>(out));
+    (void)scratch;
+    ProfScope ps("decode_attn", s);
+    decode_attn_kernel<<<dim3((unsigned)hq, (unsigned)B), 256, 0, s>>>(
+        q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), hq, hkv, L, cap,
+        static_cast<uint16_t*>(out));
     return hipGetLastError();
 }
 
