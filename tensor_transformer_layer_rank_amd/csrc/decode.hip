@@ -299,20 +299,22 @@ __global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict
     }
 }
 
-// Decode attention, one workgroup per (sequence, q head), one pass over the cache: the 16
+// Decode attention, one workgroup per (sequence, q head), one pass over the cache: the 32
 // lane groups (16 lanes x 8 dims = one 256-byte key or value row per group) take keys
-// grp, grp+16, ... four at a time (eight 16-byte loads per lane in flight), each group
-// keeping its own online softmax (running max in log2 units, sum, 128-dim output); the 16
+// grp, grp+32, ... four at a time (two sets of eight 16-byte loads per lane: the next four
+// keys are in flight while the current four are consumed), each group
+// keeping its own online softmax (running max in log2 units, sum, 128-dim output); the
 // groups are merged in LDS at the end and the normalised row is written as bf16.
-constexpr int DU = 4;   // keys per group per iteration
+constexpr int DU = 4;     // keys per group per iteration
+constexpr int NGRP = 32;  // 16-lane groups per workgroup
 
-__global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restrict__ q,
+__global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(const float* __restrict__ q,
                                                           const uint16_t* __restrict__ kc,
                                                           const uint16_t* __restrict__ vc,
                                                           int hq, int hkv, int64_t L, int64_t cap,
                                                           uint16_t* __restrict__ out) {
-    __shared__ float red_o[16][128];
-    __shared__ float red_m[16], red_l[16];
+    __shared__ float red_o[NGRP][128];
+    __shared__ float red_m[NGRP], red_l[NGRP];
     const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
     const int h = blockIdx.x;
     const int64_t b = blockIdx.y;
@@ -325,16 +327,17 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
     const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     float m = -__builtin_inff(), l = 0.f, acc[8] = {};
-    for (int64_t j0 = grp; j0 < L; j0 += 16 * DU) {
-        // keys past L are read from row L-1 (branch-free) and masked below
-        u32x4 kk[DU], vv[DU];
+    // keys past L are read from row L-1 (branch-free) and masked when consumed
+    auto load = [&](u32x4 (&kk)[DU], u32x4 (&vv)[DU], int64_t j0) {
 #pragma unroll
         for (int u = 0; u < DU; ++u) {
-            const int64_t j = j0 + 16 * u;
+            const int64_t j = j0 + NGRP * u;
             const int64_t jj = j < L ? j : L - 1;
             kk[u] = *reinterpret_cast<const u32x4*>(kb + jj * 128);
             vv[u] = *reinterpret_cast<const u32x4*>(vb + jj * 128);
         }
+    };
+    auto consume = [&](const u32x4 (&kk)[DU], const u32x4 (&vv)[DU], int64_t j0) {
         float sc[DU];
 #pragma unroll
         for (int u = 0; u < DU; ++u) {
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
             sc[u] += __shfl_xor(sc[u], 4);
             sc[u] += __shfl_xor(sc[u], 2);
             sc[u] += __shfl_xor(sc[u], 1);
-            if (j0 + 16 * u >= L) sc[u] = -__builtin_inff();
+            if (j0 + NGRP * u >= L) sc[u] = -__builtin_inff();
         }
         float mc = sc[0];
 #pragma unroll
@@ -378,8 +381,22 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
             acc[6] += p[u] * bf16_lo(vv[u].w);
             acc[7] += p[u] * bf16_hi(vv[u].w);
         }
+    };
+    // two register sets: the next DU keys of the group are in flight while the current ones
+    // are consumed
+    u32x4 k0[DU], v0[DU], k1[DU], v1[DU];
+    if (grp < L) load(k0, v0, grp);
+    for (int64_t j0 = grp; j0 < L; j0 += 2 * NGRP * DU) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(k1, v1, j0 + NGRP * DU);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(k0, v0, j0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(k0, v0, j0 + 2 * NGRP * DU);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j0 + NGRP * DU < L) consume(k1, v1, j0 + NGRP * DU);
     }
-    // merge the 16 groups (a group without keys has m = -inf and weight 0)
+    // merge the groups (a group without keys has m = -inf and weight 0)
 #pragma unroll
     for (int e = 0; e < 8; ++e) red_o[grp][8 * l16 + e] = acc[e];
     if (l16 == 0) {
@@ -389,9 +406,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const float* __restric
     __syncthreads();
     if (tid < 128) {
         float M = red_m[0];
-        for (int r = 1; r < 16; ++r) M = fmaxf(M, red_m[r]);
+        for (int r = 1; r < NGRP; ++r) M = fmaxf(M, red_m[r]);
         float num = 0.f, den = 0.f;
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < NGRP; ++r) {
             const float w = __builtin_amdgcn_exp2f(red_m[r] - M);
             num += w * red_o[r][tid];
             den += w * red_l[r];
@@ -498,7 +515,7 @@ hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache,
                        hipStream_t s) {
     (void)scratch;
     ProfScope ps("decode_attn", s);
-    decode_attn_kernel<<<dim3((unsigned)hq, (unsigned)B), 256, 0, s>>>(
+    decode_attn_kernel<<<dim3((unsigned)hq, (unsigned)B), NGRP * 16, 0, s>>>(
         q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), hq, hkv, L, cap,
         static_cast<uint16_t*>(out));
     return hipGetLastError();
