@@ -478,13 +478,13 @@ static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, 
         *part = c.take(*split_bytes);
         return c.off;
     }
-    const int64_t B = d->B, L = d->cache_len + 1;
+    const int64_t B = d->B;
     const size_t p1 = tpk::skinny_partials_bytes(B, nqkv, d->H);
     const size_t p2 = tpk::skinny_partials_bytes(B, d->H, hq * 128);
     *split_bytes = p1 > p2 ? p1 : p2;
     *part = c.take(*split_bytes);
-    *qbuf = c.take((size_t)(B * hq * 128) * 4);
-    *scratch = c.take(tpk::decode_attn_scratch_bytes(B, (int)hq, L));
+    *qbuf = nullptr;
+    *scratch = nullptr;
     *att = c.take((size_t)(B * hq * 128) * 2);
     return c.off;
 }
@@ -532,12 +532,9 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
                         "tp_attn_shard");
     }
     const int64_t B = desc->B;
-    hipError_t e = tpk::skinny_qkv_decode(X, W_qkv, static_cast<float*>(part), B, H, hq, hkv, desc->cache_len,
-                                          desc->rope_theta, static_cast<float*>(qbuf), desc->k_cache,
-                                          desc->v_cache, desc->cache_capacity, s);
-    if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
-    e = tpk::decode_attn(static_cast<const float*>(qbuf), desc->k_cache, desc->v_cache, B, hq, hkv,
-                         desc->cache_len + 1, desc->cache_capacity, static_cast<float*>(scratch), att, s);
+    hipError_t e = tpk::decode_attn_step(X, W_qkv, static_cast<float*>(part), B, H, hq, hkv, desc->cache_len,
+                                         desc->rope_theta, desc->k_cache, desc->v_cache, desc->cache_capacity,
+                                         att, s);
     if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
     return from_hip(tpk::skinny_linear(att, W_o, static_cast<float*>(part), B, H, dq, dq, Y_partial, H, 0, s),
                     "tp_attn_shard");

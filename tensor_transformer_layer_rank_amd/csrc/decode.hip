@@ -11,11 +11,12 @@
 //                        is written to a partial buffer.
 //   reduce kernels       sum the chunk partials in chunk order and apply the layer's
 //                        epilogue: fp32/bf16 store (O and down partials, vocabulary-split
-//                        logits), SiLU(gate)*up, or QKV: rotary embedding at the cache
-//                        position, key and value appended to the cache, q kept in fp32.
-//   decode_attn_kernel   attention of one query over cache slots 0..L-1 in a single pass:
-//                        16-lane groups stream 256-byte key and value rows with an online
-//                        softmax each, merged in LDS at the end.
+//                        logits) or SiLU(gate)*up.
+//   decode_attn_kernel   the QKV partials' reduction (rotary embedding at the cache position,
+//                        key and value appended to the cache) fused with the attention of
+//                        the new token over cache slots 0..pos in a single pass: 16-lane
+//                        groups stream 256-byte key and value rows with an online softmax
+//                        each, merged in LDS at the end.
 //
 // Partial sums across workgroups go through HBM-resident buffers and a separate kernel:
 // a device-scope fence per workgroup (L2 write-back and invalidate on this GPU) costs far
@@ -263,69 +264,79 @@ struct RopeRow {
     float c[64], s[64];
 };
 
-// one thread per (sequence, head, i < 64): heads 0..hq-1 are q, then hkv k heads, then hkv v
-// heads; q and k pairs (i, i+64) are rotated by the angle of pair i
-__global__ __launch_bounds__(256) void reduce_qkv_kernel(const float* __restrict__ part, int splits,
-                                                         int64_t B, int hq, int hkv, int64_t ncols,
-                                                         int64_t pos, RopeRow rope,
-                                                         float* __restrict__ qbuf,
-                                                         uint16_t* __restrict__ kc,
-                                                         uint16_t* __restrict__ vc, int64_t cap) {
-    const int nh = hq + 2 * hkv;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= B * nh * 64) return;
-    const int i = (int)(idx & 63);
-    const int head = (int)((idx >> 6) % nh);
-    const int64_t b = idx / (64 * nh);
-    const int64_t c = (int64_t)head * 128 + i;
-    const float x1 = sum_splits(part, splits, B, ncols, b, c);
-    const float x2 = sum_splits(part, splits, B, ncols, b, c + 64);
-    if (head >= hq + hkv) {
-        uint16_t* dst = vc + ((b * hkv + (head - hq - hkv)) * cap + pos) * 128;
-        dst[i] = f32_to_bf16(x1);
-        dst[i + 64] = f32_to_bf16(x2);
-        return;
-    }
-    const float cs = rope.c[i], sn = rope.s[i];
-    const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-    if (head < hq) {
-        float* dst = qbuf + (b * hq + head) * 128;
-        dst[i] = y1;
-        dst[i + 64] = y2;
-    } else {
-        uint16_t* dst = kc + ((b * hkv + (head - hq)) * cap + pos) * 128;
-        dst[i] = f32_to_bf16(y1);
-        dst[i + 64] = f32_to_bf16(y2);
-    }
-}
-
-// Decode attention, one workgroup per (sequence, q head), one pass over the cache: the 32
-// lane groups (16 lanes x 8 dims = one 256-byte key or value row per group) take keys
-// grp, grp+32, ... four at a time (two sets of eight 16-byte loads per lane: the next four
-// keys are in flight while the current four are consumed), each group
-// keeping its own online softmax (running max in log2 units, sum, 128-dim output); the
-// groups are merged in LDS at the end and the normalised row is written as bf16.
+// Decode attention, one workgroup per (sequence, q head), fused with the end of the QKV
+// projection. The workgroup first sums the split-K partials of its q head and of its kv
+// head's new key and value (fixed chunk order), rotates q and k by the angles of the cache
+// position, and - if it is the first q head of its kv group - appends the new key and
+// value (bf16) at that slot. It then attends in one pass: the 32 lane groups (16 lanes x 8
+// dims = one 256-byte key or value row per group) stream cache slots grp, grp+32, ... four
+// at a time (the next four in flight while the current ones are consumed), each group
+// keeping its own online softmax (running max in log2 units, sum, 128-dim output); the new
+// token's own key and value enter from LDS in fp32 (never read back from the cache, which
+// another workgroup of the group may still be writing). The groups are merged in LDS and
+// the normalised row is written as bf16.
 constexpr int DU = 4;     // keys per group per iteration
 constexpr int NGRP = 32;  // 16-lane groups per workgroup
 
-__global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(const float* __restrict__ q,
-                                                          const uint16_t* __restrict__ kc,
-                                                          const uint16_t* __restrict__ vc,
-                                                          int hq, int hkv, int64_t L, int64_t cap,
-                                                          uint16_t* __restrict__ out) {
+struct QkvPartials {
+    const float* part;   // [splits][B][ncols]: columns [q heads | k heads | v heads] x 128
+    int splits;
+    int64_t ncols;
+};
+
+__global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, RopeRow rope,
+                                                                int hq, int hkv, int64_t pos,
+                                                                int64_t cap, uint16_t* __restrict__ kc,
+                                                                uint16_t* __restrict__ vc,
+                                                                uint16_t* __restrict__ out) {
     __shared__ float red_o[NGRP][128];
     __shared__ float red_m[NGRP], red_l[NGRP];
+    __shared__ float qs[128], kn[128], vn[128];
     const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
     const int h = blockIdx.x;
     const int64_t b = blockIdx.y;
+    const int64_t B = gridDim.y;
     const int g = (h * hkv) / hq;
+    // q, new k (rotated pairs i, i+64) and new v of this head from the chunk partials
+    if (tid < 64) {
+        const int i = tid;
+        const float c = rope.c[i], sn = rope.s[i];
+        const int64_t cq = (int64_t)h * 128 + i, ck = (int64_t)(hq + g) * 128 + i;
+        const float q1 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, cq);
+        const float q2 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, cq + 64);
+        qs[i] = q1 * c - q2 * sn;
+        qs[i + 64] = q2 * c + q1 * sn;
+        const float k1 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, ck);
+        const float k2 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, ck + 64);
+        kn[i] = k1 * c - k2 * sn;
+        kn[i + 64] = k2 * c + k1 * sn;
+    } else if (tid < 192) {
+        const int d = tid - 64;
+        vn[d] = sum_splits(qp.part, qp.splits, B, qp.ncols, b, (int64_t)(hq + hkv + g) * 128 + d);
+    }
+    __syncthreads();
+    const int64_t slot = ((b * hkv + g) * cap + pos) * 128;
+    if (h % (hq / hkv) == 0 && tid < 128) {
+        kc[slot + tid] = f32_to_bf16(kn[tid]);
+        vc[slot + tid] = f32_to_bf16(vn[tid]);
+    }
+
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     float qv[8];
-    const float* qp = q + (b * hq + h) * 128 + 8 * l16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = qp[e] * scale;
+    for (int e = 0; e < 8; ++e) qv[e] = qs[8 * l16 + e] * scale;
+    // score of the new key (every group forms it; the 16 lanes of a group share it)
+    float s_new = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_new += qv[e] * kn[8 * l16 + e];
+    s_new += __shfl_xor(s_new, 8);
+    s_new += __shfl_xor(s_new, 4);
+    s_new += __shfl_xor(s_new, 2);
+    s_new += __shfl_xor(s_new, 1);
+
     const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
+    const int64_t L = pos;   // cached keys 0..pos-1
     float m = -__builtin_inff(), l = 0.f, acc[8] = {};
     // keys past L are read from row L-1 (branch-free) and masked when consumed
     auto load = [&](u32x4 (&kk)[DU], u32x4 (&vv)[DU], int64_t j0) {
@@ -405,9 +416,10 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(const float* __r
     }
     __syncthreads();
     if (tid < 128) {
-        float M = red_m[0];
-        for (int r = 1; r < NGRP; ++r) M = fmaxf(M, red_m[r]);
-        float num = 0.f, den = 0.f;
+        float M = s_new;   // the new key: one more "group" with max s_new, sum 1, output v_new
+        for (int r = 0; r < NGRP; ++r) M = fmaxf(M, red_m[r]);
+        const float w_new = __builtin_amdgcn_exp2f(s_new - M);
+        float num = w_new * vn[tid], den = w_new;
         for (int r = 0; r < NGRP; ++r) {
             const float w = __builtin_amdgcn_exp2f(red_m[r] - M);
             num += w * red_o[r][tid];
@@ -481,42 +493,24 @@ hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* p
     return hipGetLastError();
 }
 
-hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H,
-                             int hq, int hkv, int64_t pos, float theta, float* qbuf, void* k_cache,
-                             void* v_cache, int64_t cap, hipStream_t s) {
+hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H, int hq,
+                            int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
+                            void* out, hipStream_t s) {
     const int64_t N = (int64_t)(hq + 2 * hkv) * 128;
     SkinnyArgs a = skinny_args(X, Wqkv, nullptr, part, B, N, H, H);
     const SkinnyPlan p = plan_skinny(N, H, 1);
     hipError_t e = skinny_run(a, p, s, "skinny_gemm_qkv");
     if (e != hipSuccess) return e;
-    const int64_t n = B * (hq + 2 * hkv) * 64;
     RopeRow rope;
     for (int i = 0; i < 64; ++i) {
         const double ang = (double)pos * std::pow((double)theta, -2.0 * (double)i / 128.0);
         rope.c[i] = (float)std::cos(ang);
         rope.s[i] = (float)std::sin(ang);
     }
-    ProfScope ps("skinny_reduce_qkv", s);
-    reduce_qkv_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-        part, (int)p.splits, B, hq, hkv, p.ncols, pos, rope, qbuf,
-        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), cap);
-    return hipGetLastError();
-}
-
-size_t decode_attn_scratch_bytes(int64_t B, int hq, int64_t L) {
-    (void)B;
-    (void)hq;
-    (void)L;
-    return 0;   // one pass, no per-split partials
-}
-
-hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache, int64_t B,
-                       int hq, int hkv, int64_t L, int64_t cap, float* scratch, void* out,
-                       hipStream_t s) {
-    (void)scratch;
+    const QkvPartials qp{part, (int)p.splits, p.ncols};
     ProfScope ps("decode_attn", s);
     decode_attn_kernel<<<dim3((unsigned)hq, (unsigned)B), NGRP * 16, 0, s>>>(
-        q, static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), hq, hkv, L, cap,
+        qp, rope, hq, hkv, pos, cap, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
         static_cast<uint16_t*>(out));
     return hipGetLastError();
 }

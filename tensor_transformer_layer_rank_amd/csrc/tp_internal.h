@@ -84,14 +84,13 @@ hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* p
                          int64_t M, int64_t I, int64_t H, hipStream_t s);
 // QKV of one decode step: q (rotated, fp32) to qbuf [B, hq, 128]; rotated k and v appended to the
 // caches at slot pos
-hipError_t skinny_qkv_decode(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H,
-                             int hq, int hkv, int64_t pos, float theta, float* qbuf, void* k_cache,
-                             void* v_cache, int64_t cap, hipStream_t s);
-// split-KV decode attention: out bf16 [B, hq*128]; scratch for per-split (m, l, o)
-size_t decode_attn_scratch_bytes(int64_t B, int hq, int64_t L);
-hipError_t decode_attn(const float* q, const void* k_cache, const void* v_cache, int64_t B,
-                       int hq, int hkv, int64_t L, int64_t cap, float* scratch, void* out,
-                       hipStream_t s);
+// decode attention step of an attention shard: QKV split-K partials (workspace `part`,
+// skinny_partials_bytes(B, (hq + 2 hkv) * 128, H)), then one fused kernel that reduces them,
+// rotates q and k by position pos, appends k and v (bf16) at cache slot pos and attends over
+// slots 0..pos; out = bf16 [B, hq * 128]
+hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H, int hq,
+                            int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
+                            void* out, hipStream_t s);
 
 // ---- merges -------------------------------------------------------------------------------
 hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s);

@@ -359,7 +359,8 @@ def _decode(tp, inp):
     return host(Y), host(kc), host(vc)
 
 
-@pytest.mark.parametrize("B,H,hq,hkv,L,cap", [(4, 256, 2, 2, 37, 40), (3, 512, 4, 1, 300, 301), (32, 256, 2, 2, 1, 8)])
+@pytest.mark.parametrize("B,H,hq,hkv,L,cap", [(4, 256, 2, 2, 37, 40), (3, 512, 4, 1, 300, 301), (32, 256, 2, 2, 1, 8),
+                                              (2, 256, 4, 2, 0, 4), (5, 256, 8, 2, 1000, 1003)])
 def test_decode_attn_small(tp, B, H, hq, hkv, L, cap):
     inp = wl.random_decode(B + L, B, H, hq, hkv, 64, 64, L, cap)
     y, kc, vc = _decode(tp, inp)
