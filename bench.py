@@ -45,8 +45,20 @@ def parse():
     return ap.parse_args()
 
 
-def timed(step, warmup: int, steps: int):
-    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step."""
+STEP_STATS = {}
+
+
+def _stats(name: str, per_step_ms):
+    xs = sorted(per_step_ms)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    STEP_STATS[name] = {"median_ms": med, "min_ms": xs[0], "max_ms": xs[-1]}
+
+
+def timed(step, warmup: int, steps: int, name: str = None):
+    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step (total
+    over the window / steps). An event after every step also gives the per-step median and
+    minimum (kept in STEP_STATS[name])."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     for _ in range(warmup):
@@ -55,15 +67,17 @@ def timed(step, warmup: int, steps: int):
     tp.profile_reset()
     tp.profile_enable(True)
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    e0.record(s)
-    for _ in range(steps):
+    ev[0].record(s)
+    for i in range(steps):
         step()
-    e1.record(s)
+        ev[i + 1].record(s)
     torch.cuda.synchronize()
     tp.profile_enable(False)
-    return e0.elapsed_time(e1) / steps
+    if name:
+        _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return ev[0].elapsed_time(ev[steps]) / steps
 
 
 def kernel_avg(prefix: str):
@@ -86,7 +100,7 @@ def mlp_bench(args):
     def step():
         tp.mlp_shard(X, Wg, Wu, Wd, Y=Y, workspace=ws)
 
-    ms = timed(step, args.warmup, args.steps)
+    ms = timed(step, args.warmup, args.steps, "mlp")
     gu_ms, gu_n = kernel_avg("gemm_bf16_swiglu")
     fx_ms, fx_n = kernel_avg("fixup_swiglu")
     dn_ms, dn_n = kernel_avg("gemm_bf16_f32out")
@@ -109,6 +123,7 @@ def mlp_bench(args):
             "gemm_bf16_f32out(down)": {"avg_us": dn_ms * 1e3, "launches": dn_n,
                                        "tflops": flops_dn / (dn_ms * 1e-3) / 1e12},
         },
+        "step_stats": STEP_STATS.get("mlp"),
         "roofline": {
             "bound": "mfma", "kernel": "gemm_bf16_swiglu",
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
@@ -135,7 +150,7 @@ def fp8_mlp_bench(args):
     def step():
         tp.mlp_shard_fp8(X, Wg, Wu, Wd, scales, Y=Y, workspace=ws)
 
-    ms = timed(step, args.warmup, args.steps)
+    ms = timed(step, args.warmup, args.steps, "fp8_mlp")
     gu_ms, gu_n = kernel_avg("gemm_f8_swiglu")
     fx_ms, fx_n = kernel_avg("fixup_swiglu")
     dn_ms, _ = kernel_avg("gemm_f8_f32out")
@@ -150,6 +165,7 @@ def fp8_mlp_bench(args):
         "ms_per_step": ms,
         "tflops": tf,
         "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+        "step_stats": STEP_STATS.get("fp8_mlp"),
         "kernels": {"gemm_f8_swiglu(+fixup)": {"avg_us": gu_ms * 1e3, "tflops": flops_gu / (gu_ms * 1e-3) / 1e12},
                     "gemm_f8_f32out(down)": {"avg_us": dn_ms * 1e3, "tflops": flops_dn / (dn_ms * 1e-3) / 1e12}},
         "roofline": {"bound": "mfma", "kernel": "gemm_f8_swiglu", "achieved": flops_gu / (gu_ms * 1e-3) / 1e12,
@@ -159,8 +175,9 @@ def fp8_mlp_bench(args):
     }
 
 
-def graph_timed(step, warmup: int, steps: int):
-    """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays."""
+def graph_timed(step, warmup: int, steps: int, name: str = None):
+    """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
+    (per-replay median and minimum kept in STEP_STATS[name])."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -174,13 +191,15 @@ def graph_timed(step, warmup: int, steps: int):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    if name:
+        _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return ev[0].elapsed_time(ev[steps]) / steps
 
 
 def decode_bench(args):
@@ -227,7 +246,7 @@ def decode_bench(args):
 
     ms_eager = timed(step, args.warmup, args.steps)       # per-kernel HIP-event timing
     ms_serial = graph_timed(step, args.warmup, args.steps)
-    ms = graph_timed(step_branches, args.warmup, args.steps)   # the step as one HIP graph
+    ms = graph_timed(step_branches, args.warmup, args.steps, "decode")   # the step as one HIP graph
     d = 128
     w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
     kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
@@ -240,6 +259,7 @@ def decode_bench(args):
         "ms_per_step": ms,
         "ms_per_step_eager": ms_eager,
         "ms_per_step_graph_serial": ms_serial,
+        "step_stats": STEP_STATS.get("decode"),
         "graph": "one HIP graph per step: attention, MLP and LM-head branches on separate streams",
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
@@ -391,6 +411,7 @@ def main():
                    "decode_ms_per_step": round(dec["ms_per_step"], 5)},
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in mlp["roofline"].items()},
         "cpu_baseline": cpu and {k: v for k, v in cpu.items() if k != "seconds"},
+        "step_stats": mlp["step_stats"],
         "kernels": mlp["kernels"],
         "decode": dec,
         "fp8_mlp": fp8,

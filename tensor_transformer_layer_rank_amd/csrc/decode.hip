@@ -44,12 +44,16 @@ struct SkinnyPlan {
     int64_t strips_per_b, strips, kchunk, splits, ncols;
 };
 
+// Grid of one launch: K is split so that the launch has ~256 workgroups (one per compute
+// unit). Measured on the decode step: with the step's sub-layers as parallel graph branches,
+// grids that leave each compute unit a second workgroup slot overlap better with the other
+// branches than grids of ~512 workgroups, although the latter stream a lone GEMM faster.
 SkinnyPlan plan_skinny(int64_t N, int64_t K, int nb) {
     SkinnyPlan p;
     p.strips_per_b = (N + STRIP - 1) / STRIP;
     p.strips = p.strips_per_b * nb;
     p.ncols = p.strips * STRIP;
-    int64_t target = (256 + p.strips - 1) / p.strips;   // aim for ~256 workgroups (one round)
+    int64_t target = (256 + p.strips - 1) / p.strips;
     if (target < 1) target = 1;
     int64_t kchunk = (K + target - 1) / target;
     kchunk = ((kchunk + 4 * STEP - 1) / (4 * STEP)) * (4 * STEP);   // whole steps for all 4 waves
@@ -224,12 +228,32 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
 #undef TP_RED_ADD
 }
 
-// out[m][n] = sum over chunks (in order) of part[s][m][n]
-__device__ __forceinline__ float sum_splits(const float* part, int splits, int64_t M,
-                                            int64_t ncols, int64_t m, int64_t c) {
-    float v = part[m * ncols + c];
-    for (int s = 1; s < splits; ++s) v += part[((int64_t)s * M + m) * ncols + c];
-    return v;
+// v[i] = sum over chunks (in order) of part[s][m][c[i]] for NC columns of row m. The chunks'
+// values are loaded 8 at a time for all NC columns together, unconditionally (chunk indexes
+// past the last one re-read the last), so that a thread waits for one memory round trip per
+// 8 chunks rather than one per chunk and column.
+template <int NC>
+__device__ __forceinline__ void sum_splits(const float* part, int splits, int64_t M, int64_t ncols,
+                                           int64_t m, const int64_t (&c)[NC], float (&v)[NC]) {
+    constexpr int U = 8;
+    const float* p = part + m * ncols;
+    const int64_t stride = M * ncols;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) v[i] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += U) {
+        float t[U][NC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float* ps = p + (int64_t)(s0 + u < splits ? s0 + u : splits - 1) * stride;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) t[u][i] = ps[c[i]];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < NC; ++i)
+                if (s0 + u < splits) v[i] = (s0 + u == 0) ? t[u][i] : v[i] + t[u][i];
+    }
 }
 
 // kind: 0 fp32 store, 1 fp32 +=, 2 bf16, 3 bf16 ReLU
@@ -239,7 +263,10 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restri
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= M * N) return;
     const int64_t m = idx / N, n = idx - m * N;
-    const float v = sum_splits(part, splits, M, ncols, m, n);
+    const int64_t cols[1] = {n};
+    float sum[1];
+    sum_splits<1>(part, splits, M, ncols, m, cols, sum);
+    const float v = sum[0];
     const int64_t off = m * ldc + n;
     if (kind == 0) static_cast<float*>(C)[off] = v;
     else if (kind == 1) static_cast<float*>(C)[off] += v;
@@ -253,8 +280,10 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= M * I) return;
     const int64_t m = idx / I, c = idx - m * I;
-    const float gt = sum_splits(part, splits, M, ncols, m, c);
-    const float up = sum_splits(part, splits, M, ncols, m, up_off + c);
+    const int64_t cols[2] = {c, up_off + c};
+    float sum[2];
+    sum_splits<2>(part, splits, M, ncols, m, cols, sum);
+    const float gt = sum[0], up = sum[1];
     h[idx] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
 }
 
@@ -265,8 +294,9 @@ struct RopeRow {
 };
 
 // Decode attention, one workgroup per (sequence, q head), fused with the end of the QKV
-// projection. The workgroup first sums the split-K partials of its q head and of its kv
-// head's new key and value (fixed chunk order), rotates q and k by the angles of the cache
+// projection. With its first cached keys and values already requested, the workgroup sums
+// the split-K partials of its q head and of its kv head's new key and value (fixed chunk
+// order, all loads of 8 chunks in flight together), rotates q and k by the angles of the cache
 // position, and - if it is the first q head of its kv group - appends the new key and
 // value (bf16) at that slot. It then attends in one pass: the 32 lane groups (16 lanes x 8
 // dims = one 256-byte key or value row per group) stream cache slots grp, grp+32, ... four
@@ -297,22 +327,43 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     const int64_t b = blockIdx.y;
     const int64_t B = gridDim.y;
     const int g = (h * hkv) / hq;
+    const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
+    const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
+    const int64_t L = pos;   // cached keys 0..pos-1
+    // keys past L are read from row L-1 (branch-free) and masked when consumed
+    auto load = [&](u32x4 (&kk)[DU], u32x4 (&vv)[DU], int64_t j0) {
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+            const int64_t j = j0 + NGRP * u;
+            const int64_t jj = j < L ? j : L - 1;
+            kk[u] = *reinterpret_cast<const u32x4*>(kb + jj * 128);
+            vv[u] = *reinterpret_cast<const u32x4*>(vb + jj * 128);
+        }
+    };
+    // the group's first keys and values (slots < pos, which the append below never writes)
+    // are requested before the QKV partials are summed, so the two round trips overlap
+    u32x4 k0[DU], v0[DU];
+    if (grp < L) load(k0, v0, grp);
     // q, new k (rotated pairs i, i+64) and new v of this head from the chunk partials
     if (tid < 64) {
         const int i = tid;
         const float c = rope.c[i], sn = rope.s[i];
         const int64_t cq = (int64_t)h * 128 + i, ck = (int64_t)(hq + g) * 128 + i;
-        const float q1 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, cq);
-        const float q2 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, cq + 64);
-        qs[i] = q1 * c - q2 * sn;
-        qs[i + 64] = q2 * c + q1 * sn;
-        const float k1 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, ck);
-        const float k2 = sum_splits(qp.part, qp.splits, B, qp.ncols, b, ck + 64);
-        kn[i] = k1 * c - k2 * sn;
-        kn[i + 64] = k2 * c + k1 * sn;
-    } else if (tid < 192) {
+        const int64_t cols[4] = {cq, cq + 64, ck, ck + 64};
+        float x[4];
+        sum_splits<4>(qp.part, qp.splits, B, qp.ncols, b, cols, x);
+        qs[i] = x[0] * c - x[1] * sn;
+        qs[i + 64] = x[1] * c + x[0] * sn;
+        kn[i] = x[2] * c - x[3] * sn;
+        kn[i + 64] = x[3] * c + x[2] * sn;
+    } else if (tid < 128) {
         const int d = tid - 64;
-        vn[d] = sum_splits(qp.part, qp.splits, B, qp.ncols, b, (int64_t)(hq + hkv + g) * 128 + d);
+        const int64_t cv = (int64_t)(hq + hkv + g) * 128 + d;
+        const int64_t cols[2] = {cv, cv + 64};
+        float x[2];
+        sum_splits<2>(qp.part, qp.splits, B, qp.ncols, b, cols, x);
+        vn[d] = x[0];
+        vn[d + 64] = x[1];
     }
     __syncthreads();
     const int64_t slot = ((b * hkv + g) * cap + pos) * 128;
@@ -321,6 +372,7 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
         vc[slot + tid] = f32_to_bf16(vn[tid]);
     }
 
+    float m = -__builtin_inff(), l = 0.f, acc[8] = {};
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     float qv[8];
 #pragma unroll
@@ -334,20 +386,6 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     s_new += __shfl_xor(s_new, 2);
     s_new += __shfl_xor(s_new, 1);
 
-    const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
-    const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
-    const int64_t L = pos;   // cached keys 0..pos-1
-    float m = -__builtin_inff(), l = 0.f, acc[8] = {};
-    // keys past L are read from row L-1 (branch-free) and masked when consumed
-    auto load = [&](u32x4 (&kk)[DU], u32x4 (&vv)[DU], int64_t j0) {
-#pragma unroll
-        for (int u = 0; u < DU; ++u) {
-            const int64_t j = j0 + NGRP * u;
-            const int64_t jj = j < L ? j : L - 1;
-            kk[u] = *reinterpret_cast<const u32x4*>(kb + jj * 128);
-            vv[u] = *reinterpret_cast<const u32x4*>(vb + jj * 128);
-        }
-    };
     auto consume = [&](const u32x4 (&kk)[DU], const u32x4 (&vv)[DU], int64_t j0) {
         float sc[DU];
 #pragma unroll
@@ -395,8 +433,7 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     };
     // two register sets: the next DU keys of the group are in flight while the current ones
     // are consumed
-    u32x4 k0[DU], v0[DU], k1[DU], v1[DU];
-    if (grp < L) load(k0, v0, grp);
+    u32x4 k1[DU], v1[DU];
     for (int64_t j0 = grp; j0 < L; j0 += 2 * NGRP * DU) {
         __builtin_amdgcn_sched_barrier(0);
         load(k1, v1, j0 + NGRP * DU);
