@@ -21,7 +21,9 @@
 // S^T = K Q^T (v_mfma_f32_32x32x16_f16, keys = rows), so each lane holds 16 of the 32
 // scores of ONE query: the online-softmax max and sum need only the lane's own registers
 // plus one exchange with the lane 32 apart. P^T stays in registers as the B operand of
-// O^T += V^T P^T. Exponentials use exp2 with log2(e)/sqrt(128) folded into the scale.
+// O^T += V^T P^T. Exponentials use exp2 with log2(e)/sqrt(128) folded into the scale, and
+// the exponent base of a query moves only when a block raises its maximum by more than 2^8
+// (lazy rescaling), so the rescale of the accumulators is skipped on almost every block.
 #include "tp_internal.h"
 
 namespace tpk {
@@ -31,7 +33,12 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
+#ifndef FA_SPLIT_QK
+#define FA_SPLIT_QK 0
+#endif
+
 constexpr int QB = 128;          // queries per workgroup
+constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units): probabilities <= 256
 constexpr int NWAVE = 8;         // 4 query slabs x 2 key halves
 constexpr int NT = NWAVE * 64;
 constexpr int KB = 64;           // keys per block
@@ -152,6 +159,7 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
         if (kb + 2 < nkb) load_kv(rb, kp, vp, S, (int64_t)(kb + 2) * KB, tid);
         const int64_t key0 = (int64_t)kb * KB + kh * 32;   // this wave's 32 keys
         if (key0 <= q0 + 31 && q0 < S && key0 < S) {       // some key visible to the slab
+#if FA_SPLIT_QK
             // two independent accumulation chains (even / odd 16-dim slices)
             f32x16 sa, sb;
 #pragma unroll
@@ -171,6 +179,19 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
             f32x16 st;
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[r] = sa[r] + sb[r];
+#else
+            // one accumulation chain over the 8 16-dim slices (the other wave of the SIMD
+            // fills the dependent-issue gaps; two chains would cost 16 adds per block)
+            f32x16 st;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+#pragma unroll
+            for (int dk = 0; dk < 8; ++dk) {
+                const f16x8 a0 = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + hi)));
+                st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[dk], st, 0, 0, 0);
+            }
+#endif
             // mask (keys past the query or past S), block max of the raw scores
             const bool diag = key0 + 31 > q0 || key0 + 32 > S;
             if (diag) {
@@ -186,9 +207,23 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
 #pragma unroll
             for (int r = 1; r < 16; ++r) mblk = fmaxf(mblk, st[r]);
             mblk = fmaxf(mblk, __shfl_xor(mblk, 32)) * scale;   // scale > 0 keeps the order
-            const float m_new = fmaxf(m_run, mblk);
-            const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            // Lazy rescaling: m_run, the exponent base, moves only when some query's block
+            // maximum exceeds it by more than TAU (log2 units). Every probability is then at
+            // most 2^TAU (exact in fp16, no overflow in the fp32 sums), and the rescale of l
+            // and the 64 accumulators runs only on the few blocks that raise a base. The
+            // result is the same softmax: the base cancels in the final division. -inf + TAU
+            // is -inf, so a query's first visible key always sets its base.
+            if (__ballot(mblk > m_run + TAU)) {
+                const float m_new = fmaxf(m_run, mblk);
+                const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // all keys masked so far
             float lsum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -197,16 +232,7 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
                 lsum += p;
             }
             lsum += __shfl_xor(lsum, 32);
-            l_run = l_run * alpha + lsum;
-            m_run = m_new;
-            // the running max rarely moves once a few blocks are in: skip the rescale of the
-            // accumulators when no query of the wave needs it (alpha == 1 exactly)
-            if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
+            l_run += lsum;
             // O^T += V^T P^T over this wave's two sub-blocks of 16 keys
             const unsigned char* vs = cur + K_TILE;
 #pragma unroll

@@ -418,33 +418,47 @@ struct EpiQKV {
             const int hh = is_q ? head : head - o.hq;
             const int nh = is_q ? o.hq : o.hkv;
             uint16_t* dst = static_cast<uint16_t*>(is_q ? o.q : o.k);
+            // rows 4q..4q+3 of a lane are consecutive tokens of one sequence (M and S are
+            // multiples of 8): one 32-bit division per group of 4 (B*S < 2^31, checked on
+            // the host)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                if (row >= M) continue;
-                const int64_t b = row / S, s = row - b * S;
-                uint16_t* out = dst + ((b * nh + hh) * S + s) * 128;
+            for (int rq = 0; rq < 4; ++rq) {
+                const int64_t row0 = m0 + wm * 128 + acc_row(i, 4 * rq, hi);
+                if (row0 >= M) continue;
+                const unsigned b = (unsigned)row0 / (unsigned)S;
+                const int64_t s0 = row0 - (int64_t)b * S;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int c = j * 32 + r32;               // pair (c, c + 64)
-                    const float2 cs = o.rope[s * 64 + c];
-                    const float x1 = a[j][r], x2 = a[j + 2][r];
-                    out[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
-                    out[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rq + e;
+                    const int64_t s = s0 + e;
+                    uint16_t* out = dst + (((int64_t)b * nh + hh) * S + s) * 128;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int c = j * 32 + r32;               // pair (c, c + 64)
+                        const float2 cs = o.rope[s * 64 + c];
+                        const float x1 = a[j][r], x2 = a[j + 2][r];
+                        out[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
+                        out[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
+                    }
                 }
             }
         } else {
+            // V^T: a lane's registers 4q..4q+3 are 4 consecutive tokens of one dim, written
+            // as one 8-byte store (M and S are multiples of 8, so the 4 tokens are all valid
+            // and lie in one sequence)
             const int hv = head - o.hq - o.hkv;
             uint16_t* vt = static_cast<uint16_t*>(o.vt);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
+            for (int rq = 0; rq < 4; ++rq) {
+                const int64_t row = m0 + wm * 128 + acc_row(i, 4 * rq, hi);
                 if (row >= M) continue;
-                const int64_t b = row / S, s = row - b * S;
+                const int64_t b = (unsigned)row / (unsigned)S, s = row - b * S;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int d = j * 32 + r32;
-                    vt[((b * o.hkv + hv) * 128 + d) * S + s] = f32_to_f16(a[j][r]);
+                    const unsigned lo = (unsigned)f32_to_f16(a[j][4 * rq]) | ((unsigned)f32_to_f16(a[j][4 * rq + 1]) << 16);
+                    const unsigned hi2 = (unsigned)f32_to_f16(a[j][4 * rq + 2]) | ((unsigned)f32_to_f16(a[j][4 * rq + 3]) << 16);
+                    *reinterpret_cast<uint2*>(vt + ((b * o.hkv + hv) * 128 + d) * S + s) = make_uint2(lo, hi2);
                 }
             }
         }
