@@ -617,7 +617,7 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
     }
 }
 
-// Tail split: the first g_full tiles (one full round of the machine, or more) run whole;
+// Tail split: the first g_full tiles (whole rounds of the machine, possibly none) run whole;
 // each of the remaining tiles is cut into `pieces` K ranges of piece_steps K steps, one
 // workgroup each, whose accumulators go to `part` in register order; gemm_fixup_kernel then
 // sums a tile's pieces in piece order and runs the epilogue.
@@ -772,15 +772,27 @@ int cu_count() {
 
 // How a grid of G tiles (nk K steps each) is cut: full tiles for whole rounds of the machine,
 // the rest split into pieces so that the last round is filled.
+// The tail (the tiles past the last full round, or the whole grid if it is smaller than the
+// machine) is cut into the fewest pieces p <= 4 that minimise its duration ceil(tail*p/n_cu)/p
+// in tile times, if that saves at least a fifth of a tile time (the fix-up pass costs about
+// a tenth) and every piece keeps at least 2 K steps. Examples on 256 units: a tail of 96 or 128
+// tiles -> 2 pieces (one round of half tiles); a grid of 160 tiles -> 3 pieces (two rounds of
+// third tiles instead of one round at 5/8 occupancy).
 SplitArgs plan_split(int64_t G, int nk, int n_cu) {
     SplitArgs sp{(int)G, 1, nk, nullptr};
-    if (G <= n_cu) return sp;
     const int64_t full = (G / n_cu) * n_cu;
     const int64_t tail = G - full;
     if (tail == 0) return sp;
-    int pieces = (int)(n_cu / tail);
-    if (pieces > 4) pieces = 4;
-    if (pieces < 2 || nk < 2 * pieces) return sp;
+    int pieces = 1;
+    double best = 1.0;
+    for (int p = 2; p <= 4 && nk >= 2 * p; ++p) {
+        const double t = (double)((tail * p + n_cu - 1) / n_cu) / p;
+        if (t < best - 1e-9) {
+            best = t;
+            pieces = p;
+        }
+    }
+    if (pieces < 2 || best > 0.8) return sp;
     sp.g_full = (int)full;
     sp.pieces = pieces;
     sp.piece_steps = (nk + pieces - 1) / pieces;

@@ -170,11 +170,13 @@ def test_row_partials_sum_to_unsharded_layer(tp):
     assert_close_bf16(host(Y), O.linear(X, W), "sum of row partials")
 
 
-# Grids past one round of the 256 compute units: the tiles after the last full round are
-# cut along K into 4 (272 tiles), 3 (336 tiles) or 2 (352 tiles) pieces whose fp32 partials
-# a fix-up pass sums; ragged M, N and K so that the last piece holds the K tail.
+# Tail split on 256 compute units: the tiles after the last full round are cut along K into
+# 4 (272 tiles), 3 (336 tiles) or 2 (352 tiles) pieces whose fp32 partials a fix-up pass
+# sums; grids smaller than the machine are cut too: 160 tiles into 3 pieces (two rounds of
+# thirds), 32 tiles into 4. Ragged M, N and K so that the last piece holds the K tail.
 @pytest.mark.parametrize("T,K,N,out", [(4200, 296, 4096, "bf16"), (5376, 200, 4096, "f32"),
-                                       (5632, 136, 4096, "bf16"), (4100, 1000, 4000, "f32")])
+                                       (5632, 136, 4096, "bf16"), (4100, 1000, 4000, "f32"),
+                                       (2048, 1000, 5120, "f32"), (1000, 520, 2000, "bf16")])
 def test_column_linear_tail_split(tp, T, K, N, out):
     import torch
     rng = np.random.default_rng(T + K)
