@@ -12,9 +12,11 @@
 //
 // Work split: one workgroup = 8 wave64s = 128 consecutive queries of one (sequence, head),
 // one workgroup per compute unit (2 waves per SIMD). Keys are visited in blocks of 64 up to
-// the causal diagonal, double-buffered in LDS; wave (slab, half) owns 32 queries and the 32
-// keys `half` of every block, and the two halves of a slab are merged once at the end (max,
-// sum and output of two online softmaxes). The grid (4 sequences x 8 heads x 16 query blocks
+// the causal diagonal; wave (slab, half) owns 32 queries and the 32 keys `half` of every
+// block, and the two halves of a slab are merged once at the end (max, sum and output of two
+// online softmaxes). The block loop is software-pipelined: the QK MFMAs of block kb+1 are
+// issued while the VALU forms block kb's probabilities, with K one block ahead of V in the
+// double-buffered LDS tiles. The grid (4 sequences x 8 heads x 16 query blocks
 // = 512 for S = 2048) is twice the number of compute units and is dealt heaviest (longest
 // causal prefix) first, so a unit that finishes a short block early takes the next longest:
 // the causal triangle balances out across two rounds. The scores are formed transposed,
@@ -67,8 +69,7 @@ struct KVRegs {
 // Keys past S are fetched from the last valid row / chunk instead (branch-free loads): their
 // scores are masked to -inf, so their probabilities are exactly 0 and the finite stand-in
 // values contribute nothing. S is a multiple of 8, so an 8-key chunk is wholly in or out.
-__device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* kp, const uint16_t* vp,
-                                        int64_t S, int64_t key0, int tid) {
+__device__ __forceinline__ void load_k(KVRegs& r, const uint16_t* kp, int64_t S, int64_t key0, int tid) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int q = tid + p * NT;
@@ -76,30 +77,54 @@ __device__ __forceinline__ void load_kv(KVRegs& r, const uint16_t* kp, const uin
         const int64_t key = (key0 + row < S) ? key0 + row : S - 1;
         r.k[p] = *reinterpret_cast<const u32x4*>(kp + key * 128 + c * 8);
     }
-    {
-        const int d = tid >> 2, grp = tid & 3;
-        const int64_t key = key0 + grp * 16;
-        const int64_t k_lo = (key < S) ? key : S - 8;
-        const int64_t k_hi = (key + 8 < S) ? key + 8 : S - 8;
-        r.v[0] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_lo);
-        r.v[1] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_hi);
-    }
+}
+__device__ __forceinline__ void load_v(KVRegs& r, const uint16_t* vp, int64_t S, int64_t key0, int tid) {
+    const int d = tid >> 2, grp = tid & 3;
+    const int64_t key = key0 + grp * 16;
+    const int64_t k_lo = (key < S) ? key : S - 8;
+    const int64_t k_hi = (key + 8 < S) ? key + 8 : S - 8;
+    r.v[0] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_lo);
+    r.v[1] = *reinterpret_cast<const u32x4*>(vp + (int64_t)d * S + k_hi);
 }
 
-// V^T chunk order inside each group of 16 keys: [k0..k3, k8..k11] [k4..k7, k12..k15], so that
-// the MFMA lane half `hi` reads the 8 keys its P^T registers hold with one 16-byte load.
-__device__ __forceinline__ void store_kv(const KVRegs& r, unsigned char* st, int tid) {
+__device__ __forceinline__ void store_k(const KVRegs& r, unsigned char* ks, int tid) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int q = tid + p * NT;
-        *reinterpret_cast<u32x4*>(st + k_off(q >> 4, q & 15)) = r.k[p];
+        *reinterpret_cast<u32x4*>(ks + k_off(q >> 4, q & 15)) = r.k[p];
     }
-    unsigned char* vs = st + K_TILE;
-    {
-        const int d = tid >> 2, grp = tid & 3;
-        const u32x4 a = r.v[0], b = r.v[1];
-        *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp)) = u32x4{a.x, a.y, b.x, b.y};
-        *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp + 1)) = u32x4{a.z, a.w, b.z, b.w};
+}
+// V^T chunk order inside each group of 16 keys: [k0..k3, k8..k11] [k4..k7, k12..k15], so that
+// the MFMA lane half `hi` reads the 8 keys its P^T registers hold with one 16-byte load.
+__device__ __forceinline__ void store_v(const KVRegs& r, unsigned char* vs, int tid) {
+    const int d = tid >> 2, grp = tid & 3;
+    const u32x4 a = r.v[0], b = r.v[1];
+    *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp)) = u32x4{a.x, a.y, b.x, b.y};
+    *reinterpret_cast<u32x4*>(vs + v_off(d, 2 * grp + 1)) = u32x4{a.z, a.w, b.z, b.w};
+}
+
+// S^T of one wave: its 32 keys (rows, from the K tile in LDS) x its 32 queries (qf), d = 128
+__device__ __forceinline__ f32x16 qk_tile(const unsigned char* ks, const f16x8 (&qf)[8], int kh, int r32,
+                                          int hi) {
+    f32x16 st;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk) {
+        const f16x8 a0 = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(ks + k_off(kh * 32 + r32, dk * 2 + hi)));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[dk], st, 0, 0, 0);
+    }
+    return st;
+}
+
+// -inf on the keys past the lane's query or past S (key0 = the wave's first key of the block)
+__device__ __forceinline__ void mask_tile(f32x16& st, int64_t qrow, int64_t S, int64_t key0, int hi) {
+    const int64_t lim64 = ((qrow < S - 1) ? qrow : S - 1) - key0;   // last visible key offset
+    const int lim = (int)(lim64 < -1 ? -1 : (lim64 > 32 ? 32 : lim64));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
+        st[r] = (kr > lim) ? -__builtin_inff() : st[r];
     }
 }
 
@@ -146,110 +171,88 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
     if (kend > S) kend = S;
     const int nkb = (int)((kend + KB - 1) / KB);
 
-    // K/V of block kb+1 are in registers (ra) while block kb is computed; block kb+2 is
-    // requested (rb) before block kb's MFMAs, so every load has a whole block to land
+    // Software pipeline over key blocks: iteration kb issues the QK MFMAs of block kb+1 while
+    // the VALU turns block kb's scores into probabilities, then multiplies them into O. K runs
+    // one block ahead of V in LDS: iteration kb reads K tile kb+1 and V tile kb, and refills
+    // the K buffer of block kb (with kb+2) and the V buffer of block kb-1 (with kb+1) from
+    // registers loaded one iteration earlier (ra), while requesting K kb+3 and V kb+2 (rb).
+    // Blocks past a wave's diagonal are computed fully masked (p = 0) rather than skipped, so
+    // the pipeline has no data-dependent branches but the rare rescale.
+    unsigned char* const kbuf0 = lds;
+    unsigned char* const kbuf1 = lds + K_TILE;
+    unsigned char* const vbuf0 = lds + 2 * K_TILE;
+    unsigned char* const vbuf1 = lds + 2 * K_TILE + V_TILE;
+    auto diag = [&](int blk) {   // some key of this wave's half of block blk is invisible
+        const int64_t key0 = (int64_t)blk * KB + kh * 32;
+        return key0 + 31 > q0 || key0 + 32 > S;
+    };
     KVRegs ra, rb;
-    load_kv(ra, kp, vp, S, 0, tid);
-    store_kv(ra, lds, tid);
-    if (nkb > 1) load_kv(ra, kp, vp, S, KB, tid);
+    load_k(ra, kp, S, 0, tid);
+    load_v(ra, vp, S, 0, tid);
+    store_k(ra, kbuf0, tid);
+    store_v(ra, vbuf0, tid);
+    if (nkb > 1) {
+        load_k(ra, kp, S, KB, tid);
+        store_k(ra, kbuf1, tid);
+        load_v(ra, vp, S, KB, tid);
+    }
+    if (nkb > 2) load_k(ra, kp, S, 2 * KB, tid);
     __syncthreads();
+    f32x16 s_cur = qk_tile(kbuf0, qf, kh, r32, hi);
+    if (diag(0)) mask_tile(s_cur, qrow, S, (int64_t)kh * 32, hi);
+    __syncthreads();   // every wave has read K tile 0 before iteration 0 refills its buffer
     for (int kb = 0; kb < nkb; ++kb) {
-        const unsigned char* cur = lds + (kb & 1) * STAGE;
-        unsigned char* nxt = lds + ((kb + 1) & 1) * STAGE;
-        if (kb + 2 < nkb) load_kv(rb, kp, vp, S, (int64_t)(kb + 2) * KB, tid);
-        const int64_t key0 = (int64_t)kb * KB + kh * 32;   // this wave's 32 keys
-        if (key0 <= q0 + 31 && q0 < S && key0 < S) {       // some key visible to the slab
-#if FA_SPLIT_QK
-            // two independent accumulation chains (even / odd 16-dim slices)
-            f32x16 sa, sb;
+        const bool odd = kb & 1;
+        if (kb + 3 < nkb) load_k(rb, kp, S, (int64_t)(kb + 3) * KB, tid);
+        if (kb + 2 < nkb) load_v(rb, vp, S, (int64_t)(kb + 2) * KB, tid);
+        // block max of the raw scores; lazy rescaling: the exponent base m_run moves only
+        // when some query's block maximum exceeds it by more than TAU (log2 units), so every
+        // probability is at most 2^TAU (exact in fp16, no overflow in the fp32 sums) and the
+        // rescale of l and the 64 accumulators runs only on the few blocks that raise a base.
+        // The base cancels in the final division. -inf + TAU is -inf, so a query's first
+        // visible key always sets its base.
+        float mblk = s_cur[0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sa[r] = 0.0f;
-                sb[r] = 0.0f;
-            }
+        for (int r = 1; r < 16; ++r) mblk = fmaxf(mblk, s_cur[r]);
+        mblk = fmaxf(mblk, __shfl_xor(mblk, 32)) * scale;   // scale > 0 keeps the order
+        if (__ballot(mblk > m_run + TAU)) {
+            const float m_new = fmaxf(m_run, mblk);
+            const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
-            for (int dk = 0; dk < 8; dk += 2) {
-                const f16x8 a0 = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + hi)));
-                const f16x8 a1 = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + 2 + hi)));
-                sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[dk], sa, 0, 0, 0);
-                sb = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, qf[dk + 1], sb, 0, 0, 0);
-            }
-            f32x16 st;
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] = sa[r] + sb[r];
-#else
-            // one accumulation chain over the 8 16-dim slices (the other wave of the SIMD
-            // fills the dependent-issue gaps; two chains would cost 16 adds per block)
-            f32x16 st;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-#pragma unroll
-            for (int dk = 0; dk < 8; ++dk) {
-                const f16x8 a0 = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(cur + k_off(kh * 32 + r32, dk * 2 + hi)));
-                st = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qf[dk], st, 0, 0, 0);
-            }
-#endif
-            // mask (keys past the query or past S), block max of the raw scores
-            const bool diag = key0 + 31 > q0 || key0 + 32 > S;
-            if (diag) {
-                const int64_t lim64 = ((qrow < S - 1) ? qrow : S - 1) - key0;   // last visible key offset
-                const int lim = (int)(lim64 < -1 ? -1 : lim64);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
-                    st[r] = (kr > lim) ? -__builtin_inff() : st[r];
-                }
-            }
-            float mblk = st[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mblk = fmaxf(mblk, st[r]);
-            mblk = fmaxf(mblk, __shfl_xor(mblk, 32)) * scale;   // scale > 0 keeps the order
-            // Lazy rescaling: m_run, the exponent base, moves only when some query's block
-            // maximum exceeds it by more than TAU (log2 units). Every probability is then at
-            // most 2^TAU (exact in fp16, no overflow in the fp32 sums), and the rescale of l
-            // and the 64 accumulators runs only on the few blocks that raise a base. The
-            // result is the same softmax: the base cancels in the final division. -inf + TAU
-            // is -inf, so a query's first visible key always sets its base.
-            if (__ballot(mblk > m_run + TAU)) {
-                const float m_new = fmaxf(m_run, mblk);
-                const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // all keys masked so far
-            float lsum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], scale, -m_use));
-                st[r] = p;
-                lsum += p;
-            }
-            lsum += __shfl_xor(lsum, 32);
-            l_run += lsum;
-            // O^T += V^T P^T over this wave's two sub-blocks of 16 keys
-            const unsigned char* vs = cur + K_TILE;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                f16x8 pb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pb[e] = (_Float16)st[8 * ks + e];
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(vs + v_off(dt * 32 + r32, (2 * kh + ks) * 2 + hi)));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb, o[dt], 0, 0, 0);
-                }
-            }
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            m_run = m_new;
         }
-        if (kb + 1 < nkb) store_kv(ra, nxt, tid);
+        const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // all keys masked so far
+        // next block's scores (MFMA) alongside this block's probabilities (VALU)
+        f32x16 s_nxt = qk_tile(odd ? kbuf0 : kbuf1, qf, kh, r32, hi);
+        float lsum = 0.0f;
+        f16x8 pb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], scale, -m_use));
+            lsum += pr;
+            pb[r >> 3][r & 7] = (_Float16)pr;
+        }
+        // O^T += V^T P^T over this wave's two sub-blocks of 16 keys
+        const unsigned char* vs = odd ? vbuf1 : vbuf0;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const f16x8 a = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(vs + v_off(dt * 32 + r32, (2 * kh + ks) * 2 + hi)));
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[ks], o[dt], 0, 0, 0);
+            }
+        lsum += __shfl_xor(lsum, 32);
+        l_run += lsum;
+        if (kb + 1 < nkb && diag(kb + 1)) mask_tile(s_nxt, qrow, S, (int64_t)(kb + 1) * KB + kh * 32, hi);
+        if (kb + 2 < nkb) store_k(ra, odd ? kbuf1 : kbuf0, tid);
+        if (kb + 1 < nkb) store_v(ra, odd ? vbuf0 : vbuf1, tid);
         ra = rb;
+        s_cur = s_nxt;
         __syncthreads();
     }
     // merge the two key halves of each slab: the kh = 1 wave hands (m, l, o) to the kh = 0 wave
