@@ -80,6 +80,53 @@ def timed(step, warmup: int, steps: int, name: str = None):
     return ev[0].elapsed_time(ev[steps]) / steps
 
 
+def clock_power(step, seconds: float = 2.5):
+    """GPU clock (MHz) and socket power (W) while `step` runs back to back for `seconds`.
+    The driver refreshes its metrics table about once a second, so only readings taken after
+    a refresh (a new system-clock stamp) while the load runs are kept. None if the amdsmi
+    library is missing."""
+    try:
+        import amdsmi
+    except Exception:   # noqa: BLE001
+        return None
+    import torch
+    try:
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+        stamp0 = amdsmi.amdsmi_get_gpu_metrics_info(h).get("system_clock_counter")
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        step()
+        e1.record(s)
+        torch.cuda.synchronize()
+        n = max(1, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+        seen, fresh = {stamp0}, []
+        t0 = tlast = time.perf_counter()
+        for _ in range(n):   # launches block once the queue is full, so the reads interleave
+            step()
+            now = time.perf_counter()
+            if now - tlast > 0.05:
+                tlast = now
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                st = m.get("system_clock_counter")
+                if st not in seen and now - t0 > 0.5:
+                    fresh.append((m.get("current_gfxclk"), m.get("current_socket_power")))
+                seen.add(st)
+        torch.cuda.synchronize()
+        amdsmi.amdsmi_shut_down()
+    except Exception as e:   # noqa: BLE001
+        return {"error": str(e)}
+    if not fresh:
+        return {"error": "no metrics refresh during the load"}
+    clk = [c for c, _ in fresh if isinstance(c, (int, float))]
+    pw = [p for _, p in fresh if isinstance(p, (int, float))]
+    return {"gfx_clk_mhz": (sum(clk) / len(clk)) if clk else None,
+            "socket_power_w": (sum(pw) / len(pw)) if pw else None,
+            "readings": len(fresh), "seconds": seconds,
+            "source": "amdsmi gpu metrics (refreshed ~1/s), during back-to-back steps"}
+
+
 def kernel_avg(prefix: str):
     import tensor_transformer_layer_rank_amd as tp
     ms, n = tp.profile_read(prefix)
@@ -124,6 +171,7 @@ def mlp_bench(args):
                                        "tflops": flops_dn / (dn_ms * 1e-3) / 1e12},
         },
         "step_stats": STEP_STATS.get("mlp"),
+        "clock_power": clock_power(step),
         "roofline": {
             "bound": "mfma", "kernel": "gemm_bf16_swiglu",
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
@@ -412,6 +460,7 @@ def main():
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in mlp["roofline"].items()},
         "cpu_baseline": cpu and {k: v for k, v in cpu.items() if k != "seconds"},
         "step_stats": mlp["step_stats"],
+        "clock_power": mlp["clock_power"],
         "kernels": mlp["kernels"],
         "decode": dec,
         "fp8_mlp": fp8,
