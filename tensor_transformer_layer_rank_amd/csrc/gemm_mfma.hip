@@ -520,14 +520,17 @@ __device__ __forceinline__ void publish(unsigned char* stage, int pending, const
 // kt+1 is published (wait + barrier), after which `cur` is free; slice-1 MFMAs then
 // alternate with the reads of stage kt+1's slice 0 (into f0) and with this wave's DMA
 // refilling `cur` with step kt+4. The MFMA pipe thus always has queued work while loads
-// are issued.
-template <bool DUAL>
+// are issued. STEADY steps (every step but the last five of a tile) know at compile time
+// that a next step exists, that the refill is a whole step and that two later stages are in
+// flight, so their instruction stream has no branches.
+template <bool DUAL, bool STEADY>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                        unsigned char* cur, unsigned char* nxt, int kt, int nk,
                                        int64_t kbase, const DmaPlan& p, const Geom<false>& g,
                                        const uint16_t* a_base, int64_t m0, int64_t n0, int wm, int wn,
                                        int wave, int lane) {
     constexpr int BK = Fmt<false>::BK;
+    constexpr int GRP = DMA_A + DMA_B;
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
@@ -535,9 +538,14 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
         if (n < 8) read_piece<DUAL>(f1, n, cur, 1, wm, wn, lane);
         TP_FENCE();
     }
-    const bool has_next = kt + 1 < nk;
-    const bool refill = kt + 4 < nk;
-    if (has_next) {
+    const bool has_next = STEADY || kt + 1 < nk;
+    const bool refill = STEADY || kt + 4 < nk;
+    if constexpr (STEADY) {
+        wait_vm<2 * GRP>();                     // stage kt+1 landed; kt+2, kt+3 may be in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    } else if (has_next) {
         // stages issued after kt+1 and still allowed in flight: kt+2, kt+3
         const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
         publish<false>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
@@ -546,7 +554,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     // full refill steps interleave their DMA with the MFMAs; a partial final step takes
     // the general path up front
     const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
-    const bool inline_dma = refill && k0_full<false>(g, k_ref);
+    const bool inline_dma = STEADY || (refill && k0_full<false>(g, k_ref));
     if (refill && !inline_dma) issue_stage<DUAL, false>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
     const uint16_t* a_k = a_base + k_ref;
     const uint16_t* b_k = g.B1 + k_ref * g.ldb;
@@ -685,8 +693,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         if constexpr (!F8) {
             Frags f0, f1;
             read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
-            for (int kt = 0; kt < nk; ++kt) {
-                k_step<DUAL>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+            // steady steps: kt + 4 <= nk - 2, so step kt+1 exists, the refill (step kt+4) is
+            // whole and not the tile's last step, and two stages after kt+1 are in flight
+            int kt = 0;
+            for (; kt < nk - 5; ++kt) {
+                k_step<DUAL, true>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                unsigned char* t = sa;
+                sa = sb;
+                sb = sc;
+                sc = sd;
+                sd = t;
+            }
+            for (; kt < nk; ++kt) {
+                k_step<DUAL, false>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
                 unsigned char* t = sa;
                 sa = sb;
                 sb = sc;
