@@ -395,7 +395,7 @@ struct EpiSwiGLU {
                 const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
                 if (row >= M) continue;
                 const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
-                const float silu = gte / (1.0f + __expf(-gte));
+                const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
                 if (H8) static_cast<uint8_t*>(h)[row * N + col] = f32_to_e4m3(silu * up / h_scale);
                 else static_cast<uint16_t*>(h)[row * N + col] = f32_to_bf16(silu * up);
             }
@@ -577,13 +577,14 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
 // fragments into bn (the other weight buffer), its activation block i into a[i] as soon as
 // the last MFMA of row block i has been issued — and with the DMA refilling `cur` with
 // step kt+4.
-template <bool DUAL>
+template <bool DUAL, bool STEADY>
 __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i32x8 (&bc)[4],
                                           i32x8 (&bn)[4], unsigned char* cur, unsigned char* nxt,
                                           int kt, int nk, int64_t kbase, const DmaPlan& p,
                                           const Geom<true>& g, const uint8_t* a_base, int64_t m0,
                                           int64_t n0, int wm, int wn, int wave, int lane) {
     constexpr int BK = Fmt<true>::BK;
+    constexpr int GRP = DMA_A + DMA_B;
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -591,15 +592,20 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
         if (n < 2) set_a8(a[3], n, read_a8_half(cur, 3, n, wm, lane));
         TP_FENCE();
     }
-    const bool has_next = kt + 1 < nk;
-    const bool refill = kt + 4 < nk;
-    if (has_next) {
+    const bool has_next = STEADY || kt + 1 < nk;
+    const bool refill = STEADY || kt + 4 < nk;
+    if constexpr (STEADY) {
+        wait_vm<2 * GRP>();                     // stage kt+1 landed; kt+2, kt+3 may be in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    } else if (has_next) {
         const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
         publish<true>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
     const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
-    const bool inline_dma = refill && k0_full<true>(g, k_ref);
+    const bool inline_dma = STEADY || (refill && k0_full<true>(g, k_ref));
     if (refill && !inline_dma) issue_stage<DUAL, true>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
     const uint8_t* a_k = a_base + k_ref;
     const uint8_t* b_k = g.B1 + k_ref * g.ldb;
@@ -725,8 +731,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             // one step per iteration; the next step's weight fragments move into b0 at its
             // end (32 register moves that overlap the last MFMAs; two inlined steps with
             // swapped buffers instead would exceed the register file)
-            for (int kt = 0; kt < nk; ++kt) {
-                k_step_f8<DUAL>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+            int kt = 0;
+            for (; kt < nk - 5; ++kt) {   // steady steps, as in the bf16 loop
+                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                unsigned char* t = sa;
+                sa = sb;
+                sb = sc;
+                sc = sd;
+                sd = t;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b0[j] = b1[j];
+            }
+            for (; kt < nk; ++kt) {
+                k_step_f8<DUAL, false>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
                 unsigned char* t = sa;
                 sa = sb;
                 sb = sc;
