@@ -30,6 +30,8 @@
 // fetches.
 // Tiles are ordered so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
 // works on a compact block of 4 row tiles x n column tiles, which keeps its L2 hit rate up.
+#include <type_traits>
+
 #include "tp_internal.h"
 
 namespace tpk {
@@ -353,25 +355,37 @@ struct EpiStore {
     // accumulator row block i (acc[i][0..3]) of wave (wm, wn)
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
                          int lane) const {
+        // one row address per register r (row offsets are compile-time multiples of ldc),
+        // the four column blocks as constant offsets from it
         const int r32 = lane & 31, hi = lane >> 5;
+        const int64_t c0 = n0 + wn * 128 + r32;
+        const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
+        // interior tiles (the common case) take a copy of the loop without bounds checks
+        auto body = [&](auto check) {
+            constexpr bool CHECK = decltype(check)::value;
+            bool col_ok[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 32 + r32;
-            if (col >= N) continue;
+            for (int j = 0; j < 4; ++j) col_ok[j] = !CHECK || c0 + j * 32 < N;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                if (row >= M) continue;
-                float v = a[j][r] * scale;
-                if (RELU) v = v > 0.0f ? v : 0.0f;
-                const int64_t off = row * ldc + col;
-                if (KIND == 0) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v);
-                else if (KIND == 1) static_cast<uint16_t*>(C)[off] = f32_to_f16(v);
-                else if (KIND == 2) static_cast<float*>(C)[off] = v;
-                else if (KIND == 3) static_cast<float*>(C)[off] += v;
-                else static_cast<uint8_t*>(C)[off] = f32_to_e4m3(v / out_div);
+                const int dr = acc_row(0, r, 0);
+                if (CHECK && row0 + dr >= M) continue;
+                const int64_t off = (row0 + dr) * ldc + c0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (CHECK && !col_ok[j]) continue;
+                    float v = a[j][r] * scale;
+                    if (RELU) v = v > 0.0f ? v : 0.0f;
+                    if (KIND == 0) static_cast<uint16_t*>(C)[off + j * 32] = f32_to_bf16(v);
+                    else if (KIND == 1) static_cast<uint16_t*>(C)[off + j * 32] = f32_to_f16(v);
+                    else if (KIND == 2) static_cast<float*>(C)[off + j * 32] = v;
+                    else if (KIND == 3) static_cast<float*>(C)[off + j * 32] += v;
+                    else static_cast<uint8_t*>(C)[off + j * 32] = f32_to_e4m3(v / out_div);
+                }
             }
-        }
+        };
+        if (m0 + BM <= M && n0 + BN <= N) body(std::false_type{});
+        else body(std::true_type{});
     }
 };
 
@@ -386,20 +400,29 @@ struct EpiSwiGLU {
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
                          int lane) const {
         const int r32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 32 + r32;
-            if (col >= N) continue;
+        const int64_t c0 = n0 + wn * 64 + r32;
+        const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
+        // interior tiles (the common case) take a copy of the loop without bounds checks
+        auto body = [&](auto check) {
+            constexpr bool CHECK = decltype(check)::value;
+            const bool ok0 = !CHECK || c0 < N, ok1 = !CHECK || c0 + 32 < N;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + acc_row(i, r, hi);
-                if (row >= M) continue;
-                const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
-                const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
-                if (H8) static_cast<uint8_t*>(h)[row * N + col] = f32_to_e4m3(silu * up / h_scale);
-                else static_cast<uint16_t*>(h)[row * N + col] = f32_to_bf16(silu * up);
+                const int dr = acc_row(0, r, 0);
+                if (CHECK && row0 + dr >= M) continue;
+                const int64_t off = (row0 + dr) * N + c0;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (CHECK && !(j ? ok1 : ok0)) continue;
+                    const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
+                    const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
+                    if (H8) static_cast<uint8_t*>(h)[off + j * 32] = f32_to_e4m3(silu * up / h_scale);
+                    else static_cast<uint16_t*>(h)[off + j * 32] = f32_to_bf16(silu * up);
+                }
             }
-        }
+        };
+        if (m0 + BM <= M && n0 + BN / 2 <= N) body(std::false_type{});
+        else body(std::true_type{});
     }
 };
 
@@ -635,6 +658,9 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
 // each of the remaining tiles is cut into `pieces` K ranges of piece_steps K steps, one
 // workgroup each, whose accumulators go to `part` in register order; gemm_fixup_kernel then
 // sums a tile's pieces in piece order and runs the epilogue.
+#ifndef FIXUP_WAVES
+#define FIXUP_WAVES 4   // waves per fix-up workgroup (divides 16)
+#endif
 struct SplitArgs {
     int g_full, pieces, piece_steps;
     float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
@@ -771,10 +797,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
 // pieces in piece order, then that row block's epilogue. 16 single-wave workgroups per tile
 // keep the partial reads spread over the machine.
 template <bool DUAL, class Epi>
-__global__ __launch_bounds__(64) void gemm_fixup_kernel(Epi epi, int tiles_m, int tiles_n,
-                                                        SplitArgs sp) {
-    const int lane = threadIdx.x;
-    const int t = (int)blockIdx.x >> 4, wave = ((int)blockIdx.x >> 2) & 3, i = (int)blockIdx.x & 3;
+__global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, int tiles_m, int tiles_n,
+                                                                      SplitArgs sp) {
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)blockIdx.x * FIXUP_WAVES + (int)(threadIdx.x >> 6);   // (tile, wave, i)
+    const int t = gw >> 4, wave = (gw >> 2) & 3, i = gw & 3;
     const int wm = wave & 1, wn = wave >> 1;
     int tm, tn;
     tile_of(sp.g_full + t, tiles_m, tiles_n, tm, tn);
@@ -871,7 +898,8 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
         if (e != hipSuccess || sp.pieces < 2) return e;
     }
     ProfScope ps(DUAL ? "fixup_swiglu" : "fixup_gemm", s);
-    gemm_fixup_kernel<DUAL, Epi><<<(unsigned)((G - sp.g_full) * 16), 64, 0, s>>>(epi, (int)tiles_m, (int)tiles_n, sp);
+    gemm_fixup_kernel<DUAL, Epi><<<(unsigned)((G - sp.g_full) * 16 / FIXUP_WAVES), 64 * FIXUP_WAVES, 0, s>>>(
+        epi, (int)tiles_m, (int)tiles_n, sp);
     return hipGetLastError();
 }
 
