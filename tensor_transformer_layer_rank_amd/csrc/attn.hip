@@ -26,6 +26,8 @@
 // O^T += V^T P^T. Exponentials use exp2 with log2(e)/sqrt(128) folded into the scale, and
 // the exponent base of a query moves only when a block raises its maximum by more than 2^8
 // (lazy rescaling), so the rescale of the accumulators is skipped on almost every block.
+#include <type_traits>
+
 #include "tp_internal.h"
 
 namespace tpk {
@@ -201,10 +203,14 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
     f32x16 s_cur = qk_tile(kbuf0, qf, kh, r32, hi);
     if (diag(0)) mask_tile(s_cur, qrow, S, (int64_t)kh * 32, hi);
     __syncthreads();   // every wave has read K tile 0 before iteration 0 refills its buffer
-    for (int kb = 0; kb < nkb; ++kb) {
+    // Steady iterations (the K and V of blocks kb+2, kb+3 exist and block kb+1 lies wholly
+    // below this wave's diagonal) run a copy of the body without those checks; every wave
+    // runs nkb iterations with one barrier each, whatever its split point.
+    auto iteration = [&](int kb, auto steady_t) {
+        constexpr bool STEADY = decltype(steady_t)::value;
         const bool odd = kb & 1;
-        if (kb + 3 < nkb) load_k(rb, kp, S, (int64_t)(kb + 3) * KB, tid);
-        if (kb + 2 < nkb) load_v(rb, vp, S, (int64_t)(kb + 2) * KB, tid);
+        if (STEADY || kb + 3 < nkb) load_k(rb, kp, S, (int64_t)(kb + 3) * KB, tid);
+        if (STEADY || kb + 2 < nkb) load_v(rb, vp, S, (int64_t)(kb + 2) * KB, tid);
         // block max of the raw scores; lazy rescaling: the exponent base m_run moves only
         // when some query's block maximum exceeds it by more than TAU (log2 units), so every
         // probability is at most 2^TAU (exact in fp16, no overflow in the fp32 sums) and the
@@ -248,13 +254,19 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
             }
         lsum += __shfl_xor(lsum, 32);
         l_run += lsum;
-        if (kb + 1 < nkb && diag(kb + 1)) mask_tile(s_nxt, qrow, S, (int64_t)(kb + 1) * KB + kh * 32, hi);
-        if (kb + 2 < nkb) store_k(ra, odd ? kbuf1 : kbuf0, tid);
-        if (kb + 1 < nkb) store_v(ra, odd ? vbuf0 : vbuf1, tid);
+        if (!STEADY && kb + 1 < nkb && diag(kb + 1))
+            mask_tile(s_nxt, qrow, S, (int64_t)(kb + 1) * KB + kh * 32, hi);
+        if (STEADY || kb + 2 < nkb) store_k(ra, odd ? kbuf1 : kbuf0, tid);
+        if (STEADY || kb + 1 < nkb) store_v(ra, odd ? vbuf0 : vbuf1, tid);
         ra = rb;
         s_cur = s_nxt;
         __syncthreads();
-    }
+    };
+    int steady_end = 0;
+    while (steady_end + 3 < nkb && !diag(steady_end + 1)) ++steady_end;
+    int kb = 0;
+    for (; kb < steady_end; ++kb) iteration(kb, std::true_type{});
+    for (; kb < nkb; ++kb) iteration(kb, std::false_type{});
     // merge the two key halves of each slab: the kh = 1 wave hands (m, l, o) to the kh = 0 wave
     float* xch = reinterpret_cast<float*>(lds) + slab * XCH_FLOATS;
     if (kh == 1) {

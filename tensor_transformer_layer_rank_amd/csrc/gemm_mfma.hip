@@ -659,7 +659,7 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
 // workgroup each, whose accumulators go to `part` in register order; gemm_fixup_kernel then
 // sums a tile's pieces in piece order and runs the epilogue.
 #ifndef FIXUP_WAVES
-#define FIXUP_WAVES 4   // waves per fix-up workgroup (divides 16)
+#define FIXUP_WAVES 1   // waves per fix-up workgroup (divides 16; 4 made the QKV fix-up 1.5-2x slower)
 #endif
 struct SplitArgs {
     int g_full, pieces, piece_steps;
