@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--extra", action="store_true", help="also time the attention and 70B layer shards")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 2.5 s clock/power reading (for profiled runs)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="after timing, run a plain 256 MiB device copy (3 times): the reference that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
@@ -171,7 +173,7 @@ def mlp_bench(args):
                                        "tflops": flops_dn / (dn_ms * 1e-3) / 1e12},
         },
         "step_stats": STEP_STATS.get("mlp"),
-        "clock_power": clock_power(step),
+        "clock_power": None if args.no_clock else clock_power(step),
         "roofline": {
             "bound": "mfma", "kernel": "gemm_bf16_swiglu",
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
