@@ -7,8 +7,8 @@
 //                        (every weight byte read once, the next step's block already in
 //                        flight), transposing it in registers (v_perm) and feeding
 //                        v_mfma_f32_16x16x32_bf16 with the activations as the A operand. The
-//                        waves are summed in LDS in a fixed order and the chunk's fp32 partial
-//                        is written to a partial buffer.
+//                        waves' partials meet in LDS; each wave then sums a quarter of the rows
+//                        in wave order and writes it to the chunk's fp32 partial buffer.
 //   reduce kernels       sum the chunk partials in chunk order and apply the layer's
 //                        epilogue: fp32/bf16 store (O and down partials, vocabulary-split
 //                        logits) or SiLU(gate)*up.
@@ -139,7 +139,7 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>
 
 template <int MB>
 __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs g) {
-    __shared__ f32x4 red[2][MB * 16][STRIP / 4];
+    __shared__ f32x4 red[4][MB * 16][STRIP / 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, l16 = lane & 15;
     const int64_t strip = blockIdx.x, split = blockIdx.y;
@@ -189,43 +189,33 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
         ap += 2 * astep;
     }
 
-    // waves 2,3 -> LDS, added by waves 0,1; wave 1 -> LDS, added by wave 0 (fixed order)
+    // every wave's partial goes to LDS; after one barrier each wave sums a quarter of the rows
+    // over the four waves' partials in wave order and stores it (all waves store at once)
     // acc[mb][t][r] = C[m = mb*16 + 4*grp + r][c0 + 8*l16 + t]
-#define TP_RED_STORE(SLOT)                                                                          \
-    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) _Pragma("unroll") for (int r = 0; r < 4; ++r) { \
-        const int m = mb * 16 + 4 * grp + r;                                                        \
-        red[SLOT][m][2 * l16] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};  \
-        red[SLOT][m][2 * l16 + 1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]}; \
-    }
-#define TP_RED_ADD(SLOT)                                                                            \
-    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) _Pragma("unroll") for (int r = 0; r < 4; ++r) { \
-        const int m = mb * 16 + 4 * grp + r;                                                        \
-        const f32x4 u = red[SLOT][m][2 * l16], v = red[SLOT][m][2 * l16 + 1];                       \
-        acc[mb][0][r] += u.x; acc[mb][1][r] += u.y; acc[mb][2][r] += u.z; acc[mb][3][r] += u.w;     \
-        acc[mb][4][r] += v.x; acc[mb][5][r] += v.y; acc[mb][6][r] += v.z; acc[mb][7][r] += v.w;     \
-    }
-    if (wave >= 2) TP_RED_STORE(wave - 2)
-    __syncthreads();
-    if (wave < 2) TP_RED_ADD(wave)
-    __syncthreads();
-    if (wave == 1) TP_RED_STORE(0)
-    __syncthreads();
-    if (wave == 0) {
-        TP_RED_ADD(0)
-        float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb * 16 + 4 * grp + r;
-                if (m >= g.M) continue;
-                f32x4* o = reinterpret_cast<f32x4*>(dst + m * g.ncols + 8 * l16);
-                o[0] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
-                o[1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int m = mb * 16 + 4 * grp + r;
+            red[wave][m][2 * l16] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            red[wave][m][2 * l16 + 1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+        }
+    __syncthreads();
+    constexpr int ROWS = MB * 16 / 4;   // rows per wave
+    float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
+#pragma unroll
+    for (int rr = lane >> 3; rr < ROWS; rr += 8) {   // lane: row rr, 16-byte chunks lane%8 + 8q
+        const int m = wave * ROWS + rr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = (lane & 7) + 8 * q;
+            f32x4 v = red[0][m][c];
+            v += red[1][m][c];
+            v += red[2][m][c];
+            v += red[3][m][c];
+            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * g.ncols + 4 * c) = v;
+        }
     }
-#undef TP_RED_STORE
-#undef TP_RED_ADD
 }
 
 // v[i] = sum over chunks (in order) of part[s][m][c[i]] for NC columns of row m. The chunks'
