@@ -206,9 +206,13 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
     // Steady iterations (the K and V of blocks kb+2, kb+3 exist and block kb+1 lies wholly
     // below this wave's diagonal) run a copy of the body without those checks; every wave
     // runs nkb iterations with one barrier each, whatever its split point.
-    auto iteration = [&](int kb, auto steady_t) {
+    // The loop is unrolled by two so that the register sets (ra / rb) and the score tiles
+    // (s_cur / s_nxt) swap roles by name instead of by copy, and the LDS buffer parity is a
+    // compile-time constant.
+    auto iteration = [&](int kb, auto steady_t, auto odd_t, KVRegs& ra, KVRegs& rb, f32x16& s_cur,
+                         f32x16& s_nxt) {
         constexpr bool STEADY = decltype(steady_t)::value;
-        const bool odd = kb & 1;
+        constexpr bool odd = decltype(odd_t)::value;
         if (STEADY || kb + 3 < nkb) load_k(rb, kp, S, (int64_t)(kb + 3) * KB, tid);
         if (STEADY || kb + 2 < nkb) load_v(rb, vp, S, (int64_t)(kb + 2) * KB, tid);
         // block max of the raw scores; lazy rescaling: the exponent base m_run moves only
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
         }
         const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;   // all keys masked so far
         // next block's scores (MFMA) alongside this block's probabilities (VALU)
-        f32x16 s_nxt = qk_tile(odd ? kbuf0 : kbuf1, qf, kh, r32, hi);
+        s_nxt = qk_tile(odd ? kbuf0 : kbuf1, qf, kh, r32, hi);
         float lsum = 0.0f;
         f16x8 pb[2];
 #pragma unroll
@@ -258,15 +262,20 @@ __global__ __launch_bounds__(NT, 1) void flash_attn_kernel(const uint16_t* __res
             mask_tile(s_nxt, qrow, S, (int64_t)(kb + 1) * KB + kh * 32, hi);
         if (STEADY || kb + 2 < nkb) store_k(ra, odd ? kbuf1 : kbuf0, tid);
         if (STEADY || kb + 1 < nkb) store_v(ra, odd ? vbuf0 : vbuf1, tid);
-        ra = rb;
-        s_cur = s_nxt;
         __syncthreads();
     };
     int steady_end = 0;
     while (steady_end + 3 < nkb && !diag(steady_end + 1)) ++steady_end;
-    int kb = 0;
-    for (; kb < steady_end; ++kb) iteration(kb, std::true_type{});
-    for (; kb < nkb; ++kb) iteration(kb, std::false_type{});
+    f32x16 s_nxt;
+    for (int kb = 0; kb < nkb; kb += 2) {
+        if (kb + 1 < steady_end) {
+            iteration(kb, std::true_type{}, std::false_type{}, ra, rb, s_cur, s_nxt);
+            iteration(kb + 1, std::true_type{}, std::true_type{}, rb, ra, s_nxt, s_cur);
+        } else {
+            iteration(kb, std::false_type{}, std::false_type{}, ra, rb, s_cur, s_nxt);
+            if (kb + 1 < nkb) iteration(kb + 1, std::false_type{}, std::true_type{}, rb, ra, s_nxt, s_cur);
+        }
+    }
     // merge the two key halves of each slab: the kh = 1 wave hands (m, l, o) to the kh = 0 wave
     float* xch = reinterpret_cast<float*>(lds) + slab * XCH_FLOATS;
     if (kh == 1) {
