@@ -12,7 +12,8 @@ MFMA peak. Inputs are seeded synthetic tensors already resident in HBM. With --e
 attention shard (B=4, S=2048) and the 70B GQA layer shard are timed too.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events that libtpshard records
-around each launch on the launch stream while the timed steps run.
+around each launch on the launch stream during every 10th timed step (the events cost a few
+microseconds per kernel, so they are not recorded on the other steps).
 """
 from __future__ import annotations
 
@@ -57,29 +58,42 @@ def _stats(name: str, per_step_ms):
     STEP_STATS[name] = {"median_ms": med, "min_ms": xs[0], "max_ms": xs[-1]}
 
 
-def timed(step, warmup: int, steps: int, name: str = None):
-    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step (total
-    over the window / steps). An event after every step also gives the per-step median and
-    minimum (kept in STEP_STATS[name])."""
+def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 10):
+    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step.
+
+    Only two events bracket the timed steps. libtpshard's per-kernel HIP events (which add a
+    few microseconds per kernel) are switched on for every `sample_every`-th timed step only,
+    so the kernel averages come from inside the timed region at a cost of ~1% of it. If
+    `name` is given, a second pass of `steps` steps with one event per step gives the per-step
+    median / min / max (STEP_STATS[name])."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     tp.profile_reset()
-    tp.profile_enable(True)
     s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    ev[0].record(s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
     for i in range(steps):
+        sampled = i % sample_every == 0
+        if sampled:
+            tp.profile_enable(True)
         step()
-        ev[i + 1].record(s)
+        if sampled:
+            tp.profile_enable(False)
+    e1.record(s)
     torch.cuda.synchronize()
-    tp.profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
     if name:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(s)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
         _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-    return ev[0].elapsed_time(ev[steps]) / steps
+    return ms
 
 
 def clock_power(step, seconds: float = 2.5):
@@ -227,7 +241,8 @@ def fp8_mlp_bench(args):
 
 def graph_timed(step, warmup: int, steps: int, name: str = None):
     """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
-    (per-replay median and minimum kept in STEP_STATS[name])."""
+    between two events; a second pass with one event per replay gives the per-replay median
+    and minimum (STEP_STATS[name])."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -241,15 +256,22 @@ def graph_timed(step, warmup: int, steps: int, name: str = None):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
-    for i in range(steps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         g.replay()
-        ev[i + 1].record()
+    e1.record()
     torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
     if name:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            g.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
         _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-    return ev[0].elapsed_time(ev[steps]) / steps
+    return ms
 
 
 def decode_bench(args):
@@ -316,7 +338,7 @@ def decode_bench(args):
         "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
                     "skinny_gemm*(avg_us)": sk_ms * 1e3 if sk_ms else None,
-                    "skinny_gemm*(launches/step)": sk_n / max(args.steps, 1)},
+                    "skinny_gemm*(launches/step)": sk_n / max(-(-args.steps // 10), 1)},
         "workload": "decode7b_tp2: B=32 one token each, 16 local heads (MHA), KV cache 1024 tokens, "
                     "H=4096, I_shard=5504, LM head [4096,16000]",
     }
