@@ -754,10 +754,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) set_b8(b0[j], t, read_b8_quarter(st0 + A_BYTES, t, b_col_of<DUAL>(j, wn), lane));
-            // one step per iteration; the next step's weight fragments move into b0 at its
-            // end (32 register moves that overlap the last MFMAs; two inlined steps with
-            // swapped buffers instead would exceed the register file)
+            // Steady steps run in pairs whose second step swaps the roles of the two weight
+            // fragment buffers (no copies; the branch-free steady step leaves room for both in
+            // the register file); the remaining steps run one at a time and move the next
+            // step's weight fragments into b0 (32 register moves).
             int kt = 0;
+            for (; kt + 1 < nk - 5; kt += 2) {   // steady steps in pairs: the weight buffers swap by name
+                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step_f8<DUAL, true>(acc, a, b1, b0, sb, sc, kt + 1, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                unsigned char* t0 = sa;
+                unsigned char* t1 = sb;
+                sa = sc;
+                sb = sd;
+                sc = t0;
+                sd = t1;
+            }
             for (; kt < nk - 5; ++kt) {   // steady steps, as in the bf16 loop
                 k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
                 unsigned char* t = sa;
