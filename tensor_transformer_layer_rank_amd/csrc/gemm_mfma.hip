@@ -344,7 +344,7 @@ __device__ __forceinline__ int acc_row(int i, int r, int hi) {
 
 // ---- epilogues ----------------------------------------------------------------------
 
-// KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=, 4 OCP E4M3 code of v / out_div.
+// KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=, 4 OCP E4M3 code of v * (1 / out_div).
 // Every accumulator is first multiplied by `scale` (the product of the per-tensor operand
 // scales of fp8 operands; 1 for bf16).
 template <int KIND, bool RELU>
@@ -360,6 +360,7 @@ struct EpiStore {
         const int r32 = lane & 31, hi = lane >> 5;
         const int64_t c0 = n0 + wn * 128 + r32;
         const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
+        const float out_inv = 1.0f / out_div;
         // interior tiles (the common case) take a copy of the loop without bounds checks
         auto body = [&](auto check) {
             constexpr bool CHECK = decltype(check)::value;
@@ -380,7 +381,7 @@ struct EpiStore {
                     else if (KIND == 1) static_cast<uint16_t*>(C)[off + j * 32] = f32_to_f16(v);
                     else if (KIND == 2) static_cast<float*>(C)[off + j * 32] = v;
                     else if (KIND == 3) static_cast<float*>(C)[off + j * 32] += v;
-                    else static_cast<uint8_t*>(C)[off + j * 32] = f32_to_e4m3(v / out_div);
+                    else static_cast<uint8_t*>(C)[off + j * 32] = f32_to_e4m3(v * out_inv);
                 }
             }
         };
@@ -390,7 +391,7 @@ struct EpiStore {
 };
 
 // h = SiLU(gate * gs) * (up * us); stored as bf16 (H8 = false) or as the E4M3 code of
-// h / h_scale (H8 = true).
+// h * (1 / h_scale) (H8 = true).
 template <bool H8>
 struct EpiSwiGLU {
     void* h;   // [M, N]
@@ -402,6 +403,7 @@ struct EpiSwiGLU {
         const int r32 = lane & 31, hi = lane >> 5;
         const int64_t c0 = n0 + wn * 64 + r32;
         const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
+        const float h_inv = 1.0f / h_scale;   // one division per row block, not per element
         // interior tiles (the common case) take a copy of the loop without bounds checks
         auto body = [&](auto check) {
             constexpr bool CHECK = decltype(check)::value;
@@ -416,7 +418,7 @@ struct EpiSwiGLU {
                     if (CHECK && !(j ? ok1 : ok0)) continue;
                     const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
                     const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
-                    if (H8) static_cast<uint8_t*>(h)[off + j * 32] = f32_to_e4m3(silu * up / h_scale);
+                    if (H8) static_cast<uint8_t*>(h)[off + j * 32] = f32_to_e4m3(silu * up * h_inv);
                     else static_cast<uint16_t*>(h)[off + j * 32] = f32_to_bf16(silu * up);
                 }
             }
