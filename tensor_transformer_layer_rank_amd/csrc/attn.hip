@@ -37,10 +37,6 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-#ifndef FA_SPLIT_QK
-#define FA_SPLIT_QK 0
-#endif
-
 constexpr int QB = 128;          // queries per workgroup
 constexpr float TAU = 8.0f;      // lazy-rescale threshold (log2 units): probabilities <= 256
 constexpr int NWAVE = 8;         // 4 query slabs x 2 key halves
