@@ -660,9 +660,9 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
 // each of the remaining tiles is cut into `pieces` K ranges of piece_steps K steps, one
 // workgroup each, whose accumulators go to `part` in register order; gemm_fixup_kernel then
 // sums a tile's pieces in piece order and runs the epilogue.
-#ifndef FIXUP_WAVES
-#define FIXUP_WAVES 1   // waves per fix-up workgroup (divides 16; 4 made the QKV fix-up 1.5-2x slower)
-#endif
+// waves per fix-up workgroup (divides 16); single-wave workgroups spread a tile's row blocks
+// over the machine (4-wave ones made the QKV fix-up 1.5-2x slower)
+constexpr int FIXUP_WAVES = 1;
 struct SplitArgs {
     int g_full, pieces, piece_steps;
     float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
