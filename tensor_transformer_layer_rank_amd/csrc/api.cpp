@@ -463,8 +463,7 @@ static tp_status check_attn_desc(const tp_attn_desc* d, bool* decode) {
 }
 
 static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, void** k,
-                      void** vt, void** rope, void** att, void** part, void** qbuf, void** scratch,
-                      size_t* split_bytes) {
+                      void** vt, void** rope, void** att, void** part, size_t* split_bytes) {
     Carver c(base);
     const int64_t hq = d->n_q_heads, hkv = d->n_kv_heads;
     const int64_t nqkv = (hq + 2 * hkv) * 128;
@@ -486,8 +485,6 @@ static size_t attn_ws(const tp_attn_desc* d, bool decode, void* base, void** q, 
     const size_t p2 = tpk::skinny_partials_bytes(B, d->H, hq * 128);
     *split_bytes = p1 > p2 ? p1 : p2;
     *part = c.take(*split_bytes);
-    *qbuf = nullptr;
-    *scratch = nullptr;
     *att = c.take((size_t)(B * hq * 128) * 2);
     return c.off;
 }
@@ -496,9 +493,9 @@ size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt) {
     if (in_dt != TP_BF16) return 0;
     bool decode = false;
     if (check_attn_desc(desc, &decode) != TP_OK) return 0;
-    void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
+    void *q, *k, *vt, *rope, *att, *part;
     size_t split_bytes = 0;
-    return attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
+    return attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &split_bytes);
 }
 
 tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float* Y_partial,
@@ -512,13 +509,13 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
     if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_attn_shard: the attention shard takes bf16 inputs");
     if (!aligned(X, 16) || !aligned(W_qkv, 16) || !aligned(W_o, 16) || !aligned(Y_partial, 16))
         return fail(TP_ERR_MISALIGNED, "tp_attn_shard: X, W_qkv, W_o and Y_partial must be 16-byte aligned");
-    void *q, *k, *vt, *rope, *att, *part, *qbuf, *scratch;
+    void *q, *k, *vt, *rope, *att, *part;
     size_t split_bytes = 0;
-    const size_t need = attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
+    const size_t need = attn_ws(desc, decode, nullptr, &q, &k, &vt, &rope, &att, &part, &split_bytes);
     if (!workspace || ws_bytes < need)
         return fail(TP_ERR_WORKSPACE, "tp_attn_shard: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
     if (!aligned(workspace, 16)) return fail(TP_ERR_MISALIGNED, "tp_attn_shard: workspace must be 16-byte aligned");
-    attn_ws(desc, decode, workspace, &q, &k, &vt, &rope, &att, &part, &qbuf, &scratch, &split_bytes);
+    attn_ws(desc, decode, workspace, &q, &k, &vt, &rope, &att, &part, &split_bytes);
     hipStream_t s = as_stream(stream);
     const int hq = desc->n_q_heads, hkv = desc->n_kv_heads;
     const int64_t H = desc->H, dq = (int64_t)hq * 128;

@@ -82,8 +82,6 @@ hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, i
 // h bf16 [M, I] = SiLU(X . Wg) * (X . Wu)
 hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
                          int64_t M, int64_t I, int64_t H, hipStream_t s);
-// QKV of one decode step: q (rotated, fp32) to qbuf [B, hq, 128]; rotated k and v appended to the
-// caches at slot pos
 // decode attention step of an attention shard: QKV split-K partials (workspace `part`,
 // skinny_partials_bytes(B, (hq + 2 hkv) * 128, H)), then one fused kernel that reduces them,
 // rotates q and k by position pos, appends k and v (bf16) at cache slot pos and attends over
