@@ -44,6 +44,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -343,6 +344,40 @@ __device__ __forceinline__ int acc_row(int i, int r, int hi) {
 }
 
 // ---- epilogues ----------------------------------------------------------------------
+// An epilogue turns one accumulator row block of a wave (32 rows) into outputs. The values go
+// through a wave-private LDS tile first: in the MFMA layout a lane holds one column of 4
+// consecutive rows, so direct stores would be 2- or 4-byte scatters (one store instruction per
+// register); from the tile, every lane stores 16-byte chunks of whole rows (1 KB per
+// instruction). EPI_LDS bytes of LDS per wave.
+constexpr int EPI_LDS = 32 * 544;
+static_assert(EPI_LDS <= STAGE_BYTES, "an epilogue tile must fit in one stage");
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Store ROWS x CHUNKS 16-byte chunks of the tile (row pitch PITCH) to dest(r, c) (nullptr =
+// skip); RMW adds the fp32 chunk to what is in memory (accumulating fp32 epilogue).
+template <int ROWS, int CHUNKS, int PITCH, bool RMW = false, class Dest>
+__device__ __forceinline__ void flush_tile(const unsigned char* lds, Dest dest, int lane) {
+    wave_lds_sync();
+#pragma unroll
+    for (int idx = lane; idx < ROWS * CHUNKS; idx += 64) {
+        const int r = idx / CHUNKS, c = idx % CHUNKS;
+        unsigned char* d = dest(r, c);
+        if (!d) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * PITCH + 16 * c);
+        if (RMW) {
+            const f32x4 old = *reinterpret_cast<const f32x4*>(d);
+            *reinterpret_cast<f32x4*>(d) = old + __builtin_bit_cast(f32x4, v);
+        } else {
+            *reinterpret_cast<u32x4*>(d) = v;
+        }
+    }
+    wave_lds_sync();   // the tile is free for the next row block
+}
 
 // KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=, 4 OCP E4M3 code of v * (1 / out_div).
 // Every accumulator is first multiplied by `scale` (the product of the per-tensor operand
@@ -352,41 +387,35 @@ struct EpiStore {
     void* C;
     int64_t ldc, M, N;
     float scale, out_div;
-    // accumulator row block i (acc[i][0..3]) of wave (wm, wn)
+    // accumulator row block i (acc[i][0..3]) of wave (wm, wn): 32 rows x 128 columns
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
-                         int lane) const {
-        // one row address per register r (row offsets are compile-time multiples of ldc),
-        // the four column blocks as constant offsets from it
+                         int lane, unsigned char* lds) const {
+        using T = std::conditional_t<(KIND >= 2 && KIND <= 3), float, std::conditional_t<KIND == 4, uint8_t, uint16_t>>;
+        constexpr int ES = sizeof(T);
+        constexpr int PITCH = 128 * ES + (ES == 4 ? 32 : 16);   // pads spread the two lane halves over the banks
+        constexpr int CHUNKS = 128 * ES / 16;
         const int r32 = lane & 31, hi = lane >> 5;
-        const int64_t c0 = n0 + wn * 128 + r32;
-        const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
         const float out_inv = 1.0f / out_div;
-        // interior tiles (the common case) take a copy of the loop without bounds checks
-        auto body = [&](auto check) {
-            constexpr bool CHECK = decltype(check)::value;
-            bool col_ok[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) col_ok[j] = !CHECK || c0 + j * 32 < N;
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dr = acc_row(0, r, 0);
-                if (CHECK && row0 + dr >= M) continue;
-                const int64_t off = (row0 + dr) * ldc + c0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (CHECK && !col_ok[j]) continue;
-                    float v = a[j][r] * scale;
-                    if (RELU) v = v > 0.0f ? v : 0.0f;
-                    if (KIND == 0) static_cast<uint16_t*>(C)[off + j * 32] = f32_to_bf16(v);
-                    else if (KIND == 1) static_cast<uint16_t*>(C)[off + j * 32] = f32_to_f16(v);
-                    else if (KIND == 2) static_cast<float*>(C)[off + j * 32] = v;
-                    else if (KIND == 3) static_cast<float*>(C)[off + j * 32] += v;
-                    else static_cast<uint8_t*>(C)[off + j * 32] = f32_to_e4m3(v * out_inv);
-                }
+            for (int j = 0; j < 4; ++j) {
+                float v = a[j][r] * scale;
+                if (RELU) v = v > 0.0f ? v : 0.0f;
+                T t;
+                if constexpr (KIND == 0) t = f32_to_bf16(v);
+                else if constexpr (KIND == 1) t = f32_to_f16(v);
+                else if constexpr (KIND <= 3) t = v;
+                else t = f32_to_e4m3(v * out_inv);
+                *reinterpret_cast<T*>(lds + acc_row(0, r, hi) * PITCH + (j * 32 + r32) * ES) = t;
             }
-        };
-        if (m0 + BM <= M && n0 + BN <= N) body(std::false_type{});
-        else body(std::true_type{});
+        const int64_t row0 = m0 + wm * 128 + i * 32, col0 = n0 + wn * 128;
+        const int64_t rows_ok = M - row0, chunks_ok = (N - col0) * ES / 16;   // N is a multiple of 16 / ES
+        unsigned char* base = static_cast<unsigned char*>(C) + (row0 * ldc + col0) * ES;
+        flush_tile<32, CHUNKS, PITCH, KIND == 3>(
+            lds, [&](int r, int c) -> unsigned char* {
+                return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * ldc) * ES + 16 * c : nullptr;
+            }, lane);
     }
 };
 
@@ -397,95 +426,115 @@ struct EpiSwiGLU {
     void* h;   // [M, N]
     int64_t M, N;
     float gs, us, h_scale;
-    // acc[i][0..1] hold gate columns, acc[i][2..3] the matching up columns
+    // acc[i][0..1] hold gate columns, acc[i][2..3] the matching up columns: 32 rows x 64 h
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
-                         int lane) const {
+                         int lane, unsigned char* lds) const {
+        constexpr int ES = H8 ? 1 : 2;
+        constexpr int PITCH = 64 * ES + 16;
+        constexpr int CHUNKS = 64 * ES / 16;
         const int r32 = lane & 31, hi = lane >> 5;
-        const int64_t c0 = n0 + wn * 64 + r32;
-        const int64_t row0 = m0 + wm * 128 + acc_row(i, 0, hi);
         const float h_inv = 1.0f / h_scale;   // one division per row block, not per element
-        // interior tiles (the common case) take a copy of the loop without bounds checks
-        auto body = [&](auto check) {
-            constexpr bool CHECK = decltype(check)::value;
-            const bool ok0 = !CHECK || c0 < N, ok1 = !CHECK || c0 + 32 < N;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dr = acc_row(0, r, 0);
-                if (CHECK && row0 + dr >= M) continue;
-                const int64_t off = (row0 + dr) * N + c0;
+        for (int r = 0; r < 16; ++r)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (CHECK && !(j ? ok1 : ok0)) continue;
-                    const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
-                    const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
-                    if (H8) static_cast<uint8_t*>(h)[off + j * 32] = f32_to_e4m3(silu * up * h_inv);
-                    else static_cast<uint16_t*>(h)[off + j * 32] = f32_to_bf16(silu * up);
-                }
+            for (int j = 0; j < 2; ++j) {
+                const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
+                const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
+                unsigned char* t = lds + acc_row(0, r, hi) * PITCH + (j * 32 + r32) * ES;
+                if (H8) *t = f32_to_e4m3(silu * up * h_inv);
+                else *reinterpret_cast<uint16_t*>(t) = f32_to_bf16(silu * up);
             }
-        };
-        if (m0 + BM <= M && n0 + BN / 2 <= N) body(std::false_type{});
-        else body(std::true_type{});
+        const int64_t row0 = m0 + wm * 128 + i * 32, col0 = n0 + wn * 64;
+        const int64_t rows_ok = M - row0, chunks_ok = (N - col0) * ES / 16;   // N is a multiple of 16
+        unsigned char* base = static_cast<unsigned char*>(h) + (row0 * N + col0) * ES;
+        flush_tile<32, CHUNKS, PITCH>(
+            lds, [&](int r, int c) -> unsigned char* {
+                return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * N) * ES + 16 * c : nullptr;
+            }, lane);
     }
 };
 
+// QKV projection epilogue: wave = one head (128 columns). q and k heads are rotated (rotate-
+// half pairs (c, c+64), angles of the token's position from the table) and stored fp16 head-
+// major [B, heads, S, 128]; v heads are stored transposed, [B, hkv, 128, S]. M and S are
+// multiples of 8, so a group of 8 consecutive rows (one 16-byte chunk of V^T) lies in one
+// sequence; B*S < 2^31 (checked on the host), so token indexes divide in 32 bits.
 struct EpiQKV {
     QKVOut o;
     int64_t M;   // B*S
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
-                         int lane) const {
+                         int lane, unsigned char* lds) const {
         const int r32 = lane & 31, hi = lane >> 5;
-        const int head = (int)((n0 + wn * 128) >> 7);   // one wave = one head of 128 columns
+        const int head = (int)((n0 + wn * 128) >> 7);
         const int n_heads = o.hq + 2 * o.hkv;
         if (head >= n_heads) return;
-        const int64_t S = o.S;
+        const unsigned S = (unsigned)o.S;
+        const int64_t row0 = m0 + wm * 128 + i * 32;
+        const int64_t rows_ok = M - row0;
         if (head < o.hq + o.hkv) {
+            constexpr int PITCH = 272;
             const bool is_q = head < o.hq;
             const int hh = is_q ? head : head - o.hq;
             const int nh = is_q ? o.hq : o.hkv;
-            uint16_t* dst = static_cast<uint16_t*>(is_q ? o.q : o.k);
-            // rows 4q..4q+3 of a lane are consecutive tokens of one sequence (M and S are
-            // multiples of 8): one 32-bit division per group of 4 (B*S < 2^31, checked on
-            // the host)
+            // positions: rows come in groups of 4 consecutive tokens 8 apart; a group starts at a
+            // multiple of 4 and S is a multiple of 8, so a group never wraps into the next
+            // sequence, and stepping 8 rows wraps at most once. Rows past M keep a valid angle.
+            unsigned s4 = (unsigned)(row0 + 4 * hi) % S;
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int64_t row0 = m0 + wm * 128 + acc_row(i, 4 * rq, hi);
-                if (row0 >= M) continue;
-                const unsigned b = (unsigned)row0 / (unsigned)S;
-                const int64_t s0 = row0 - (int64_t)b * S;
+            for (int g = 0; g < 4; ++g) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rq + e;
-                    const int64_t s = s0 + e;
-                    uint16_t* out = dst + (((int64_t)b * nh + hh) * S + s) * 128;
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 4 * g + k, rl = acc_row(0, r, hi);
+                    const float2* cs_row = o.rope + (int64_t)(s4 + k) * 64;
+                    uint16_t* t = reinterpret_cast<uint16_t*>(lds + rl * PITCH);
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int c = j * 32 + r32;               // pair (c, c + 64)
-                        const float2 cs = o.rope[s * 64 + c];
+                        const int c = j * 32 + r32;   // pair (c, c + 64)
+                        const float2 cs = cs_row[c];
                         const float x1 = a[j][r], x2 = a[j + 2][r];
-                        out[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
-                        out[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
+                        t[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
+                        t[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
                     }
                 }
+                s4 += 8;
+                if (s4 >= S) s4 -= S;
             }
-        } else {
-            // V^T: a lane's registers 4q..4q+3 are 4 consecutive tokens of one dim, written
-            // as one 8-byte store (M and S are multiples of 8, so the 4 tokens are all valid
-            // and lie in one sequence)
-            const int hv = head - o.hq - o.hkv;
-            uint16_t* vt = static_cast<uint16_t*>(o.vt);
+            // 32 rows x 16 chunks: lane -> chunk lane % 16 of rows lane / 16 + 4 it
+            unsigned char* dst = static_cast<unsigned char*>(is_q ? o.q : o.k);
+            const unsigned tok = (unsigned)(row0 + (lane >> 4));
+            unsigned b = tok / S, sq = tok - b * S;
+            wave_lds_sync();
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int64_t row = m0 + wm * 128 + acc_row(i, 4 * rq, hi);
-                if (row >= M) continue;
-                const int64_t b = (unsigned)row / (unsigned)S, s = row - b * S;
+            for (int it = 0; it < 8; ++it) {
+                const int r = (lane >> 4) + 4 * it;
+                if (r < rows_ok)
+                    *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * nh + hh) * S + sq) * 128) * 2 +
+                                              16 * (lane & 15)) =
+                        *reinterpret_cast<const u32x4*>(lds + r * PITCH + 16 * (lane & 15));
+                sq += 4;
+                if (sq >= S) { sq -= S; ++b; }
+            }
+            wave_lds_sync();
+        } else {
+            // V^T tile: 128 dims x 32 tokens
+            constexpr int PITCH = 80;
+            const int hv = head - o.hq - o.hkv;
+            // a lane holds 4 consecutive tokens of one dim per register group: 8-byte writes
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int d = j * 32 + r32;
-                    const unsigned lo = (unsigned)f32_to_f16(a[j][4 * rq]) | ((unsigned)f32_to_f16(a[j][4 * rq + 1]) << 16);
-                    const unsigned hi2 = (unsigned)f32_to_f16(a[j][4 * rq + 2]) | ((unsigned)f32_to_f16(a[j][4 * rq + 3]) << 16);
-                    *reinterpret_cast<uint2*>(vt + ((b * o.hkv + hv) * 128 + d) * S + s) = make_uint2(lo, hi2);
+                    const unsigned lo = f32_to_f16(a[j][4 * g]) | ((unsigned)f32_to_f16(a[j][4 * g + 1]) << 16);
+                    const unsigned hw = f32_to_f16(a[j][4 * g + 2]) | ((unsigned)f32_to_f16(a[j][4 * g + 3]) << 16);
+                    *reinterpret_cast<u32x2*>(lds + (j * 32 + r32) * PITCH + acc_row(0, 4 * g, hi) * 2) = u32x2{lo, hw};
                 }
-            }
+            unsigned char* vt = static_cast<unsigned char*>(o.vt);
+            flush_tile<128, 4, PITCH>(
+                lds, [&](int d, int c) -> unsigned char* {
+                    if (8 * c >= rows_ok) return nullptr;
+                    const unsigned tok = (unsigned)(row0 + 8 * c), b = tok / S, s = tok - b * S;
+                    return vt + ((((int64_t)b * o.hkv + hv) * 128 + d) * S + s) * 2;
+                }, lane);
         }
     }
 };
@@ -493,9 +542,9 @@ struct EpiQKV {
 // the whole 128x128 accumulator of one wave through an epilogue
 template <class Epi>
 __device__ __forceinline__ void run_epilogue(const Epi& epi, f32x16 (&acc)[4][4], int64_t m0,
-                                             int64_t n0, int wm, int wn, int lane) {
+                                             int64_t n0, int wm, int wn, int lane, unsigned char* lds) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) epi.rows(acc[i], i, m0, n0, wm, wn, lane);
+    for (int i = 0; i < 4; ++i) epi.rows(acc[i], i, m0, n0, wm, wn, lane, lds);
 }
 
 // Logical tile L -> (row tile, column tile): groups of 4 row tiles, row fastest.
@@ -794,7 +843,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         }
     }
     if (q < 0) {
-        run_epilogue(epi, acc, m0, n0, wm, wn, lane);
+        __syncthreads();   // every wave is done with the stages; each now uses one as its tile
+        unsigned char* tile = wave == 0 ? st0 : wave == 1 ? st1 : wave == 2 ? st2 : st3;
+        run_epilogue(epi, acc, m0, n0, wm, wn, lane, tile);
         return;
     }
     float* dst = sp.part + ((int64_t)q * 4 + wave) * (256 * 64) + lane;
@@ -812,6 +863,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
 template <bool DUAL, class Epi>
 __global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, int tiles_m, int tiles_n,
                                                                       SplitArgs sp) {
+    __shared__ __attribute__((aligned(16))) unsigned char tile[FIXUP_WAVES * EPI_LDS];
     const int lane = threadIdx.x & 63;
     const int gw = (int)blockIdx.x * FIXUP_WAVES + (int)(threadIdx.x >> 6);   // (tile, wave, i)
     const int t = gw >> 4, wave = (gw >> 2) & 3, i = gw & 3;
@@ -831,7 +883,8 @@ __global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, i
 #pragma unroll
             for (int r = 0; r < 16; ++r) a[j][r] += s2[(j * 16 + r) * 64];
     }
-    epi.rows(a, i, (int64_t)tm * BM, (int64_t)tn * (DUAL ? BN / 2 : BN), wm, wn, lane);
+    epi.rows(a, i, (int64_t)tm * BM, (int64_t)tn * (DUAL ? BN / 2 : BN), wm, wn, lane,
+             tile + (threadIdx.x >> 6) * EPI_LDS);
 }
 
 int cu_count() {
