@@ -173,8 +173,8 @@ size_t tp_mlp_fp8_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_k
  * ("TensorRT LLM 中的并行策略", 注意力模块): q head j reads kv head
  * floor(j * n_kv_heads / n_q_heads).
  *   B, S, H        sequences, tokens per sequence, hidden size (T = B*S rows of X);
- *                  prefill: S a multiple of 8 and T < 2^31 (else TP_ERR_MISALIGNED /
- *                  TP_ERR_UNSUPPORTED)
+ *                  prefill: S a multiple of 8, S <= 2^24 and T < 2^31 (else
+ *                  TP_ERR_MISALIGNED / TP_ERR_UNSUPPORTED)
  *   head_dim       must be 128
  *   rope_theta     rotary base; rotate-half pairs (i, i+64), angle pos*theta^(-2i/128),
  *                  applied to q and k; pos = index in the sequence (decode: cache_len)

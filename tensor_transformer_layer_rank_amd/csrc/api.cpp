@@ -454,6 +454,8 @@ static tp_status check_attn_desc(const tp_attn_desc* d, bool* decode) {
             return fail(TP_ERR_MISALIGNED, "tp_attn_shard: caches must be 16-byte aligned");
     } else if (d->S % 8) {
         return fail(TP_ERR_MISALIGNED, "tp_attn_shard: prefill needs S to be a multiple of 8 (S=%lld)", (long long)d->S);
+    } else if (d->S > ((int64_t)1 << 24)) {
+        return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: prefill offers S <= 2^24 (S=%lld)", (long long)d->S);
     } else if (d->B * d->S >= ((int64_t)1 << 31)) {
         return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: prefill offers fewer than 2^31 tokens (B*S=%lld)",
                     (long long)(d->B * d->S));

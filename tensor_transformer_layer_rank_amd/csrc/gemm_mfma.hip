@@ -456,9 +456,10 @@ struct EpiSwiGLU {
 
 // QKV projection epilogue: wave = one head (128 columns). q and k heads are rotated (rotate-
 // half pairs (c, c+64), angles of the token's position from the table) and stored fp16 head-
-// major [B, heads, S, 128]; v heads are stored transposed, [B, hkv, 128, S]. M and S are
-// multiples of 8, so a group of 8 consecutive rows (one 16-byte chunk of V^T) lies in one
-// sequence; B*S < 2^31 (checked on the host), so token indexes divide in 32 bits.
+// major [B, heads, S, 128] (q times ATTN_Q_SCALE); v heads are stored transposed,
+// [B, hkv, 128, S]. M and S are multiples of 8, so a group of 8 consecutive rows (one
+// 16-byte chunk of V^T) lies in one sequence; B*S < 2^31 (checked on the host), so token
+// indexes divide in 32 bits.
 struct EpiQKV {
     QKVOut o;
     int64_t M;   // B*S
@@ -476,6 +477,7 @@ struct EpiQKV {
             const bool is_q = head < o.hq;
             const int hh = is_q ? head : head - o.hq;
             const int nh = is_q ? o.hq : o.hkv;
+            const float qs = is_q ? ATTN_Q_SCALE : 1.0f;
             // positions: rows come in groups of 4 consecutive tokens 8 apart; a group starts at a
             // multiple of 4 and S is a multiple of 8, so a group never wraps into the next
             // sequence, and stepping 8 rows wraps at most once. Rows past M keep a valid angle.
@@ -492,8 +494,8 @@ struct EpiQKV {
                         const int c = j * 32 + r32;   // pair (c, c + 64)
                         const float2 cs = cs_row[c];
                         const float x1 = a[j][r], x2 = a[j + 2][r];
-                        t[c] = f32_to_f16(x1 * cs.x - x2 * cs.y);
-                        t[c + 64] = f32_to_f16(x2 * cs.x + x1 * cs.y);
+                        t[c] = f32_to_f16((x1 * cs.x - x2 * cs.y) * qs);
+                        t[c + 64] = f32_to_f16((x2 * cs.x + x1 * cs.y) * qs);
                     }
                 }
                 s4 += 8;

@@ -53,9 +53,12 @@ hipError_t gemm_f8_swiglu(const void* A, const void* Bg, const void* Bu, void* h
                           int64_t N, int64_t K, float gate_scale, float up_scale, float h_scale,
                           void* ws, size_t ws_bytes, hipStream_t s);
 
-// QKV projection of a prefill with rotary embedding and head-major scatter.
+// QKV projection of a prefill with rotary embedding and head-major scatter. The queries are
+// stored multiplied by ATTN_Q_SCALE = log2(e) / sqrt(128), so the attention kernel's scores
+// come out in log2 units of the softmax argument (one fp16 rounding, as without the scale).
+constexpr float ATTN_Q_SCALE = 1.4426950408889634f * 0.08838834764831845f;
 struct QKVOut {
-    void* q;        // fp16 [B, hq, S, 128]
+    void* q;        // fp16 [B, hq, S, 128], times ATTN_Q_SCALE
     void* k;        // fp16 [B, hkv, S, 128]
     void* vt;       // fp16 [B, hkv, 128, S]   (values stored transposed)
     const float2* rope;   // [S, 64] (cos, sin)

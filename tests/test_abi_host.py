@@ -169,6 +169,7 @@ def test_attn_validation(L):
     assert st(_desc(causal=0)) == "TP_ERR_UNSUPPORTED"
     assert st(_desc(S=60)) == "TP_ERR_MISALIGNED"
     assert st(_desc(B=1 << 20, S=1 << 11)) == "TP_ERR_UNSUPPORTED"   # B*S = 2^31 tokens
+    assert st(_desc(B=1, S=(1 << 24) + 8)) == "TP_ERR_UNSUPPORTED"   # S past 2^24
     assert st(_desc(k_cache=0x1000)) == "TP_ERR_NULL_POINTER"
     assert st(_desc(S=1, k_cache=0x1000, v_cache=0x2000, cache_len=8, cache_capacity=8)) == "TP_ERR_BAD_SHAPE"
     assert st(_desc(S=4, k_cache=0x1000, v_cache=0x2000, cache_len=2, cache_capacity=8)) == "TP_ERR_UNSUPPORTED"

@@ -278,7 +278,8 @@ def test_mlp7b_tp4_full_size_sampled(tp):
 
 # ---------------------------------------------------------------- attention shard
 
-@pytest.mark.parametrize("B,S,hq,hkv,H", [(2, 136, 4, 4, 256), (1, 200, 4, 2, 128), (3, 64, 8, 1, 256), (1, 8, 2, 2, 128)])
+@pytest.mark.parametrize("B,S,hq,hkv,H", [(2, 136, 4, 4, 256), (1, 200, 4, 2, 128), (3, 64, 8, 1, 256), (1, 8, 2, 2, 128),
+                                         (1, 1000, 4, 1, 128), (2, 520, 2, 2, 128)])
 def test_attn_prefill_small(tp, B, S, hq, hkv, H):
     import torch
     inp = wl.random_attn(B * 100 + S, B, S, H, hq, hkv)
