@@ -295,6 +295,21 @@ struct RopeRow {
 // token's own key and value enter from LDS in fp32 (never read back from the cache, which
 // another workgroup of the group may still be writing). The groups are merged in LDS and
 // the normalised row is written as bf16.
+// Sum over the 16 lanes of a row (lane group) with DPP moves folded into the adds: swap
+// neighbours, swap pairs, mirror within 8, mirror within 16. Every lane ends with the same
+// bits (each step adds the same two values, in either order).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    return v;
+}
+
 constexpr int DU = 4;     // keys per group per iteration
 constexpr int NGRP = 32;  // 16-lane groups per workgroup
 
@@ -371,10 +386,7 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     float s_new = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_new += qv[e] * kn[8 * l16 + e];
-    s_new += __shfl_xor(s_new, 8);
-    s_new += __shfl_xor(s_new, 4);
-    s_new += __shfl_xor(s_new, 2);
-    s_new += __shfl_xor(s_new, 1);
+    s_new = sum16(s_new);
 
     auto consume = [&](const u32x4 (&kk)[DU], const u32x4 (&vv)[DU], int64_t j0) {
         float sc[DU];
@@ -388,10 +400,7 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
         }
 #pragma unroll
         for (int u = 0; u < DU; ++u) {
-            sc[u] += __shfl_xor(sc[u], 8);
-            sc[u] += __shfl_xor(sc[u], 4);
-            sc[u] += __shfl_xor(sc[u], 2);
-            sc[u] += __shfl_xor(sc[u], 1);
+            sc[u] = sum16(sc[u]);
             if (j0 + NGRP * u >= L) sc[u] = -__builtin_inff();
         }
         float mc = sc[0];
