@@ -24,9 +24,11 @@ Every function is the plain definition of what a rank computes, in float64 NumPy
 Parity status per function (pins live in ``tests/test_oracle_pins.py``):
 all functions are pinned (the E4M3 table and rounding against torch's float8_e4m3fn
 conversion and a bit-by-bit construction; the fp8 layers against pure-Python loops)
-except the rotary-embedding *convention* (rotate-half
-pairs (i, i+d/2), frequency theta^(-2i/d)), which the pages never state: its
-closed-form properties are pinned, the choice of convention is "parity unpinned".
+except two conventions the pages never state: the rotary-embedding *convention*
+(rotate-half pairs (i, i+d/2), frequency theta^(-2i/d)) and the RMSNorm *formula* (the
+pages name RMSNorm but not its formula; the usual x / sqrt(mean(x^2) + eps) * gamma is
+used). Their closed-form properties are pinned; the choice of convention is "parity
+unpinned".
 """
 from .tp_ref import *  # noqa: F401,F403
 from .fp8_ref import *  # noqa: F401,F403

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import math
 
-__all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row", "e4m3_to_float", "fp8_matmul"]
+__all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row", "e4m3_to_float", "fp8_matmul",
+           "rms_norm_row"]
 
 
 def matmul(X, W):
@@ -101,3 +102,13 @@ def fp8_matmul(Xc, x_scale, Wc, w_scale):
     X = [[e4m3_to_float(c) for c in row] for row in Xc]
     W = [[e4m3_to_float(c) for c in row] for row in Wc]
     return [[v * x_scale * w_scale for v in row] for row in matmul(X, W)]
+
+
+def rms_norm_row(x, gamma, eps):
+    """One row: x_j / sqrt((sum_j x_j^2) / n + eps) * gamma_j, with Python floats."""
+    n = len(x)
+    ss = 0.0
+    for v in x:
+        ss += float(v) * float(v)
+    inv = 1.0 / math.sqrt(ss / n + float(eps))
+    return [float(x[j]) * inv * float(gamma[j]) for j in range(n)]

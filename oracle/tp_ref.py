@@ -36,7 +36,7 @@ __all__ = [
     "mlp_swiglu_shard", "mlp_shard", "rope_cos_sin", "apply_rope", "softmax_rows",
     "sdpa_causal", "kv_head_of", "split_qkv_heads", "attn_heads", "attn_shard",
     "attn_shard_rows", "attn_shard_weights", "full_attention_block", "decode_qkv",
-    "decode_attn_shard", "lm_head_shard", "mlp_full",
+    "decode_attn_shard", "lm_head_shard", "mlp_full", "rms_norm", "merge_rmsnorm",
 ]
 
 
@@ -366,3 +366,29 @@ def decode_attn_shard(X, W_qkv, W_o, k_cache, v_cache, cache_len: int, hq: int,
 def lm_head_shard(X, W_lm_shard) -> np.ndarray:
     """Vocabulary-parallel output layer: this rank's logits columns X @ W_lm[:, vocab_r]."""
     return linear(X, W_lm_shard)
+
+
+# ---------------------------------------------------------------------------
+# The step after the merge: residual add and RMS normalisation of the block output
+# ---------------------------------------------------------------------------
+
+def rms_norm(x, gamma, eps: float) -> np.ndarray:
+    """RMS normalisation over the hidden dimension (last axis): x / sqrt(mean(x^2) + eps) * gamma.
+
+    "CUDA tensor parallel computations", 第五类 局部逐元素计算: a norm reads a whole row of
+    the hidden dimension, so on a rank it runs on the merged (replicated) output. The
+    pages name RMSNorm without its formula; this is its usual definition (mean of squares
+    over the row, eps inside the square root, per-column gain gamma)."""
+    x = f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * f64(gamma)
+
+
+def merge_rmsnorm(partials, residual, gamma, eps: float):
+    """Residual stream after a row-parallel block and the next block's normalised input.
+
+    r = residual + (((P_0 + P_1) + ...) + P_{k-1}) (the all-reduce result of
+    "CUDA tensor parallel computations", 第四类, added to the block input) and
+    normed = rms_norm(r, gamma, eps). Returns (r, normed)."""
+    r = f64(residual) + partial_sum(partials)
+    return r, rms_norm(r, gamma, eps)

@@ -520,3 +520,43 @@ def test_fp8_workload_codes_and_scales():
         assert np.all(np.isfinite(v)) and np.max(np.abs(v)) <= 448.0
         assert np.max(np.abs(v)) >= 400.0            # scale = amax / 448 uses the range
         assert scale > 0
+
+
+# --- residual add + RMSNorm after the merge ("CUDA tensor parallel computations", 第四类 and
+# 第五类: a norm needs a whole hidden row, so it follows the all-reduce)
+
+def test_merge_residual_is_input_plus_left_to_right_sum():
+    rng = np.random.default_rng(7)
+    parts = [rng.integers(-4, 5, size=(3, 8)).astype(np.float32) for _ in range(3)]
+    res = rng.integers(-4, 5, size=(3, 8)).astype(np.float32)
+    r, _ = O.merge_rmsnorm(parts, res, np.ones(8), 1e-6)
+    assert np.array_equal(r, res.astype(float) + parts[0] + parts[1] + parts[2])
+
+
+def test_rms_norm_worked_numbers():
+    # row [3, 4]: mean of squares 12.5; gain [1, 2]
+    y = O.rms_norm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    assert np.allclose(y, [[3 / math.sqrt(12.5), 8 / math.sqrt(12.5)]], rtol=0, atol=1e-15)
+    y = O.rms_norm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.5)   # eps inside the root
+    assert np.allclose(y, [[3 / math.sqrt(13.0), 8 / math.sqrt(13.0)]], rtol=0, atol=1e-15)
+
+
+def test_rms_norm_unit_rms_scale_invariance_and_gain_per_column():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 64))
+    y = O.rms_norm(x, np.ones(64), 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)         # mean, not sum
+    assert np.allclose(O.rms_norm(7.5 * x, np.ones(64), 0.0), y, rtol=1e-13)
+    assert np.allclose(O.rms_norm(-x, np.ones(64), 0.0), -y, rtol=1e-13)  # odd in x
+    g = rng.standard_normal(64)
+    assert np.allclose(O.rms_norm(np.ones((2, 64)), g, 0.0), np.tile(g, (2, 1)), rtol=1e-13)
+    assert np.array_equal(O.rms_norm(np.zeros((1, 64)), g, 1e-5), np.zeros((1, 64)))
+
+
+def test_rms_norm_matches_brute_force():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((4, 24))
+    g = rng.standard_normal(24)
+    y = O.rms_norm(x, g, 1e-3)
+    for i in range(4):
+        assert np.allclose(y[i], brute.rms_norm_row(list(x[i]), list(g), 1e-3), rtol=1e-13, atol=0)
