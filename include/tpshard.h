@@ -221,6 +221,27 @@ size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt);
 tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out,
                          int64_t n_elems, void* stream);
 
+/*
+ * tp_merge_rmsnorm — the step after the merge of a row-parallel block: add the block
+ *   output to the residual stream and normalise it for the next block. The merge is the
+ *   all-reduce result ("CUDA tensor parallel computations", 第四类 跨卡通信计算); a norm
+ *   reads a whole hidden row, so it runs on that merged output (same page, 第五类
+ *   局部逐元素计算, on LayerNorm / RMSNorm). Per row t of T:
+ *     r            = residual[t, :] + (((P_0 + P_1) + P_2) + ... + P_{k-1})[t, :]   (fp32)
+ *     residual_out = bf16(r)                                         (round to nearest even)
+ *     normed       = bf16(r * (1 / sqrt(mean_j r_j^2 + eps)) * gamma)
+ *   (the usual RMSNorm: the pages do not print its formula).
+ *   partials: HOST array of k device pointers to [T, H] fp32, 1 <= k <= 16;
+ *   residual, residual_out, normed: [T, H] bf16 row-major; gamma: [H] bf16.
+ *   All device buffers 16-byte aligned; H a multiple of 8 and <= 16384; T < 2^31;
+ *   eps finite and >= 0 (else TP_ERR_BAD_SHAPE / TP_ERR_UNSUPPORTED / TP_ERR_MISALIGNED).
+ *   residual_out may be residual (in-place update); normed must not overlap any input.
+ *   No workspace; asynchronous on `stream`; deterministic (fixed reduction order).
+ */
+tp_status tp_merge_rmsnorm(const float* const* partials, int32_t k, const void* residual,
+                           const void* gamma, float eps, void* residual_out, void* normed,
+                           int64_t T, int64_t H, void* stream);
+
 /* Status text, thread-local detail of this thread's last non-OK status, ABI version. */
 const char* tp_status_string(tp_status st);
 const char* tp_last_error(void);

@@ -17,7 +17,7 @@ __all__ = [
     "TpError", "lib", "load", "LIB_PATH", "column_linear", "row_linear_partial", "mlp_shard",
     "attn_shard", "partial_sum", "linear_workspace_size", "mlp_workspace_size",
     "attn_workspace_size", "mlp_shard_fp8", "mlp_fp8_workspace_size", "AttnDesc",
-    "profile_enable", "profile_reset", "profile_read",
+    "profile_enable", "profile_reset", "profile_read", "merge_rmsnorm",
     "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
     "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
 ]
@@ -35,6 +35,7 @@ EXPORTS = [
     "tp_mlp_workspace_size", "tp_attn_shard", "tp_attn_workspace_size", "tp_partial_sum",
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
+    "tp_merge_rmsnorm",
 ]
 
 
@@ -97,6 +98,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tp_mlp_shard_fp8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, ctypes.POINTER(Fp8MlpScales),
                               _P, _SZ, _P], _I32),
         "tp_mlp_fp8_workspace_size": ([_I64, _I64, _I64, _I32], _SZ),
+        "tp_merge_rmsnorm": ([ctypes.POINTER(_P), _I32, _P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P], _I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -292,6 +294,25 @@ def partial_sum(partials, out=None, stream=None):
         _ptr(p)
     _check(lib().tp_partial_sum(arr, k, _ptr(out), n, _stream(stream)))
     return out
+
+
+def merge_rmsnorm(partials, residual, gamma, eps: float = 1e-5, residual_out=None, normed=None, stream=None):
+    """r = residual + ((P0 + P1) + ...), returns (bf16(r), bf16(rms_norm(r) * gamma)).
+    partials: fp32 [T, H] GPU tensors; residual bf16 [T, H]; gamma bf16 [H].
+    residual_out may be residual (in-place)."""
+    import torch
+    T, H = residual.shape
+    k = len(partials)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if normed is None:
+        normed = torch.empty_like(residual)
+    for p in partials:
+        _ptr(p)
+    arr = (ctypes.c_void_p * k)(*[p.data_ptr() for p in partials])
+    _check(lib().tp_merge_rmsnorm(arr, k, _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out),
+                                  _ptr(normed), T, H, _stream(stream)))
+    return residual_out, normed
 
 
 # --- kernel timing ------------------------------------------------------------------------------

@@ -557,4 +557,26 @@ tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out, in
     return from_hip(tpk::partial_sum(partials, k, out, n_elems, as_stream(stream)), "tp_partial_sum");
 }
 
+tp_status tp_merge_rmsnorm(const float* const* partials, int32_t k, const void* residual, const void* gamma,
+                           float eps, void* residual_out, void* normed, int64_t T, int64_t H, void* stream) {
+    const char* fn = "tp_merge_rmsnorm";
+    if (!partials || !residual || !gamma || !residual_out || !normed)
+        return fail(TP_ERR_NULL_POINTER, "%s: partials, residual, gamma, residual_out and normed must be non-NULL", fn);
+    if (k < 1 || k > 16) return fail(TP_ERR_BAD_SHAPE, "%s: k=%d outside 1..16", fn, (int)k);
+    if (T <= 0 || H <= 0) return fail(TP_ERR_BAD_SHAPE, "%s: T and H must be positive (T=%lld H=%lld)", fn,
+                                      (long long)T, (long long)H);
+    if (T >= ((int64_t)1 << 31)) return fail(TP_ERR_UNSUPPORTED, "%s: T=%lld rows (at most 2^31 - 1)", fn, (long long)T);
+    if (H % 8 || H > 16384)
+        return fail(TP_ERR_UNSUPPORTED, "%s: H=%lld (a multiple of 8, at most 16384)", fn, (long long)H);
+    if (!(eps >= 0.0f) || !(eps <= 1e30f)) return fail(TP_ERR_BAD_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(normed, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: residual, gamma, residual_out and normed must be 16-byte aligned", fn);
+    for (int i = 0; i < k; ++i) {
+        if (!partials[i]) return fail(TP_ERR_NULL_POINTER, "%s: partials[%d] is NULL", fn, i);
+        if (!aligned(partials[i], 16)) return fail(TP_ERR_MISALIGNED, "%s: partials[%d] must be 16-byte aligned", fn, i);
+    }
+    return from_hip(tpk::merge_rmsnorm(partials, k, residual, gamma, eps, residual_out, normed, T, H,
+                                       as_stream(stream)), fn);
+}
+
 }  // extern "C"

@@ -95,5 +95,9 @@ hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_
 
 // ---- merges -------------------------------------------------------------------------------
 hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s);
+// r = residual + ((P0 + P1) + ...) (fp32), residual_out = bf16(r),
+// normed = bf16(r / sqrt(mean_row(r^2) + eps) * gamma); bf16 [T, H], H % 8 == 0, H <= 16384
+hipError_t merge_rmsnorm(const float* const* parts, int k, const void* residual, const void* gamma, float eps,
+                         void* residual_out, void* normed, int64_t T, int64_t H, hipStream_t s);
 
 }  // namespace tpk

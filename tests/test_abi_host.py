@@ -197,6 +197,31 @@ def test_partial_sum_validation(L):
     assert _st(f(arr3, 2, FAKE, 8, None)) == "TP_ERR_MISALIGNED"
 
 
+def test_merge_rmsnorm_validation(L):
+    f = L.tp_merge_rmsnorm
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    ok = (arr, 2, FAKE, FAKE, 1e-5, FAKE, FAKE, 4, 64, None)
+
+    def st(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return _st(f(*a))
+    assert st(a1=0) == "TP_ERR_BAD_SHAPE" and st(a1=17) == "TP_ERR_BAD_SHAPE"
+    assert st(a0=None) == "TP_ERR_NULL_POINTER"
+    assert st(a0=(ctypes.c_void_p * 2)(0x1000, None)) == "TP_ERR_NULL_POINTER"
+    for i in (2, 3, 5, 6):
+        assert st(**{f"a{i}": None}) == "TP_ERR_NULL_POINTER"
+        assert st(**{f"a{i}": FAKE_ODD}) == "TP_ERR_MISALIGNED"
+    assert st(a0=(ctypes.c_void_p * 2)(0x1000, 0x2004)) == "TP_ERR_MISALIGNED"
+    assert st(a7=0) == "TP_ERR_BAD_SHAPE" and st(a8=0) == "TP_ERR_BAD_SHAPE"
+    assert st(a8=60) == "TP_ERR_UNSUPPORTED"                      # H % 8
+    assert st(a8=16384 + 8) == "TP_ERR_UNSUPPORTED"               # H past 16384
+    assert st(a7=1 << 31) == "TP_ERR_UNSUPPORTED"                 # T rows
+    assert st(a4=-1.0) == "TP_ERR_BAD_SHAPE" and st(a4=float("nan")) == "TP_ERR_BAD_SHAPE"
+    assert st(a4=float("inf")) == "TP_ERR_BAD_SHAPE"
+
+
 def test_profile_api_without_launches(L):
     assert L.tp_profile_reset() == 0
     ms, n = tp.profile_read("")

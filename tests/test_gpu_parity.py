@@ -113,6 +113,59 @@ def test_partial_sum_accumulate_in_place(tp):
     assert host(a).tolist() == (np.arange(12) + 1.0).tolist()
 
 
+# ---------------------------------------------------------------- merge + residual + RMSNorm
+
+def _merge_call(tp, inp, residual=None, residual_out=None):
+    import torch
+    T, H = inp.T, inp.H
+    parts = [dev(p, "f32") for p in inp.partials]
+    res = dev(inp.residual) if residual is None else residual
+    R = _nan((T, H), torch.bfloat16) if residual_out is None else residual_out
+    R, N = tp.merge_rmsnorm(parts, res, dev(inp.gamma), inp.eps, residual_out=R,
+                            normed=_nan((T, H), torch.bfloat16))
+    torch.cuda.synchronize()
+    return R, N
+
+
+# H covers every chunk count per thread (1, 2, 4, 8 chunks of 8 for 256 threads) and ragged
+# ones (H/8 = 125, 257, 1); k from 1 to 16 partials
+@pytest.mark.parametrize("T,H,k", [(5, 136, 1), (37, 1000, 3), (3, 8, 2), (2, 16384, 4), (9, 2056, 16),
+                                   (4, 6144, 2)])
+def test_merge_rmsnorm_small(tp, T, H, k):
+    inp = wl.random_merge(T * 31 + H + k, T, H, k)
+    R, N = _merge_call(tp, inp)
+    r_ref, n_ref = O.merge_rmsnorm(inp.partials, inp.residual, inp.gamma, inp.eps)
+    assert_close_bf16(host(R), r_ref, f"residual T{T} H{H} k{k}", out="bf16")
+    assert_close_bf16(host(N), n_ref, f"normed T{T} H{H} k{k}", out="bf16")
+
+
+def test_merge_rmsnorm_in_place_deterministic_and_zero_rows(tp):
+    inp = wl.random_merge(77, 6, 4096, 4)
+    R1, N1 = _merge_call(tp, inp)
+    res = dev(inp.residual)
+    R2, N2 = _merge_call(tp, inp, residual=res, residual_out=res)   # residual updated in place
+    assert R2.data_ptr() == res.data_ptr()
+    assert np.array_equal(host(R1), host(R2)) and np.array_equal(host(N1), host(N2))
+    z = wl.random_merge(78, 3, 1024, 2)
+    z.partials = [np.zeros_like(p) for p in z.partials]
+    z.residual = np.zeros_like(z.residual)
+    R, N = _merge_call(tp, z)
+    assert not np.any(host(R)) and not np.any(host(N))               # eps > 0: exact zeros, no NaN
+
+
+def test_merge7b_tp4_full_size_sampled(tp):
+    """The merge step of the 7B TP=4 block at its full size: [8192, 4096], 4 partials."""
+    inp = wl.merge7b_tp4()
+    R, N = _merge_call(tp, inp)
+    R2, N2 = _merge_call(tp, inp)
+    r, n = host(R), host(N)
+    assert np.array_equal(r, host(R2)) and np.array_equal(n, host(N2)), "two launches differ bitwise"
+    rows = sample_rows(inp.T, 64, seed=3)
+    r_ref, n_ref = O.merge_rmsnorm([p[rows] for p in inp.partials], inp.residual[rows], inp.gamma, inp.eps)
+    assert_close_bf16(r[rows], r_ref, "merge7b_tp4 residual", out="bf16")
+    assert_close_bf16(n[rows], n_ref, "merge7b_tp4 normed", out="bf16")
+
+
 # ---------------------------------------------------------------- bf16 linear layers
 
 @pytest.mark.parametrize("T,K,N", [(300, 256, 200), (513, 520, 264), (256, 64, 256), (65, 4096, 384)])

@@ -37,7 +37,8 @@ __all__ = [
     "bf16_round", "bf16_bits", "bits_to_f32", "MLPInputs", "AttnInputs", "DecodeInputs",
     "mlp_relu_tp2", "mlp7b_tp4", "attn7b_tp4", "layer70b_tp8", "decode7b_tp2",
     "random_mlp", "random_attn", "random_decode", "int_matrix", "WORKLOADS",
-    "e4m3_codes", "FP8MLPInputs", "random_mlp_fp8", "mlp7b_tp4_fp8",
+    "e4m3_codes", "FP8MLPInputs", "random_mlp_fp8", "mlp7b_tp4_fp8", "MergeInputs", "random_merge",
+    "merge7b_tp4",
 ]
 
 
@@ -292,6 +293,39 @@ def mlp7b_tp4_fp8(seed: int = 5) -> FP8MLPInputs:
     return random_mlp_fp8(seed, 4096, 4096, 2752, "mlp7b_tp4_fp8")
 
 
+@dataclass
+class MergeInputs:
+    """The step after a row-parallel block's merge: k fp32 partials, the bf16 residual stream
+    and the bf16 RMSNorm gain."""
+    name: str
+    partials: list                 # k x [T, H] float32
+    residual: np.ndarray           # [T, H] float32, bf16-rounded
+    gamma: np.ndarray              # [H] float32, bf16-rounded
+    eps: float
+
+    @property
+    def T(self): return self.residual.shape[0]
+
+    @property
+    def H(self): return self.residual.shape[1]
+
+
+def random_merge(seed: int, T: int, H: int, k: int, eps: float = 1e-5, name: str = "merge") -> MergeInputs:
+    """Partials N(0, 0.5^2) in fp32 (GEMM outputs), residual N(0,1) and gain 1 + N(0, 0.1^2),
+    both bf16-rounded."""
+    rng = np.random.default_rng(seed)
+    partials = [rng.standard_normal(size=(T, H), dtype=np.float32) * np.float32(0.5) for _ in range(k)]
+    residual = _normal(rng, (T, H), 1.0)
+    gamma = bf16_round(np.float32(1.0) + _normal(rng, (H,), 0.1))
+    return MergeInputs(name, partials, residual, gamma, eps)
+
+
+def merge7b_tp4(seed: int = 6) -> MergeInputs:
+    """Merge step of the 7B TP=4 block: the 4 ranks' fp32 partials of [8192, 4096] (B=4,
+    S=2048) summed into the residual stream, then RMSNorm (eps 1e-5)."""
+    return random_merge(seed, 8192, 4096, 4, 1e-5, name="merge7b_tp4")
+
+
 WORKLOADS = {
     "mlp_relu_tp2": mlp_relu_tp2,
     "mlp7b_tp4": mlp7b_tp4,
@@ -299,4 +333,5 @@ WORKLOADS = {
     "layer70b_tp8": layer70b_tp8,
     "decode7b_tp2": decode7b_tp2,
     "mlp7b_tp4_fp8": mlp7b_tp4_fp8,
+    "merge7b_tp4": merge7b_tp4,
 }
