@@ -8,8 +8,10 @@ SiLU(gate)*up GEMM + down GEMM). `value` is shard TFLOP/s (2*M*K*N per GEMM, 277
 GFLOP per step). Alongside: the 7B TP=2 decode step (attention shard over a 1024-token
 KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compulsory HBM
 bytes, and the same MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8) against the fp8
-MFMA peak. Inputs are seeded synthetic tensors already resident in HBM. With --extra the
-attention shard (B=4, S=2048) and the 70B GQA layer shard are timed too.
+MFMA peak, and the step after the merge (tp_merge_rmsnorm: 4 fp32 partials of [8192, 4096]
+summed into the bf16 residual stream, then RMSNorm) against the HBM bandwidth. Inputs are
+seeded synthetic tensors already resident in HBM. With --extra the attention shard (B=4,
+S=2048) and the 70B GQA layer shard are timed too.
 
 Prints ONE JSON line. Per-kernel durations come from HIP events that libtpshard records
 around each launch on the launch stream during every 10th timed step (the events cost a few
@@ -239,6 +241,38 @@ def fp8_mlp_bench(args):
     }
 
 
+def merge_bench(args):
+    """The step after the merge (tp_merge_rmsnorm): 4 fp32 partials of [8192, 4096] summed
+    into the bf16 residual stream, then RMSNorm; HBM-bound."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.merge7b_tp4()
+    T, H, k = inp.T, inp.H, len(inp.partials)
+    parts = [dev(p, "f32") for p in inp.partials]
+    res, gamma = dev(inp.residual), dev(inp.gamma)
+    R = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    N = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        tp.merge_rmsnorm(parts, res, gamma, inp.eps, residual_out=R, normed=N)
+
+    ms = timed(step, args.warmup, args.steps, "merge")
+    k_ms, _ = kernel_avg("merge_rmsnorm")
+    nbytes = float(T * H * (4 * k + 2 + 2 + 2) + 2 * H)   # partials, residual, 2 outputs, gain
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    return {
+        "workload": "merge7b_tp4: 4 fp32 partials [8192,4096] + bf16 residual -> bf16 residual, bf16 RMSNorm(eps 1e-5)",
+        "ms_per_step": ms,
+        "gbs": nbytes / (ms * 1e-3) / 1e9,
+        "step_stats": STEP_STATS.get("merge"),
+        "roofline": {"bound": "hbm", "kernel": "merge_rmsnorm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": recorded_traffic("merge_rmsnorm"),
+                     "bytes_per_launch": nbytes},
+    }
+
+
 def graph_timed(step, warmup: int, steps: int, name: str = None):
     """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
     between two events; a second pass with one event per replay gives the per-replay median
@@ -454,6 +488,7 @@ def main():
     mlp, inp = mlp_bench(args)
     dec = decode_bench(args)
     fp8 = fp8_mlp_bench(args)
+    merge = merge_bench(args)
     extra = {}
     if args.extra:
         extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
@@ -488,6 +523,7 @@ def main():
         "kernels": mlp["kernels"],
         "decode": dec,
         "fp8_mlp": fp8,
+        "merge_rmsnorm": merge,
         "extra": extra or None,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},
