@@ -37,6 +37,7 @@ __all__ = [
     "sdpa_causal", "kv_head_of", "split_qkv_heads", "attn_heads", "attn_shard",
     "attn_shard_rows", "attn_shard_weights", "full_attention_block", "decode_qkv",
     "decode_attn_shard", "lm_head_shard", "mlp_full", "rms_norm", "merge_rmsnorm",
+    "reduce_scatter_tokens",
 ]
 
 
@@ -392,3 +393,19 @@ def merge_rmsnorm(partials, residual, gamma, eps: float):
     normed = rms_norm(r, gamma, eps). Returns (r, normed)."""
     r = f64(residual) + partial_sum(partials)
     return r, rms_norm(r, gamma, eps)
+
+
+def reduce_scatter_tokens(partials, rank: int, tp: int) -> np.ndarray:
+    """This rank's share of a reduce-scatter of row-parallel partials over the token axis:
+    the r-th contiguous block of T/tp rows of ((P0 + P1) + ...).
+
+    "CUDA tensor parallel computations", 第四类 跨卡通信计算 (3. reduce-scatter: sum the
+    contributions, then cut the result and give each rank only the piece it needs next).
+    The cut is along tokens in rank order (the sequence-parallel layout; contiguous blocks,
+    rank 0 first, as for the weight splits); T must divide evenly."""
+    total = partial_sum(partials)
+    T = total.shape[0]
+    if T % tp:
+        raise ValueError(f"{T} tokens do not split evenly over {tp} ranks")
+    n = T // tp
+    return total[rank * n:(rank + 1) * n]

@@ -153,6 +153,31 @@ def test_merge_rmsnorm_in_place_deterministic_and_zero_rows(tp):
     assert not np.any(host(R)) and not np.any(host(N))               # eps > 0: exact zeros, no NaN
 
 
+@pytest.mark.parametrize("tp_ranks", [2, 4])
+def test_merge_on_token_slices_is_the_sequence_parallel_share(tp, tp_ranks):
+    """Sequence-parallel layout: each rank reduce-scatters the partials over tokens and
+    normalises only its T/tp rows. The merge call on a rank's row slice (pointer offsets into
+    the same buffers) gives exactly the rows of the full call and matches the oracle's
+    reduce-scatter share."""
+    import torch
+    inp = wl.random_merge(91, 64, 2048, 4)
+    T, H = inp.T, inp.H
+    R_full, N_full = _merge_call(tp, inp)
+    parts = [dev(p, "f32") for p in inp.partials]
+    res, gamma = dev(inp.residual), dev(inp.gamma)
+    n = T // tp_ranks
+    for r in range(tp_ranks):
+        sl = slice(r * n, (r + 1) * n)
+        R, N = tp.merge_rmsnorm([p[sl] for p in parts], res[sl], gamma, inp.eps,
+                                residual_out=_nan((n, H), torch.bfloat16), normed=_nan((n, H), torch.bfloat16))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(R), host(R_full)[sl]) and np.array_equal(host(N), host(N_full)[sl])
+        share = O.reduce_scatter_tokens(inp.partials, r, tp_ranks)
+        r_ref, n_ref = O.merge_rmsnorm([share], inp.residual[sl], inp.gamma, inp.eps)
+        assert_close_bf16(host(R), r_ref, f"rank {r} residual", out="bf16")
+        assert_close_bf16(host(N), n_ref, f"rank {r} normed", out="bf16")
+
+
 def test_merge7b_tp4_full_size_sampled(tp):
     """The merge step of the 7B TP=4 block at its full size: [8192, 4096], 4 partials."""
     inp = wl.merge7b_tp4()

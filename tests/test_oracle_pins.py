@@ -560,3 +560,14 @@ def test_rms_norm_matches_brute_force():
     y = O.rms_norm(x, g, 1e-3)
     for i in range(4):
         assert np.allclose(y[i], brute.rms_norm_row(list(x[i]), list(g), 1e-3), rtol=1e-13, atol=0)
+
+
+def test_reduce_scatter_tokens_concatenates_to_the_sum_and_rejects_uneven():
+    rng = np.random.default_rng(10)
+    parts = [rng.integers(-4, 5, size=(8, 6)).astype(np.float32) for _ in range(3)]
+    pieces = [O.reduce_scatter_tokens(parts, r, 4) for r in range(4)]
+    assert all(p.shape == (2, 6) for p in pieces)
+    assert np.array_equal(np.concatenate(pieces), parts[0] + parts[1] + parts[2])
+    assert np.array_equal(pieces[1], (parts[0] + parts[1] + parts[2])[2:4])   # rank 1: rows 2, 3
+    with pytest.raises(ValueError):
+        O.reduce_scatter_tokens(parts, 0, 3)
