@@ -9,7 +9,7 @@ from __future__ import annotations
 import math
 
 __all__ = ["matmul", "relu", "silu", "mlp", "attention_head", "rope_row", "e4m3_to_float", "fp8_matmul",
-           "rms_norm_row"]
+           "rms_norm_row", "finite_difference_grads"]
 
 
 def matmul(X, W):
@@ -112,3 +112,25 @@ def rms_norm_row(x, gamma, eps):
         ss += float(v) * float(v)
     inv = 1.0 / math.sqrt(ss / n + float(eps))
     return [float(x[j]) * inv * float(gamma[j]) for j in range(n)]
+
+
+def finite_difference_grads(X, W, dY, h=1e-3):
+    """Central differences of L(X, W) = sum_ij dY_ij (X W)_ij over every entry of X and W."""
+    def loss(Xm, Wm):
+        P = matmul(Xm, Wm)
+        return sum(dY[i][j] * P[i][j] for i in range(len(P)) for j in range(len(P[0])))
+    X = [list(map(float, r)) for r in X]
+    W = [list(map(float, r)) for r in W]
+    gX = [[0.0] * len(X[0]) for _ in X]
+    gW = [[0.0] * len(W[0]) for _ in W]
+    for M, G in ((X, gX), (W, gW)):
+        for i in range(len(M)):
+            for j in range(len(M[0])):
+                v = M[i][j]
+                M[i][j] = v + h
+                up = loss(X, W)
+                M[i][j] = v - h
+                dn = loss(X, W)
+                M[i][j] = v
+                G[i][j] = (up - dn) / (2 * h)
+    return gX, gW

@@ -37,7 +37,7 @@ __all__ = [
     "sdpa_causal", "kv_head_of", "split_qkv_heads", "attn_heads", "attn_shard",
     "attn_shard_rows", "attn_shard_weights", "full_attention_block", "decode_qkv",
     "decode_attn_shard", "lm_head_shard", "mlp_full", "rms_norm", "merge_rmsnorm",
-    "reduce_scatter_tokens",
+    "reduce_scatter_tokens", "linear_backward",
 ]
 
 
@@ -409,3 +409,19 @@ def reduce_scatter_tokens(partials, rank: int, tp: int) -> np.ndarray:
         raise ValueError(f"{T} tokens do not split evenly over {tp} ranks")
     n = T // tp
     return total[rank * n:(rank + 1) * n]
+
+
+# ---------------------------------------------------------------------------
+# Backward of a rank's linear shard (the training half of the same split rules)
+# ---------------------------------------------------------------------------
+
+def linear_backward(X, W_shard, dY_shard):
+    """Gradients of one rank's linear shard Y_r = X_r . W_r: (dX, dW) = (dY_r . W_r^T, X_r^T . dY_r).
+
+    "张量并行：切分 Transformer 层的分布式训练", 列切分 / 行切分 and 前向与反向的通信对称: the same two
+    products serve both splits. Column shard (X replicated, dY_r = the gradient of the rank's
+    output columns): dX is a partial that the ranks sum; dW_r is local. Row shard (X_r the
+    rank's input columns, dY replicated): dX is the rank's slice of the input gradient, complete;
+    dW_r is local. The pages only name the collectives; the products are the chain rule."""
+    dY = f64(dY_shard)
+    return dY @ f64(W_shard).T, f64(X).T @ dY

@@ -571,3 +571,32 @@ def test_reduce_scatter_tokens_concatenates_to_the_sum_and_rejects_uneven():
     assert np.array_equal(pieces[1], (parts[0] + parts[1] + parts[2])[2:4])   # rank 1: rows 2, 3
     with pytest.raises(ValueError):
         O.reduce_scatter_tokens(parts, 0, 3)
+
+
+# --- backward of a linear shard (the chain rule of Y = X W; split rules of "张量并行：切分
+# Transformer 层的分布式训练", 列切分 / 行切分)
+
+def test_linear_backward_matches_finite_differences():
+    rng = np.random.default_rng(11)
+    X, W, dY = rng.standard_normal((3, 4)), rng.standard_normal((4, 5)), rng.standard_normal((3, 5))
+    dX, dW = O.linear_backward(X, W, dY)
+    gX, gW = brute.finite_difference_grads(X.tolist(), W.tolist(), dY.tolist())
+    assert np.allclose(dX, gX, rtol=0, atol=1e-8) and np.allclose(dW, gW, rtol=0, atol=1e-8)
+    assert dX.shape == X.shape and dW.shape == W.shape
+
+
+@pytest.mark.parametrize("tp", [2, 4])
+def test_linear_backward_split_rules(tp):
+    rng = np.random.default_rng(12 + tp)
+    X = rng.integers(-3, 4, size=(6, 8)).astype(np.float32)
+    W = rng.integers(-3, 4, size=(8, 12)).astype(np.float32)
+    dY = rng.integers(-3, 4, size=(6, 12)).astype(np.float32)
+    dX_full, dW_full = O.linear_backward(X, W, dY)
+    # column shards: dX partials sum to the full dX, dW shards are its column blocks
+    cols = [O.linear_backward(X, O.column_shard(W, r, tp), O.column_shard(dY, r, tp)) for r in range(tp)]
+    assert np.array_equal(O.partial_sum([c[0] for c in cols]), dX_full)
+    assert np.array_equal(np.concatenate([c[1] for c in cols], axis=1), dW_full)
+    # row shards: dX shards are the column blocks of dX (complete), dW shards its row blocks
+    rows = [O.linear_backward(O.column_shard(X, r, tp), O.row_shard(W, r, tp), dY) for r in range(tp)]
+    assert np.array_equal(np.concatenate([r_[0] for r_ in rows], axis=1), dX_full)
+    assert np.array_equal(np.concatenate([r_[1] for r_ in rows], axis=0), dW_full)
