@@ -242,6 +242,24 @@ tp_status tp_merge_rmsnorm(const float* const* partials, int32_t k, const void* 
                            const void* gamma, float eps, void* residual_out, void* normed,
                            int64_t T, int64_t H, void* stream);
 
+/*
+ * tp_linear_backward — gradients of one rank's linear shard Y_r = X_r . W_r for the backward
+ *   pass: dX = dY_r . W_r^T and dW_r = X_r^T . dY_r ("张量并行：切分 Transformer 层的分布式
+ *   训练", 列切分 / 行切分, 前向与反向的通信对称). The same two products serve both splits:
+ *   a column shard passes the replicated X and the gradient of its output columns, and its dX
+ *   is a partial that the ranks sum (tp_partial_sum on one GPU); a row shard passes its input
+ *   columns X_r and the replicated dY, and its dX is its complete slice of the input gradient.
+ *   dW_r is local in both.
+ *   X [T, K], W_shard [K, N], dY [T, N]: in_dt (BF16) row-major; dX [T, K] and dW [K, N] fp32
+ *   (overwritten). T, K, N multiples of 8 and below 2^23; all pointers 16-byte aligned;
+ *   workspace >= tp_linear_backward_workspace_size(T, K, N) bytes, 16-byte aligned (holds
+ *   W^T and X^T in bf16). fp32 accumulation; deterministic.
+ */
+tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY, float* dX, float* dW,
+                             int64_t T, int64_t K, int64_t N, tp_dtype in_dt, void* workspace,
+                             size_t ws_bytes, void* stream);
+size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N);
+
 /* Status text, thread-local detail of this thread's last non-OK status, ABI version. */
 const char* tp_status_string(tp_status st);
 const char* tp_last_error(void);

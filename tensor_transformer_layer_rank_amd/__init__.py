@@ -17,7 +17,8 @@ __all__ = [
     "TpError", "lib", "load", "LIB_PATH", "column_linear", "row_linear_partial", "mlp_shard",
     "attn_shard", "partial_sum", "linear_workspace_size", "mlp_workspace_size",
     "attn_workspace_size", "mlp_shard_fp8", "mlp_fp8_workspace_size", "AttnDesc",
-    "profile_enable", "profile_reset", "profile_read", "merge_rmsnorm",
+    "profile_enable", "profile_reset", "profile_read", "merge_rmsnorm", "linear_backward",
+    "linear_backward_workspace_size",
     "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
     "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
 ]
@@ -35,7 +36,7 @@ EXPORTS = [
     "tp_mlp_workspace_size", "tp_attn_shard", "tp_attn_workspace_size", "tp_partial_sum",
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
-    "tp_merge_rmsnorm",
+    "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size",
 ]
 
 
@@ -99,6 +100,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                               _P, _SZ, _P], _I32),
         "tp_mlp_fp8_workspace_size": ([_I64, _I64, _I64, _I32], _SZ),
         "tp_merge_rmsnorm": ([ctypes.POINTER(_P), _I32, _P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P], _I32),
+        "tp_linear_backward": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P], _I32),
+        "tp_linear_backward_workspace_size": ([_I64, _I64, _I64], _SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -313,6 +316,27 @@ def merge_rmsnorm(partials, residual, gamma, eps: float = 1e-5, residual_out=Non
     _check(lib().tp_merge_rmsnorm(arr, k, _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out),
                                   _ptr(normed), T, H, _stream(stream)))
     return residual_out, normed
+
+
+def linear_backward_workspace_size(T: int, K: int, N: int) -> int:
+    return int(lib().tp_linear_backward_workspace_size(T, K, N))
+
+
+def linear_backward(X, W, dY, dX=None, dW=None, workspace=None, stream=None):
+    """(dX, dW) = (dY . W^T, X^T . dY) in fp32 for bf16 X [T, K], W [K, N], dY [T, N]."""
+    import torch
+    T, K = X.shape
+    N = W.shape[1]
+    if dX is None:
+        dX = torch.empty((T, K), dtype=torch.float32, device=X.device)
+    if dW is None:
+        dW = torch.empty((K, N), dtype=torch.float32, device=X.device)
+    need = linear_backward_workspace_size(T, K, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check(lib().tp_linear_backward(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), T, K, N, TP_BF16,
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dX, dW
 
 
 # --- kernel timing ------------------------------------------------------------------------------

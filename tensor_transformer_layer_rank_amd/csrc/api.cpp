@@ -557,6 +557,33 @@ tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out, in
     return from_hip(tpk::partial_sum(partials, k, out, n_elems, as_stream(stream)), "tp_partial_sum");
 }
 
+size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N) {
+    if (T <= 0 || K <= 0 || N <= 0) return 0;
+    return round_up(tpk::linear_backward_ws_bytes(T, K, N), WS_ALIGN);
+}
+
+tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY, float* dX, float* dW,
+                             int64_t T, int64_t K, int64_t N, tp_dtype in_dt, void* workspace,
+                             size_t ws_bytes, void* stream) {
+    const char* fn = "tp_linear_backward";
+    if (!X || !W_shard || !dY || !dX || !dW)
+        return fail(TP_ERR_NULL_POINTER, "%s: X, W_shard, dY, dX and dW must be non-NULL", fn);
+    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "%s: input dtype %d not offered (bf16 only)", fn, (int)in_dt);
+    if (T <= 0 || K <= 0 || N <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "%s: sizes must be positive (T=%lld K=%lld N=%lld)", fn, (long long)T,
+                    (long long)K, (long long)N);
+    if (T % 8 || K % 8 || N % 8)
+        return fail(TP_ERR_MISALIGNED, "%s: T, K and N must be multiples of 8 (T=%lld K=%lld N=%lld)", fn,
+                    (long long)T, (long long)K, (long long)N);
+    if (T >= ((int64_t)1 << 23) || K >= ((int64_t)1 << 23) || N >= ((int64_t)1 << 23))
+        return fail(TP_ERR_UNSUPPORTED, "%s: T, K and N must be below 2^23", fn);
+    if (!aligned(X, 16) || !aligned(W_shard, 16) || !aligned(dY, 16) || !aligned(dX, 16) || !aligned(dW, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: X, W_shard, dY, dX and dW must be 16-byte aligned", fn);
+    tp_status st = check_ws(fn, workspace, ws_bytes, tp_linear_backward_workspace_size(T, K, N));
+    if (st != TP_OK) return st;
+    return from_hip(tpk::linear_backward(X, W_shard, dY, dX, dW, T, K, N, workspace, as_stream(stream)), fn);
+}
+
 tp_status tp_merge_rmsnorm(const float* const* partials, int32_t k, const void* residual, const void* gamma,
                            float eps, void* residual_out, void* normed, int64_t T, int64_t H, void* stream) {
     const char* fn = "tp_merge_rmsnorm";

@@ -93,6 +93,13 @@ hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_
                             int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
                             void* out, hipStream_t s);
 
+// ---- backward of a linear shard ---------------------------------------------------------
+// dX [T, K] fp32 = dY [T, N] . W^T, dW [K, N] fp32 = X^T [K, T] . dY (bf16 operands; T, K, N
+// multiples of 8). Workspace: W^T and X^T (bf16) and the GEMMs' tail-split partials.
+size_t linear_backward_ws_bytes(int64_t T, int64_t K, int64_t N);
+hipError_t linear_backward(const void* X, const void* W, const void* dY, float* dX, float* dW, int64_t T,
+                           int64_t K, int64_t N, void* ws, hipStream_t s);
+
 // ---- merges -------------------------------------------------------------------------------
 hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s);
 // r = residual + ((P0 + P1) + ...) (fp32), residual_out = bf16(r),

@@ -222,6 +222,28 @@ def test_merge_rmsnorm_validation(L):
     assert st(a4=float("inf")) == "TP_ERR_BAD_SHAPE"
 
 
+def test_linear_backward_validation(L):
+    f = L.tp_linear_backward
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 128, 256, tp.TP_BF16, FAKE, 1 << 30, None]
+
+    def st(i, v):
+        a = list(ok)
+        a[i] = v
+        return _st(f(*a))
+    for i in range(5):
+        assert st(i, None) == "TP_ERR_NULL_POINTER"
+        assert st(i, FAKE_ODD) == "TP_ERR_MISALIGNED"
+    assert st(8, tp.TP_F32) == "TP_ERR_BAD_DTYPE"
+    for i in (5, 6, 7):
+        assert st(i, 0) == "TP_ERR_BAD_SHAPE"
+        assert st(i, 60) == "TP_ERR_MISALIGNED"
+        assert st(i, 1 << 23) == "TP_ERR_UNSUPPORTED"
+    assert st(10, 16) == "TP_ERR_WORKSPACE"
+    assert st(9, None) == "TP_ERR_WORKSPACE"
+    need = L.tp_linear_backward_workspace_size(64, 128, 256)
+    assert need >= (256 * 128 + 128 * 64) * 2 and need % 256 == 0
+
+
 def test_profile_api_without_launches(L):
     assert L.tp_profile_reset() == 0
     ms, n = tp.profile_read("")

@@ -191,6 +191,63 @@ def test_merge7b_tp4_full_size_sampled(tp):
     assert_close_bf16(n[rows], n_ref, "merge7b_tp4 normed", out="bf16")
 
 
+# ---------------------------------------------------------------- backward of a linear shard
+
+# partial tiles in every dimension, T below one 256-row tile, K and N not multiples of 128
+@pytest.mark.parametrize("T,K,N", [(64, 136, 200), (24, 512, 256), (264, 1000, 72), (520, 256, 1032)])
+def test_linear_backward_small(tp, T, K, N):
+    import torch
+    inp = wl.random_backward(T + 3 * K + 7 * N, T, K, N)
+    dX, dW = tp.linear_backward(dev(inp.X), dev(inp.W), dev(inp.dY), dX=_nan((T, K), torch.float32),
+                                dW=_nan((K, N), torch.float32))
+    torch.cuda.synchronize()
+    rX, rW = O.linear_backward(inp.X, inp.W, inp.dY)
+    assert_close_bf16(host(dX), rX, f"dX T{T} K{K} N{N}")
+    assert_close_bf16(host(dW), rW, f"dW T{T} K{K} N{N}")
+
+
+def test_linear_backward_split_ranks_sum_to_full(tp):
+    """Column shards' dX partials, merged with tp_partial_sum, give the unsharded dX; their dW are
+    its column blocks; row shards' dX are its column blocks (GPU products, oracle reference)."""
+    import torch
+    inp = wl.random_backward(501, 128, 256, 512)
+    X, W, dY = dev(inp.X), dev(inp.W), dev(inp.dY)
+    rX, rW = O.linear_backward(inp.X, inp.W, inp.dY)
+    tpn = 2
+    parts, dWs = [], []
+    for r in range(tpn):
+        cols = slice(r * 256, (r + 1) * 256)
+        dXr, dWr = tp.linear_backward(X, W[:, cols].contiguous(), dY[:, cols].contiguous())
+        parts.append(dXr)
+        dWs.append(dWr)
+    full = tp.partial_sum(parts)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(full), rX, "column shards: summed dX")
+    assert_close_bf16(np.concatenate([host(d) for d in dWs], axis=1), rW, "column shards: dW blocks")
+    for r in range(tpn):
+        rows = slice(r * 128, (r + 1) * 128)
+        dXr, dWr = tp.linear_backward(X[:, rows].contiguous(), W[rows].contiguous(), dY)
+        torch.cuda.synchronize()
+        assert_close_bf16(host(dXr), rX[:, rows], f"row shard {r}: dX slice")
+        assert_close_bf16(host(dWr), rW[rows], f"row shard {r}: dW rows")
+
+
+def test_backward7b_tp4_full_size_sampled(tp):
+    """Backward of the 7B TP=4 MLP down shard at its full size (sampled rows of dX and dW)."""
+    inp = wl.backward7b_tp4()
+    X, W, dY = dev(inp.X), dev(inp.W), dev(inp.dY)
+    dX, dW = tp.linear_backward(X, W, dY)
+    dX2, dW2 = tp.linear_backward(X, W, dY)
+    gx, gw = host(dX), host(dW)
+    assert np.array_equal(gx, host(dX2)) and np.array_equal(gw, host(dW2)), "two launches differ bitwise"
+    rows = sample_rows(inp.X.shape[0], 24, seed=4)
+    krows = sample_rows(inp.X.shape[1], 24, seed=5)
+    ref_x, _ = O.linear_backward(inp.X[rows], inp.W, inp.dY[rows])            # dX rows need dY rows only
+    _, ref_w = O.linear_backward(inp.X[:, krows], inp.W[krows], inp.dY)       # dW rows need X columns only
+    assert_close_bf16(gx[rows], ref_x, "backward7b_tp4 dX rows")
+    assert_close_bf16(gw[krows], ref_w, "backward7b_tp4 dW rows")
+
+
 # ---------------------------------------------------------------- bf16 linear layers
 
 @pytest.mark.parametrize("T,K,N", [(300, 256, 200), (513, 520, 264), (256, 64, 256), (65, 4096, 384)])

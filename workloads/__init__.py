@@ -38,7 +38,7 @@ __all__ = [
     "mlp_relu_tp2", "mlp7b_tp4", "attn7b_tp4", "layer70b_tp8", "decode7b_tp2",
     "random_mlp", "random_attn", "random_decode", "int_matrix", "WORKLOADS",
     "e4m3_codes", "FP8MLPInputs", "random_mlp_fp8", "mlp7b_tp4_fp8", "MergeInputs", "random_merge",
-    "merge7b_tp4",
+    "merge7b_tp4", "BackwardInputs", "random_backward", "backward7b_tp4",
 ]
 
 
@@ -326,6 +326,27 @@ def merge7b_tp4(seed: int = 6) -> MergeInputs:
     return random_merge(seed, 8192, 4096, 4, 1e-5, name="merge7b_tp4")
 
 
+@dataclass
+class BackwardInputs:
+    """Backward of one rank's linear shard: forward input X, weight shard W, output gradient dY."""
+    name: str
+    X: np.ndarray      # [T, K] float32, bf16-rounded
+    W: np.ndarray      # [K, N] float32, bf16-rounded
+    dY: np.ndarray     # [T, N] float32, bf16-rounded
+
+
+def random_backward(seed: int, T: int, K: int, N: int, name: str = "backward") -> BackwardInputs:
+    """X N(0,1), W N(0, 0.02^2), dY N(0,1), all bf16-rounded."""
+    rng = np.random.default_rng(seed)
+    return BackwardInputs(name, _normal(rng, (T, K), 1.0), _normal(rng, (K, N), 0.02), _normal(rng, (T, N), 1.0))
+
+
+def backward7b_tp4(seed: int = 7) -> BackwardInputs:
+    """Backward of the 7B TP=4 MLP down shard (row-parallel): X = h [4096, 2752],
+    W_down shard [2752, 4096], dY [4096, 4096] replicated."""
+    return random_backward(seed, 4096, 2752, 4096, name="backward7b_tp4")
+
+
 WORKLOADS = {
     "mlp_relu_tp2": mlp_relu_tp2,
     "mlp7b_tp4": mlp7b_tp4,
@@ -334,4 +355,5 @@ WORKLOADS = {
     "decode7b_tp2": decode7b_tp2,
     "mlp7b_tp4_fp8": mlp7b_tp4_fp8,
     "merge7b_tp4": merge7b_tp4,
+    "backward7b_tp4": backward7b_tp4,
 }
