@@ -9,7 +9,8 @@ GFLOP per step). Alongside: the 7B TP=2 decode step (attention shard over a 1024
 KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compulsory HBM
 bytes, and the same MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8) against the fp8
 MFMA peak, and the step after the merge (tp_merge_rmsnorm: 4 fp32 partials of [8192, 4096]
-summed into the bf16 residual stream, then RMSNorm) against the HBM bandwidth. Inputs are
+summed into the bf16 residual stream, then RMSNorm) against the HBM bandwidth, and the
+backward of the MLP down shard (tp_linear_backward). Inputs are
 seeded synthetic tensors already resident in HBM. With --extra the attention shard (B=4,
 S=2048) and the 70B GQA layer shard are timed too.
 
@@ -273,6 +274,44 @@ def merge_bench(args):
     }
 
 
+def backward_bench(args):
+    """Backward of the 7B TP=4 MLP down shard (tp_linear_backward: dX = dY.W^T, dW = X^T.dY
+    after the bf16 transposes of W and X)."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.backward7b_tp4()
+    T, K = inp.X.shape
+    N = inp.W.shape[1]
+    X, W, dY = dev(inp.X), dev(inp.W), dev(inp.dY)
+    dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    dW = torch.empty((K, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.linear_backward_workspace_size(T, K, N), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.linear_backward(X, W, dY, dX=dX, dW=dW, workspace=ws)
+
+    ms = timed(step, args.warmup, args.steps, "backward")
+    flops = 4.0 * T * K * N
+    g_ms, g_n = kernel_avg("gemm_bf16_f32out")
+    t_ms, t_n = kernel_avg("transpose_bf16")
+    fx_ms, fx_n = kernel_avg("fixup_gemm")
+    g_ms, t_ms, fx_ms = g_ms or 0.0, t_ms or 0.0, fx_ms or 0.0
+    per_gemm_ms = (g_ms * g_n + fx_ms * fx_n) / max(g_n, 1)
+    gemm_tf = flops / 2 / (per_gemm_ms * 1e-3) / 1e12 if per_gemm_ms else None
+    return {
+        "workload": "backward7b_tp4: X = h [4096,2752], W_down shard [2752,4096], dY [4096,4096] bf16 -> dX, dW fp32",
+        "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "step_stats": STEP_STATS.get("backward"),
+        "kernels": {"gemm (dX, dW; avg per GEMM incl. tail fix-up)": {"avg_us": per_gemm_ms * 1e3,
+                                                                    "tflops": gemm_tf},
+                    "transpose_bf16 (W, X)": {"avg_us": t_ms * 1e3, "launches_per_step": t_n / max(g_n / 2, 1)}},
+    }
+
+
 def graph_timed(step, warmup: int, steps: int, name: str = None):
     """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
     between two events; a second pass with one event per replay gives the per-replay median
@@ -489,6 +528,7 @@ def main():
     dec = decode_bench(args)
     fp8 = fp8_mlp_bench(args)
     merge = merge_bench(args)
+    bwd = backward_bench(args)
     extra = {}
     if args.extra:
         extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
@@ -524,6 +564,7 @@ def main():
         "decode": dec,
         "fp8_mlp": fp8,
         "merge_rmsnorm": merge,
+        "backward": bwd,
         "extra": extra or None,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},

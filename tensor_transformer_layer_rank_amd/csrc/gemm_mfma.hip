@@ -904,26 +904,32 @@ int cu_count() {
 // How a grid of G tiles (nk K steps each) is cut: full tiles for whole rounds of the machine,
 // the rest split into pieces so that the last round is filled.
 // The tail (the tiles past the last full round, or the whole grid if it is smaller than the
-// machine) is cut into the fewest pieces p <= 4 that minimise its duration ceil(tail*p/n_cu)/p
-// in tile times, if that saves at least a fifth of a tile time (the fix-up pass costs about
-// a tenth) and every piece keeps at least 2 K steps. Examples on 256 units: a tail of 96 or 128
-// tiles -> 2 pieces (one round of half tiles); a grid of 160 tiles -> 3 pieces (two rounds of
-// third tiles instead of one round at 5/8 occupancy).
+// machine) is cut into p = 2..4 pieces (each keeping >= 2 K steps) when that shortens the
+// tail by more than the fix-up pass costs. In K-step times: the tail takes nk tile steps
+// unsplit and nk * ceil(tail*p/n_cu)/p split; every piece costs its 256 KB of fp32 partials
+// written and read back, ~0.1 us at the streaming bandwidth, against ~0.75 us per K step
+// (~1300 cycles at the power-limited clock), i.e. ~0.14 step per piece spread over the
+// machine. Examples on 256 units: the 7B TP=4 gate/up grid (352 tiles, tail 96, nk 128) -> 2
+// pieces; a grid of 160 tiles with nk 256 (70B TP=8 QKV) -> 3 pieces (two rounds of thirds);
+// a grid of 176 tiles with nk 128 (the 7B MLP down shard's backward) stays whole: 4 pieces
+// would save a quarter tile (32 steps) but cost ~98 steps of fix-up.
 SplitArgs plan_split(int64_t G, int nk, int n_cu) {
     SplitArgs sp{(int)G, 1, nk, nullptr};
     const int64_t full = (G / n_cu) * n_cu;
     const int64_t tail = G - full;
     if (tail == 0) return sp;
+    constexpr double FIXUP_STEPS_PER_PIECE = 0.14;
     int pieces = 1;
-    double best = 1.0;
+    double best = (double)nk;   // tail duration in K steps, unsplit
     for (int p = 2; p <= 4 && nk >= 2 * p; ++p) {
-        const double t = (double)((tail * p + n_cu - 1) / n_cu) / p;
+        const double t = (double)nk * (double)((tail * p + n_cu - 1) / n_cu) / p +
+                         FIXUP_STEPS_PER_PIECE * (double)(tail * p);
         if (t < best - 1e-9) {
             best = t;
             pieces = p;
         }
     }
-    if (pieces < 2 || best > 0.8) return sp;
+    if (pieces < 2) return sp;
     sp.g_full = (int)full;
     sp.pieces = pieces;
     sp.piece_steps = (nk + pieces - 1) / pieces;

@@ -85,11 +85,12 @@ def test_fp8_linear_validation(L):
     assert _st(col(*bad)) == "TP_ERR_BAD_DTYPE"                      # no fp8 output
     assert _st(row(FAKE, FAKE, FAKE, 64, 32, 32, tp.TP_FP8_E4M3, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
     assert _st(row(FAKE, FAKE, FAKE, 64, 40, 32, tp.TP_FP8_E4M3, 0, q, None, 0, None)) == "TP_ERR_MISALIGNED"
-    # a grid past one round of the device needs the split workspace (256 compute units assumed
-    # when no device is visible)
-    need = L.tp_linear_workspace_size(4200, 512, 4096, tp.TP_FP8_E4M3)
+    # a grid past one round of the device with enough K steps needs the split workspace (256
+    # compute units assumed when no device is visible); a short K leaves it whole
+    need = L.tp_linear_workspace_size(4200, 2048, 4096, tp.TP_FP8_E4M3)
     assert need > 0
-    assert _st(row(FAKE, FAKE, FAKE, 4200, 512, 4096, tp.TP_FP8_E4M3, 0, q, None, 0, None)) == "TP_ERR_WORKSPACE"
+    assert L.tp_linear_workspace_size(4200, 512, 4096, tp.TP_FP8_E4M3) == 0
+    assert _st(row(FAKE, FAKE, FAKE, 4200, 2048, 4096, tp.TP_FP8_E4M3, 0, q, None, 0, None)) == "TP_ERR_WORKSPACE"
 
 
 def test_fp8_mlp_validation(L):

@@ -306,12 +306,14 @@ def test_row_partials_sum_to_unsharded_layer(tp):
 
 
 # Tail split on 256 compute units: the tiles after the last full round are cut along K into
-# 4 (272 tiles), 3 (336 tiles) or 2 (352 tiles) pieces whose fp32 partials a fix-up pass
-# sums; grids smaller than the machine are cut too: 160 tiles into 3 pieces (two rounds of
-# thirds), 32 tiles into 4. Ragged M, N and K so that the last piece holds the K tail.
-@pytest.mark.parametrize("T,K,N,out", [(4200, 296, 4096, "bf16"), (5376, 200, 4096, "f32"),
-                                       (5632, 136, 4096, "bf16"), (4100, 1000, 4000, "f32"),
-                                       (2048, 1000, 5120, "f32"), (1000, 520, 2000, "bf16")])
+# 2, 3 or 4 pieces whose fp32 partials a fix-up pass sums, when the shorter tail outweighs the
+# fix-up (272 tiles: 2 pieces at 10 K steps, 4 at 32; 336 tiles: 3 at 96); grids smaller than
+# the machine are cut too (32 tiles: 3 pieces at 32 steps, 4 at 64; 160 tiles: 3 at 202).
+# Ragged M, N and K so that the last piece holds the K tail; the two largest grids are
+# compared with the oracle on sampled rows.
+@pytest.mark.parametrize("T,K,N,out", [(4200, 296, 4096, "bf16"), (4100, 1000, 4000, "f32"),
+                                       (5376, 3072, 4096, "f32"), (1000, 1024, 2000, "bf16"),
+                                       (1000, 2048, 2000, "f32"), (2048, 6464, 5120, "bf16")])
 def test_column_linear_tail_split(tp, T, K, N, out):
     import torch
     rng = np.random.default_rng(T + K)
@@ -324,7 +326,8 @@ def test_column_linear_tail_split(tp, T, K, N, out):
     torch.cuda.synchronize()
     y = host(Y)
     assert np.array_equal(y, host(Y2)), "split launches differ bitwise"
-    assert_close_bf16(y, O.linear(X, W), f"split column {T}x{K}x{N}", out=out)
+    rows = sample_rows(T, 96, seed=T) if T * K * N > 2e10 else np.arange(T)
+    assert_close_bf16(y[rows], O.linear(X[rows], W), f"split column {T}x{K}x{N}", out=out)
 
 
 def test_row_linear_partial_tail_split_accumulate(tp):
