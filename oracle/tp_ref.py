@@ -37,7 +37,7 @@ __all__ = [
     "sdpa_causal", "kv_head_of", "split_qkv_heads", "attn_heads", "attn_shard",
     "attn_shard_rows", "attn_shard_weights", "full_attention_block", "decode_qkv",
     "decode_attn_shard", "lm_head_shard", "mlp_full", "rms_norm", "merge_rmsnorm",
-    "reduce_scatter_tokens", "linear_backward",
+    "reduce_scatter_tokens", "linear_backward", "moe_mlp_shard",
 ]
 
 
@@ -425,3 +425,38 @@ def linear_backward(X, W_shard, dY_shard):
     dW_r is local. The pages only name the collectives; the products are the chain rule."""
     dY = f64(dY_shard)
     return dY @ f64(W_shard).T, f64(X).T @ dY
+
+
+# ---------------------------------------------------------------------------
+# Mixture-of-experts MLP on one rank (experts' weights TP-sharded: "TensorRT LLM 中的并行
+# 策略", 混合专家 (MoE): TP and hybrid ETP modes)
+# ---------------------------------------------------------------------------
+
+def moe_mlp_shard(X, row_token, expert_offsets, W_gate, W_up, W_down, token_rows, gates) -> np.ndarray:
+    """This rank's fp32 partial of a top-k MoE MLP over its local experts.
+
+    The router has chosen up to k experts per token and their gates. Dispatched rows are
+    grouped by expert: row r (expert e for offsets[e] <= r < offsets[e+1]) holds token
+    row_token[r]; each local expert is an MLP shard with its own column/row-split weights
+    (W_gate[e], W_up[e] [H, I_shard], W_down[e] [I_shard, H]), so its row outputs are
+    partials like the dense shard's. Token t's partial is the gate-weighted sum of the rows
+    token_rows[t, :] (-1 = a slot whose expert is not on this rank), slots in order:
+    Y[t] = sum_j gates[t, j] * Yrows[token_rows[t, j]]. Summed over the TP group it is the
+    layer's MoE output (the weighted sum is linear, so it commutes with the merge)."""
+    X = f64(X)
+    offs = [int(v) for v in expert_offsets]
+    R = offs[-1]
+    rows = np.zeros((R, X.shape[1]), np.float64)
+    for e in range(len(offs) - 1):
+        a, b = offs[e], offs[e + 1]
+        if b > a:
+            rows[a:b] = mlp_swiglu_shard(X[np.asarray(row_token[a:b], np.int64)], W_gate[e], W_up[e], W_down[e])
+    T = X.shape[0]
+    Y = np.zeros((T, X.shape[1]), np.float64)
+    tr = np.asarray(token_rows, np.int64)
+    g = f64(gates)
+    for t in range(T):
+        for j in range(tr.shape[1]):
+            if tr[t, j] >= 0:
+                Y[t] = Y[t] + g[t, j] * rows[tr[t, j]]
+    return Y

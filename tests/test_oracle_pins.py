@@ -600,3 +600,64 @@ def test_linear_backward_split_rules(tp):
     rows = [O.linear_backward(O.column_shard(X, r, tp), O.row_shard(W, r, tp), dY) for r in range(tp)]
     assert np.array_equal(np.concatenate([r_[0] for r_ in rows], axis=1), dX_full)
     assert np.array_equal(np.concatenate([r_[1] for r_ in rows], axis=0), dW_full)
+
+
+# --- MoE MLP on one rank ("TensorRT LLM 中的并行策略", 混合专家 (MoE))
+
+def _route(rng, T, E, k):
+    """top-k distinct experts per token, gates, and the dispatch grouped by expert."""
+    ex = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    gates = rng.random((T, k))
+    order = sorted(((int(ex[t, j]), t, j) for t in range(T) for j in range(k)))
+    row_token = np.array([t for _, t, _ in order], np.int32)
+    offsets = np.searchsorted([e for e, _, _ in order], np.arange(E + 1), side="left")
+    token_rows = np.full((T, k), -1, np.int32)
+    for r, (_, t, j) in enumerate(order):
+        token_rows[t, j] = r
+    return row_token, offsets, token_rows, gates
+
+
+def test_moe_one_expert_identity_routing_is_the_dense_shard():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((6, 8))
+    Wg, Wu, Wd = rng.standard_normal((1, 8, 4)), rng.standard_normal((1, 8, 4)), rng.standard_normal((1, 4, 8))
+    Y = O.moe_mlp_shard(X, np.arange(6), [0, 6], Wg, Wu, Wd, np.arange(6)[:, None], np.ones((6, 1)))
+    assert np.allclose(Y, O.mlp_swiglu_shard(X, Wg[0], Wu[0], Wd[0]), rtol=1e-14, atol=1e-14)
+
+
+def test_moe_matches_per_token_brute_force_and_is_linear_in_gates():
+    rng = np.random.default_rng(14)
+    T, H, I, E, k = 5, 6, 4, 3, 2
+    X = rng.standard_normal((T, H))
+    Wg, Wu, Wd = rng.standard_normal((E, H, I)), rng.standard_normal((E, H, I)), rng.standard_normal((E, I, H))
+    row_token, offsets, token_rows, gates = _route(rng, T, E, k)
+    token_rows[2, 1] = -1                                   # a slot whose expert is elsewhere
+    Y = O.moe_mlp_shard(X, row_token, offsets, Wg, Wu, Wd, token_rows, gates)
+    for t in range(T):
+        want = [0.0] * H
+        for j in range(k):
+            r = token_rows[t, j]
+            if r < 0:
+                continue
+            e = int(np.searchsorted(offsets, r, side="right") - 1)
+            y = brute.mlp([list(X[t])], Wg[e].tolist(), Wu[e].tolist(), Wd[e].tolist(), "swiglu")[0]
+            want = [want[i] + gates[t, j] * y[i] for i in range(H)]
+        assert np.allclose(Y[t], want, rtol=1e-12, atol=1e-12)
+    Y2 = O.moe_mlp_shard(X, row_token, offsets, Wg, Wu, Wd, token_rows, 2.5 * gates)
+    assert np.allclose(Y2, 2.5 * Y, rtol=1e-13)
+
+
+@pytest.mark.parametrize("tp", [2, 4])
+def test_moe_tp_within_experts_sums_to_unsharded(tp):
+    rng = np.random.default_rng(15 + tp)
+    T, H, I, E, k = 7, 8, 16, 4, 2
+    X = rng.standard_normal((T, H))
+    Wg, Wu, Wd = rng.standard_normal((E, H, I)), rng.standard_normal((E, H, I)), rng.standard_normal((E, I, H))
+    route = _route(rng, T, E, k)
+    full = O.moe_mlp_shard(X, route[0], route[1], Wg, Wu, Wd, route[2], route[3])
+    shards = [O.moe_mlp_shard(X, route[0], route[1],
+                              np.stack([O.column_shard(Wg[e], r, tp) for e in range(E)]),
+                              np.stack([O.column_shard(Wu[e], r, tp) for e in range(E)]),
+                              np.stack([O.row_shard(Wd[e], r, tp) for e in range(E)]), route[2], route[3])
+              for r in range(tp)]
+    assert np.allclose(O.partial_sum(shards), full, rtol=1e-12, atol=1e-12)
