@@ -440,7 +440,8 @@ def moe_mlp_shard(X, row_token, expert_offsets, W_gate, W_up, W_down, token_rows
     row_token[r]; each local expert is an MLP shard with its own column/row-split weights
     (W_gate[e], W_up[e] [H, I_shard], W_down[e] [I_shard, H]), so its row outputs are
     partials like the dense shard's. Token t's partial is the gate-weighted sum of the rows
-    token_rows[t, :] (-1 = a slot whose expert is not on this rank), slots in order:
+    token_rows[t, :] (-1, or any index outside the dispatched rows, = a slot whose expert is
+    not on this rank), slots in order:
     Y[t] = sum_j gates[t, j] * Yrows[token_rows[t, j]]. Summed over the TP group it is the
     layer's MoE output (the weighted sum is linear, so it commutes with the merge)."""
     X = f64(X)
@@ -457,6 +458,6 @@ def moe_mlp_shard(X, row_token, expert_offsets, W_gate, W_up, W_down, token_rows
     g = f64(gates)
     for t in range(T):
         for j in range(tr.shape[1]):
-            if tr[t, j] >= 0:
+            if 0 <= tr[t, j] < R:
                 Y[t] = Y[t] + g[t, j] * rows[tr[t, j]]
     return Y

@@ -632,12 +632,13 @@ def test_moe_matches_per_token_brute_force_and_is_linear_in_gates():
     Wg, Wu, Wd = rng.standard_normal((E, H, I)), rng.standard_normal((E, H, I)), rng.standard_normal((E, I, H))
     row_token, offsets, token_rows, gates = _route(rng, T, E, k)
     token_rows[2, 1] = -1                                   # a slot whose expert is elsewhere
+    token_rows[4, 0] = len(row_token) + 3                   # so is a row index past the rows
     Y = O.moe_mlp_shard(X, row_token, offsets, Wg, Wu, Wd, token_rows, gates)
     for t in range(T):
         want = [0.0] * H
         for j in range(k):
             r = token_rows[t, j]
-            if r < 0:
+            if r < 0 or r >= len(row_token):
                 continue
             e = int(np.searchsorted(offsets, r, side="right") - 1)
             y = brute.mlp([list(X[t])], Wg[e].tolist(), Wu[e].tolist(), Wd[e].tolist(), "swiglu")[0]
