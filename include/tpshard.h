@@ -260,6 +260,32 @@ tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY,
                              size_t ws_bytes, void* stream);
 size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N);
 
+/*
+ * tp_moe_mlp_shard — one rank's fp32 partial of a top-k mixture-of-experts MLP over its local
+ *   experts, each expert's weights TP-sharded like a dense MLP shard ("TensorRT LLM 中的并行
+ *   策略", 混合专家 (MoE): the TP and hybrid ETP modes). The router's choice arrives as:
+ *   expert_offsets: HOST array [E+1], offsets[0] = 0, non-decreasing; the R = offsets[E]
+ *     dispatched rows are grouped by expert (rows offsets[e] .. offsets[e+1]-1 go to expert e);
+ *   row_token: device int32 [R], the token of each row (a token outside [0, T) gives a zero row);
+ *   token_rows: device int32 [T, k], the rows of each token's k slots (-1, or any index outside
+ *     [0, R): an expert not on this rank); gates: device fp32 [T, k].
+ *   Y_partial[t] = sum_j gates[t, j] * MLP_e(X[t]) over the valid slots, in slot order, where
+ *   MLP_e(x) = (SiLU(x.W_gate[e]) * (x.W_up[e])) . W_down[e] (fp32; summed over the TP group it
+ *   is the layer's MoE output, since the combine is linear).
+ *   X [T, H] bf16; W_gate, W_up [E, H, I_shard], W_down [E, I_shard, H] bf16 row-major; Y_partial
+ *   [T, H] fp32 (overwritten; tokens without a valid slot get 0). H, I_shard multiples of 8;
+ *   1 <= E <= 1024; 1 <= k <= 16; X, weights, Y_partial 16-byte aligned; the int32/fp32
+ *   routing arrays 4-byte aligned; workspace >= tp_moe_workspace_size(...) bytes (dispatched rows,
+ *   their fp32 outputs, one expert's MLP workspace). Experts run one after another on `stream`.
+ */
+tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard, int32_t E,
+                           const void* W_gate, const void* W_up, const void* W_down,
+                           const int64_t* expert_offsets, const int32_t* row_token, int32_t k,
+                           const int32_t* token_rows, const float* gates, float* Y_partial,
+                           void* workspace, size_t ws_bytes, void* stream);
+size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E,
+                             const int64_t* expert_offsets);
+
 /* Status text, thread-local detail of this thread's last non-OK status, ABI version. */
 const char* tp_status_string(tp_status st);
 const char* tp_last_error(void);

@@ -18,7 +18,7 @@ __all__ = [
     "attn_shard", "partial_sum", "linear_workspace_size", "mlp_workspace_size",
     "attn_workspace_size", "mlp_shard_fp8", "mlp_fp8_workspace_size", "AttnDesc",
     "profile_enable", "profile_reset", "profile_read", "merge_rmsnorm", "linear_backward",
-    "linear_backward_workspace_size",
+    "linear_backward_workspace_size", "moe_mlp_shard", "moe_workspace_size",
     "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
     "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
 ]
@@ -36,7 +36,8 @@ EXPORTS = [
     "tp_mlp_workspace_size", "tp_attn_shard", "tp_attn_workspace_size", "tp_partial_sum",
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
-    "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size",
+    "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size", "tp_moe_mlp_shard",
+    "tp_moe_workspace_size",
 ]
 
 
@@ -102,6 +103,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tp_merge_rmsnorm": ([ctypes.POINTER(_P), _I32, _P, _P, ctypes.c_float, _P, _P, _I64, _I64, _P], _I32),
         "tp_linear_backward": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P], _I32),
         "tp_linear_backward_workspace_size": ([_I64, _I64, _I64], _SZ),
+        "tp_moe_mlp_shard": ([_P, _I64, _I64, _I64, _I32, _P, _P, _P, ctypes.POINTER(_I64), _P, _I32, _P, _P, _P,
+                              _P, _SZ, _P], _I32),
+        "tp_moe_workspace_size": ([_I64, _I64, _I64, _I32, ctypes.POINTER(_I64)], _SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -337,6 +341,40 @@ def linear_backward(X, W, dY, dX=None, dW=None, workspace=None, stream=None):
     _check(lib().tp_linear_backward(_ptr(X), _ptr(W), _ptr(dY), _ptr(dX), _ptr(dW), T, K, N, TP_BF16,
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
     return dX, dW
+
+
+def _offsets(expert_offsets):
+    offs = [int(v) for v in expert_offsets]
+    return (ctypes.c_int64 * len(offs))(*offs), len(offs) - 1
+
+
+def moe_workspace_size(T: int, H: int, I: int, expert_offsets) -> int:
+    arr, E = _offsets(expert_offsets)
+    return int(lib().tp_moe_workspace_size(T, H, I, E, arr))
+
+
+def moe_mlp_shard(X, W_gate, W_up, W_down, expert_offsets, row_token, token_rows, gates, Y=None,
+                  workspace=None, stream=None):
+    """fp32 partial of a top-k MoE MLP over local experts (bf16 X [T, H], W_gate/W_up [E, H, I],
+    W_down [E, I, H]; expert_offsets: host sequence [E+1]; row_token int32 [R], token_rows
+    int32 [T, k], gates fp32 [T, k] on the GPU)."""
+    import torch
+    T, H = X.shape
+    E, _, I = W_gate.shape
+    arr, E2 = _offsets(expert_offsets)
+    if E2 != E:
+        raise ValueError(f"expert_offsets has {E2 + 1} entries for {E} experts")
+    k = token_rows.shape[1]
+    if Y is None:
+        Y = torch.empty((T, H), dtype=torch.float32, device=X.device)
+    need = moe_workspace_size(T, H, I, expert_offsets)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    rt = _ptr(row_token) if row_token is not None and row_token.numel() else None
+    _check(lib().tp_moe_mlp_shard(_ptr(X), T, H, I, E, _ptr(W_gate), _ptr(W_up), _ptr(W_down), arr, rt, k,
+                                  _ptr(token_rows), _ptr(gates), _ptr(Y), _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+    return Y
 
 
 # --- kernel timing ------------------------------------------------------------------------------

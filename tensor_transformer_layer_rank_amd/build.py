@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_mfma.hip", "attn.hip", "decode.hip", "norm.hip", "backward.hip"]
+SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_mfma.hip", "attn.hip", "decode.hip", "norm.hip", "backward.hip", "moe.hip"]
 
 
 def hipcc() -> str:

@@ -317,6 +317,30 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
     return bytes;
 }
 
+// The bf16 MLP shard on T rows (validated arguments): gate/up (SwiGLU, or ReLU without W_up)
+// into h in the workspace, then the down projection's fp32 partial. `need` is
+// tp_mlp_workspace_size of the same arguments.
+static hipError_t mlp_bf16(const void* X, const void* W_gate, const void* W_up, const void* W_down, float* Y,
+                           int64_t T, int64_t H, int64_t I, tp_mlp_kind kind, void* workspace, size_t need,
+                           hipStream_t s) {
+    Carver c(workspace);
+    void* h = c.take((size_t)(T * I) * 2);
+    if (T <= SKINNY_MAX_T) {
+        float* part = static_cast<float*>(c.take(0));
+        hipError_t e = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I, H, s)
+                                             : tpk::skinny_linear(X, W_gate, part, T, I, H, H, h, I, 3, s);
+        if (e != hipSuccess) return e;
+        return tpk::skinny_linear(h, W_down, part, T, H, I, I, Y, H, 0, s);
+    }
+    void* split = c.take(0);
+    const size_t split_bytes = need - c.off;
+    hipError_t e = kind == TP_MLP_SWIGLU
+                       ? tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I, H, split, split_bytes, s)
+                       : tpk::gemm_bf16_store(X, W_gate, h, T, I, H, H, I, I, 0, 1, split, split_bytes, s);
+    if (e != hipSuccess) return e;
+    return tpk::gemm_bf16_store(h, W_down, Y, T, H, I, I, H, H, 2, 0, split, split_bytes, s);
+}
+
 tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, const void* W_down,
                        float* Y_partial, int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind kind,
                        tp_dtype in_dt, tp_dtype h_dt, void* workspace, size_t ws_bytes,
@@ -354,29 +378,7 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
         return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs 16-byte aligned pointers");
     if (H % 8 || I_shard % 8)
         return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs H and I_shard multiples of 8");
-    Carver c(workspace);
-    void* h = c.take((size_t)(T * I_shard) * 2);
-    if (T <= SKINNY_MAX_T) {
-        float* part = static_cast<float*>(c.take(0));
-        hipError_t e;
-        if (kind == TP_MLP_SWIGLU)
-            e = tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I_shard, H, s);
-        else
-            e = tpk::skinny_linear(X, W_gate, part, T, I_shard, H, H, h, I_shard, 3, s);
-        if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
-        return from_hip(tpk::skinny_linear(h, W_down, part, T, H, I_shard, I_shard, Y_partial, H, 0, s),
-                        "tp_mlp_shard");
-    }
-    void* split = c.take(0);
-    const size_t split_bytes = need - c.off;
-    hipError_t e;
-    if (kind == TP_MLP_SWIGLU)
-        e = tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I_shard, H, split, split_bytes, s);
-    else
-        e = tpk::gemm_bf16_store(X, W_gate, h, T, I_shard, H, H, I_shard, I_shard, 0, 1, split, split_bytes, s);
-    if (e != hipSuccess) return from_hip(e, "tp_mlp_shard");
-    return from_hip(tpk::gemm_bf16_store(h, W_down, Y_partial, T, H, I_shard, I_shard, H, H, 2, 0, split,
-                                         split_bytes, s),
+    return from_hip(mlp_bf16(X, W_gate, W_up, W_down, Y_partial, T, H, I_shard, kind, workspace, need, s),
                     "tp_mlp_shard");
 }
 
@@ -555,6 +557,74 @@ tp_status tp_partial_sum(const float* const* partials, int32_t k, float* out, in
         if (!aligned(partials[i], 16)) return fail(TP_ERR_MISALIGNED, "tp_partial_sum: partials[%d] must be 16-byte aligned", i);
     }
     return from_hip(tpk::partial_sum(partials, k, out, n_elems, as_stream(stream)), "tp_partial_sum");
+}
+
+// ---- MoE MLP shard ----------------------------------------------------------------------
+
+static bool moe_offsets_ok(const int64_t* offs, int32_t E) {
+    if (!offs || offs[0] != 0) return false;
+    for (int32_t e = 0; e < E; ++e)
+        if (offs[e + 1] < offs[e]) return false;
+    return offs[E] < ((int64_t)1 << 31);
+}
+
+size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E, const int64_t* expert_offsets) {
+    if (T <= 0 || H <= 0 || I_shard <= 0 || E < 1 || E > 1024 || !moe_offsets_ok(expert_offsets, E)) return 0;
+    const int64_t R = expert_offsets[E];
+    size_t mlp = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        const int64_t n = expert_offsets[e + 1] - expert_offsets[e];
+        if (n > 0) {
+            const size_t b = tp_mlp_workspace_size(n, H, I_shard, TP_MLP_SWIGLU, TP_BF16, TP_BF16);
+            mlp = b > mlp ? b : mlp;
+        }
+    }
+    return round_up((size_t)(R * H) * 2, WS_ALIGN) + round_up((size_t)(R * H) * 4, WS_ALIGN) + mlp;
+}
+
+tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard, int32_t E, const void* W_gate,
+                           const void* W_up, const void* W_down, const int64_t* expert_offsets,
+                           const int32_t* row_token, int32_t k, const int32_t* token_rows, const float* gates,
+                           float* Y_partial, void* workspace, size_t ws_bytes, void* stream) {
+    const char* fn = "tp_moe_mlp_shard";
+    if (!X || !W_gate || !W_up || !W_down || !expert_offsets || !token_rows || !gates || !Y_partial)
+        return fail(TP_ERR_NULL_POINTER, "%s: X, the weights, expert_offsets, token_rows, gates and Y_partial must be "
+                                         "non-NULL", fn);
+    if (T <= 0 || H <= 0 || I_shard <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "%s: sizes must be positive (T=%lld H=%lld I=%lld)", fn, (long long)T,
+                    (long long)H, (long long)I_shard);
+    if (E < 1 || E > 1024) return fail(TP_ERR_BAD_SHAPE, "%s: E=%d outside 1..1024", fn, (int)E);
+    if (k < 1 || k > 16) return fail(TP_ERR_BAD_SHAPE, "%s: k=%d outside 1..16", fn, (int)k);
+    if (T >= ((int64_t)1 << 31)) return fail(TP_ERR_UNSUPPORTED, "%s: T=%lld tokens (at most 2^31 - 1)", fn, (long long)T);
+    if (!moe_offsets_ok(expert_offsets, E))
+        return fail(TP_ERR_BAD_SHAPE, "%s: expert_offsets must start at 0, not decrease, and end below 2^31", fn);
+    const int64_t R = expert_offsets[E];
+    if (R > 0 && !row_token) return fail(TP_ERR_NULL_POINTER, "%s: row_token must be non-NULL when rows exist", fn);
+    if (H % 8 || I_shard % 8) return fail(TP_ERR_MISALIGNED, "%s: H and I_shard must be multiples of 8", fn);
+    if (!aligned(X, 16) || !aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(W_down, 16) || !aligned(Y_partial, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: X, the weights and Y_partial must be 16-byte aligned", fn);
+    if ((row_token && !aligned(row_token, 4)) || !aligned(token_rows, 4) || !aligned(gates, 4))
+        return fail(TP_ERR_MISALIGNED, "%s: row_token, token_rows and gates must be 4-byte aligned", fn);
+    const size_t need = tp_moe_workspace_size(T, H, I_shard, E, expert_offsets);
+    tp_status st = check_ws(fn, workspace, ws_bytes, need);
+    if (st != TP_OK) return st;
+    hipStream_t s = as_stream(stream);
+    Carver c(workspace);
+    void* Xg = c.take((size_t)(R * H) * 2);
+    float* Yg = static_cast<float*>(c.take((size_t)(R * H) * 4));
+    void* mlp_ws = c.take(0);   // the largest expert's MLP workspace, reused expert after expert
+    hipError_t e = tpk::moe_gather(X, row_token, Xg, R, T, H, s);
+    for (int32_t x = 0; x < E && e == hipSuccess; ++x) {
+        const int64_t a = expert_offsets[x], n = expert_offsets[x + 1] - a;
+        if (n == 0) continue;
+        const size_t wo = (size_t)(x * H * I_shard) * 2;
+        e = mlp_bf16(static_cast<const unsigned char*>(Xg) + (size_t)(a * H) * 2,
+                     static_cast<const unsigned char*>(W_gate) + wo, static_cast<const unsigned char*>(W_up) + wo,
+                     static_cast<const unsigned char*>(W_down) + wo, Yg + a * H, n, H, I_shard, TP_MLP_SWIGLU,
+                     mlp_ws, tp_mlp_workspace_size(n, H, I_shard, TP_MLP_SWIGLU, TP_BF16, TP_BF16), s);
+    }
+    if (e == hipSuccess) e = tpk::moe_combine(Yg, token_rows, gates, k, Y_partial, T, R, H, s);
+    return from_hip(e, fn);
 }
 
 size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N) {

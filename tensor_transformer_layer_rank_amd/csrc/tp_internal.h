@@ -100,6 +100,14 @@ size_t linear_backward_ws_bytes(int64_t T, int64_t K, int64_t N);
 hipError_t linear_backward(const void* X, const void* W, const void* dY, float* dX, float* dW, int64_t T,
                            int64_t K, int64_t N, void* ws, hipStream_t s);
 
+// ---- mixture of experts ------------------------------------------------------------------
+// Xg[r] = X[row_token[r]] (bf16 [R, H]; out-of-range tokens give a zero row);
+// Y[t] = sum_j gates[t, j] * Yg[token_rows[t, j]] (fp32 [T, H]; out-of-range rows skipped).
+hipError_t moe_gather(const void* X, const int32_t* row_token, void* Xg, int64_t R, int64_t T, int64_t H,
+                      hipStream_t s);
+hipError_t moe_combine(const float* Yg, const int32_t* token_rows, const float* gates, int k, float* Y, int64_t T,
+                       int64_t R, int64_t H, hipStream_t s);
+
 // ---- merges -------------------------------------------------------------------------------
 hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s);
 // r = residual + ((P0 + P1) + ...) (fp32), residual_out = bf16(r),

@@ -245,6 +245,34 @@ def test_linear_backward_validation(L):
     assert need >= (256 * 128 + 128 * 64) * 2 and need % 256 == 0
 
 
+def test_moe_validation(L):
+    f = L.tp_moe_mlp_shard
+    offs = (ctypes.c_int64 * 3)(0, 4, 8)
+    ok = [FAKE, 4, 64, 32, 2, FAKE, FAKE, FAKE, offs, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def st(i, v):
+        a = list(ok)
+        a[i] = v
+        return _st(f(*a))
+    for i in (0, 5, 6, 7, 8, 11, 12, 13):
+        assert st(i, None) == "TP_ERR_NULL_POINTER", i
+    assert st(9, None) == "TP_ERR_NULL_POINTER"                       # rows exist
+    for i in (1, 2, 3):
+        assert st(i, 0) == "TP_ERR_BAD_SHAPE"
+    assert st(4, 0) == "TP_ERR_BAD_SHAPE" and st(4, 1025) == "TP_ERR_BAD_SHAPE"
+    assert st(10, 0) == "TP_ERR_BAD_SHAPE" and st(10, 17) == "TP_ERR_BAD_SHAPE"
+    assert st(8, (ctypes.c_int64 * 3)(1, 4, 8)) == "TP_ERR_BAD_SHAPE"  # offsets must start at 0
+    assert st(8, (ctypes.c_int64 * 3)(0, 4, 2)) == "TP_ERR_BAD_SHAPE"  # and not decrease
+    assert st(2, 60) == "TP_ERR_MISALIGNED" and st(3, 36) == "TP_ERR_MISALIGNED"
+    for i in (0, 5, 6, 7, 13):
+        assert st(i, FAKE_ODD) == "TP_ERR_MISALIGNED", i
+    assert st(12, ctypes.c_void_p(0x1002)) == "TP_ERR_MISALIGNED"
+    assert st(15, 16) == "TP_ERR_WORKSPACE" and st(14, None) == "TP_ERR_WORKSPACE"
+    need = L.tp_moe_workspace_size(4, 64, 32, 2, offs)
+    assert need >= 8 * 64 * (2 + 4)
+    assert L.tp_moe_workspace_size(4, 64, 32, 2, (ctypes.c_int64 * 3)(0, 5, 2)) == 0
+
+
 def test_profile_api_without_launches(L):
     assert L.tp_profile_reset() == 0
     ms, n = tp.profile_read("")

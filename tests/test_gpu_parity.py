@@ -248,6 +248,75 @@ def test_backward7b_tp4_full_size_sampled(tp):
     assert_close_bf16(gw[krows], ref_w, "backward7b_tp4 dW rows")
 
 
+# ---------------------------------------------------------------- MoE MLP shard
+
+def _moe_dev(inp):
+    import torch
+    return dict(X=dev(inp.X), W_gate=dev(inp.W_gate), W_up=dev(inp.W_up), W_down=dev(inp.W_down),
+                expert_offsets=inp.expert_offsets,
+                row_token=torch.from_numpy(np.ascontiguousarray(inp.row_token)).cuda(),
+                token_rows=torch.from_numpy(np.ascontiguousarray(inp.token_rows)).cuda(),
+                gates=dev(inp.gates, "f32"))
+
+
+def _moe_oracle(inp, tokens=None):
+    """The oracle on all tokens, or on a token subset with its rows re-dispatched."""
+    if tokens is None:
+        return O.moe_mlp_shard(inp.X, inp.row_token, inp.expert_offsets, inp.W_gate, inp.W_up, inp.W_down,
+                               inp.token_rows, inp.gates)
+    E = inp.W_gate.shape[0]
+    eoff = inp.expert_offsets
+    slots = sorted((int(np.searchsorted(eoff, r, side="right") - 1), i, j)
+                   for i, t in enumerate(tokens) for j, r in enumerate(inp.token_rows[t]) if 0 <= r < eoff[-1])
+    row_token = np.array([i for _, i, _ in slots], np.int32)
+    offsets = np.searchsorted([e for e, _, _ in slots], np.arange(E + 1), side="left")
+    token_rows = np.full((len(tokens), inp.token_rows.shape[1]), -1, np.int32)
+    for r, (_, i, j) in enumerate(slots):
+        token_rows[i, j] = r
+    return O.moe_mlp_shard(inp.X[tokens], row_token, offsets, inp.W_gate, inp.W_up, inp.W_down, token_rows,
+                           inp.gates[tokens])
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(40, 136, 72, 4, 2), (300, 256, 520, 3, 1), (9, 64, 32, 8, 3)])
+def test_moe_mlp_small(tp, T, H, I, E, k):
+    import torch
+    inp = wl.random_moe(T + H + E, T, H, I, E, k)
+    inp.token_rows[1, 0] = -1                          # a slot whose expert is not on this rank
+    if T > 2:
+        inp.token_rows[2, k - 1] = len(inp.row_token) + 5   # an index outside the rows: skipped
+    d = _moe_dev(inp)
+    Y = tp.moe_mlp_shard(Y=_nan((T, H), torch.float32), **d)
+    Y2 = tp.moe_mlp_shard(**d)
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.array_equal(y, host(Y2)), "two launches differ bitwise"
+    assert_close_bf16(y, _moe_oracle(inp), f"moe T{T} H{H} I{I} E{E} k{k}")
+
+
+def test_moe_expert_without_rows_and_unrouted_token(tp):
+    import torch
+    inp = wl.random_moe(5, 12, 64, 32, 3, 1)
+    # every token to expert 0 or 2: expert 1 gets no rows; token 3's only slot is elsewhere
+    inp = wl.MoEInputs(inp.name, inp.X, inp.W_gate, inp.W_up, inp.W_down,
+                       np.array([0, 6, 6, 12], np.int64), np.array(list(range(6)) + list(range(6, 12)), np.int32),
+                       np.arange(12, dtype=np.int32)[:, None].copy(), inp.gates[:, :1] * 0 + 1)
+    inp.token_rows[3, 0] = -1
+    Y = tp.moe_mlp_shard(Y=_nan((12, 64), torch.float32), **_moe_dev(inp))
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert not np.any(y[3]), "a token without a local slot gets a zero partial"
+    assert_close_bf16(y, _moe_oracle(inp), "moe with an empty expert")
+
+
+def test_moe8x7b_tp4_full_size_sampled(tp):
+    """Mixtral-8x7B-like MoE MLP at TP=4 within the experts at full size (sampled tokens)."""
+    inp = wl.moe8x7b_tp4()
+    d = _moe_dev(inp)
+    y = host(tp.moe_mlp_shard(**d))
+    tokens = sample_rows(inp.X.shape[0], 16, seed=6)
+    assert_close_bf16(y[tokens], _moe_oracle(inp, tokens), "moe8x7b_tp4 sampled tokens")
+
+
 # ---------------------------------------------------------------- bf16 linear layers
 
 @pytest.mark.parametrize("T,K,N", [(300, 256, 200), (513, 520, 264), (256, 64, 256), (65, 4096, 384)])

@@ -38,7 +38,8 @@ __all__ = [
     "mlp_relu_tp2", "mlp7b_tp4", "attn7b_tp4", "layer70b_tp8", "decode7b_tp2",
     "random_mlp", "random_attn", "random_decode", "int_matrix", "WORKLOADS",
     "e4m3_codes", "FP8MLPInputs", "random_mlp_fp8", "mlp7b_tp4_fp8", "MergeInputs", "random_merge",
-    "merge7b_tp4", "BackwardInputs", "random_backward", "backward7b_tp4",
+    "merge7b_tp4", "BackwardInputs", "random_backward", "backward7b_tp4", "MoEInputs", "random_moe",
+    "moe8x7b_tp4",
 ]
 
 
@@ -347,6 +348,47 @@ def backward7b_tp4(seed: int = 7) -> BackwardInputs:
     return random_backward(seed, 4096, 2752, 4096, name="backward7b_tp4")
 
 
+@dataclass
+class MoEInputs:
+    """A top-k MoE MLP on one rank: tokens, the local experts' TP-sharded SwiGLU weights and a
+    router's choice laid out as the dispatch (rows grouped by expert) and the combine map."""
+    name: str
+    X: np.ndarray              # [T, H] float32, bf16-rounded
+    W_gate: np.ndarray         # [E, H, I] float32, bf16-rounded
+    W_up: np.ndarray           # [E, H, I]
+    W_down: np.ndarray         # [E, I, H]
+    expert_offsets: np.ndarray # [E+1] int64
+    row_token: np.ndarray      # [R] int32
+    token_rows: np.ndarray     # [T, k] int32
+    gates: np.ndarray          # [T, k] float32
+
+
+def random_moe(seed: int, T: int, H: int, I: int, E: int, k: int, name: str = "moe") -> MoEInputs:
+    """X N(0,1), weights N(0, 0.02^2) (bf16-rounded); every token picks k distinct experts
+    uniformly at random with gates uniform in (0, 1) scaled to sum to 1; dispatched rows are
+    ordered by (expert, token, slot)."""
+    rng = np.random.default_rng(seed)
+    X = _normal(rng, (T, H), 1.0)
+    Wg, Wu, Wd = _normal(rng, (E, H, I), 0.02), _normal(rng, (E, H, I), 0.02), _normal(rng, (E, I, H), 0.02)
+    experts = np.argsort(rng.random((T, E)), axis=1)[:, :k]
+    g = rng.random((T, k)).astype(np.float32) + np.float32(1e-3)
+    gates = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+    key = experts.astype(np.int64) * (T * k) + np.arange(T)[:, None] * k + np.arange(k)[None, :]
+    order = np.argsort(key.ravel(), kind="stable")
+    row_token = (order // k).astype(np.int32)
+    counts = np.bincount(experts.ravel(), minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    token_rows = np.empty(T * k, np.int32)
+    token_rows[order] = np.arange(T * k, dtype=np.int32)
+    return MoEInputs(name, X, Wg, Wu, Wd, offsets, row_token, token_rows.reshape(T, k), gates)
+
+
+def moe8x7b_tp4(seed: int = 8) -> MoEInputs:
+    """Mixtral-8x7B-like MoE MLP at TP=4 within the experts: 2048 tokens, H 4096, the 8
+    experts' I = 14336 split 4 ways (3584), top-2 routing."""
+    return random_moe(seed, 2048, 4096, 3584, 8, 2, name="moe8x7b_tp4")
+
+
 WORKLOADS = {
     "mlp_relu_tp2": mlp_relu_tp2,
     "mlp7b_tp4": mlp7b_tp4,
@@ -356,4 +398,5 @@ WORKLOADS = {
     "mlp7b_tp4_fp8": mlp7b_tp4_fp8,
     "merge7b_tp4": merge7b_tp4,
     "backward7b_tp4": backward7b_tp4,
+    "moe8x7b_tp4": moe8x7b_tp4,
 }
