@@ -10,7 +10,8 @@ KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compuls
 bytes, and the same MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8) against the fp8
 MFMA peak, and the step after the merge (tp_merge_rmsnorm: 4 fp32 partials of [8192, 4096]
 summed into the bf16 residual stream, then RMSNorm) against the HBM bandwidth, and the
-backward of the MLP down shard (tp_linear_backward). Inputs are
+backward of the MLP down shard (tp_linear_backward), and a top-2 MoE MLP over 8 local
+experts (tp_moe_mlp_shard, 2048 tokens; TFLOP/s of the expert MLPs). Inputs are
 seeded synthetic tensors already resident in HBM. With --extra the attention shard (B=4,
 S=2048) and the 70B GQA layer shard are timed too.
 
@@ -312,6 +313,47 @@ def backward_bench(args):
     }
 
 
+def moe_bench(args):
+    """Top-2 MoE MLP on one rank (tp_moe_mlp_shard): 2048 tokens, 8 local experts whose SwiGLU
+    MLPs are TP=4 shards (H 4096, I 3584); gather, per-expert gate/up + down, gated combine."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    from tests._util import dev
+    inp = wl.moe8x7b_tp4()
+    T, H = inp.X.shape
+    I = inp.W_gate.shape[2]
+    R = int(inp.expert_offsets[-1])
+    X, Wg, Wu, Wd = dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down)
+    rt = torch.from_numpy(inp.row_token.copy()).cuda()
+    tr = torch.from_numpy(inp.token_rows.copy()).cuda()
+    gates = dev(inp.gates, "f32")
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(tp.moe_workspace_size(T, H, I, inp.expert_offsets), 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.moe_mlp_shard(X, Wg, Wu, Wd, inp.expert_offsets, rt, tr, gates, Y=Y, workspace=ws)
+
+    ms = timed(step, args.warmup, args.steps, "moe")
+    flops = 6.0 * R * H * I
+    kern = {}
+    for name in ("moe_gather", "gemm_bf16_swiglu", "fixup_swiglu", "gemm_bf16_f32out", "fixup_gemm",
+                 "skinny", "moe_combine"):
+        k_ms, k_n = kernel_avg(name)
+        if k_n:
+            kern[name] = {"avg_us": k_ms * 1e3, "launches_per_step": k_n / len(range(0, args.steps, 10))}
+    return {
+        "workload": f"moe8x7b_tp4: T={T} tokens, top-2 of 8 experts ({R} dispatched rows), "
+                    f"expert shards gate/up [{H},{I}], down [{I},{H}] bf16 -> fp32 partial",
+        "ms_per_step": ms,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "flops_per_step": flops,
+        "step_stats": STEP_STATS.get("moe"),
+        "kernels": kern,
+    }
+
+
 def graph_timed(step, warmup: int, steps: int, name: str = None):
     """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
     between two events; a second pass with one event per replay gives the per-replay median
@@ -529,6 +571,7 @@ def main():
     fp8 = fp8_mlp_bench(args)
     merge = merge_bench(args)
     bwd = backward_bench(args)
+    moe = moe_bench(args)
     extra = {}
     if args.extra:
         extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
@@ -565,6 +608,7 @@ def main():
         "fp8_mlp": fp8,
         "merge_rmsnorm": merge,
         "backward": bwd,
+        "moe": moe,
         "extra": extra or None,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},

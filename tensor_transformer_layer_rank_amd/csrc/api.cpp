@@ -568,9 +568,23 @@ static bool moe_offsets_ok(const int64_t* offs, int32_t E) {
     return offs[E] < ((int64_t)1 << 31);
 }
 
+static int64_t moe_max_rows(const int64_t* offs, int32_t E) {
+    int64_t m = 0;
+    for (int32_t e = 0; e < E; ++e) m = offs[e + 1] - offs[e] > m ? offs[e + 1] - offs[e] : m;
+    return m;
+}
+
+// Experts of at most SKINNY_MAX_T rows each run one after another through the weight-streaming
+// kernels; otherwise all experts share one grouped gate/up launch and one grouped down launch.
 size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E, const int64_t* expert_offsets) {
     if (T <= 0 || H <= 0 || I_shard <= 0 || E < 1 || E > 1024 || !moe_offsets_ok(expert_offsets, E)) return 0;
     const int64_t R = expert_offsets[E];
+    const size_t rows = round_up((size_t)(R * H) * 2, WS_ALIGN) + round_up((size_t)(R * H) * 4, WS_ALIGN);
+    if (moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
+        const size_t gu = tpk::gemm_bf16_grouped_split_bytes(expert_offsets, E, I_shard, H, 1);
+        const size_t dn = tpk::gemm_bf16_grouped_split_bytes(expert_offsets, E, H, I_shard, 0);
+        return rows + round_up((size_t)(R * I_shard) * 2, WS_ALIGN) + round_up(gu > dn ? gu : dn, WS_ALIGN);
+    }
     size_t mlp = 0;
     for (int32_t e = 0; e < E; ++e) {
         const int64_t n = expert_offsets[e + 1] - expert_offsets[e];
@@ -579,7 +593,7 @@ size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E, c
             mlp = b > mlp ? b : mlp;
         }
     }
-    return round_up((size_t)(R * H) * 2, WS_ALIGN) + round_up((size_t)(R * H) * 4, WS_ALIGN) + mlp;
+    return rows + mlp;
 }
 
 tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard, int32_t E, const void* W_gate,
@@ -612,8 +626,18 @@ tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard,
     Carver c(workspace);
     void* Xg = c.take((size_t)(R * H) * 2);
     float* Yg = static_cast<float*>(c.take((size_t)(R * H) * 4));
-    void* mlp_ws = c.take(0);   // the largest expert's MLP workspace, reused expert after expert
     hipError_t e = tpk::moe_gather(X, row_token, Xg, R, T, H, s);
+    if (e == hipSuccess && moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
+        void* h = c.take((size_t)(R * I_shard) * 2);
+        void* split = c.take(0);
+        const size_t split_bytes = need - c.off;
+        e = tpk::gemm_bf16_swiglu_grouped(Xg, W_gate, W_up, h, expert_offsets, E, I_shard, H, split, split_bytes, s);
+        if (e == hipSuccess)
+            e = tpk::gemm_bf16_f32out_grouped(h, W_down, Yg, expert_offsets, E, H, I_shard, split, split_bytes, s);
+        if (e == hipSuccess) e = tpk::moe_combine(Yg, token_rows, gates, k, Y_partial, T, R, H, s);
+        return from_hip(e, fn);
+    }
+    void* mlp_ws = c.take(0);   // the largest expert's MLP workspace, reused expert after expert
     for (int32_t x = 0; x < E && e == hipSuccess; ++x) {
         const int64_t a = expert_offsets[x], n = expert_offsets[x + 1] - a;
         if (n == 0) continue;

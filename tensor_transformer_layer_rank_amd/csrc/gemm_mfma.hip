@@ -417,6 +417,12 @@ struct EpiStore {
                 return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * ldc) * ES + 16 * c : nullptr;
             }, lane);
     }
+    // grouped launches: this group's output rows r0 .. r0+m-1
+    __device__ void shift_rows(int64_t r0, int64_t m) {
+        using T = std::conditional_t<(KIND >= 2 && KIND <= 3), float, std::conditional_t<KIND == 4, uint8_t, uint16_t>>;
+        C = static_cast<unsigned char*>(C) + r0 * ldc * (int64_t)sizeof(T);
+        M = m;
+    }
 };
 
 // h = SiLU(gate * gs) * (up * us); stored as bf16 (H8 = false) or as the E4M3 code of
@@ -451,6 +457,10 @@ struct EpiSwiGLU {
             lds, [&](int r, int c) -> unsigned char* {
                 return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * N) * ES + 16 * c : nullptr;
             }, lane);
+    }
+    __device__ void shift_rows(int64_t r0, int64_t m) {
+        h = static_cast<unsigned char*>(h) + r0 * N * (H8 ? 1 : 2);
+        M = m;
     }
 };
 
@@ -714,14 +724,52 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
 // waves per fix-up workgroup (divides 16); single-wave workgroups spread a tile's row blocks
 // over the machine (4-wave ones made the QKV fix-up 1.5-2x slower)
 constexpr int FIXUP_WAVES = 1;
+
+// Grouped launches (one launch over several independent GEMMs that share N and K, e.g. the
+// experts of an MoE layer): group e multiplies activation rows row0[e] .. row0[e+1]-1 by
+// weight e (b_stride elements after weight e-1) into the same output rows. Its tiles are the
+// logical tiles tile0[e] .. tile0[e+1]-1, ceil(rows / BM) row tiles x tiles_n each, so the
+// split plan, the XCD mapping and the fix-up run over the launch's tiles as over one grid.
+constexpr int MAX_GROUPS = 32;
+struct NoGroups {
+    static constexpr bool ON = false;
+};
+struct Groups {
+    static constexpr bool ON = true;
+    int n;
+    int tile0[MAX_GROUPS + 1];
+    int64_t row0[MAX_GROUPS + 1];
+    int64_t b_stride;
+    // logical tile L of the launch -> its group (scalar, fixed-index selects: the argument
+    // block is never indexed dynamically); L becomes the tile's index within the group
+    __device__ __forceinline__ int locate(int& L, int tiles_n, int& tiles_m, int64_t& r0, int64_t& m) const {
+        int e = 0, t0 = tile0[0], t1 = tile0[1];
+        int64_t a = row0[0], b = row0[1];
+#pragma unroll
+        for (int j = 1; j < MAX_GROUPS; ++j)
+            if (j < n && L >= tile0[j]) {
+                e = j;
+                t0 = tile0[j];
+                t1 = tile0[j + 1];
+                a = row0[j];
+                b = row0[j + 1];
+            }
+        L -= t0;
+        tiles_m = (t1 - t0) / tiles_n;
+        r0 = a;
+        m = b - a;
+        return e;
+    }
+};
+
 struct SplitArgs {
     int g_full, pieces, piece_steps;
     float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
 };
 
-template <bool F8, bool DUAL, class Epi>
+template <bool F8, bool DUAL, class Epi, class Grp>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
-                                                            int tiles_n, SplitArgs sp) {
+                                                            int tiles_n, SplitArgs sp, Grp gr) {
     constexpr int BK = Fmt<F8>::BK;
     __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
@@ -737,6 +785,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
     } else {
         q = bid - sp.g_full;
         L = sp.g_full + q / sp.pieces;
+    }
+    if constexpr (Grp::ON) {
+        int64_t r0, m;
+        const int e = gr.locate(L, tiles_n, tiles_m, r0, m);
+        g.A += r0 * g.lda;
+        g.B1 += e * gr.b_stride;
+        if constexpr (DUAL) g.B2 += e * gr.b_stride;
+        g.M = m;
+        epi.shift_rows(r0, m);
     }
     int tm, tn;
     tile_of(L, tiles_m, tiles_n, tm, tn);
@@ -862,16 +919,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
 // One wave per (split tile, wave of the tile, accumulator row block i): sum the tile's
 // pieces in piece order, then that row block's epilogue. 16 single-wave workgroups per tile
 // keep the partial reads spread over the machine.
-template <bool DUAL, class Epi>
+template <bool DUAL, class Epi, class Grp>
 __global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, int tiles_m, int tiles_n,
-                                                                      SplitArgs sp) {
+                                                                      SplitArgs sp, Grp gr) {
     __shared__ __attribute__((aligned(16))) unsigned char tile[FIXUP_WAVES * EPI_LDS];
     const int lane = threadIdx.x & 63;
     const int gw = (int)blockIdx.x * FIXUP_WAVES + (int)(threadIdx.x >> 6);   // (tile, wave, i)
     const int t = gw >> 4, wave = (gw >> 2) & 3, i = gw & 3;
     const int wm = wave & 1, wn = wave >> 1;
+    int L = sp.g_full + t;
+    if constexpr (Grp::ON) {
+        int64_t r0, m;
+        gr.locate(L, tiles_n, tiles_m, r0, m);
+        epi.shift_rows(r0, m);
+    }
     int tm, tn;
-    tile_of(sp.g_full + t, tiles_m, tiles_n, tm, tn);
+    tile_of(L, tiles_m, tiles_n, tm, tn);
     f32x16 a[4];
     const float* src = sp.part + ((int64_t)t * sp.pieces * 4 + wave) * (256 * 64) + i * (64 * 64) + lane;
 #pragma unroll
@@ -951,14 +1014,17 @@ size_t split_bytes_of(int64_t M, int64_t N, int64_t K, bool dual, int bk) {
     return (size_t)(tm * tn - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
 }
 
-// ws may be NULL (or too small): the tiles then all run whole
-template <bool F8, bool DUAL, class Epi>
+// ws may be NULL (or too small): the tiles then all run whole. A grouped launch takes its
+// tile count from the groups (g.M then only bounds nothing: each group sets its own).
+template <bool F8, bool DUAL, class Epi, class Grp = NoGroups>
 hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
-                  const char* name) {
+                  const char* name, const Grp& gr = Grp{}) {
     constexpr int BK = Fmt<F8>::BK;
     int64_t tiles_m, tiles_n;
     tiles_of<DUAL>(g.M, g.N, tiles_m, tiles_n);
-    const int64_t G = tiles_m * tiles_n;
+    int64_t G = tiles_m * tiles_n;
+    if constexpr (Grp::ON) G = gr.tile0[gr.n];
+    if (G == 0) return hipSuccess;
     const int nk = (int)((g.K + BK - 1) / BK);
     SplitArgs sp = plan_split(G, nk, cu_count());
     const size_t need = sp.pieces >= 2 ? (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float) : 0;
@@ -967,13 +1033,13 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
     const int64_t blocks = sp.pieces >= 2 ? sp.g_full + (G - sp.g_full) * sp.pieces : G;
     {
         ProfScope ps(name, s);
-        gemm_mfma_kernel<F8, DUAL, Epi><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp);
+        gemm_mfma_kernel<F8, DUAL, Epi, Grp><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp, gr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || sp.pieces < 2) return e;
     }
     ProfScope ps(DUAL ? "fixup_swiglu" : "fixup_gemm", s);
-    gemm_fixup_kernel<DUAL, Epi><<<(unsigned)((G - sp.g_full) * 16 / FIXUP_WAVES), 64 * FIXUP_WAVES, 0, s>>>(
-        epi, (int)tiles_m, (int)tiles_n, sp);
+    gemm_fixup_kernel<DUAL, Epi, Grp><<<(unsigned)((G - sp.g_full) * 16 / FIXUP_WAVES), 64 * FIXUP_WAVES, 0, s>>>(
+        epi, (int)tiles_m, (int)tiles_n, sp, gr);
     return hipGetLastError();
 }
 
@@ -1044,6 +1110,72 @@ hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void*
                   static_cast<const uint16_t*>(Bu), M, N, K, K, N};
     return launch<false, true>(g, EpiSwiGLU<false>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
                                "gemm_bf16_swiglu");
+}
+
+namespace {
+
+// groups 0..n-1 from their row offsets (n+1 entries, relative to the launch's A and output)
+Groups make_groups(const int64_t* row_offsets, int n, int64_t tiles_n, int64_t b_stride) {
+    Groups gr{};
+    gr.n = n;
+    gr.b_stride = b_stride;
+    int64_t t = 0;
+    for (int e = 0; e <= n; ++e) {
+        gr.row0[e] = row_offsets[e];
+        gr.tile0[e] = (int)t;
+        if (e < n) t += (row_offsets[e + 1] - row_offsets[e] + BM - 1) / BM * tiles_n;
+    }
+    return gr;
+}
+
+int64_t tiles_n_of(int64_t N, bool dual) { return (N + (dual ? BN / 2 : BN) - 1) / (dual ? BN / 2 : BN); }
+
+}  // namespace
+
+// Launches of at most MAX_GROUPS groups each run one after another and reuse one split
+// workspace: its size is the largest launch's.
+size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, int dual) {
+    const int64_t tn = tiles_n_of(N, dual != 0);
+    const int nk = (int)((K + Fmt<false>::BK - 1) / Fmt<false>::BK);
+    size_t best = 0;
+    for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
+        const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
+        const int64_t G = make_groups(row_offsets + x0, n, tn, 0).tile0[n];
+        const SplitArgs sp = plan_split(G, nk, cu_count());
+        const size_t b = sp.pieces < 2 ? 0 : (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
+        best = b > best ? b : best;
+    }
+    return best;
+}
+
+hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
+                                    const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, void* ws,
+                                    size_t ws_bytes, hipStream_t s) {
+    const int64_t M = row_offsets[n_groups], tn = tiles_n_of(N, true);
+    for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
+        const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
+        const int64_t wo = (int64_t)x0 * K * N;
+        Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg) + wo,
+                      static_cast<const uint16_t*>(Bu) + wo, M, N, K, K, N};
+        hipError_t e = launch<false, true>(g, EpiSwiGLU<false>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
+                                           "gemm_bf16_swiglu", make_groups(row_offsets + x0, n, tn, K * N));
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, const int64_t* row_offsets,
+                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+    const int64_t M = row_offsets[n_groups], tn = tiles_n_of(N, false);
+    for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
+        const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
+        Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B) + (int64_t)x0 * K * N,
+                      nullptr, M, N, K, K, N};
+        hipError_t e = launch<false, false>(g, EpiStore<2, false>{C, N, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
+                                            "gemm_bf16_f32out", make_groups(row_offsets + x0, n, tn, K * N));
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t gemm_f8_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,

@@ -38,6 +38,15 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
                            int relu, void* ws, size_t ws_bytes, hipStream_t s);
 // h[M, N] (bf16, ld = N) = SiLU(A . Bg) * (A . Bu)
+// Grouped forms (the experts of an MoE layer): group e = rows row_offsets[e] ..
+// row_offsets[e+1]-1 of A and of the output, times weight e ([K, N], weights contiguous);
+// n_groups >= 1, row_offsets non-decreasing from 0.
+size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, int dual);
+hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
+                                    const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, void* ws,
+                                    size_t ws_bytes, hipStream_t s);
+hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, const int64_t* row_offsets,
+                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
                             int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 

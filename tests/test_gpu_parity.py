@@ -308,6 +308,22 @@ def test_moe_expert_without_rows_and_unrouted_token(tp):
     assert_close_bf16(y, _moe_oracle(inp), "moe with an empty expert")
 
 
+def test_moe_grouped_skewed_many_experts(tp):
+    """A skewed load over 37 experts: more than one grouped launch (32 experts each), experts
+    of several row tiles with a ragged last one, small and empty experts between them."""
+    import torch
+    E = 37
+    w = np.ones(E)
+    w[0], w[5], w[33], w[36] = 60.0, 25.0, 40.0, 12.0
+    w[[2, 3, 20, 34]] = 0.0
+    inp = wl.random_moe(11, 700, 128, 96, E, 2, expert_p=w / w.sum())
+    counts = np.diff(inp.expert_offsets)
+    assert counts.max() > 256 and (counts == 0).sum() == 4 and counts[32:].max() > 64
+    Y = tp.moe_mlp_shard(Y=_nan((700, 128), torch.float32), **_moe_dev(inp))
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), _moe_oracle(inp), "moe 37 experts, skewed")
+
+
 def test_moe8x7b_tp4_full_size_sampled(tp):
     """Mixtral-8x7B-like MoE MLP at TP=4 within the experts at full size (sampled tokens)."""
     inp = wl.moe8x7b_tp4()

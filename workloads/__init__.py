@@ -363,14 +363,19 @@ class MoEInputs:
     gates: np.ndarray          # [T, k] float32
 
 
-def random_moe(seed: int, T: int, H: int, I: int, E: int, k: int, name: str = "moe") -> MoEInputs:
+def random_moe(seed: int, T: int, H: int, I: int, E: int, k: int, name: str = "moe",
+               expert_p=None) -> MoEInputs:
     """X N(0,1), weights N(0, 0.02^2) (bf16-rounded); every token picks k distinct experts
-    uniformly at random with gates uniform in (0, 1) scaled to sum to 1; dispatched rows are
-    ordered by (expert, token, slot)."""
+    uniformly at random (or drawn without replacement with probabilities expert_p, for skewed
+    loads) with gates uniform in (0, 1) scaled to sum to 1; dispatched rows are ordered by
+    (expert, token, slot)."""
     rng = np.random.default_rng(seed)
     X = _normal(rng, (T, H), 1.0)
     Wg, Wu, Wd = _normal(rng, (E, H, I), 0.02), _normal(rng, (E, H, I), 0.02), _normal(rng, (E, I, H), 0.02)
-    experts = np.argsort(rng.random((T, E)), axis=1)[:, :k]
+    if expert_p is None:
+        experts = np.argsort(rng.random((T, E)), axis=1)[:, :k]
+    else:
+        experts = np.array([rng.choice(E, size=k, replace=False, p=expert_p) for _ in range(T)]).reshape(T, k)
     g = rng.random((T, k)).astype(np.float32) + np.float32(1e-3)
     gates = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
     key = experts.astype(np.int64) * (T * k) + np.arange(T)[:, None] * k + np.arange(k)[None, :]
