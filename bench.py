@@ -547,7 +547,19 @@ def cpu_baseline(inp, target_s: float):
     except Exception:
         pass
     cores = threads or len(os.sched_getaffinity(0))
+    cpu_model, blas = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{cfg.get('name')} {cfg.get('version', '')}".strip()
+    except Exception:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model, "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
             "sample": f"fp64 NumPy oracle on rows 0..{rows - 1} of the 4096-row MLP shard "
                       f"({flops / 1e9:.1f} GFLOP in {dt:.2f} s)",
             "seconds": dt}

@@ -275,8 +275,13 @@ size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N);
  *   X [T, H] bf16; W_gate, W_up [E, H, I_shard], W_down [E, I_shard, H] bf16 row-major; Y_partial
  *   [T, H] fp32 (overwritten; tokens without a valid slot get 0). H, I_shard multiples of 8;
  *   1 <= E <= 1024; 1 <= k <= 16; X, weights, Y_partial 16-byte aligned; the int32/fp32
- *   routing arrays 4-byte aligned; workspace >= tp_moe_workspace_size(...) bytes (dispatched rows,
- *   their fp32 outputs, one expert's MLP workspace). Experts run one after another on `stream`.
+ *   routing arrays 4-byte aligned; workspace >= tp_moe_workspace_size(...) bytes, 16-byte
+ *   aligned (the gathered rows, their fp32 outputs, and either h for all rows plus the GEMM
+ *   split partials or one expert's MLP workspace). Broken rules return TP_ERR_NULL_POINTER /
+ *   TP_ERR_BAD_SHAPE / TP_ERR_UNSUPPORTED / TP_ERR_MISALIGNED / TP_ERR_WORKSPACE before any
+ *   launch. When an expert has more than 64 rows all experts share one grouped gate/up and one
+ *   grouped down GEMM launch (per 32 experts); otherwise the experts run one after another
+ *   through the weight-streaming kernels. Asynchronous on `stream`; deterministic.
  */
 tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard, int32_t E,
                            const void* W_gate, const void* W_up, const void* W_down,

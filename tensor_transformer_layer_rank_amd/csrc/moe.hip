@@ -4,8 +4,9 @@
 // linear, can run before the TP merge).
 //
 // Three steps on one stream: gather the dispatched rows (grouped by expert) from the token
-// activations, run each expert's MLP shard on its rows with the dense bf16 kernels, and
-// combine every token's rows, gate-weighted, in slot order. Row indices come from device
+// activations, run the experts' MLP shards on their rows (grouped GEMM launches across the
+// experts, or the weight-streaming kernels expert by expert for small loads), and combine
+// every token's rows, gate-weighted, in slot order. Row indices come from device
 // arrays the host cannot see: an index outside its range contributes nothing (gathered
 // row of zeros, skipped slot) instead of being dereferenced.
 #include "tp_internal.h"
