@@ -619,6 +619,16 @@ tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard,
         return fail(TP_ERR_MISALIGNED, "%s: X, the weights and Y_partial must be 16-byte aligned", fn);
     if ((row_token && !aligned(row_token, 4)) || !aligned(token_rows, 4) || !aligned(gates, 4))
         return fail(TP_ERR_MISALIGNED, "%s: row_token, token_rows and gates must be 4-byte aligned", fn);
+    if (moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
+        // grouped launches number their 256-row x 128-column tiles in 32 bits (with up to 4
+        // tail pieces each): keep every launch far below that
+        int64_t row_tiles = 0;
+        for (int32_t x = 0; x < E; ++x) row_tiles += (expert_offsets[x + 1] - expert_offsets[x] + 255) / 256;
+        const int64_t col_tiles = ((H > I_shard ? H : I_shard) + 127) / 128;
+        if (row_tiles * col_tiles >= ((int64_t)1 << 28))
+            return fail(TP_ERR_UNSUPPORTED, "%s: %lld row tiles x %lld column tiles exceed the grouped GEMM's 2^28 tiles",
+                        fn, (long long)row_tiles, (long long)col_tiles);
+    }
     const size_t need = tp_moe_workspace_size(T, H, I_shard, E, expert_offsets);
     tp_status st = check_ws(fn, workspace, ws_bytes, need);
     if (st != TP_OK) return st;

@@ -271,6 +271,13 @@ def test_moe_validation(L):
     need = L.tp_moe_workspace_size(4, 64, 32, 2, offs)
     assert need >= 8 * 64 * (2 + 4)
     assert L.tp_moe_workspace_size(4, 64, 32, 2, (ctypes.c_int64 * 3)(0, 5, 2)) == 0
+    # experts of more than 64 rows take the grouped GEMMs: h for every row joins the workspace
+    big = (ctypes.c_int64 * 3)(0, 100, 300)
+    assert L.tp_moe_workspace_size(200, 64, 32, 2, big) >= 300 * 64 * (2 + 4) + 300 * 32 * 2
+    # a grouped launch past 2^28 tiles is refused before anything runs
+    a = list(ok)
+    a[1], a[2], a[4], a[8] = 1 << 30, 8192, 1, (ctypes.c_int64 * 2)(0, 1 << 30)
+    assert _st(f(*a)) == "TP_ERR_UNSUPPORTED"
 
 
 def test_profile_api_without_launches(L):
