@@ -308,6 +308,20 @@ def test_moe_expert_without_rows_and_unrouted_token(tp):
     assert_close_bf16(y, _moe_oracle(inp), "moe with an empty expert")
 
 
+def test_moe_no_dispatched_rows(tp):
+    """No row reaches this rank's experts: every token's partial is exactly zero."""
+    import torch
+    inp = wl.random_moe(12, 20, 64, 32, 4, 2)
+    inp = wl.MoEInputs(inp.name, inp.X, inp.W_gate, inp.W_up, inp.W_down, np.zeros(5, np.int64),
+                       np.zeros(0, np.int32), np.full((20, 2), -1, np.int32), inp.gates)
+    d = _moe_dev(inp)
+    Y = tp.moe_mlp_shard(Y=_nan((20, 64), torch.float32), **d)
+    torch.cuda.synchronize()
+    y = host(Y)
+    assert np.array_equal(y, np.zeros_like(y))
+    assert np.array_equal(y, _moe_oracle(inp))
+
+
 def test_moe_grouped_skewed_many_experts(tp):
     """A skewed load over 37 experts: more than one grouped launch (32 experts each), experts
     of several row tiles with a ragged last one, small and empty experts between them."""
