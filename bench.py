@@ -102,7 +102,7 @@ def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 1
 
 def clock_power(step, seconds: float = 2.5):
     """GPU clock (MHz) and socket power (W) while `step` runs back to back for `seconds`.
-    The driver refreshes its metrics table about once a second, so only readings taken after
+    The amdgpu kernel driver refreshes its metrics table about once a second, so only readings taken after
     a refresh (a new system-clock stamp) while the load runs are kept. None if the amdsmi
     library is missing."""
     try:
