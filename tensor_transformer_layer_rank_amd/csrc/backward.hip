@@ -65,11 +65,15 @@ hipError_t transpose_bf16(const void* in, void* out, int64_t R, int64_t C, hipSt
 
 size_t linear_backward_ws_bytes(int64_t T, int64_t K, int64_t N) {
     const size_t wt = (size_t)(N * K) * 2, xt = (size_t)(K * T) * 2;
-    const size_t a = gemm_bf16_split_bytes(T, K, N, 0), b = gemm_bf16_split_bytes(K, N, T, 0);
     const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    if (N == T) return up(wt) + up(xt) + up(gemm_bf16_pair_split_bytes(T, K, K, N, N));
+    const size_t a = gemm_bf16_split_bytes(T, K, N, 0), b = gemm_bf16_split_bytes(K, N, T, 0);
     return up(wt) + up(xt) + up(a > b ? a : b);
 }
 
+// dX [T, K] = dY [T, N] . W^T [N, K] and dW [K, N] = X^T [K, T] . dY [T, N]. When the two
+// products share their inner size (N == T) they run as one launch, so the tail split fills
+// the machine across both grids (two 176-tile grids on 256 units would each leave 80 idle).
 hipError_t linear_backward(const void* X, const void* W, const void* dY, float* dX, float* dW, int64_t T,
                            int64_t K, int64_t N, void* ws, hipStream_t s) {
     const auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -80,12 +84,15 @@ hipError_t linear_backward(const void* X, const void* W, const void* dY, float* 
     const size_t split_bytes = linear_backward_ws_bytes(T, K, N) - (size_t)(split - base);
     hipError_t e = transpose_bf16(W, wt, K, N, s);
     if (e != hipSuccess) return e;
-    // dX [T, K] = dY [T, N] . W^T [N, K]
+    if (N == T) {
+        e = transpose_bf16(X, xt, T, K, s);
+        if (e != hipSuccess) return e;
+        return gemm_bf16_f32out_pair(dY, wt, dX, T, K, N, K, K, xt, dY, dW, K, N, T, N, N, N, split, split_bytes, s);
+    }
     e = gemm_bf16_store(dY, wt, dX, T, K, N, N, K, K, 2, 0, split, split_bytes, s);
     if (e != hipSuccess) return e;
     e = transpose_bf16(X, xt, T, K, s);
     if (e != hipSuccess) return e;
-    // dW [K, N] = X^T [K, T] . dY [T, N]
     return gemm_bf16_store(xt, dY, dW, K, N, T, T, N, N, 2, 0, split, split_bytes, s);
 }
 

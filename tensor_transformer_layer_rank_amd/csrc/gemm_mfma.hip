@@ -732,10 +732,10 @@ constexpr int FIXUP_WAVES = 1;
 // split plan, the XCD mapping and the fix-up run over the launch's tiles as over one grid.
 constexpr int MAX_GROUPS = 32;
 struct NoGroups {
-    static constexpr bool ON = false;
+    static constexpr int MODE = 0;
 };
 struct Groups {
-    static constexpr bool ON = true;
+    static constexpr int MODE = 1;
     int n;
     int tile0[MAX_GROUPS + 1];
     int64_t row0[MAX_GROUPS + 1];
@@ -767,6 +767,22 @@ struct SplitArgs {
     float* part;   // [tail tiles * pieces][4 waves][256 registers][64 lanes]
 };
 
+// Two independent GEMMs with the same K and epilogue type in one launch (the dX and dW
+// products of a backward step): logical tiles below tiles0 belong to the kernel's own
+// geometry, the rest to (g1, e1). One grid lets the tail split balance both.
+template <bool F8, class Epi>
+struct Pair {
+    static constexpr int MODE = 2;
+    Geom<F8> g1;
+    Epi e1;
+    int tiles_m1, tiles_n1, tiles0;
+    __device__ __forceinline__ bool second(int& L) const {
+        if (L < tiles0) return false;
+        L -= tiles0;
+        return true;
+    }
+};
+
 template <bool F8, bool DUAL, class Epi, class Grp>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
                                                             int tiles_n, SplitArgs sp, Grp gr) {
@@ -786,7 +802,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         q = bid - sp.g_full;
         L = sp.g_full + q / sp.pieces;
     }
-    if constexpr (Grp::ON) {
+    if constexpr (Grp::MODE == 2) {
+        if (gr.second(L)) {
+            g = gr.g1;
+            epi = gr.e1;
+            tiles_m = gr.tiles_m1;
+            tiles_n = gr.tiles_n1;
+        }
+    }
+    if constexpr (Grp::MODE == 1) {
         int64_t r0, m;
         const int e = gr.locate(L, tiles_n, tiles_m, r0, m);
         g.A += r0 * g.lda;
@@ -928,7 +952,14 @@ __global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, i
     const int t = gw >> 4, wave = (gw >> 2) & 3, i = gw & 3;
     const int wm = wave & 1, wn = wave >> 1;
     int L = sp.g_full + t;
-    if constexpr (Grp::ON) {
+    if constexpr (Grp::MODE == 2) {
+        if (gr.second(L)) {
+            epi = gr.e1;
+            tiles_m = gr.tiles_m1;
+            tiles_n = gr.tiles_n1;
+        }
+    }
+    if constexpr (Grp::MODE == 1) {
         int64_t r0, m;
         gr.locate(L, tiles_n, tiles_m, r0, m);
         epi.shift_rows(r0, m);
@@ -1023,7 +1054,8 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
     int64_t tiles_m, tiles_n;
     tiles_of<DUAL>(g.M, g.N, tiles_m, tiles_n);
     int64_t G = tiles_m * tiles_n;
-    if constexpr (Grp::ON) G = gr.tile0[gr.n];
+    if constexpr (Grp::MODE == 1) G = gr.tile0[gr.n];
+    if constexpr (Grp::MODE == 2) G = gr.tiles0 + (int64_t)gr.tiles_m1 * gr.tiles_n1;
     if (G == 0) return hipSuccess;
     const int nk = (int)((g.K + BK - 1) / BK);
     SplitArgs sp = plan_split(G, nk, cu_count());
@@ -1146,6 +1178,30 @@ size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, i
         best = b > best ? b : best;
     }
     return best;
+}
+
+size_t gemm_bf16_pair_split_bytes(int64_t M0, int64_t N0, int64_t M1, int64_t N1, int64_t K) {
+    int64_t tm0, tn0, tm1, tn1;
+    tiles_of<false>(M0, N0, tm0, tn0);
+    tiles_of<false>(M1, N1, tm1, tn1);
+    const int64_t G = tm0 * tn0 + tm1 * tn1;
+    const SplitArgs sp = plan_split(G, (int)((K + Fmt<false>::BK - 1) / Fmt<false>::BK), cu_count());
+    return sp.pieces < 2 ? 0 : (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
+}
+
+hipError_t gemm_bf16_f32out_pair(const void* A0, const void* B0, float* C0, int64_t M0, int64_t N0,
+                                 int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1, const void* B1,
+                                 float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
+                                 int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+    using Epi = EpiStore<2, false>;
+    Geom<false> g0{static_cast<const uint16_t*>(A0), static_cast<const uint16_t*>(B0), nullptr, M0, N0, K, lda0, ldb0};
+    int64_t tm0, tn0, tm1, tn1;
+    tiles_of<false>(M0, N0, tm0, tn0);
+    tiles_of<false>(M1, N1, tm1, tn1);
+    Pair<false, Epi> pr{Geom<false>{static_cast<const uint16_t*>(A1), static_cast<const uint16_t*>(B1), nullptr,
+                                    M1, N1, K, lda1, ldb1},
+                        Epi{C1, ldc1, M1, N1, 1.0f, 1.0f}, (int)tm1, (int)tn1, (int)(tm0 * tn0)};
+    return launch<false, false>(g0, Epi{C0, ldc0, M0, N0, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_f32out", pr);
 }
 
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,

@@ -41,6 +41,12 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
 // Grouped forms (the experts of an MoE layer): group e = rows row_offsets[e] ..
 // row_offsets[e+1]-1 of A and of the output, times weight e ([K, N], weights contiguous);
 // n_groups >= 1, row_offsets non-decreasing from 0.
+// Two fp32-out GEMMs with the same K in one launch (C_i = A_i [M_i, K] . B_i [K, N_i]).
+size_t gemm_bf16_pair_split_bytes(int64_t M0, int64_t N0, int64_t M1, int64_t N1, int64_t K);
+hipError_t gemm_bf16_f32out_pair(const void* A0, const void* B0, float* C0, int64_t M0, int64_t N0,
+                                 int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1, const void* B1,
+                                 float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
+                                 int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, int dual);
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
                                     const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, void* ws,

@@ -194,7 +194,8 @@ def test_merge7b_tp4_full_size_sampled(tp):
 # ---------------------------------------------------------------- backward of a linear shard
 
 # partial tiles in every dimension, T below one 256-row tile, K and N not multiples of 128
-@pytest.mark.parametrize("T,K,N", [(64, 136, 200), (24, 512, 256), (264, 1000, 72), (520, 256, 1032)])
+@pytest.mark.parametrize("T,K,N", [(64, 136, 200), (24, 512, 256), (264, 1000, 72), (520, 256, 1032),
+                                   (200, 136, 200), (2056, 1000, 2056)])   # N == T: one paired launch
 def test_linear_backward_small(tp, T, K, N):
     import torch
     inp = wl.random_backward(T + 3 * K + 7 * N, T, K, N)
