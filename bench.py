@@ -1,23 +1,28 @@
 """Throughput of one tensor-parallel rank's shard on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Headline: the LLaMA-7B MLP shard at TP=4 (X[4096,4096] bf16, gate/up [4096,2752],
 down [2752,4096], fp32 partial out) — one step = one tp_mlp_shard call (fused
 SiLU(gate)*up GEMM + down GEMM). `value` is shard TFLOP/s (2*M*K*N per GEMM, 277.03
-GFLOP per step). Alongside: the 7B TP=2 decode step (attention shard over a 1024-token
-KV cache + MLP shard at 32 tokens + vocabulary-split LM head) in GB/s of compulsory HBM
-bytes, and the same MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8) against the fp8
-MFMA peak, and the step after the merge (tp_merge_rmsnorm: 4 fp32 partials of [8192, 4096]
-summed into the bf16 residual stream, then RMSNorm) against the HBM bandwidth, and the
-backward of the MLP down shard (tp_linear_backward), and a top-2 MoE MLP over 8 local
-experts (tp_moe_mlp_shard, 2048 tokens; TFLOP/s of the expert MLPs). Inputs are
-seeded synthetic tensors already resident in HBM. With --extra the attention shard (B=4,
-S=2048) and the 70B GQA layer shard are timed too.
+GFLOP per step). Every workload of the shard is timed in the same run, each checked
+element by element against the fp64 oracle afterwards, with the oracle's own time on
+this host's cores:
+  c0 the integer fp32 TP=2 MLP, both ranks in turn plus the partial sum (latency, bit-exact);
+  c1 the 7B TP=4 MLP shard (headline);
+  c2 the 7B TP=4 attention shard (B=4, S=2048, 8 heads: QKV + RoPE, flash attention, O);
+  c3 the 70B TP=8 GQA layer shard (attention with 8 q heads / 1 kv head, plus the MLP shard);
+  c4 the 7B TP=2 decode step (attention over a 1024-token KV cache + MLP at 32 tokens +
+     vocabulary-split LM head, one HIP graph) in GB/s of compulsory HBM bytes.
+Beside them: the MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8), the step after the
+merge (tp_merge_rmsnorm), the backward of the MLP down shard (tp_linear_backward) and a
+top-2 MoE MLP over 8 local experts (tp_moe_mlp_shard). Inputs are seeded synthetic tensors
+already resident in HBM when timing starts.
 
-Prints ONE JSON line. Per-kernel durations come from HIP events that libtpshard records
-around each launch on the launch stream during every 10th timed step (the events cost a few
-microseconds per kernel, so they are not recorded on the other steps).
+Prints ONE JSON line. Each leg's timed steps are bracketed by events recorded after every
+step (per-step times come from the timed pass). Per-kernel durations come from HIP events
+that libtpshard records around each launch on the launch stream during every 5th timed
+step (they cost a few microseconds per kernel, so the other steps run without them).
 """
 from __future__ import annotations
 
@@ -41,7 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--extra", action="store_true", help="also time the attention and 70B layer shards")
+    ap.add_argument("--prewarm", type=float, default=1.5,
+                    help="seconds of untimed back-to-back headline steps before the first leg (clock settling)")
+    ap.add_argument("--no-parity", action="store_true", help="skip the element-wise oracle comparison")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
     ap.add_argument("--no-clock", action="store_true",
@@ -53,23 +60,46 @@ def parse():
 
 
 STEP_STATS = {}
+PREWARM = {}
 
 
 def _stats(name: str, per_step_ms):
     xs = sorted(per_step_ms)
     n = len(xs)
     med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
-    STEP_STATS[name] = {"median_ms": med, "min_ms": xs[0], "max_ms": xs[-1]}
+    STEP_STATS[name] = {"median_ms": med, "min_ms": xs[0], "max_ms": xs[-1],
+                        "first_ms": per_step_ms[0], "last_ms": per_step_ms[-1]}
 
 
-def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 10):
-    """Run warmup untimed steps, then time exactly `steps` steps; returns ms per step.
+def prewarm(step, seconds: float):
+    """Run `step` back to back for about `seconds` before anything is timed. From an idle GPU the
+    clock takes far longer than a few short steps to settle (it ramps under load and then falls
+    to what the board's power limit allows), so without this the first timed steps of the first
+    leg run at a different clock than the rest. Untimed; its length is reported."""
+    import torch
+    if seconds <= 0:
+        return 0
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+    return n
 
-    Only two events bracket the timed steps. libtpshard's per-kernel HIP events (which add a
-    few microseconds per kernel) are switched on for every `sample_every`-th timed step only,
-    so the kernel averages come from inside the timed region at a cost of ~1% of it. If
-    `name` is given, a second pass of `steps` steps with one event per step gives the per-step
-    median / min / max (STEP_STATS[name])."""
+
+def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 5, keep_steps: bool = False):
+    """Run `warmup` untimed steps, then time exactly `steps` steps; returns ms per step.
+
+    The timed region is bracketed by the first and last of steps+1 events, one recorded after
+    each step, so the per-step times come from the timed pass itself (STEP_STATS[name]; the whole
+    list when keep_steps). libtpshard's per-kernel HIP events (a few microseconds per kernel) are
+    switched on for every `sample_every`-th timed step only, starting with the step after the
+    first, so the kernel averages come from inside the timed region."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     for _ in range(warmup):
@@ -77,27 +107,29 @@ def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 1
     torch.cuda.synchronize()
     tp.profile_reset()
     s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(s)
     for i in range(steps):
-        sampled = i % sample_every == 0
+        sampled = i % sample_every == sample_every - 1 or (steps < sample_every and i == steps - 1)
         if sampled:
             tp.profile_enable(True)
         step()
         if sampled:
             tp.profile_enable(False)
-    e1.record(s)
+        ev[i + 1].record(s)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     if name:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record(s)
-        for i in range(steps):
-            step()
-            ev[i + 1].record(s)
-        torch.cuda.synchronize()
-        _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+        _stats(name, per)
+        if keep_steps:
+            STEP_STATS[name]["per_step_ms"] = [round(x, 5) for x in per]
     return ms
+
+
+def sampled_steps(steps: int, sample_every: int = 5) -> int:
+    n = sum(1 for i in range(steps) if i % sample_every == sample_every - 1)
+    return n if n else 1
 
 
 def clock_power(step, seconds: float = 2.5):
@@ -153,21 +185,66 @@ def kernel_avg(prefix: str):
     return (ms / n if n else None), n
 
 
+def _dev(a, dtype="bf16"):
+    from workloads.device import to_device
+    return to_device(a, dtype)
+
+
+def _host(t):
+    from workloads.device import to_host
+    return to_host(t)
+
+
+# ---------------------------------------------------------------------------- c0
+
+def int_mlp_bench(args):
+    """c0: the integer fp32 TP=2 MLP, both ranks in turn (column + ReLU, row partial), then the
+    partial sum; latency-bound, reported in microseconds per step."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    inp = wl.mlp_relu_tp2()
+    X = _dev(inp.X, "f32")
+    # rank r holds columns r*128.. of W1 and rows r*128.. of W2
+    W1 = [_dev(inp.W_gate[:, r * 128:(r + 1) * 128], "f32") for r in range(2)]
+    W2 = [_dev(inp.W_down[r * 128:(r + 1) * 128, :], "f32") for r in range(2)]
+    H = [torch.empty((16, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+    P = [torch.empty((16, 64), dtype=torch.float32, device="cuda") for _ in range(2)]
+    Y = torch.empty((16, 64), dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(2):
+            tp.column_linear(X, W1[r], Y=H[r], act=tp.TP_ACT_RELU)
+            tp.row_linear_partial(H[r], W2[r], Y=P[r])
+        tp.partial_sum(P, out=Y)
+
+    ms = timed(step, args.warmup, args.steps, "c0")
+    return {"workload": "mlp_relu_tp2: integer fp32 MLP, X[16,64], W1[64,256] column-split into 2x[64,128] + ReLU, "
+                        "W2[256,64] row-split into 2x[128,64]; both ranks in turn, then tp_partial_sum (5 launches)",
+            "us_per_step": ms * 1e3, "flops_per_step": 2.0 * 16 * 64 * 256 * 2,
+            "step_stats": STEP_STATS.get("c0")}, {"inp": inp, "Y": Y}
+
+
+# ---------------------------------------------------------------------------- c1
+
 def mlp_bench(args):
     import torch
     import tensor_transformer_layer_rank_amd as tp
     import workloads as wl
-    from tests._util import dev
     inp = wl.mlp7b_tp4()
     T, H, I = inp.T, inp.H, inp.I
-    X, Wg, Wu, Wd = dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down)
+    X, Wg, Wu, Wd = _dev(inp.X), _dev(inp.W_gate), _dev(inp.W_up), _dev(inp.W_down)
     Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
 
     def step():
         tp.mlp_shard(X, Wg, Wu, Wd, Y=Y, workspace=ws)
 
-    ms = timed(step, args.warmup, args.steps, "mlp")
+    t0 = time.perf_counter()
+    n_pre = prewarm(step, args.prewarm)
+    PREWARM.update({"seconds": round(time.perf_counter() - t0, 3), "steps": n_pre,
+                    "what": "untimed back-to-back headline steps before any timing (clock settling)"})
+    ms = timed(step, args.warmup, args.steps, "mlp", keep_steps=True)
     gu_ms, gu_n = kernel_avg("gemm_bf16_swiglu")
     fx_ms, fx_n = kernel_avg("fixup_swiglu")
     dn_ms, dn_n = kernel_avg("gemm_bf16_f32out")
@@ -199,18 +276,185 @@ def mlp_bench(args):
             "traffic": recorded_traffic("gemm_bf16_swiglu"),
         },
     }
-    return res, inp
+    return res, {"inp": inp, "Y": Y}
 
+
+# ---------------------------------------------------------------------------- c2, c3
+
+def attn_bench(args, name):
+    """c2 (attn7b_tp4) or c3 (layer70b_tp8: the attention shard and the MLP shard on the same X,
+    two fp32 partials)."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    inp = wl.WORKLOADS[name]()
+    B, S, H, hq, hkv = inp.B, inp.S, inp.H, inp.hq, inp.hkv
+    X, Wqkv, Wo = _dev(inp.X), _dev(inp.W_qkv), _dev(inp.W_o)
+    T = B * S
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.attn_workspace_size(B, S, H, hq, hkv, inp.theta), dtype=torch.uint8, device="cuda")
+    mlp = None
+    if inp.mlp is not None:
+        m = inp.mlp
+        I = m.W_gate.shape[1]
+        mlp = (_dev(m.W_gate), _dev(m.W_up), _dev(m.W_down),
+               torch.empty((T, H), dtype=torch.float32, device="cuda"),
+               torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8,
+                           device="cuda"))
+
+    def step():
+        tp.attn_shard(X, Wqkv, Wo, B, S, hq, hkv, inp.theta, Y=Y, workspace=ws)
+        if mlp:
+            tp.mlp_shard(X, mlp[0], mlp[1], mlp[2], Y=mlp[3], workspace=mlp[4])
+
+    ms = timed(step, args.warmup, args.steps, name)
+    d = 128
+    f_qkv = 2.0 * T * H * (hq + 2 * hkv) * d
+    f_att = 2.0 * 2 * d * B * hq * S * (S + 1) / 2      # causal triangle only: QK^T and PV
+    f_o = 2.0 * T * hq * d * H
+    f_mlp = 0.0
+    if inp.mlp is not None:
+        f_mlp = 2.0 * T * H * inp.mlp.W_gate.shape[1] * 3
+    flops = f_qkv + f_att + f_o + f_mlp
+    nsamp = sampled_steps(args.steps)
+    kern = {}
+    for kname, f in (("gemm_bf16_qkv_rope", f_qkv), ("flash_attn_fwd", f_att), ("gemm_bf16_swiglu", None),
+                     ("gemm_bf16_f32out", None), ("fixup_gemm", None), ("fixup_swiglu", None), ("rope_table", None)):
+        k_ms, k_n = kernel_avg(kname)
+        if k_n:
+            kern[kname] = {"avg_us": k_ms * 1e3, "launches_per_step": k_n / nsamp}
+            if f:
+                kern[kname]["tflops"] = f / (k_ms * 1e-3) / 1e12
+    out = {"workload": inp.name, "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+           "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "flops_per_step": flops,
+           "flops": {"qkv": f_qkv, "attention_causal": f_att, "o": f_o, "mlp": f_mlp},
+           "step_stats": STEP_STATS.get(name), "kernels": kern}
+    return out, {"inp": inp, "Y": Y, "Ym": mlp[3] if mlp else None}
+
+
+# ---------------------------------------------------------------------------- c4
+
+def graph_timed(step, warmup: int, steps: int, name: str = None):
+    """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays, one event
+    after each replay (per-replay times: STEP_STATS[name]). Returns (ms per replay, graph)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # eager run on the capture stream first
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    if name:
+        _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return ms, g
+
+
+def decode_bench(args):
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    import workloads as wl
+    inp = wl.decode7b_tp2()
+    B, H, hq, hkv, L = inp.B, inp.H, inp.hq, inp.hkv, inp.cache_len + 1
+    X = _dev(inp.X)
+    Wqkv, Wo, Wg, Wu, Wd, Wlm = (_dev(w) for w in (inp.W_qkv, inp.W_o, inp.W_gate, inp.W_up, inp.W_down, inp.W_lm))
+    kc, vc = _dev(inp.k_cache), _dev(inp.v_cache)
+    I, V = inp.W_gate.shape[1], inp.W_lm.shape[1]
+    Ya = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    Ym = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
+    ws_a = torch.empty(tp.attn_workspace_size(B, 1, H, hq, hkv, inp.theta, kc, vc, inp.cache_len),
+                       dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(tp.mlp_workspace_size(B, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+    ws_l = torch.empty(tp.linear_workspace_size(B, H, V, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        tp.attn_shard(X, Wqkv, Wo, B, 1, hq, hkv, inp.theta, k_cache=kc, v_cache=vc,
+                      cache_len=inp.cache_len, Y=Ya, workspace=ws_a)
+        tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
+        tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
+
+    # the three parts are independent: in the graph they are branches on their own streams
+    # (default priority), joined at the end of the step
+    s_attn, s_mlp = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def step_branches():
+        cur = torch.cuda.current_stream()
+        s_attn.wait_stream(cur)
+        s_mlp.wait_stream(cur)
+        with torch.cuda.stream(s_attn):
+            tp.attn_shard(X, Wqkv, Wo, B, 1, hq, hkv, inp.theta, k_cache=kc, v_cache=vc,
+                          cache_len=inp.cache_len, Y=Ya, workspace=ws_a)
+        with torch.cuda.stream(s_mlp):
+            tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
+        tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
+        cur.wait_stream(s_attn)
+        cur.wait_stream(s_mlp)
+
+    outs = (Ya, Ym, logits)
+    ms_eager = timed(step, args.warmup, args.steps)       # per-kernel HIP-event timing
+    eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
+    ms_serial, _ = graph_timed(step, args.warmup, args.steps)
+    for t in outs:
+        t.fill_(float("nan"))
+    ms, _ = graph_timed(step_branches, args.warmup, args.steps, "decode")   # the step as one HIP graph
+    torch.cuda.synchronize()
+    # the outputs left by the last timed replay must equal the eager step's, bit for bit
+    replay = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
+    same = all(a.tobytes() == b.tobytes() for a, b in zip(eager, replay))
+    d = 128
+    w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
+    kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
+    new_kv = 2 * 2 * B * hkv * d                       # the new key/value written (and read back)
+    act = 2 * B * H + 4 * (2 * B * H + B * V)          # X in; two fp32 partials and the logits out
+    total = w_bytes + kv_bytes + 2 * new_kv + act
+    att_ms, att_n = kernel_avg("decode_attn")
+    sk_ms, sk_n = kernel_avg("skinny_gemm")
+    rd_ms, rd_n = kernel_avg("skinny_reduce")
+    nsamp = sampled_steps(args.steps)
+    return {
+        "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "ms_per_step_graph_serial": ms_serial,
+        "step_stats": STEP_STATS.get("decode"),
+        "graph": "one HIP graph per step: attention, MLP and LM-head branches on separate streams",
+        "graph_outputs_equal_eager": same,
+        "bytes_per_step": total,
+        "gbs": total / (ms * 1e-3) / 1e9,
+        "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
+                    "skinny_gemm*(avg_us)": sk_ms * 1e3 if sk_ms else None,
+                    "skinny_gemm*(launches/step)": sk_n / nsamp,
+                    "skinny_reduce*(avg_us)": rd_ms * 1e3 if rd_ms else None,
+                    "skinny_reduce*(launches/step)": rd_n / nsamp},
+        "workload": "decode7b_tp2: B=32 one token each, 16 local heads (MHA), KV cache 1024 tokens, "
+                    "H=4096, I_shard=5504, LM head [4096,16000]",
+    }, {"inp": inp, "eager": eager}
+
+
+# ---------------------------------------------------------------------------- other legs
 
 def fp8_mlp_bench(args):
     """The same MLP shard on OCP E4M3 codes with per-tensor scales (tp_mlp_shard_fp8)."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     import workloads as wl
-    from tests._util import dev_codes
+    from workloads.device import codes_to_device
     inp = wl.mlp7b_tp4_fp8()
     T, H, I = inp.T, inp.H, inp.I
-    X, Wg, Wu, Wd = (dev_codes(a) for a in (inp.X, inp.W_gate, inp.W_up, inp.W_down))
+    X, Wg, Wu, Wd = (codes_to_device(a) for a in (inp.X, inp.W_gate, inp.W_up, inp.W_down))
     Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.mlp_fp8_workspace_size(T, H, I, tp.TP_MLP_SWIGLU), dtype=torch.uint8, device="cuda")
     scales = (inp.x_scale, inp.wg_scale, inp.wu_scale, inp.wd_scale, inp.h_scale)
@@ -249,11 +493,10 @@ def merge_bench(args):
     import torch
     import tensor_transformer_layer_rank_amd as tp
     import workloads as wl
-    from tests._util import dev
     inp = wl.merge7b_tp4()
     T, H, k = inp.T, inp.H, len(inp.partials)
-    parts = [dev(p, "f32") for p in inp.partials]
-    res, gamma = dev(inp.residual), dev(inp.gamma)
+    parts = [_dev(p, "f32") for p in inp.partials]
+    res, gamma = _dev(inp.residual), _dev(inp.gamma)
     R = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     N = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
 
@@ -276,16 +519,14 @@ def merge_bench(args):
 
 
 def backward_bench(args):
-    """Backward of the 7B TP=4 MLP down shard (tp_linear_backward: dX = dY.W^T, dW = X^T.dY
-    after the bf16 transposes of W and X)."""
+    """Backward of the 7B TP=4 MLP down shard (tp_linear_backward: dX = dY.W^T, dW = X^T.dY)."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     import workloads as wl
-    from tests._util import dev
     inp = wl.backward7b_tp4()
     T, K = inp.X.shape
     N = inp.W.shape[1]
-    X, W, dY = dev(inp.X), dev(inp.W), dev(inp.dY)
+    X, W, dY = _dev(inp.X), _dev(inp.W), _dev(inp.dY)
     dX = torch.empty((T, K), dtype=torch.float32, device="cuda")
     dW = torch.empty((K, N), dtype=torch.float32, device="cuda")
     ws = torch.empty(tp.linear_backward_workspace_size(T, K, N), dtype=torch.uint8, device="cuda")
@@ -295,41 +536,40 @@ def backward_bench(args):
 
     ms = timed(step, args.warmup, args.steps, "backward")
     flops = 4.0 * T * K * N
-    g_ms, g_n = kernel_avg("gemm_bf16_f32out")
-    t_ms, t_n = kernel_avg("transpose_bf16")
-    fx_ms, fx_n = kernel_avg("fixup_gemm")
-    g_ms, t_ms, fx_ms = g_ms or 0.0, t_ms or 0.0, fx_ms or 0.0
-    sampled = len(range(0, args.steps, 10))
-    gemm_ms = (g_ms * g_n + fx_ms * fx_n) / sampled       # both products (one paired launch when N == T)
-    gemm_tf = flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    nsamp = sampled_steps(args.steps)
+    kern = {}
+    gemm_ms = 0.0
+    for name in ("gemm_bf16_f32out", "fixup_gemm", "transpose_bf16"):
+        k_ms, k_n = kernel_avg(name)
+        if k_n:
+            kern[name] = {"avg_us": k_ms * 1e3, "launches_per_step": k_n / nsamp}
+            if name != "transpose_bf16":
+                gemm_ms += k_ms * k_n / nsamp
     return {
         "workload": "backward7b_tp4: X = h [4096,2752], W_down shard [2752,4096], dY [4096,4096] bf16 -> dX, dW fp32",
         "ms_per_step": ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "step_stats": STEP_STATS.get("backward"),
-        "kernels": {"gemm (dX and dW per step, incl. tail fix-up)": {"us_per_step": gemm_ms * 1e3,
-                                                                    "launches_per_step": g_n / sampled,
-                                                                    "tflops": gemm_tf},
-                    "transpose_bf16 (W, X)": {"avg_us": t_ms * 1e3, "launches_per_step": t_n / sampled}},
+        "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+        "kernels": kern,
     }
 
 
 def moe_bench(args):
     """Top-2 MoE MLP on one rank (tp_moe_mlp_shard): 2048 tokens, 8 local experts whose SwiGLU
-    MLPs are TP=4 shards (H 4096, I 3584); gather, per-expert gate/up + down, gated combine."""
+    MLPs are TP=4 shards (H 4096, I 3584); gather, grouped gate/up + down, gated combine."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     import workloads as wl
-    from tests._util import dev
     inp = wl.moe8x7b_tp4()
     T, H = inp.X.shape
     I = inp.W_gate.shape[2]
     R = int(inp.expert_offsets[-1])
-    X, Wg, Wu, Wd = dev(inp.X), dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down)
+    X, Wg, Wu, Wd = _dev(inp.X), _dev(inp.W_gate), _dev(inp.W_up), _dev(inp.W_down)
     rt = torch.from_numpy(inp.row_token.copy()).cuda()
     tr = torch.from_numpy(inp.token_rows.copy()).cuda()
-    gates = dev(inp.gates, "f32")
+    gates = _dev(inp.gates, "f32")
     Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(tp.moe_workspace_size(T, H, I, inp.expert_offsets), 1), dtype=torch.uint8, device="cuda")
 
@@ -338,12 +578,13 @@ def moe_bench(args):
 
     ms = timed(step, args.warmup, args.steps, "moe")
     flops = 6.0 * R * H * I
+    nsamp = sampled_steps(args.steps)
     kern = {}
     for name in ("moe_gather", "gemm_bf16_swiglu", "fixup_swiglu", "gemm_bf16_f32out", "fixup_gemm",
                  "skinny", "moe_combine"):
         k_ms, k_n = kernel_avg(name)
         if k_n:
-            kern[name] = {"avg_us": k_ms * 1e3, "launches_per_step": k_n / len(range(0, args.steps, 10))}
+            kern[name] = {"avg_us": k_ms * 1e3, "launches_per_step": k_n / nsamp}
     return {
         "workload": f"moe8x7b_tp4: T={T} tokens, top-2 of 8 experts ({R} dispatched rows), "
                     f"expert shards gate/up [{H},{I}], down [{I},{H}] bf16 -> fp32 partial",
@@ -354,153 +595,6 @@ def moe_bench(args):
         "step_stats": STEP_STATS.get("moe"),
         "kernels": kern,
     }
-
-
-def graph_timed(step, warmup: int, steps: int, name: str = None):
-    """Capture one step into a HIP graph (torch.cuda.CUDAGraph) and time `steps` replays
-    between two events; a second pass with one event per replay gives the per-replay median
-    and minimum (STEP_STATS[name])."""
-    import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()                                   # eager run on the capture stream first
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    if name:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        ev[0].record()
-        for i in range(steps):
-            g.replay()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        _stats(name, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-    return ms
-
-
-def decode_bench(args):
-    import torch
-    import tensor_transformer_layer_rank_amd as tp
-    import workloads as wl
-    from tests._util import dev
-    inp = wl.decode7b_tp2()
-    B, H, hq, hkv, L = inp.B, inp.H, inp.hq, inp.hkv, inp.cache_len + 1
-    X = dev(inp.X)
-    Wqkv, Wo, Wg, Wu, Wd, Wlm = (dev(w) for w in (inp.W_qkv, inp.W_o, inp.W_gate, inp.W_up, inp.W_down, inp.W_lm))
-    kc, vc = dev(inp.k_cache), dev(inp.v_cache)
-    I, V = inp.W_gate.shape[1], inp.W_lm.shape[1]
-    Ya = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    Ym = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    logits = torch.empty((B, V), dtype=torch.float32, device="cuda")
-    ws_a = torch.empty(tp.attn_workspace_size(B, 1, H, hq, hkv, inp.theta, kc, vc, inp.cache_len),
-                       dtype=torch.uint8, device="cuda")
-    ws_m = torch.empty(tp.mlp_workspace_size(B, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
-    ws_l = torch.empty(tp.linear_workspace_size(B, H, V, tp.TP_BF16), dtype=torch.uint8, device="cuda")
-
-    def step():
-        tp.attn_shard(X, Wqkv, Wo, B, 1, hq, hkv, inp.theta, k_cache=kc, v_cache=vc,
-                      cache_len=inp.cache_len, Y=Ya, workspace=ws_a)
-        tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
-        tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
-
-    # the three parts are independent: in the graph they are branches on their own streams
-    # (default priority), joined at the end of the step
-    s_attn, s_mlp = torch.cuda.Stream(), torch.cuda.Stream()
-
-    def step_branches():
-        cur = torch.cuda.current_stream()
-        s_attn.wait_stream(cur)
-        s_mlp.wait_stream(cur)
-        with torch.cuda.stream(s_attn):
-            tp.attn_shard(X, Wqkv, Wo, B, 1, hq, hkv, inp.theta, k_cache=kc, v_cache=vc,
-                          cache_len=inp.cache_len, Y=Ya, workspace=ws_a)
-        with torch.cuda.stream(s_mlp):
-            tp.mlp_shard(X, Wg, Wu, Wd, Y=Ym, workspace=ws_m)
-        tp.column_linear(X, Wlm, Y=logits, workspace=ws_l)
-        cur.wait_stream(s_attn)
-        cur.wait_stream(s_mlp)
-
-    ms_eager = timed(step, args.warmup, args.steps)       # per-kernel HIP-event timing
-    ms_serial = graph_timed(step, args.warmup, args.steps)
-    ms = graph_timed(step_branches, args.warmup, args.steps, "decode")   # the step as one HIP graph
-    d = 128
-    w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
-    kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
-    new_kv = 2 * 2 * B * hkv * d                       # the new key/value written (and read back)
-    act = 2 * B * H + 4 * (2 * B * H + B * V)          # X in; two fp32 partials and the logits out
-    total = w_bytes + kv_bytes + 2 * new_kv + act
-    att_ms, att_n = kernel_avg("decode_attn")
-    sk_ms, sk_n = kernel_avg("skinny_gemm")
-    return {
-        "ms_per_step": ms,
-        "ms_per_step_eager": ms_eager,
-        "ms_per_step_graph_serial": ms_serial,
-        "step_stats": STEP_STATS.get("decode"),
-        "graph": "one HIP graph per step: attention, MLP and LM-head branches on separate streams",
-        "bytes_per_step": total,
-        "gbs": total / (ms * 1e-3) / 1e9,
-        "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
-                    "skinny_gemm*(avg_us)": sk_ms * 1e3 if sk_ms else None,
-                    "skinny_gemm*(launches/step)": sk_n / max(-(-args.steps // 10), 1)},
-        "workload": "decode7b_tp2: B=32 one token each, 16 local heads (MHA), KV cache 1024 tokens, "
-                    "H=4096, I_shard=5504, LM head [4096,16000]",
-    }
-
-
-def attn_bench(args, name):
-    import torch
-    import tensor_transformer_layer_rank_amd as tp
-    import workloads as wl
-    from tests._util import dev
-    inp = wl.WORKLOADS[name]()
-    B, S, H, hq, hkv = inp.B, inp.S, inp.H, inp.hq, inp.hkv
-    X, Wqkv, Wo = dev(inp.X), dev(inp.W_qkv), dev(inp.W_o)
-    T = B * S
-    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(tp.attn_workspace_size(B, S, H, hq, hkv, inp.theta), dtype=torch.uint8, device="cuda")
-    mlp = None
-    if inp.mlp is not None:
-        m = inp.mlp
-        I = m.W_gate.shape[1]
-        mlp = (dev(m.W_gate), dev(m.W_up), dev(m.W_down),
-               torch.empty((T, H), dtype=torch.float32, device="cuda"),
-               torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda"))
-
-    def step():
-        tp.attn_shard(X, Wqkv, Wo, B, S, hq, hkv, inp.theta, Y=Y, workspace=ws)
-        if mlp:
-            tp.mlp_shard(X, mlp[0], mlp[1], mlp[2], Y=mlp[3], workspace=mlp[4])
-
-    ms = timed(step, max(2, args.warmup // 2), max(5, args.steps // 2))
-    d = 128
-    f_qkv = 2.0 * T * H * (hq + 2 * hkv) * d
-    f_att = 2.0 * 2 * d * B * hq * S * (S + 1) / 2      # causal triangle only: QK^T and PV
-    f_o = 2.0 * T * hq * d * H
-    f_mlp = 0.0
-    if inp.mlp is not None:
-        I = inp.mlp.W_gate.shape[1]
-        f_mlp = 2.0 * T * H * I * 3
-    flops = f_qkv + f_att + f_o + f_mlp
-    fa_ms, _ = kernel_avg("flash_attn_fwd")
-    q_ms, _ = kernel_avg("gemm_bf16_qkv_rope")
-    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-            "frac_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "flash_attn_tflops": f_att / (fa_ms * 1e-3) / 1e12 if fa_ms else None,
-            "qkv_rope_tflops": f_qkv / (q_ms * 1e-3) / 1e12 if q_ms else None}
 
 
 def traffic_probe():
@@ -528,8 +622,82 @@ def recorded_traffic(kernel: str):
         return None
 
 
+# ---------------------------------------------------------------------------- parity + CPU oracle
+
+def _cmp(got, ref, out="f32"):
+    """relF, max-abs, and max-abs past half an ulp of the stored value (bf16 outputs)."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = np.abs(got - ref)
+    half_ulp = {"f32": 0.0, "bf16": 2.0 ** -8}[out]
+    rf = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    return {"relF": rf, "max_abs": float(diff.max()),
+            "max_abs_past_storage_rounding": float((diff - half_ulp * np.abs(ref)).max()),
+            "elements": int(got.size), "finite": bool(np.all(np.isfinite(got))),
+            "pass": bool(np.all(np.isfinite(got)) and rf <= 5e-3 and float((diff - half_ulp * np.abs(ref)).max()) <= 3e-2)}
+
+
+def cpu_oracle_leg(keep):
+    """The CPU baseline leg, per workload: the fp64 oracle computes each workload's whole output
+    on this host's cores (its wall time is reported as that workload's CPU baseline), and every
+    element of the GPU's output (as left by its timed steps) is compared with it. Runs after all
+    GPU timing."""
+    import numpy as np
+    import oracle as O
+    res = {}
+    if "c0" in keep:
+        k = keep["c0"]
+        inp = k["inp"]
+        t0 = time.perf_counter()
+        refs = [O.mlp_relu_shard(inp.X, O.column_shard(inp.W_gate, r, 2), O.row_shard(inp.W_down, r, 2))
+                for r in range(2)]
+        ref = O.partial_sum(refs)
+        dt = time.perf_counter() - t0
+        got = _host(k["Y"])
+        res["c0"] = {"bit_exact": bool(np.array_equal(got, ref)), "oracle_s": dt, "elements": int(got.size)}
+    if "c1" in keep:
+        k = keep["c1"]
+        inp = k["inp"]
+        t0 = time.perf_counter()
+        ref = O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down)
+        dt = time.perf_counter() - t0
+        res["c1"] = {**_cmp(_host(k["Y"]), ref), "oracle_s": dt}
+    for c in ("c2", "c3"):
+        if c not in keep:
+            continue
+        k = keep[c]
+        inp = k["inp"]
+        t0 = time.perf_counter()
+        ref = O.attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.B, inp.S, inp.hq, inp.hkv, inp.d, inp.theta)
+        dt = time.perf_counter() - t0
+        r = {"attention": {**_cmp(_host(k["Y"]), ref), "oracle_s": dt}}
+        del ref
+        if k["Ym"] is not None:
+            m = inp.mlp
+            t0 = time.perf_counter()
+            ref = O.mlp_swiglu_shard(m.X, m.W_gate, m.W_up, m.W_down)
+            dt = time.perf_counter() - t0
+            r["mlp"] = {**_cmp(_host(k["Ym"]), ref), "oracle_s": dt}
+            del ref
+        res[c] = r
+    if "c4" in keep:
+        k = keep["c4"]
+        inp = k["inp"]
+        ya, ym, lg, kn = k["eager"]
+        t0 = time.perf_counter()
+        att, knew, _ = O.decode_attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.k_cache, inp.v_cache, inp.cache_len,
+                                           inp.hq, inp.hkv, inp.d, inp.theta)
+        mlp = O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down)
+        lm = O.lm_head_shard(inp.X, inp.W_lm)
+        dt = time.perf_counter() - t0
+        res["c4"] = {"attention": _cmp(ya, att), "mlp": _cmp(ym, mlp), "logits": _cmp(lg, lm),
+                     "appended_keys": _cmp(kn, knew, "bf16"), "oracle_s": dt}
+    return res
+
+
 def cpu_baseline(inp, target_s: float):
-    """The fp64 oracle on a row sample of the same MLP shard, on this host's cores."""
+    """The fp64 oracle on the same MLP shard (c1), on this host's cores, repeated to about target_s."""
     import numpy as np
     import oracle as O
     rows0 = 32
@@ -573,6 +741,16 @@ def cpu_baseline(inp, target_s: float):
             "seconds": dt}
 
 
+def _round(x, nd=5):
+    if isinstance(x, float):
+        return round(x, nd)
+    if isinstance(x, dict):
+        return {k: _round(v, nd) for k, v in x.items()}
+    if isinstance(x, list):
+        return [_round(v, nd) for v in x]
+    return x
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -586,20 +764,31 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     tp.load()
-    mlp, inp = mlp_bench(args)
-    dec = decode_bench(args)
+    keep = {}
+    mlp, keep["c1"] = mlp_bench(args)            # headline first, after the clock-settling prewarm
+    c0, keep["c0"] = int_mlp_bench(args)
+    c2, keep["c2"] = attn_bench(args, "attn7b_tp4")
+    c3, keep["c3"] = attn_bench(args, "layer70b_tp8")
+    dec, keep["c4"] = decode_bench(args)
     fp8 = fp8_mlp_bench(args)
     merge = merge_bench(args)
     bwd = backward_bench(args)
     moe = moe_bench(args)
-    extra = {}
-    if args.extra:
-        extra["attn7b_tp4"] = attn_bench(args, "attn7b_tp4")
-        extra["layer70b_tp8"] = attn_bench(args, "layer70b_tp8")
     if args.traffic_probe:
         traffic_probe()
-    cpu = None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds)
+    torch.cuda.synchronize()
+    par = None if args.no_parity else cpu_oracle_leg(keep)
+    cpu = None if args.no_cpu else cpu_baseline(keep["c1"]["inp"], args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
+    c1 = {"workload": "mlp7b_tp4", "ms_per_step": mlp["ms_per_step"], "tflops": mlp["tflops"],
+          "frac_bf16_peak": mlp["tflops"] / PEAK_BF16_TFLOPS}
+    configs = {"c0_mlp_relu_tp2": c0, "c1_mlp7b_tp4": c1, "c2_attn7b_tp4": c2, "c3_layer70b_tp8": c3,
+               "c4_decode7b_tp2": {k: dec[k] for k in ("ms_per_step", "gbs", "frac_hbm", "graph_outputs_equal_eager")}}
+    if par:
+        for key, c in (("c0_mlp_relu_tp2", "c0"), ("c1_mlp7b_tp4", "c1"), ("c2_attn7b_tp4", "c2"),
+                       ("c3_layer70b_tp8", "c3"), ("c4_decode7b_tp2", "c4")):
+            if c in par:
+                configs[key]["parity"] = par[c]
     out = {
         "metric": "shard TFLOP/s (+% bf16 MFMA peak) for 7B TP=4 MLP; decode GB/s (%HBM)",
         "value": round(mlp["tflops"], 2),
@@ -621,19 +810,20 @@ def main():
                    "decode_ms_per_step": round(dec["ms_per_step"], 5)},
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in mlp["roofline"].items()},
         "cpu_baseline": cpu and {k: v for k, v in cpu.items() if k != "seconds"},
+        "prewarm": PREWARM,
         "step_stats": mlp["step_stats"],
         "clock_power": mlp["clock_power"],
         "kernels": mlp["kernels"],
+        "configs": configs,
         "decode": dec,
         "fp8_mlp": fp8,
         "merge_rmsnorm": merge,
         "backward": bwd,
         "moe": moe,
-        "extra": extra or None,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},
     }
-    print(json.dumps(out))
+    print(json.dumps(_round(out)))
 
 
 if __name__ == "__main__":

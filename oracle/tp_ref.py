@@ -15,10 +15,11 @@ Conventions (the readings of the pages that everything below follows):
   注意力模块).
 * Activations are ``[T, H]`` with T = B*S tokens, sequence-major.
 * A fused QKV shard holds whole heads: columns [Q_0..Q_{hq-1} | K_0..K_{hkv-1} |
-  V_0..V_{hkv-1}], ``d`` contiguous columns per head ("每个设备持有若干完整头",
-  自注意力块切分).
+  V_0..V_{hkv-1}], ``d`` contiguous columns per head (each rank keeps whole heads:
+  "张量并行：切分 Transformer 层的分布式训练", 自注意力块切分).
 * Grouped queries: q head j reads kv head floor(j*hkv/hq).
-* Attention is scaled dot-product with scale 1/sqrt(d) ("缩放点积"), causal within
+* Attention is scaled dot-product with scale 1/sqrt(d) (the page names the scaling but
+  prints no constant), causal within
   a sequence (key position <= query position), no attention across sequences.
 * Rotary embedding (not described on the pages; the rotary base comes with the
   workload): rotate-half pairs (i, i + d/2) with angle pos * theta^(-2i/d), applied

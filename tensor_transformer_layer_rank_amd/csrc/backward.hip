@@ -54,7 +54,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 }
 
 hipError_t transpose_bf16(const void* in, void* out, int64_t R, int64_t C, hipStream_t s) {
-    const int64_t tiles_c = (C + 63) / 64, tiles = tiles_c * ((R + 63) / 64);   // < 2^32 for R, C < 2^23
+    // 64x64 tiles of 256 threads: the caller keeps tiles below 2^24, so the grid's thread
+    // count (tiles * 256) stays below 2^32
+    const int64_t tiles_c = (C + 63) / 64, tiles = tiles_c * ((R + 63) / 64);
     ProfScope ps("transpose_bf16", s);
     transpose_bf16_kernel<<<(unsigned)tiles, 256, 0, s>>>(static_cast<const uint16_t*>(in),
                                                           static_cast<uint16_t*>(out), R, C, tiles_c);

@@ -19,7 +19,8 @@ def test_step_statistics_helper():
     sys.path.insert(0, ROOT)
     import bench
     bench._stats("t", [3.0, 1.0, 2.0, 4.0])
-    assert bench.STEP_STATS["t"] == {"median_ms": 2.5, "min_ms": 1.0, "max_ms": 4.0}
+    assert bench.STEP_STATS["t"] == {"median_ms": 2.5, "min_ms": 1.0, "max_ms": 4.0, "first_ms": 3.0,
+                                     "last_ms": 4.0}
     bench._stats("u", [5.0, 1.0, 3.0])
     assert bench.STEP_STATS["u"]["median_ms"] == 3.0
 
@@ -34,3 +35,14 @@ def test_recorded_traffic_tracks_the_kernel_source():
         assert os.path.exists(os.path.join(ROOT, r["source"]))
         got = bench.recorded_traffic(name)
         assert got is None or abs(got - r["bytes_per_launch"]) < 1.0
+
+
+def test_sampled_steps_counts_the_kernel_timed_steps():
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.sampled_steps(20) == 4 and bench.sampled_steps(100) == 20 and bench.sampled_steps(3) == 1
+
+
+def test_bench_does_not_import_the_tests():
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert "tests._util" not in src and "from tests" not in src

@@ -17,7 +17,7 @@ import pytest
 
 import oracle as O
 import workloads as wl
-from tests._util import assert_close_bf16, dev_codes, host, sample_rows
+from tests._util import assert_close_bf16, dev_codes, host
 
 pytestmark = pytest.mark.gpu
 
@@ -139,10 +139,10 @@ def test_fp8_mlp(tp, T, H, I, kind):
     assert_close_bf16(got, ref, f"fp8 mlp {kind} {T}x{H}x{I}")
 
 
-def test_mlp7b_tp4_fp8_full_size_sampled(tp):
-    """mlp7b_tp4's shapes on E4M3 codes: X[4096,4096], gate/up [4096,2752], down [2752,4096]."""
+def test_mlp7b_tp4_fp8_full_size(tp):
+    """mlp7b_tp4's shapes on E4M3 codes: X[4096,4096], gate/up [4096,2752], down [2752,4096]
+    (every element of the partial)."""
     inp = wl.mlp7b_tp4_fp8()
-    rows = sample_rows(4096, 40, seed=2)
-    got, ref, y = _mlp(tp, inp, "swiglu", rows)
+    got, ref, y = _mlp(tp, inp, "swiglu")
     assert np.all(np.isfinite(y))
-    assert_close_bf16(got, ref, "mlp7b_tp4_fp8 sampled rows")
+    assert_close_bf16(got, ref, "mlp7b_tp4_fp8 full output")
