@@ -37,6 +37,17 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr size_t WS_ALIGN = 256;
 constexpr int64_t SKINNY_MAX_T = 64;   // rows at or below which the decode (weight-streaming) kernels run
+// The MFMA GEMM tiles address a 256-row activation block with 32-bit element offsets
+// (row * lda + column): a contraction length / activation leading dimension must stay below
+// 2^31 / 256 = 2^23 elements.
+constexpr int64_t LD_LIMIT = (int64_t)1 << 23;
+
+tp_status check_ld(const char* fn, const char* what, int64_t v) {
+    if (v >= LD_LIMIT)
+        return fail(TP_ERR_UNSUPPORTED, "%s: %s = %lld (the 16-bit and fp8 paths offer fewer than 2^23)", fn, what,
+                    (long long)v);
+    return TP_OK;
+}
 
 // carve consecutive 256-byte aligned sub-buffers out of a workspace
 struct Carver {
@@ -161,7 +172,7 @@ tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launche
 size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt) {
     if (T <= 0 || K <= 0 || N <= 0) return 0;
     if (in_dt == TP_FP8_E4M3) return round_up(tpk::gemm_f8_split_bytes(T, N, K, 0), WS_ALIGN);
-    if (in_dt != TP_BF16) return 0;
+    if (in_dt != TP_BF16 && in_dt != TP_F16) return 0;
     if (T > SKINNY_MAX_T) return round_up(tpk::gemm_bf16_split_bytes(T, N, K, 0), WS_ALIGN);
     return round_up(tpk::skinny_partials_bytes(T, N, K), WS_ALIGN);
 }
@@ -224,6 +235,8 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
         tp_status st = check_f8("tp_column_linear", X, W_shard, Y, K, N, q);
         if (st != TP_OK) return st;
         if (ldy % 8) return fail(TP_ERR_MISALIGNED, "tp_column_linear: ldy must be a multiple of 8");
+        st = check_ld("tp_column_linear", "K", K);
+        if (st != TP_OK) return st;
         st = check_ws("tp_column_linear", workspace, ws_bytes, tp_linear_workspace_size(T, K, N, in_dt));
         if (st != TP_OK) return st;
         const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
@@ -231,11 +244,15 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
                                            q->x_scale * q->w_scale, 1.0f, workspace, ws_bytes, s),
                         "tp_column_linear");
     }
-    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: input dtype %d not offered", (int)in_dt);
+    if (in_dt != TP_BF16 && in_dt != TP_F16)
+        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: input dtype %d not offered", (int)in_dt);
     if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
-        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: bf16 input needs bf16, fp16 or fp32 output");
+        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: bf16/fp16 input needs bf16, fp16 or fp32 output");
     tp_status st = check_bf16_gemm("tp_column_linear", X, W_shard, Y, K, N, ldy);
     if (st != TP_OK) return st;
+    st = check_ld("tp_column_linear", "K", K);
+    if (st != TP_OK) return st;
+    const int f16 = in_dt == TP_F16;
     const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
     if (T <= SKINNY_MAX_T && out_dt == TP_F16)
         return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp16 output is not offered for T <= %d", (int)SKINNY_MAX_T);
@@ -244,11 +261,11 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t 
     if (T <= SKINNY_MAX_T) {
         const int rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
         if (rk < 0) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: ReLU with fp32 output is not offered for T <= %d", (int)SKINNY_MAX_T);
-        return from_hip(tpk::skinny_linear(X, W_shard, static_cast<float*>(workspace), T, N, K, K, Y, ldy, rk, s),
+        return from_hip(tpk::skinny_linear(X, W_shard, static_cast<float*>(workspace), T, N, K, K, Y, ldy, rk, s, f16),
                         "tp_column_linear");
     }
-    return from_hip(tpk::gemm_bf16_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU,
-                                         workspace, ws_bytes, s),
+    return from_hip((f16 ? tpk::gemm_f16_store : tpk::gemm_bf16_store)(X, W_shard, Y, T, N, K, K, N, ldy, kind,
+                                                                       act == TP_ACT_RELU, workspace, ws_bytes, s),
                     "tp_column_linear");
 }
 
@@ -273,6 +290,8 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
     if (in_dt == TP_FP8_E4M3) {
         tp_status st = check_f8("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, q);
         if (st != TP_OK) return st;
+        st = check_ld("tp_row_linear_partial", "K_shard", K_shard);
+        if (st != TP_OK) return st;
         st = check_ws("tp_row_linear_partial", workspace, ws_bytes, tp_linear_workspace_size(T, K_shard, N, in_dt));
         if (st != TP_OK) return st;
         return from_hip(tpk::gemm_f8_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
@@ -280,18 +299,23 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
                                            ws_bytes, s),
                         "tp_row_linear_partial");
     }
-    if (in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_row_linear_partial: input dtype %d not offered", (int)in_dt);
+    if (in_dt != TP_BF16 && in_dt != TP_F16)
+        return fail(TP_ERR_BAD_DTYPE, "tp_row_linear_partial: input dtype %d not offered", (int)in_dt);
     tp_status st = check_bf16_gemm("tp_row_linear_partial", X_shard, W_shard, Y_partial, K_shard, N, N);
     if (st != TP_OK) return st;
+    st = check_ld("tp_row_linear_partial", "K_shard", K_shard);
+    if (st != TP_OK) return st;
+    const int f16 = in_dt == TP_F16;
     st = check_ws("tp_row_linear_partial", workspace, ws_bytes, tp_linear_workspace_size(T, K_shard, N, in_dt));
     if (st != TP_OK) return st;
     if (T <= SKINNY_MAX_T) {
         return from_hip(tpk::skinny_linear(X_shard, W_shard, static_cast<float*>(workspace), T, N, K_shard, K_shard,
-                                           Y_partial, N, accumulate ? 1 : 0, s),
+                                           Y_partial, N, accumulate ? 1 : 0, s, f16),
                         "tp_row_linear_partial");
     }
-    return from_hip(tpk::gemm_bf16_store(X_shard, W_shard, Y_partial, T, N, K_shard, K_shard, N, N,
-                                         accumulate ? 3 : 2, 0, workspace, ws_bytes, s),
+    return from_hip((f16 ? tpk::gemm_f16_store : tpk::gemm_bf16_store)(X_shard, W_shard, Y_partial, T, N, K_shard,
+                                                                       K_shard, N, N, accumulate ? 3 : 2, 0,
+                                                                       workspace, ws_bytes, s),
                     "tp_row_linear_partial");
 }
 
@@ -378,6 +402,9 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
         return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs 16-byte aligned pointers");
     if (H % 8 || I_shard % 8)
         return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs H and I_shard multiples of 8");
+    tp_status st = check_ld("tp_mlp_shard", "H", H);
+    if (st == TP_OK) st = check_ld("tp_mlp_shard", "I_shard", I_shard);
+    if (st != TP_OK) return st;
     return from_hip(mlp_bf16(X, W_gate, W_up, W_down, Y_partial, T, H, I_shard, kind, workspace, need, s),
                     "tp_mlp_shard");
 }
@@ -410,8 +437,11 @@ tp_status tp_mlp_shard_fp8(const void* X, const void* W_gate, const void* W_up, 
         !aligned(Y_partial, 16))
         return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs 16-byte aligned pointers", fn);
     if (H % 16 || I_shard % 16) return fail(TP_ERR_MISALIGNED, "%s: fp8 path needs H and I_shard multiples of 16", fn);
+    tp_status st = check_ld(fn, "H", H);
+    if (st == TP_OK) st = check_ld(fn, "I_shard", I_shard);
+    if (st != TP_OK) return st;
     const size_t need = tp_mlp_fp8_workspace_size(T, H, I_shard, kind);
-    tp_status st = check_ws(fn, workspace, ws_bytes, need);
+    st = check_ws(fn, workspace, ws_bytes, need);
     if (st != TP_OK) return st;
     hipStream_t s = as_stream(stream);
     Carver c(workspace);
@@ -444,6 +474,8 @@ static tp_status check_attn_desc(const tp_attn_desc* d, bool* decode) {
     if (d->causal != 1) return fail(TP_ERR_UNSUPPORTED, "tp_attn_shard: only causal attention is offered");
     if (!(d->rope_theta > 0.0f)) return fail(TP_ERR_BAD_SHAPE, "tp_attn_shard: rope_theta must be positive");
     if (d->H % 8) return fail(TP_ERR_MISALIGNED, "tp_attn_shard: H must be a multiple of 8");
+    if (check_ld("tp_attn_shard", "H", d->H) != TP_OK) return TP_ERR_UNSUPPORTED;
+    if (check_ld("tp_attn_shard", "n_q_heads * 128", (int64_t)d->n_q_heads * 128) != TP_OK) return TP_ERR_UNSUPPORTED;
     const bool has_cache = d->k_cache || d->v_cache;
     if (has_cache) {
         if (!d->k_cache || !d->v_cache) return fail(TP_ERR_NULL_POINTER, "tp_attn_shard: k_cache and v_cache go together");
@@ -615,6 +647,7 @@ tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard,
     const int64_t R = expert_offsets[E];
     if (R > 0 && !row_token) return fail(TP_ERR_NULL_POINTER, "%s: row_token must be non-NULL when rows exist", fn);
     if (H % 8 || I_shard % 8) return fail(TP_ERR_MISALIGNED, "%s: H and I_shard must be multiples of 8", fn);
+    if (check_ld(fn, "H", H) != TP_OK || check_ld(fn, "I_shard", I_shard) != TP_OK) return TP_ERR_UNSUPPORTED;
     if (!aligned(X, 16) || !aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(W_down, 16) || !aligned(Y_partial, 16))
         return fail(TP_ERR_MISALIGNED, "%s: X, the weights and Y_partial must be 16-byte aligned", fn);
     if ((row_token && !aligned(row_token, 4)) || !aligned(token_rows, 4) || !aligned(gates, 4))
@@ -681,6 +714,10 @@ tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY,
                     (long long)T, (long long)K, (long long)N);
     if (T >= ((int64_t)1 << 23) || K >= ((int64_t)1 << 23) || N >= ((int64_t)1 << 23))
         return fail(TP_ERR_UNSUPPORTED, "%s: T, K and N must be below 2^23", fn);
+    // the transposes of W [K, N] and X [T, K] launch one 256-thread workgroup per 64 x 64 tile;
+    // a grid holds fewer than 2^32 threads, i.e. fewer than 2^24 tiles
+    if (((K + 63) / 64) * ((N + 63) / 64) >= ((int64_t)1 << 24) || ((T + 63) / 64) * ((K + 63) / 64) >= ((int64_t)1 << 24))
+        return fail(TP_ERR_UNSUPPORTED, "%s: the transposes of W and X need fewer than 2^24 tiles of 64 x 64", fn);
     if (!aligned(X, 16) || !aligned(W_shard, 16) || !aligned(dY, 16) || !aligned(dX, 16) || !aligned(dW, 16))
         return fail(TP_ERR_MISALIGNED, "%s: X, W_shard, dY, dX and dW must be 16-byte aligned", fn);
     tp_status st = check_ws(fn, workspace, ws_bytes, tp_linear_backward_workspace_size(T, K, N));

@@ -34,6 +34,7 @@ namespace tpk {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
@@ -115,13 +116,12 @@ __device__ __forceinline__ void load_step(StepRegs<MB>& s, const uint16_t* wp, c
 
 // acc[mb][t][r] += A[m = mb*16 + 4*grp + r][kr..] . W[kr..][col + t]: the 8 x 8 block of
 // weights a lane loaded (rows kr..kr+7, columns col..col+7) is transposed so that column t
-// becomes the 8-k operand of MFMA t.
-template <int MB>
+// becomes the 8-k operand of MFMA t. F16: the 16-bit operands are IEEE half values.
+template <int MB, bool F16>
 __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>& s) {
-    bf16x8 a[MB];
+    u32x4 a[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-        a[mb] = __builtin_bit_cast(bf16x8, s.k_ok ? s.a[mb] : u32x4{0u, 0u, 0u, 0u});
+    for (int mb = 0; mb < MB; ++mb) a[mb] = s.k_ok ? s.a[mb] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const unsigned sel = (t & 1) ? 0x07060302u : 0x05040100u;
@@ -130,14 +130,19 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>
         bt.y = __builtin_amdgcn_perm(s.w[3][t >> 1], s.w[2][t >> 1], sel);
         bt.z = __builtin_amdgcn_perm(s.w[5][t >> 1], s.w[4][t >> 1], sel);
         bt.w = __builtin_amdgcn_perm(s.w[7][t >> 1], s.w[6][t >> 1], sel);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, bt);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b, acc[mb][t], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (F16)
+                acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[mb]),
+                                                                    __builtin_bit_cast(f16x8, bt), acc[mb][t], 0, 0, 0);
+            else
+                acc[mb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb]),
+                                                                     __builtin_bit_cast(bf16x8, bt), acc[mb][t], 0, 0, 0);
+        }
     }
 }
 
-template <int MB>
+template <int MB, bool F16>
 __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs g) {
     __shared__ f32x4 red[4][MB * 16][STRIP / 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -179,12 +184,12 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
         __builtin_amdgcn_sched_barrier(0);
         load_step<MB>(s1, wp + wstep, ap + astep, wsafe, asafe, g.N, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
         __builtin_amdgcn_sched_barrier(0);
-        mma_step<MB>(acc, s0);
+        mma_step<MB, F16>(acc, s0);
         __builtin_amdgcn_sched_barrier(0);
         load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, wsafe, asafe, g.N, g.lda, kr + 8 * STEP, kend, col_ok,
                       m_ok);
         __builtin_amdgcn_sched_barrier(0);
-        if (kr + 4 * STEP - 8 * grp < kend) mma_step<MB>(acc, s1);
+        if (kr + 4 * STEP - 8 * grp < kend) mma_step<MB, F16>(acc, s1);
         wp += 2 * wstep;
         ap += 2 * astep;
     }
@@ -465,17 +470,24 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     }
 }
 
-hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name) {
+hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name, bool f16 = false) {
     a.kchunk = p.kchunk;
     a.strips_per_b = p.strips_per_b;
     a.ncols = p.ncols;
     a.splits = (int)p.splits;
     dim3 grid((unsigned)p.strips, (unsigned)p.splits);
     ProfScope ps(name, s);
-    if (a.M <= 32)
-        skinny_kernel<2><<<grid, 256, 0, s>>>(a);
-    else
-        skinny_kernel<4><<<grid, 256, 0, s>>>(a);
+    if (f16) {
+        if (a.M <= 32)
+            skinny_kernel<2, true><<<grid, 256, 0, s>>>(a);
+        else
+            skinny_kernel<4, true><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (a.M <= 32)
+            skinny_kernel<2, false><<<grid, 256, 0, s>>>(a);
+        else
+            skinny_kernel<4, false><<<grid, 256, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -505,10 +517,10 @@ size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H) {
 }
 
 hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, int64_t N, int64_t K,
-                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s) {
+                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s, int f16_in) {
     SkinnyArgs a = skinny_args(A, B, nullptr, part, M, N, K, lda);
     const SkinnyPlan p = plan_skinny(N, K, 1);
-    hipError_t e = skinny_run(a, p, s, "skinny_gemm");
+    hipError_t e = skinny_run(a, p, s, "skinny_gemm", f16_in != 0);
     if (e != hipSuccess) return e;
     const int64_t n = M * N;
     ProfScope ps("skinny_reduce", s);

@@ -38,6 +38,7 @@ namespace tpk {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -292,9 +293,15 @@ __device__ __forceinline__ void read_frags(Frags& f, const unsigned char* stage,
     for (int q = 0; q < 8; ++q) read_piece<DUAL>(f, q, stage, ks, wm, wn, lane);
 }
 
+// F16: the 16-bit operands are IEEE half values (same LDS layout and fragments as bf16)
+template <bool F16>
 __device__ __forceinline__ void mfma1(f32x16 (&acc)[4][4], const Frags& f, int n) {
     const int i = n >> 2, j = n & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    if constexpr (F16)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, f.a[i]),
+                                                           __builtin_bit_cast(f16x8, f.b[j]), acc[i][j], 0, 0, 0);
+    else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // ---- fp8 operand fragments ----------------------------------------------------------
@@ -609,7 +616,7 @@ __device__ __forceinline__ void publish(unsigned char* stage, int pending, const
 // are issued. STEADY steps (every step but the last five of a tile) know at compile time
 // that a next step exists, that the refill is a whole step and that two later stages are in
 // flight, so their instruction stream has no branches.
-template <bool DUAL, bool STEADY>
+template <bool DUAL, bool STEADY, bool F16>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                        unsigned char* cur, unsigned char* nxt, int kt, int nk,
                                        int64_t kbase, const DmaPlan& p, const Geom<false>& g,
@@ -620,7 +627,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-        mfma1(acc, f0, n);
+        mfma1<F16>(acc, f0, n);
         if (n < 8) read_piece<DUAL>(f1, n, cur, 1, wm, wn, lane);
         TP_FENCE();
     }
@@ -648,7 +655,7 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-        mfma1(acc, f1, n);
+        mfma1<F16>(acc, f1, n);
         if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
         if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
         if (inline_dma && n >= 10 && n < 10 + DMA_B) dma16(b_k + p.b_off[n - 10], b_dst + (n - 10) * 1024);
@@ -783,7 +790,8 @@ struct Pair {
     }
 };
 
-template <bool F8, bool DUAL, class Epi, class Grp>
+// F16 (with F8 false): fp16 operands instead of bf16
+template <bool F8, bool DUAL, class Epi, class Grp, bool F16 = false>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
                                                             int tiles_n, SplitArgs sp, Grp gr) {
     constexpr int BK = Fmt<F8>::BK;
@@ -863,7 +871,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             // whole and not the tile's last step, and two stages after kt+1 are in flight
             int kt = 0;
             for (; kt < nk - 5; ++kt) {
-                k_step<DUAL, true>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step<DUAL, true, F16>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
                 unsigned char* t = sa;
                 sa = sb;
                 sb = sc;
@@ -871,7 +879,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
                 sd = t;
             }
             for (; kt < nk; ++kt) {
-                k_step<DUAL, false>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step<DUAL, false, F16>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
                 unsigned char* t = sa;
                 sa = sb;
                 sb = sc;
@@ -983,13 +991,22 @@ __global__ __launch_bounds__(64 * FIXUP_WAVES) void gemm_fixup_kernel(Epi epi, i
              tile + (threadIdx.x >> 6) * EPI_LDS);
 }
 
-int cu_count() {
+// Workspace sizes are planned for gfx950's 256 compute units, so the size queries (and the
+// argument checks that use them) make no HIP call. A launch plans with the CU count of the
+// stream's device; if that plan needs more workspace than was given, its tiles all run whole.
+constexpr int PLAN_CU = 256;
+
+int cu_count_of(hipStream_t s) {
     static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int dev = -1;
+    if (!s || hipStreamGetDevice(s, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess) return PLAN_CU;
+    }
+    if (dev < 0 || dev >= 64) return PLAN_CU;
     if (!cached[dev]) {
         int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = PLAN_CU;
         cached[dev] = n;
     }
     return cached[dev];
@@ -1040,14 +1057,14 @@ size_t split_bytes_of(int64_t M, int64_t N, int64_t K, bool dual, int bk) {
     int64_t tm, tn;
     if (dual) tiles_of<true>(M, N, tm, tn);
     else tiles_of<false>(M, N, tm, tn);
-    const SplitArgs sp = plan_split(tm * tn, (int)((K + bk - 1) / bk), cu_count());
+    const SplitArgs sp = plan_split(tm * tn, (int)((K + bk - 1) / bk), PLAN_CU);
     if (sp.pieces < 2) return 0;
     return (size_t)(tm * tn - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
 }
 
 // ws may be NULL (or too small): the tiles then all run whole. A grouped launch takes its
 // tile count from the groups (g.M then only bounds nothing: each group sets its own).
-template <bool F8, bool DUAL, class Epi, class Grp = NoGroups>
+template <bool F8, bool DUAL, class Epi, class Grp = NoGroups, bool F16 = false>
 hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
                   const char* name, const Grp& gr = Grp{}) {
     constexpr int BK = Fmt<F8>::BK;
@@ -1058,14 +1075,14 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
     if constexpr (Grp::MODE == 2) G = gr.tiles0 + (int64_t)gr.tiles_m1 * gr.tiles_n1;
     if (G == 0) return hipSuccess;
     const int nk = (int)((g.K + BK - 1) / BK);
-    SplitArgs sp = plan_split(G, nk, cu_count());
+    SplitArgs sp = plan_split(G, nk, cu_count_of(s));
     const size_t need = sp.pieces >= 2 ? (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float) : 0;
     if (sp.pieces >= 2 && (!ws || ws_bytes < need)) sp = SplitArgs{(int)G, 1, nk, nullptr};
     sp.part = static_cast<float*>(ws);
     const int64_t blocks = sp.pieces >= 2 ? sp.g_full + (G - sp.g_full) * sp.pieces : G;
     {
         ProfScope ps(name, s);
-        gemm_mfma_kernel<F8, DUAL, Epi, Grp><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp, gr);
+        gemm_mfma_kernel<F8, DUAL, Epi, Grp, F16><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp, gr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || sp.pieces < 2) return e;
     }
@@ -1104,6 +1121,27 @@ hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int
     if (out_kind == KIND && (relu != 0) == RELU)                                                    \
         return launch<false, false>(g, EpiStore<KIND, RELU>{C, ldc, M, N, 1.0f, 1.0f}, ws, ws_bytes, s, \
                                     KIND >= 2 ? "gemm_bf16_f32out" : "gemm_bf16_store");
+    TP_STORE_CASE(0, false)
+    TP_STORE_CASE(0, true)
+    TP_STORE_CASE(1, false)
+    TP_STORE_CASE(1, true)
+    TP_STORE_CASE(2, false)
+    TP_STORE_CASE(2, true)
+    TP_STORE_CASE(3, false)
+#undef TP_STORE_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t gemm_f16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                          int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
+                          int relu, void* ws, size_t ws_bytes, hipStream_t s) {
+    Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), nullptr,
+                  M, N, K, lda, ldb};
+#define TP_STORE_CASE(KIND, RELU)                                                                      \
+    if (out_kind == KIND && (relu != 0) == RELU)                                                       \
+        return launch<false, false, EpiStore<KIND, RELU>, NoGroups, true>(                             \
+            g, EpiStore<KIND, RELU>{C, ldc, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,                        \
+            KIND >= 2 ? "gemm_f16_f32out" : "gemm_f16_store");
     TP_STORE_CASE(0, false)
     TP_STORE_CASE(0, true)
     TP_STORE_CASE(1, false)
@@ -1173,7 +1211,7 @@ size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, i
     for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
         const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
         const int64_t G = make_groups(row_offsets + x0, n, tn, 0).tile0[n];
-        const SplitArgs sp = plan_split(G, nk, cu_count());
+        const SplitArgs sp = plan_split(G, nk, PLAN_CU);
         const size_t b = sp.pieces < 2 ? 0 : (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
         best = b > best ? b : best;
     }
@@ -1185,7 +1223,7 @@ size_t gemm_bf16_pair_split_bytes(int64_t M0, int64_t N0, int64_t M1, int64_t N1
     tiles_of<false>(M0, N0, tm0, tn0);
     tiles_of<false>(M1, N1, tm1, tn1);
     const int64_t G = tm0 * tn0 + tm1 * tn1;
-    const SplitArgs sp = plan_split(G, (int)((K + Fmt<false>::BK - 1) / Fmt<false>::BK), cu_count());
+    const SplitArgs sp = plan_split(G, (int)((K + Fmt<false>::BK - 1) / Fmt<false>::BK), PLAN_CU);
     return sp.pieces < 2 ? 0 : (size_t)(G - sp.g_full) * sp.pieces * 4 * 256 * 64 * sizeof(float);
 }
 

@@ -37,6 +37,10 @@ size_t gemm_bf16_split_bytes(int64_t M, int64_t N, int64_t K, int dual);
 hipError_t gemm_bf16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
                            int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
                            int relu, void* ws, size_t ws_bytes, hipStream_t s);
+// the same on fp16 operands (fp32 accumulation, same output kinds)
+hipError_t gemm_f16_store(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                          int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int out_kind,
+                          int relu, void* ws, size_t ws_bytes, hipStream_t s);
 // h[M, N] (bf16, ld = N) = SiLU(A . Bg) * (A . Bu)
 // Grouped forms (the experts of an MoE layer): group e = rows row_offsets[e] ..
 // row_offsets[e+1]-1 of A and of the output, times weight e ([K, N], weights contiguous);
@@ -94,9 +98,10 @@ hipError_t flash_attn_fwd(const void* q, const void* k, const void* vt, void* ou
 // in chunk order and applies the epilogue.
 size_t skinny_partials_bytes(int64_t M, int64_t N, int64_t K);
 size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H);
-// kind: 0 = fp32 store (ldc), 1 = fp32 +=, 2 = bf16 store, 3 = bf16 ReLU
+// kind: 0 = fp32 store (ldc), 1 = fp32 +=, 2 = bf16 store, 3 = bf16 ReLU; f16_in: the operands
+// are fp16 instead of bf16
 hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, int64_t N, int64_t K,
-                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s);
+                         int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s, int f16_in = 0);
 // h bf16 [M, I] = SiLU(X . Wg) * (X . Wu)
 hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
                          int64_t M, int64_t I, int64_t H, hipStream_t s);

@@ -126,7 +126,9 @@ def test_row_linear_validation(L):
     assert _st(f(FAKE, None, FAKE, 4, 8, 8, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_NULL_POINTER"
     assert _st(f(FAKE, FAKE, FAKE, 4, -8, 8, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_BAD_SHAPE"
     assert _st(f(FAKE, FAKE, FAKE, 4, 8, 10, tp.TP_BF16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
-    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 9, 0, None, None, 0, None)) == "TP_ERR_BAD_DTYPE"
+    # fp16 operands are offered; a decode-size call needs its split workspace
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_WORKSPACE"
 
 
 def test_mlp_validation(L):
@@ -284,3 +286,48 @@ def test_profile_api_without_launches(L):
     assert L.tp_profile_reset() == 0
     ms, n = tp.profile_read("")
     assert ms == 0.0 and n == 0
+
+
+def test_fp16_operands_follow_the_bf16_rules(L):
+    col, row = L.tp_column_linear, L.tp_row_linear_partial
+    assert L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_F16) == L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_BF16)
+    assert _st(col(FAKE, FAKE, FAKE, 100, 12, 8, 8, tp.TP_F16, tp.TP_F32, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+    assert _st(col(FAKE_ODD, FAKE, FAKE, 100, 8, 8, 8, tp.TP_F16, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+    # the weight-streaming kernels of the few-row regime store fp32 or bf16 only
+    assert _st(col(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_F16, tp.TP_F16, 0, None, FAKE, 1 << 20, None)) == "TP_ERR_UNSUPPORTED"
+    assert _st(row(FAKE, FAKE, FAKE, 100, 12, 8, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
+
+
+def test_contraction_lengths_past_2_pow_23_are_refused(L):
+    """The MFMA tiles address a 256-row activation block with 32-bit offsets (row * lda), so every
+    16-bit / fp8 GEMM entry point refuses an activation row length of 2^23 elements or more before
+    any launch (the pointers here are fake and never touched)."""
+    big = 1 << 23
+    q = ctypes.byref(tp.Fp8Scales(0.5, 0.25))
+    col, row = L.tp_column_linear, L.tp_row_linear_partial
+    for dt, qq in ((tp.TP_BF16, None), (tp.TP_F16, None), (tp.TP_FP8_E4M3, q)):
+        assert _st(col(FAKE, FAKE, FAKE, 512, big, 64, 64, dt, tp.TP_F32, 0, qq, FAKE, 1 << 40, None)) == "TP_ERR_UNSUPPORTED"
+        assert _st(row(FAKE, FAKE, FAKE, 512, big, 64, dt, 0, qq, FAKE, 1 << 40, None)) == "TP_ERR_UNSUPPORTED"
+        assert "2^23" in L.tp_last_error().decode()
+    mlp = L.tp_mlp_shard
+    assert _st(mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 512, big, 64, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16, FAKE,
+                   1 << 40, None)) == "TP_ERR_UNSUPPORTED"
+    assert _st(mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 512, 64, big, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16, FAKE,
+                   1 << 40, None)) == "TP_ERR_UNSUPPORTED"
+    fq = ctypes.byref(tp.Fp8MlpScales(0.01, 0.001, 0.001, 0.001, 0.125))
+    assert _st(L.tp_mlp_shard_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 512, big, 64, tp.TP_MLP_SWIGLU, fq, FAKE, 1 << 40,
+                                  None)) == "TP_ERR_UNSUPPORTED"
+    d = tp._desc(1, 256, big, 8, 8)
+    assert _st(L.tp_attn_shard(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), tp.TP_BF16, FAKE, 1 << 40, None)) == \
+        "TP_ERR_UNSUPPORTED"
+    offs = (ctypes.c_int64 * 2)(0, 300)
+    assert _st(L.tp_moe_mlp_shard(FAKE, 300, big, 64, 1, FAKE, FAKE, FAKE, offs, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None)) == "TP_ERR_UNSUPPORTED"
+
+
+def test_backward_transpose_grid_limit(L):
+    """2^23 - 8 in two dimensions would need about 2^34 transpose tiles: refused before launch."""
+    n = (1 << 23) - 8
+    assert _st(L.tp_linear_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 64, n, n, tp.TP_BF16, FAKE, 1 << 40, None)) == \
+        "TP_ERR_UNSUPPORTED"
+    assert "2^24 tiles" in L.tp_last_error().decode()

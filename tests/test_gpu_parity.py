@@ -437,6 +437,43 @@ def test_row_linear_partial_tail_split_accumulate(tp):
     assert_close_bf16(host(P), 2 * O.linear(X, W), "split row partial accumulate")
 
 
+def _f16(a):
+    """float32 values rounded to IEEE half (input preparation for the fp16-operand calls)."""
+    return np.asarray(a, np.float32).astype(np.float16).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 520, 264), (16, 1024, 392), (64, 4096, 512), (4100, 1000, 4000)])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_column_linear_fp16_operands(tp, T, K, N, out):
+    """fp16 X and W (fp32 accumulation): the prefill tiles (ragged, and a grid split past the first
+    round) and the few-row weight-streaming kernels (which store fp32 or bf16 only)."""
+    import torch
+    if T <= 64 and out == "f16":
+        pytest.skip("the few-row kernels offer fp32 and bf16 outputs")
+    rng = np.random.default_rng(T + K + N)
+    X = _f16(rng.standard_normal((T, K)))
+    W = _f16(rng.standard_normal((K, N)) * 0.05)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[out]
+    Y = tp.column_linear(dev(X, "f16"), dev(W, "f16"), Y=_nan((T, N), dt))
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.linear(X, W), f"fp16 column {T}x{K}x{N} -> {out}", out=out)
+
+
+@pytest.mark.parametrize("T,K,N", [(513, 1000, 264), (32, 2048, 4096)])
+def test_row_linear_partial_fp16_operands(tp, T, K, N):
+    import torch
+    rng = np.random.default_rng(3 * T + K)
+    X = _f16(rng.standard_normal((T, K)))
+    W = _f16(rng.standard_normal((K, N)) * 0.02)
+    P = tp.row_linear_partial(dev(X, "f16"), dev(W, "f16"), Y=_nan((T, N), torch.float32))
+    torch.cuda.synchronize()
+    ref = O.linear(X, W)
+    assert_close_bf16(host(P), ref, f"fp16 row partial {T}x{K}x{N}")
+    tp.row_linear_partial(dev(X, "f16"), dev(W, "f16"), Y=P, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(P), 2 * ref, f"fp16 row partial {T}x{K}x{N} accumulate")
+
+
 @pytest.mark.parametrize("kind", ["swiglu", "relu"])
 def test_mlp_tail_split(tp, kind):
     import torch
