@@ -21,7 +21,8 @@
  *     sequence-major.
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
  *     never allocates, frees or keeps a pointer; scratch space is a caller-owned
- *     workspace whose size is queried first.
+ *     workspace whose size is queried first (one call, tp_column_linear_noalloc, uses a
+ *     fixed static device array instead).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream). Buffers must stay alive until the stream has finished with them.
  *   - Arguments are validated on the host before any HIP call; on failure the call
@@ -81,9 +82,11 @@ typedef struct { float x_scale; float w_scale; } tp_fp8_scales;
  *   Y       [T, ldy] out_dt         row t of the result at Y + t*ldy; ldy >= N lets a
  *                                   rank write its slice of a full [T, N*tp] buffer
  *                                   (the concatenation happens in place).
- *   in_dt/out_dt: (F32, F32) — exact fp32 path; (BF16, BF16|F16|F32);
+ *   in_dt/out_dt: (F32, F32) — exact fp32 path; (BF16 or F16, BF16|F16|F32) with fp32
+ *                 accumulation (T <= 64: BF16|F32 output only);
  *                 (FP8_E4M3, BF16|F16|F32) with scales q: Y = act(x_scale * w_scale *
  *                 (codes(X) . codes(W))), accumulated in fp32.
+ *   16-bit and fp8 operands: K < 2^23 (else TP_ERR_UNSUPPORTED).
  *   workspace: >= tp_linear_workspace_size(T, K, N, in_dt) bytes.
  *   act: TP_ACT_NONE or TP_ACT_RELU (applied in fp32 before the output rounding).
  */
@@ -100,8 +103,9 @@ tp_status tp_column_linear(const void* X, const void* W_shard, void* Y,
  *   X_shard [T, K_shard] in_dt      this rank's slice of the input features
  *   W_shard [K_shard, N] in_dt      this rank's rows of the full weight
  *   Y_partial [T, N] fp32           overwritten, or += when accumulate != 0
- *   in_dt: F32 (exact path), BF16, or FP8_E4M3 with scales q (P = x_scale * w_scale *
- *          (codes(X_shard) . codes(W_shard)), fp32 accumulation).
+ *   in_dt: F32 (exact path), BF16 or F16 (fp32 accumulation), or FP8_E4M3 with scales q
+ *          (P = x_scale * w_scale * (codes(X_shard) . codes(W_shard)), fp32 accumulation).
+ *   16-bit and fp8 operands: K_shard < 2^23 (else TP_ERR_UNSUPPORTED).
  *   workspace: >= tp_linear_workspace_size(T, K_shard, N, in_dt) bytes (both calls).
  */
 tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float* Y_partial,
@@ -111,11 +115,14 @@ tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float*
 
 /*
  * Workspace bytes needed by tp_column_linear / tp_row_linear_partial for these sizes
- * (K = the contraction length), on the current device. Two cases use it, both fp32
- * partials summed in a fixed order (results are run-to-run identical):
+ * (K = the contraction length). Pure host arithmetic (no HIP call): the tile split is
+ * planned for gfx950's 256 compute units. Two cases use it, both fp32 partials summed in
+ * a fixed order (results are run-to-run identical):
  *   - the few-row (decode) regime, T <= 64: the contraction is split into chunks;
- *   - larger bf16 products whose 256x256 output tiles do not fill whole rounds of the
- *     device's compute units: the tiles past the last full round are split along K.
+ *   - larger 16-bit / fp8 products whose 256x256 output tiles do not fill whole rounds of
+ *     the compute units: the tiles past the last full round are split along K (a launch
+ *     on a device with another CU count runs every tile whole if its own plan needs more
+ *     than was given).
  * When it returns 0, workspace may be NULL.
  */
 size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt);
@@ -130,7 +137,11 @@ size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt)
  *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: in_dt (F32 or BF16)
  *   Y_partial [T, H] fp32 (overwritten).
  *   h_dt: storage type of the activated intermediate h [T, I_shard], which lives
- *   only in the workspace: F32 for the F32 path, BF16 for the BF16 path.
+ *   only in the workspace: F32 for the F32 path; BF16 or F16 for the BF16 path. F16 (T > 64
+ *   only, else TP_ERR_UNSUPPORTED) keeps 3 more bits of h for wide shards (h's rounding is the
+ *   largest error term of the block): the down projection then runs on fp16 operands, with
+ *   W_down converted to fp16 into the workspace first (exact for |w| >= 2^-14; smaller
+ *   weights round to fp16 subnormals, an error below 2^-25).
  *   The gate/up pre-activations never leave registers.
  *   workspace: >= tp_mlp_workspace_size(T, H, I_shard, kind, in_dt, h_dt) bytes,
  *   16-byte aligned; contents on return are unspecified.
@@ -154,7 +165,9 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
  *     P = h_scale*wd_scale * (code(h) . W_down)   fp32, overwritten
  *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: E4M3 codes.
  *   Requires H and I_shard multiples of 16 and 16-byte aligned pointers.
- *   workspace >= tp_mlp_fp8_workspace_size(T, H, I_shard, kind) bytes, 16-byte aligned.
+ *   workspace >= tp_mlp_fp8_workspace_size(T, H, I_shard, kind) bytes, 16-byte aligned. On
+ *   return its first T * I_shard bytes hold code(h), [T, I_shard] row-major (the rest is
+ *   unspecified).
  */
 typedef struct {
     float x_scale, w_gate_scale, w_up_scale, w_down_scale, h_scale;
@@ -290,6 +303,28 @@ tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard,
                            void* workspace, size_t ws_bytes, void* stream);
 size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E,
                              const int64_t* expert_offsets);
+
+/*
+ * tp_column_linear_noalloc — tp_column_linear without a workspace argument, for callers that
+ *   cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ *   that forbid allocation). Same arguments, rules, results and error statuses as
+ *   tp_column_linear, minus workspace/ws_bytes; it calls no allocator. Its scratch (the few-row
+ *   regime's fp32 partial sums, or the split of the tiles past the last full round of the
+ *   machine) is a static array of TP_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ *   runs on until the process ends:
+ *     - T <= 64 needs tp_linear_workspace_size(T, K, N, in_dt) bytes of it; a call that needs more
+ *       returns TP_ERR_UNSUPPORTED before any HIP call;
+ *     - larger T uses the split only when it fits (otherwise every tile runs whole; same result).
+ *   The first call on a device looks the array's address up on that device (a HIP call that can
+ *   fail with TP_ERR_HIP). All calls on one GPU share the array: calls that overlap on one GPU
+ *   (other streams, other host threads) race and must be ordered by the caller. Nothing in it
+ *   needs to start at zero; its contents after a call are unspecified.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES (16u << 20)
+tp_status tp_column_linear_noalloc(const void* X, const void* W_shard, void* Y,
+                                   int64_t T, int64_t K, int64_t N, int64_t ldy,
+                                   tp_dtype in_dt, tp_dtype out_dt, tp_act act,
+                                   const tp_fp8_scales* q, void* stream);
 
 /* Status text, thread-local detail of this thread's last non-OK status, ABI version. */
 const char* tp_status_string(tp_status st);

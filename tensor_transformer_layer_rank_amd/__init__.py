@@ -37,7 +37,7 @@ EXPORTS = [
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
     "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size", "tp_moe_mlp_shard",
-    "tp_moe_workspace_size",
+    "tp_moe_workspace_size", "tp_column_linear_noalloc",
 ]
 
 
@@ -106,6 +106,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tp_moe_mlp_shard": ([_P, _I64, _I64, _I64, _I32, _P, _P, _P, ctypes.POINTER(_I64), _P, _I32, _P, _P, _P,
                               _P, _SZ, _P], _I32),
         "tp_moe_workspace_size": ([_I64, _I64, _I64, _I32, ctypes.POINTER(_I64)], _SZ),
+        "tp_column_linear_noalloc": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P], _I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -198,6 +199,24 @@ def column_linear(X, W, Y=None, act: int = TP_ACT_NONE, out_dtype=None, ldy: int
     return Y
 
 
+def column_linear_noalloc(X, W, Y=None, act: int = TP_ACT_NONE, out_dtype=None, ldy: int | None = None,
+                          scales=None, stream=None):
+    """column_linear through tp_column_linear_noalloc: no workspace, the library's static scratch."""
+    import torch
+    T, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [*, {K}] but W is [{K2}, *]")
+    if Y is None:
+        default = torch.bfloat16 if _dt(X) == TP_FP8_E4M3 else X.dtype
+        Y = torch.empty((T, N), dtype=out_dtype or default, device=X.device)
+    ldy = ldy if ldy is not None else Y.shape[-1]
+    q = _scales(X, scales)
+    _check(lib().tp_column_linear_noalloc(_ptr(X), _ptr(W), ctypes.c_void_p(Y.data_ptr()), T, K, N, ldy,
+                                          _dt(X), _dt(Y), act, q, _stream(stream)))
+    return Y
+
+
 def row_linear_partial(X, W, Y=None, accumulate: bool = False, scales=None, workspace=None, stream=None):
     """fp32 partial X_shard @ W_shard [K_shard, N] of a row-parallel layer (E4M3 operands:
     scales=(x_scale, w_scale))."""
@@ -220,17 +239,20 @@ def mlp_workspace_size(T: int, H: int, I: int, kind: int, in_dt: int, h_dt: int 
     return int(lib().tp_mlp_workspace_size(T, H, I, kind, in_dt, h_dt))
 
 
-def mlp_shard(X, W_gate, W_up, W_down, Y=None, kind: int = TP_MLP_SWIGLU, workspace=None, stream=None):
-    """fp32 partial of this rank's MLP block (ReLU form: W_up=None)."""
+def mlp_shard(X, W_gate, W_up, W_down, Y=None, kind: int = TP_MLP_SWIGLU, workspace=None, stream=None,
+              h_dtype: int | None = None):
+    """fp32 partial of this rank's MLP block (ReLU form: W_up=None). h_dtype: storage of the
+    intermediate h (TP_BF16 by default for bf16 inputs, or TP_F16)."""
     import torch
     T, H = X.shape
     I = W_gate.shape[1]
     if Y is None:
         Y = torch.empty((T, H), dtype=torch.float32, device=X.device)
     dt = _dt(X)
-    ws, wsb = _workspace(mlp_workspace_size(T, H, I, kind, dt), X.device, workspace)
+    hdt = dt if h_dtype is None else h_dtype
+    ws, wsb = _workspace(mlp_workspace_size(T, H, I, kind, dt, hdt), X.device, workspace)
     _check(lib().tp_mlp_shard(_ptr(X), _ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(Y), T, H, I,
-                              kind, dt, dt, _ptr(ws), wsb, _stream(stream)))
+                              kind, dt, hdt, _ptr(ws), wsb, _stream(stream)))
     return Y
 
 

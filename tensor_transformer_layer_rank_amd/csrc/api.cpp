@@ -209,64 +209,120 @@ static tp_status check_bf16_gemm(const char* fn, const void* X, const void* W, c
     return TP_OK;
 }
 
+// tp_column_linear in two halves: the argument checks (pure host code) choose the kernel path
+// and the workspace it needs; the launch runs it. The allocation-free variant shares both.
+struct ColumnPlan {
+    enum { F32, FP8, SKINNY, MFMA16 } path;
+    int kind;       // store kind of the prefill tiles (0 bf16, 1 fp16, 2 fp32)
+    int rk;         // epilogue of the few-row reduce (0 fp32, 2 bf16, 3 bf16 ReLU)
+    int f16;        // fp16 operands (else bf16)
+    size_t need;    // tp_linear_workspace_size of the call
+};
+
+static tp_status column_linear_check(const char* fn, const void* X, const void* W_shard, void* Y, int64_t T,
+                                     int64_t K, int64_t N, int64_t ldy, tp_dtype in_dt, tp_dtype out_dt, tp_act act,
+                                     const tp_fp8_scales* q, ColumnPlan* p) {
+    if (!X || !W_shard || !Y) return fail(TP_ERR_NULL_POINTER, "%s: X, W_shard and Y must be non-NULL", fn);
+    if (T <= 0 || K <= 0 || N <= 0)
+        return fail(TP_ERR_BAD_SHAPE, "%s: sizes must be positive (T=%lld K=%lld N=%lld)", fn, (long long)T,
+                    (long long)K, (long long)N);
+    if (ldy < N) return fail(TP_ERR_BAD_SHAPE, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+    if (act != TP_ACT_NONE && act != TP_ACT_RELU) return fail(TP_ERR_BAD_SHAPE, "%s: unknown activation %d", fn, (int)act);
+    *p = ColumnPlan{ColumnPlan::F32, 0, 0, 0, 0};
+    if (in_dt == TP_F32) {
+        if (out_dt != TP_F32) return fail(TP_ERR_BAD_DTYPE, "%s: fp32 input needs fp32 output", fn);
+        if (!aligned(X, 4) || !aligned(W_shard, 4) || !aligned(Y, 4))
+            return fail(TP_ERR_MISALIGNED, "%s: fp32 pointers must be 4-byte aligned", fn);
+        return TP_OK;
+    }
+    p->kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
+    if (in_dt == TP_FP8_E4M3) {
+        if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
+            return fail(TP_ERR_BAD_DTYPE, "%s: fp8 input needs bf16, fp16 or fp32 output", fn);
+        tp_status st = check_f8(fn, X, W_shard, Y, K, N, q);
+        if (st != TP_OK) return st;
+        if (ldy % 8) return fail(TP_ERR_MISALIGNED, "%s: ldy must be a multiple of 8", fn);
+        st = check_ld(fn, "K", K);
+        if (st != TP_OK) return st;
+        p->path = ColumnPlan::FP8;
+        p->need = tp_linear_workspace_size(T, K, N, in_dt);
+        return TP_OK;
+    }
+    if (in_dt != TP_BF16 && in_dt != TP_F16) return fail(TP_ERR_BAD_DTYPE, "%s: input dtype %d not offered", fn, (int)in_dt);
+    if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
+        return fail(TP_ERR_BAD_DTYPE, "%s: bf16/fp16 input needs bf16, fp16 or fp32 output", fn);
+    tp_status st = check_bf16_gemm(fn, X, W_shard, Y, K, N, ldy);
+    if (st != TP_OK) return st;
+    st = check_ld(fn, "K", K);
+    if (st != TP_OK) return st;
+    p->f16 = in_dt == TP_F16;
+    p->need = tp_linear_workspace_size(T, K, N, in_dt);
+    if (T <= SKINNY_MAX_T) {
+        if (out_dt == TP_F16) return fail(TP_ERR_UNSUPPORTED, "%s: fp16 output is not offered for T <= %d", fn, (int)SKINNY_MAX_T);
+        p->rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
+        if (p->rk < 0) return fail(TP_ERR_UNSUPPORTED, "%s: ReLU with fp32 output is not offered for T <= %d", fn, (int)SKINNY_MAX_T);
+        p->path = ColumnPlan::SKINNY;
+        return TP_OK;
+    }
+    p->path = ColumnPlan::MFMA16;
+    return TP_OK;
+}
+
+// ws may be smaller than p.need on the prefill paths only (their tiles then all run whole)
+static hipError_t column_linear_launch(const ColumnPlan& p, const void* X, const void* W_shard, void* Y, int64_t T,
+                                       int64_t K, int64_t N, int64_t ldy, tp_act act, const tp_fp8_scales* q,
+                                       void* ws, size_t ws_bytes, hipStream_t s) {
+    const int relu = act == TP_ACT_RELU;
+    switch (p.path) {
+        case ColumnPlan::F32:
+            return tpk::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W_shard),
+                                 static_cast<float*>(Y), T, N, K, K, N, ldy, relu, 0, s);
+        case ColumnPlan::FP8:
+            return tpk::gemm_f8_store(X, W_shard, Y, T, N, K, K, N, ldy, p.kind, relu, q->x_scale * q->w_scale, 1.0f,
+                                      ws, ws_bytes, s);
+        case ColumnPlan::SKINNY:
+            return tpk::skinny_linear(X, W_shard, static_cast<float*>(ws), T, N, K, K, Y, ldy, p.rk, s, p.f16);
+        case ColumnPlan::MFMA16:
+            return (p.f16 ? tpk::gemm_f16_store : tpk::gemm_bf16_store)(X, W_shard, Y, T, N, K, K, N, ldy, p.kind,
+                                                                        relu, ws, ws_bytes, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 tp_status tp_column_linear(const void* X, const void* W_shard, void* Y, int64_t T, int64_t K,
                            int64_t N, int64_t ldy, tp_dtype in_dt, tp_dtype out_dt, tp_act act,
                            const tp_fp8_scales* q, void* workspace, size_t ws_bytes,
                            void* stream) {
-    (void)q;
-    if (!X || !W_shard || !Y) return fail(TP_ERR_NULL_POINTER, "tp_column_linear: X, W_shard and Y must be non-NULL");
-    if (T <= 0 || K <= 0 || N <= 0)
-        return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: sizes must be positive (T=%lld K=%lld N=%lld)",
-                    (long long)T, (long long)K, (long long)N);
-    if (ldy < N) return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
-    if (act != TP_ACT_NONE && act != TP_ACT_RELU) return fail(TP_ERR_BAD_SHAPE, "tp_column_linear: unknown activation %d", (int)act);
+    const char* fn = "tp_column_linear";
+    ColumnPlan p;
+    tp_status st = column_linear_check(fn, X, W_shard, Y, T, K, N, ldy, in_dt, out_dt, act, q, &p);
+    if (st != TP_OK) return st;
+    st = check_ws(fn, workspace, ws_bytes, p.need);
+    if (st != TP_OK) return st;
+    return from_hip(column_linear_launch(p, X, W_shard, Y, T, K, N, ldy, act, q, workspace, ws_bytes, as_stream(stream)),
+                    fn);
+}
+
+tp_status tp_column_linear_noalloc(const void* X, const void* W_shard, void* Y, int64_t T, int64_t K, int64_t N,
+                                   int64_t ldy, tp_dtype in_dt, tp_dtype out_dt, tp_act act, const tp_fp8_scales* q,
+                                   void* stream) {
+    const char* fn = "tp_column_linear_noalloc";
+    ColumnPlan p;
+    tp_status st = column_linear_check(fn, X, W_shard, Y, T, K, N, ldy, in_dt, out_dt, act, q, &p);
+    if (st != TP_OK) return st;
+    if (p.path == ColumnPlan::SKINNY && p.need > (size_t)TP_NOALLOC_SCRATCH_BYTES)
+        return fail(TP_ERR_UNSUPPORTED, "%s: T=%lld K=%lld N=%lld needs %zu bytes of partial sums; the library's "
+                    "scratch holds %zu", fn, (long long)T, (long long)K, (long long)N, p.need,
+                    (size_t)TP_NOALLOC_SCRATCH_BYTES);
     hipStream_t s = as_stream(stream);
-    if (in_dt == TP_F32) {
-        if (out_dt != TP_F32) return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: fp32 input needs fp32 output");
-        if (!aligned(X, 4) || !aligned(W_shard, 4) || !aligned(Y, 4))
-            return fail(TP_ERR_MISALIGNED, "tp_column_linear: fp32 pointers must be 4-byte aligned");
-        return from_hip(tpk::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W_shard),
-                                      static_cast<float*>(Y), T, N, K, K, N, ldy, act == TP_ACT_RELU, 0, s),
-                        "tp_column_linear");
+    void* scratch = nullptr;
+    if (p.path != ColumnPlan::F32) {
+        hipError_t e = tpk::noalloc_scratch(s, &scratch);
+        if (e != hipSuccess) return from_hip(e, fn);
     }
-    if (in_dt == TP_FP8_E4M3) {
-        if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
-            return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: fp8 input needs bf16, fp16 or fp32 output");
-        tp_status st = check_f8("tp_column_linear", X, W_shard, Y, K, N, q);
-        if (st != TP_OK) return st;
-        if (ldy % 8) return fail(TP_ERR_MISALIGNED, "tp_column_linear: ldy must be a multiple of 8");
-        st = check_ld("tp_column_linear", "K", K);
-        if (st != TP_OK) return st;
-        st = check_ws("tp_column_linear", workspace, ws_bytes, tp_linear_workspace_size(T, K, N, in_dt));
-        if (st != TP_OK) return st;
-        const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
-        return from_hip(tpk::gemm_f8_store(X, W_shard, Y, T, N, K, K, N, ldy, kind, act == TP_ACT_RELU,
-                                           q->x_scale * q->w_scale, 1.0f, workspace, ws_bytes, s),
-                        "tp_column_linear");
-    }
-    if (in_dt != TP_BF16 && in_dt != TP_F16)
-        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: input dtype %d not offered", (int)in_dt);
-    if (out_dt != TP_BF16 && out_dt != TP_F16 && out_dt != TP_F32)
-        return fail(TP_ERR_BAD_DTYPE, "tp_column_linear: bf16/fp16 input needs bf16, fp16 or fp32 output");
-    tp_status st = check_bf16_gemm("tp_column_linear", X, W_shard, Y, K, N, ldy);
-    if (st != TP_OK) return st;
-    st = check_ld("tp_column_linear", "K", K);
-    if (st != TP_OK) return st;
-    const int f16 = in_dt == TP_F16;
-    const int kind = out_dt == TP_BF16 ? 0 : (out_dt == TP_F16 ? 1 : 2);
-    if (T <= SKINNY_MAX_T && out_dt == TP_F16)
-        return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: fp16 output is not offered for T <= %d", (int)SKINNY_MAX_T);
-    st = check_ws("tp_column_linear", workspace, ws_bytes, tp_linear_workspace_size(T, K, N, in_dt));
-    if (st != TP_OK) return st;
-    if (T <= SKINNY_MAX_T) {
-        const int rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
-        if (rk < 0) return fail(TP_ERR_UNSUPPORTED, "tp_column_linear: ReLU with fp32 output is not offered for T <= %d", (int)SKINNY_MAX_T);
-        return from_hip(tpk::skinny_linear(X, W_shard, static_cast<float*>(workspace), T, N, K, K, Y, ldy, rk, s, f16),
-                        "tp_column_linear");
-    }
-    return from_hip((f16 ? tpk::gemm_f16_store : tpk::gemm_bf16_store)(X, W_shard, Y, T, N, K, K, N, ldy, kind,
-                                                                       act == TP_ACT_RELU, workspace, ws_bytes, s),
-                    "tp_column_linear");
+    return from_hip(column_linear_launch(p, X, W_shard, Y, T, K, N, ldy, act, q, scratch,
+                                         scratch ? (size_t)TP_NOALLOC_SCRATCH_BYTES : 0, s),
+                    fn);
 }
 
 tp_status tp_row_linear_partial(const void* X_shard, const void* W_shard, float* Y_partial,
@@ -326,8 +382,10 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
     (void)kind;
     if (T <= 0 || H <= 0 || I_shard <= 0) return 0;
     if (in_dt == TP_F32) return round_up((size_t)(T * I_shard) * 4, WS_ALIGN);
-    if (in_dt != TP_BF16 || h_dt != TP_BF16) return 0;
+    if (in_dt != TP_BF16 || (h_dt != TP_BF16 && h_dt != TP_F16)) return 0;
+    if (h_dt == TP_F16 && T <= SKINNY_MAX_T) return 0;
     size_t bytes = round_up((size_t)(T * I_shard) * 2, WS_ALIGN);   // h
+    if (h_dt == TP_F16) bytes += round_up((size_t)(I_shard * H) * 2, WS_ALIGN);   // W_down in fp16
     if (T <= SKINNY_MAX_T) {
         const size_t first = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu_partials_bytes(T, I_shard, H)
                                                    : tpk::skinny_partials_bytes(T, I_shard, H);
@@ -343,12 +401,24 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
 
 // The bf16 MLP shard on T rows (validated arguments): gate/up (SwiGLU, or ReLU without W_up)
 // into h in the workspace, then the down projection's fp32 partial. `need` is
-// tp_mlp_workspace_size of the same arguments.
+// tp_mlp_workspace_size of the same arguments. h_f16 (T > 64 only): h is stored in fp16, W_down
+// is converted to fp16 into the workspace, and the down projection runs on fp16 operands.
 static hipError_t mlp_bf16(const void* X, const void* W_gate, const void* W_up, const void* W_down, float* Y,
                            int64_t T, int64_t H, int64_t I, tp_mlp_kind kind, void* workspace, size_t need,
-                           hipStream_t s) {
+                           hipStream_t s, bool h_f16 = false) {
     Carver c(workspace);
     void* h = c.take((size_t)(T * I) * 2);
+    if (h_f16) {
+        void* wd16 = c.take((size_t)(I * H) * 2);
+        void* split = c.take(0);
+        const size_t split_bytes = need - c.off;
+        hipError_t e = kind == TP_MLP_SWIGLU
+                           ? tpk::gemm_bf16_swiglu(X, W_gate, W_up, h, T, I, H, split, split_bytes, s, 1)
+                           : tpk::gemm_bf16_store(X, W_gate, h, T, I, H, H, I, I, 1, 1, split, split_bytes, s);
+        if (e == hipSuccess) e = tpk::bf16_to_f16(W_down, wd16, I * H, s);
+        if (e != hipSuccess) return e;
+        return tpk::gemm_f16_store(h, wd16, Y, T, H, I, I, H, H, 2, 0, split, split_bytes, s);
+    }
     if (T <= SKINNY_MAX_T) {
         float* part = static_cast<float*>(c.take(0));
         hipError_t e = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I, H, s)
@@ -378,7 +448,10 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
         return fail(TP_ERR_BAD_SHAPE, "tp_mlp_shard: sizes must be positive (T=%lld H=%lld I=%lld)",
                     (long long)T, (long long)H, (long long)I_shard);
     if (in_dt == TP_F32 && h_dt != TP_F32) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: fp32 input keeps h in fp32");
-    if (in_dt == TP_BF16 && h_dt != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: bf16 input keeps h in bf16");
+    if (in_dt == TP_BF16 && h_dt != TP_BF16 && h_dt != TP_F16)
+        return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: bf16 input keeps h in bf16 or fp16");
+    if (in_dt == TP_BF16 && h_dt == TP_F16 && T <= SKINNY_MAX_T)
+        return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: an fp16 h is offered for T > %d", (int)SKINNY_MAX_T);
     if (in_dt != TP_F32 && in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: input dtype %d not offered", (int)in_dt);
     if (in_dt == TP_F32 && kind == TP_MLP_SWIGLU) return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: the fp32 path offers the ReLU form");
     const size_t need = tp_mlp_workspace_size(T, H, I_shard, kind, in_dt, h_dt);
@@ -405,7 +478,8 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
     tp_status st = check_ld("tp_mlp_shard", "H", H);
     if (st == TP_OK) st = check_ld("tp_mlp_shard", "I_shard", I_shard);
     if (st != TP_OK) return st;
-    return from_hip(mlp_bf16(X, W_gate, W_up, W_down, Y_partial, T, H, I_shard, kind, workspace, need, s),
+    return from_hip(mlp_bf16(X, W_gate, W_up, W_down, Y_partial, T, H, I_shard, kind, workspace, need, s,
+                             h_dt == TP_F16),
                     "tp_mlp_shard");
 }
 

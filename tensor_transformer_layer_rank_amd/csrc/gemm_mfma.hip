@@ -432,9 +432,9 @@ struct EpiStore {
     }
 };
 
-// h = SiLU(gate * gs) * (up * us); stored as bf16 (H8 = false) or as the E4M3 code of
-// h * (1 / h_scale) (H8 = true).
-template <bool H8>
+// h = SiLU(gate * gs) * (up * us); stored as bf16 (HK = 0), fp16 (HK = 1) or as the E4M3 code of
+// h * (1 / h_scale) (HK = 2).
+template <int HK>
 struct EpiSwiGLU {
     void* h;   // [M, N]
     int64_t M, N;
@@ -442,7 +442,7 @@ struct EpiSwiGLU {
     // acc[i][0..1] hold gate columns, acc[i][2..3] the matching up columns: 32 rows x 64 h
     __device__ void rows(const f32x16 (&a)[4], int i, int64_t m0, int64_t n0, int wm, int wn,
                          int lane, unsigned char* lds) const {
-        constexpr int ES = H8 ? 1 : 2;
+        constexpr int ES = HK == 2 ? 1 : 2;
         constexpr int PITCH = 64 * ES + 16;
         constexpr int CHUNKS = 64 * ES / 16;
         const int r32 = lane & 31, hi = lane >> 5;
@@ -454,7 +454,8 @@ struct EpiSwiGLU {
                 const float gte = a[j][r] * gs, up = a[j + 2][r] * us;
                 const float silu = gte * __builtin_amdgcn_rcpf(1.0f + __expf(-gte));   // rcp: 1 ulp
                 unsigned char* t = lds + acc_row(0, r, hi) * PITCH + (j * 32 + r32) * ES;
-                if (H8) *t = f32_to_e4m3(silu * up * h_inv);
+                if constexpr (HK == 2) *t = f32_to_e4m3(silu * up * h_inv);
+                else if constexpr (HK == 1) *reinterpret_cast<uint16_t*>(t) = f32_to_f16(silu * up);
                 else *reinterpret_cast<uint16_t*>(t) = f32_to_bf16(silu * up);
             }
         const int64_t row0 = m0 + wm * 128 + i * 32, col0 = n0 + wn * 64;
@@ -466,7 +467,7 @@ struct EpiSwiGLU {
             }, lane);
     }
     __device__ void shift_rows(int64_t r0, int64_t m) {
-        h = static_cast<unsigned char*>(h) + r0 * N * (H8 ? 1 : 2);
+        h = static_cast<unsigned char*>(h) + r0 * N * (HK == 2 ? 1 : 2);
         M = m;
     }
 };
@@ -1092,6 +1093,22 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
     return hipGetLastError();
 }
 
+// bf16 -> fp16, 8 elements (16 bytes) per thread: the exponent range of fp16 is narrower, so
+// values below 2^-14 in magnitude round to fp16 subnormals (RNE) and values past 65504 to inf
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out,
+                                                          int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const u32x4 v = in[i];
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float lo = __uint_as_float(v[k] << 16), hi = __uint_as_float(v[k] & 0xffff0000u);
+        o[k] = (unsigned)f32_to_f16(lo) | ((unsigned)f32_to_f16(hi) << 16);
+    }
+    out[i] = o;
+}
+
 __global__ void rope_table_kernel(float2* t, int64_t pos0, int64_t npos, double theta) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= npos * 64) return;
@@ -1175,10 +1192,12 @@ hipError_t gemm_f8_store(const void* A, const void* B, void* C, int64_t M, int64
 }
 
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
-                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s, int h_f16) {
     Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg),
                   static_cast<const uint16_t*>(Bu), M, N, K, K, N};
-    return launch<false, true>(g, EpiSwiGLU<false>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
+    if (h_f16)
+        return launch<false, true>(g, EpiSwiGLU<1>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_swiglu");
+    return launch<false, true>(g, EpiSwiGLU<0>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
                                "gemm_bf16_swiglu");
 }
 
@@ -1251,7 +1270,7 @@ hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* B
         const int64_t wo = (int64_t)x0 * K * N;
         Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg) + wo,
                       static_cast<const uint16_t*>(Bu) + wo, M, N, K, K, N};
-        hipError_t e = launch<false, true>(g, EpiSwiGLU<false>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
+        hipError_t e = launch<false, true>(g, EpiSwiGLU<0>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
                                            "gemm_bf16_swiglu", make_groups(row_offsets + x0, n, tn, K * N));
         if (e != hipSuccess) return e;
     }
@@ -1277,7 +1296,7 @@ hipError_t gemm_f8_swiglu(const void* A, const void* Bg, const void* Bu, void* h
                           void* ws, size_t ws_bytes, hipStream_t s) {
     Geom<true> g{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(Bg),
                  static_cast<const uint8_t*>(Bu), M, N, K, K, N};
-    return launch<true, true>(g, EpiSwiGLU<true>{h, M, N, gate_scale, up_scale, h_scale}, ws, ws_bytes, s,
+    return launch<true, true>(g, EpiSwiGLU<2>{h, M, N, gate_scale, up_scale, h_scale}, ws, ws_bytes, s,
                               "gemm_f8_swiglu");
 }
 
@@ -1287,6 +1306,15 @@ hipError_t gemm_bf16_qkv_rope(const void* X, const void* Wqkv, int64_t H, const 
     Geom<false> g{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wqkv), nullptr,
                   M, N, H, H, N};
     return launch<false, false>(g, EpiQKV{o, M}, ws, ws_bytes, s, "gemm_bf16_qkv_rope");
+}
+
+hipError_t bf16_to_f16(const void* in, void* out, int64_t n, hipStream_t s) {
+    const int64_t n8 = n / 8;
+    if (n8 == 0) return hipSuccess;
+    ProfScope ps("bf16_to_f16", s);
+    bf16_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(static_cast<const u32x4*>(in),
+                                                                     static_cast<u32x4*>(out), n8);
+    return hipGetLastError();
 }
 
 hipError_t rope_table(float2* table, int64_t pos0, int64_t npos, float theta, hipStream_t s) {

@@ -22,6 +22,11 @@ struct ProfScope {
     ~ProfScope() { prof_end(s); }
 };
 
+// ---- the allocation-free column linear call ------------------------------------------
+// Device address of the library's static scratch array (TP_NOALLOC_SCRATCH_BYTES) on the
+// device of stream s; looked up once per device.
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+
 // ---- exact fp32 path ---------------------------------------------------------------
 // C[M, N] (ldc) = act(A[M, K] (lda) . B[K, N] (ldb)); accumulate: C += A.B.
 hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K,
@@ -57,8 +62,11 @@ hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* B
                                     size_t ws_bytes, hipStream_t s);
 hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, const int64_t* row_offsets,
                                     int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
+// h_f16: h stored as fp16 instead of bf16
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
-                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
+                            int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s, int h_f16 = 0);
+// out[i] = fp16(in[i]) for n bf16 values (n a multiple of 8, 16-byte aligned buffers)
+hipError_t bf16_to_f16(const void* in, void* out, int64_t n, hipStream_t s);
 
 // ---- fp8 (OCP E4M3) MFMA path: operands are uint8 codes; every accumulator is scaled ----
 size_t gemm_f8_split_bytes(int64_t M, int64_t N, int64_t K, int dual);

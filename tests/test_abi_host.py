@@ -145,7 +145,13 @@ def test_mlp_validation(L):
     bad = list(args); bad[11] = None
     assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
     bad = list(args); bad[10] = tp.TP_F16
-    assert _st(f(*bad)) == "TP_ERR_UNSUPPORTED"
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"                       # fp16 h also holds W_down in fp16
+    ws16 = L.tp_mlp_workspace_size(512, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_F16)
+    assert ws16 >= ws + 256 * 128 * 2
+    bad = list(args); bad[10] = tp.TP_FP8_E4M3
+    assert _st(f(*bad)) == "TP_ERR_BAD_DTYPE"
+    bad = list(args); bad[10] = tp.TP_F16; bad[5] = 64; bad[12] = 1 << 30
+    assert _st(f(*bad)) == "TP_ERR_UNSUPPORTED"                     # fp16 h is a prefill-size option
     bad = list(args); bad[7] = 100
     bws = L.tp_mlp_workspace_size(512, 256, 100, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16)
     bad[12] = bws
@@ -331,3 +337,15 @@ def test_backward_transpose_grid_limit(L):
     assert _st(L.tp_linear_backward(FAKE, FAKE, FAKE, FAKE, FAKE, 64, n, n, tp.TP_BF16, FAKE, 1 << 40, None)) == \
         "TP_ERR_UNSUPPORTED"
     assert "2^24 tiles" in L.tp_last_error().decode()
+
+
+def test_noalloc_column_linear_validation(L):
+    """The allocation-free variant checks like tp_column_linear and refuses a few-row call whose
+    partial sums exceed its static scratch, before any HIP call."""
+    f = L.tp_column_linear_noalloc
+    assert _st(f(None, FAKE, FAKE, 4, 8, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 12, 8, 8, tp.TP_BF16, tp.TP_BF16, 0, None, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE, FAKE, FAKE, 4, 8, 8, 8, 9, tp.TP_BF16, 0, None, None)) == "TP_ERR_BAD_DTYPE"
+    assert L.tp_linear_workspace_size(64, 512, 131072, tp.TP_BF16) > 16 << 20
+    assert _st(f(FAKE, FAKE, FAKE, 64, 512, 131072, 131072, tp.TP_BF16, tp.TP_F32, 0, None, None)) == "TP_ERR_UNSUPPORTED"
+    assert "scratch" in L.tp_last_error().decode()

@@ -40,7 +40,7 @@ def test_recorded_traffic_tracks_the_kernel_source():
 def test_sampled_steps_counts_the_kernel_timed_steps():
     sys.path.insert(0, ROOT)
     import bench
-    assert bench.sampled_steps(20) == 4 and bench.sampled_steps(100) == 20 and bench.sampled_steps(3) == 1
+    assert bench.sampled_steps(20) == 2 and bench.sampled_steps(100) == 10 and bench.sampled_steps(3) == 1
 
 
 def test_bench_does_not_import_the_tests():

@@ -437,6 +437,22 @@ def test_row_linear_partial_tail_split_accumulate(tp):
     assert_close_bf16(host(P), 2 * O.linear(X, W), "split row partial accumulate")
 
 
+@pytest.mark.parametrize("T,H,I,kind", [(300, 256, 200, "swiglu"), (520, 512, 264, "relu"), (4200, 296, 2048, "swiglu"),
+                                        (65, 1024, 136, "swiglu")])
+def test_mlp_fp16_h(tp, T, H, I, kind):
+    """bf16 inputs with h stored in fp16 (down projection on fp16 operands, W_down converted)."""
+    import torch
+    inp = wl.random_mlp(T + 2 * H + I, T, H, I)
+    k = tp.TP_MLP_SWIGLU if kind == "swiglu" else tp.TP_MLP_RELU
+    Y = tp.mlp_shard(dev(inp.X), dev(inp.W_gate), dev(inp.W_up) if kind == "swiglu" else None, dev(inp.W_down),
+                     Y=_nan((T, H), torch.float32), kind=k, h_dtype=tp.TP_F16)
+    torch.cuda.synchronize()
+    ref = (O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down) if kind == "swiglu"
+           else O.mlp_relu_shard(inp.X, inp.W_gate, inp.W_down))
+    rf, _ = assert_close_bf16(host(Y), ref, f"mlp fp16 h {kind} {T}x{H}x{I}")
+    assert rf < 1e-3, "an fp16 h should leave far less error than a bf16 one"
+
+
 def _f16(a):
     """float32 values rounded to IEEE half (input preparation for the fp16-operand calls)."""
     return np.asarray(a, np.float32).astype(np.float16).astype(np.float32)
@@ -608,13 +624,15 @@ def test_layer70b_tp8_full_size(tp):
     inp = wl.layer70b_tp8()
     Xd = _attn_full_size(tp, inp)
     m = inp.mlp
-    Y = tp.mlp_shard(Xd, dev(m.W_gate), dev(m.W_up), dev(m.W_down), Y=_nan((8192, 8192), torch.float32))
+    # h in fp16: with bf16 h this shard's worst element lands at 2.8e-2 of the 3e-2 bar
+    Y = tp.mlp_shard(Xd, dev(m.W_gate), dev(m.W_up), dev(m.W_down), Y=_nan((8192, 8192), torch.float32),
+                     h_dtype=tp.TP_F16)
     torch.cuda.synchronize()
     y = host(Y)
     del Y
     assert np.all(np.isfinite(y))
     ref = O.mlp_swiglu_shard(m.X, m.W_gate, m.W_up, m.W_down)
-    assert_close_bf16(y, ref, "layer70b_tp8 mlp full output")
+    assert_close_bf16(y, ref, "layer70b_tp8 mlp (fp16 h) full output")
 
 
 # ---------------------------------------------------------------- decode step
