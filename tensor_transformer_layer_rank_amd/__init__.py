@@ -23,7 +23,8 @@ __all__ = [
     "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
+# TPSHARD_LIB names another build of the same library (e.g. the host-checked one)
+LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
 
 TP_F32, TP_BF16, TP_F16, TP_FP8_E4M3 = 0, 1, 2, 3
 TP_ACT_NONE, TP_ACT_RELU = 0, 1

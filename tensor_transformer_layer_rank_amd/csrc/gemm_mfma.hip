@@ -15,11 +15,11 @@
 // per SIMD; each wave owns 128 x 128 outputs = 4 x 4 MFMA 32x32 blocks (256 fp32
 // accumulators per lane, held in the accumulation registers).
 // Staging: K steps (32 bf16 or 64 fp8 = 64 bytes of each activation row) go global -> LDS
-// directly (global_load_lds_dwordx4, no register staging) into a ring of 4 LDS stages of
-// 32 KB, so three K steps of loads are in flight while the MFMAs consume the fourth. One
-// barrier per K step, placed inside the step: it publishes the next stage and releases the
-// oldest one for refilling, so the next stage's first operand fragments are read while the
-// current step's MFMAs still run.
+// directly (global_load_lds_dwordx4, no register staging) into a ring of 5 LDS stages of
+// 32 KB (all 160 KB of the CU's LDS): while one step is computed the next three are landing
+// or in flight and the fifth stage, released by the previous step, is being refilled. One
+// barrier per K step, placed inside the step: it publishes the next stage, so the next
+// stage's first operand fragments are read while the current step's MFMAs still run.
 // LDS layouts: the activation tile is kept [m][k] (64-byte rows) and read with
 // ds_read_b128; the weight tile is kept in its memory order [k][n] (512-byte rows for bf16,
 // 256 for fp8) and read with the gfx950 transposing loads ds_read_b64_tr_b16 / _b8, which
@@ -50,7 +50,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int BM = 256, BN = 256, NTHR = 256, NSTAGE = 4;
+constexpr int BM = 256, BN = 256, NTHR = 256, NSTAGE = 5;
 constexpr int A_STRIDE = 64;              // bytes per activation row (one K step)
 constexpr int A_BYTES = BM * A_STRIDE;    // 16384
 constexpr int B_BYTES = 16384;            // one K step of the weight tile
@@ -168,24 +168,29 @@ __device__ __forceinline__ void make_plan(DmaPlan& p, const Geom<F8>& g, int64_t
 }
 
 // One 16-byte global -> LDS transfer per lane; the lanes of a wave fill 64 consecutive
-// granules starting at dst (wave-uniform). Written as a volatile asm statement with no
-// register outputs: the compiler then neither reorders it against other memory accesses
-// nor adds its own vmcnt waits before LDS reads (it cannot tell which stage a DMA writes),
-// and the kernel keeps the exact per-stage vmcnt accounting itself.
-__device__ __forceinline__ void dma16(const void* src, unsigned char* dst) {
-    const unsigned lds = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)(dst)));
+// granules starting at LDS byte address `lds` (wave-uniform). Written as a volatile asm
+// statement with no register outputs: the compiler then neither reorders it against other
+// memory accesses nor adds its own vmcnt waits before LDS reads (it cannot tell which stage a
+// DMA writes), and the kernel keeps the exact per-stage vmcnt accounting itself. The LDS
+// address is a plain 32-bit offset carried in scalar registers (a generic pointer would need
+// a null check per transfer to become one).
+__device__ __forceinline__ void dma16(const void* src, unsigned lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ buffer (a link-time constant)
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+    return (unsigned)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)(p));
 }
 
 // Issue this wave's DMA_A + DMA_B loads for the K step starting at k0 into `stage`.
 template <bool DUAL, bool F8>
-__device__ __forceinline__ void issue_stage(unsigned char* stage, const DmaPlan& p, const Geom<F8>& g,
+__device__ __forceinline__ void issue_stage(unsigned stage, const DmaPlan& p, const Geom<F8>& g,
                                             const typename Fmt<F8>::E* a_base, int64_t m0, int64_t n0,
                                             int64_t k0, int wave, int lane) {
     constexpr int BK = Fmt<F8>::BK, EPG = Fmt<F8>::EPG;
-    unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
-    unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
+    const unsigned a_dst = stage + wave * A_PER_WAVE * 16;
+    const unsigned b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
     if (k0 + BK <= g.K) {
         const auto* a_k = a_base + k0;
         const auto* b_k = g.B1 + k0 * g.ldb;
@@ -589,16 +594,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 template <bool F8>
 __device__ __forceinline__ bool k0_full(const Geom<F8>& g, int64_t k0) { return k0 + Fmt<F8>::BK <= g.K; }
 
-// Wait until this wave's DMA for a stage has landed while `pending` later stages (0..3) may
-// still be in flight, zero its granules past K if it is the partial final step, then
-// barrier: after it the stage is readable by every wave.
+// Wait until this wave's DMA for a stage has landed while the `ops` DMA instructions it issued
+// after that stage's may still be in flight, zero its granules past K if it is the partial
+// final step, then barrier: after it the stage is readable by every wave.
 template <bool F8>
-__device__ __forceinline__ void publish(unsigned char* stage, int pending, const Geom<F8>& g,
+__device__ __forceinline__ void publish(unsigned char* stage, int ops, const Geom<F8>& g,
                                         int64_t k0, int wave, int lane) {
     constexpr int GRP = DMA_A + DMA_B;
-    if (pending >= 3) wait_vm<3 * GRP>();
-    else if (pending == 2) wait_vm<2 * GRP>();
-    else if (pending == 1) wait_vm<GRP>();
+    if (ops >= 3 * GRP) wait_vm<3 * GRP>();
+    else if (ops >= 2 * GRP + DMA_A) wait_vm<2 * GRP + DMA_A>();
+    else if (ops >= 2 * GRP) wait_vm<2 * GRP>();
+    else if (ops >= GRP + DMA_A) wait_vm<GRP + DMA_A>();
+    else if (ops >= GRP) wait_vm<GRP>();
+    else if (ops >= DMA_A) wait_vm<DMA_A>();
     else wait_vm<0>();
     if (k0 + Fmt<F8>::BK > g.K) {
         wait_vm<0>();
@@ -609,57 +617,68 @@ __device__ __forceinline__ void publish(unsigned char* stage, int pending, const
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One bf16 K step kt on stage `cur` (slice-0 fragments already in f0). The instruction
-// order is pinned: slice-0 MFMAs alternate with the reads of slice 1 (into f1); then stage
-// kt+1 is published (wait + barrier), after which `cur` is free; slice-1 MFMAs then
-// alternate with the reads of stage kt+1's slice 0 (into f0) and with this wave's DMA
-// refilling `cur` with step kt+4. The MFMA pipe thus always has queued work while loads
-// are issued. STEADY steps (every step but the last five of a tile) know at compile time
-// that a next step exists, that the refill is a whole step and that two later stages are in
-// flight, so their instruction stream has no branches.
+// DMA instructions this wave issued after those of stage kt+1 and before publishing it: the
+// stages kt+2 and kt+3 that exist, plus `refill_ops` of step kt+4
+__device__ __forceinline__ int ops_after_next(int kt, int nk, int refill_ops) {
+    constexpr int GRP = DMA_A + DMA_B;
+    const int last = nk - 1 < kt + 3 ? nk - 1 : kt + 3;
+    return GRP * (last - (kt + 1)) + refill_ops;
+}
+
+// One bf16 K step kt on stage `cur` (slice-0 fragments already in f0). Five LDS stages: while
+// step kt is computed, kt+1 has landed or is landing, kt+2 and kt+3 are in flight, and step
+// kt+4 is loaded into the stage of step kt-1 (`ref`), which every wave finished reading before
+// the previous step's barrier. The instruction order is pinned: slice-0 MFMAs alternate with
+// the reads of slice 1 (into f1) and with this wave's activation DMA for step kt+4; stage kt+1
+// is published (wait + barrier); slice-1 MFMAs then alternate with the reads of stage kt+1's
+// slice 0 (into f0) and with the weight DMA for step kt+4. Splitting the step's DMA over both
+// halves keeps the four waves from queueing all their DMA at the texture units at once (with
+// all of it after the barrier, that queue stalled the MFMA issue for ~190 of ~1340 cycles).
+// STEADY steps (every step but the last five of a tile) know at compile time that a next step
+// exists, that the refill is a whole step and that two later stages are in flight, so their
+// instruction stream has no branches.
 template <bool DUAL, bool STEADY, bool F16>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
-                                       unsigned char* cur, unsigned char* nxt, int kt, int nk,
+                                       unsigned char* cur, unsigned char* nxt, unsigned ref_lds, int kt, int nk,
                                        int64_t kbase, const DmaPlan& p, const Geom<false>& g,
                                        const uint16_t* a_base, int64_t m0, int64_t n0, int wm, int wn,
                                        int wave, int lane) {
     constexpr int BK = Fmt<false>::BK;
     constexpr int GRP = DMA_A + DMA_B;
+    const bool has_next = STEADY || kt + 1 < nk;
+    const bool refill = STEADY || kt + 4 < nk;
+    const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
+    // whole refill steps interleave their DMA with the MFMAs; a partial final step takes the
+    // general path up front
+    const bool inline_dma = STEADY || (refill && k0_full<false>(g, k_ref));
+    if (refill && !inline_dma) issue_stage<DUAL, false>(ref_lds, p, g, a_base, m0, n0, k_ref, wave, lane);
+    const uint16_t* a_k = a_base + k_ref;
+    const uint16_t* b_k = g.B1 + k_ref * g.ldb;
+    const unsigned a_dst = ref_lds + wave * A_PER_WAVE * 16;
+    const unsigned b_dst = ref_lds + A_BYTES + wave * B_PER_WAVE * 16;
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         mfma1<F16>(acc, f0, n);
         if (n < 8) read_piece<DUAL>(f1, n, cur, 1, wm, wn, lane);
+        if (inline_dma && (n & 3) == 2) dma16(a_k + p.a_off[n >> 2], a_dst + (n >> 2) * 1024);
         TP_FENCE();
     }
-    const bool has_next = STEADY || kt + 1 < nk;
-    const bool refill = STEADY || kt + 4 < nk;
     if constexpr (STEADY) {
-        wait_vm<2 * GRP>();                     // stage kt+1 landed; kt+2, kt+3 may be in flight
+        wait_vm<2 * GRP + DMA_A>();             // stage kt+1 landed; kt+2, kt+3, kt+4 (A) may be in flight
         __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     } else if (has_next) {
-        // stages issued after kt+1 and still allowed in flight: kt+2, kt+3
-        const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
-        publish<false>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
+        publish<false>(nxt, ops_after_next(kt, nk, refill ? (inline_dma ? DMA_A : GRP) : 0), g,
+                       kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
-    // full refill steps interleave their DMA with the MFMAs; a partial final step takes
-    // the general path up front
-    const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
-    const bool inline_dma = STEADY || (refill && k0_full<false>(g, k_ref));
-    if (refill && !inline_dma) issue_stage<DUAL, false>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
-    const uint16_t* a_k = a_base + k_ref;
-    const uint16_t* b_k = g.B1 + k_ref * g.ldb;
-    unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
-    unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         mfma1<F16>(acc, f1, n);
         if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
-        if (inline_dma && n >= 6 && n < 6 + DMA_A) dma16(a_k + p.a_off[n - 6], a_dst + (n - 6) * 1024);
-        if (inline_dma && n >= 10 && n < 10 + DMA_B) dma16(b_k + p.b_off[n - 10], b_dst + (n - 10) * 1024);
+        if (inline_dma && (n & 3) == 2) dma16(b_k + p.b_off[n >> 2], b_dst + (n >> 2) * 1024);
         TP_FENCE();
     }
 }
@@ -669,11 +688,11 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
 // the first four MFMAs. The barrier that publishes stage kt+1 (and frees `cur`) follows
 // them; the remaining twelve MFMAs then alternate with the reads of stage kt+1 — its weight
 // fragments into bn (the other weight buffer), its activation block i into a[i] as soon as
-// the last MFMA of row block i has been issued — and with the DMA refilling `cur` with
-// step kt+4.
+// the last MFMA of row block i has been issued — and with the DMA loading step kt+4 into the
+// stage of step kt-1 (`ref`).
 template <bool DUAL, bool STEADY>
 __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i32x8 (&bc)[4],
-                                          i32x8 (&bn)[4], unsigned char* cur, unsigned char* nxt,
+                                          i32x8 (&bn)[4], unsigned char* cur, unsigned char* nxt, unsigned ref_lds,
                                           int kt, int nk, int64_t kbase, const DmaPlan& p,
                                           const Geom<true>& g, const uint8_t* a_base, int64_t m0,
                                           int64_t n0, int wm, int wn, int wave, int lane) {
@@ -694,17 +713,17 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     } else if (has_next) {
-        const int pending = (nk - kt - 2 < 2) ? nk - kt - 2 : 2;
-        publish<true>(nxt, pending, g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
+        publish<true>(nxt, ops_after_next(kt, nk, 0), g, kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
+    // step kt+4 goes to the stage of step kt-1 (free since the previous step's barrier)
     const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
     const bool inline_dma = STEADY || (refill && k0_full<true>(g, k_ref));
-    if (refill && !inline_dma) issue_stage<DUAL, true>(cur, p, g, a_base, m0, n0, k_ref, wave, lane);
+    if (refill && !inline_dma) issue_stage<DUAL, true>(ref_lds, p, g, a_base, m0, n0, k_ref, wave, lane);
     const uint8_t* a_k = a_base + k_ref;
     const uint8_t* b_k = g.B1 + k_ref * g.ldb;
-    unsigned char* a_dst = cur + wave * A_PER_WAVE * 16;
-    unsigned char* b_dst = cur + A_BYTES + wave * B_PER_WAVE * 16;
+    const unsigned a_dst = ref_lds + wave * A_PER_WAVE * 16;
+    const unsigned b_dst = ref_lds + A_BYTES + wave * B_PER_WAVE * 16;
     const unsigned char* nb = nxt + A_BYTES;
 #pragma unroll
     for (int n = 4; n < 16; ++n) {
@@ -800,6 +819,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
     __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st4[STAGE_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
@@ -854,17 +874,38 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     if (nk > 0) {
-        // prologue: steps 0..3 in flight, publish step 0
-        issue_stage<DUAL, F8>(st0, p, g, a_base, m0, n0, kbase, wave, lane);
-        if (nk > 1) issue_stage<DUAL, F8>(st1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
-        if (nk > 2) issue_stage<DUAL, F8>(st2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
-        if (nk > 3) issue_stage<DUAL, F8>(st3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
-        publish<F8>(st0, (nk - 1 < 3) ? nk - 1 : 3, g, kbase, wave, lane);
+        // prologue: steps 0..3 in flight, publish step 0; step 4 is loaded during step 0
+        const unsigned l0 = lds_addr(st0), l1 = lds_addr(st1), l2 = lds_addr(st2), l3 = lds_addr(st3),
+                       l4 = lds_addr(st4);
+        issue_stage<DUAL, F8>(l0, p, g, a_base, m0, n0, kbase, wave, lane);
+        if (nk > 1) issue_stage<DUAL, F8>(l1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
+        if (nk > 2) issue_stage<DUAL, F8>(l2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
+        if (nk > 3) issue_stage<DUAL, F8>(l3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
+        publish<F8>(st0, (DMA_A + DMA_B) * ((nk - 1 < 3) ? nk - 1 : 3), g, kbase, wave, lane);
 
-        unsigned char* sa = st0;   // stage of step kt; sb, sc, sd hold steps kt+1, kt+2, kt+3
+        // stage of step kt (and its LDS address); sb, sc, sd hold steps kt+1, kt+2, kt+3 and se
+        // (the stage of step kt-1) receives step kt+4
+        unsigned char* sa = st0;
         unsigned char* sb = st1;
         unsigned char* sc = st2;
         unsigned char* sd = st3;
+        unsigned char* se = st4;
+        unsigned la = l0, lb = l1, lc = l2, ld = l3, le = l4;
+#define TP_ROTATE1()            \
+    do {                        \
+        unsigned char* t = sa;  \
+        sa = sb;                \
+        sb = sc;                \
+        sc = sd;                \
+        sd = se;                \
+        se = t;                 \
+        const unsigned u = la;  \
+        la = lb;                \
+        lb = lc;                \
+        lc = ld;                \
+        ld = le;                \
+        le = u;                 \
+    } while (0)
         if constexpr (!F8) {
             Frags f0, f1;
             read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
@@ -872,20 +913,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             // whole and not the tile's last step, and two stages after kt+1 are in flight
             int kt = 0;
             for (; kt < nk - 5; ++kt) {
-                k_step<DUAL, true, F16>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                unsigned char* t = sa;
-                sa = sb;
-                sb = sc;
-                sc = sd;
-                sd = t;
+                k_step<DUAL, true, F16>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                TP_ROTATE1();
             }
             for (; kt < nk; ++kt) {
-                k_step<DUAL, false, F16>(acc, f0, f1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                unsigned char* t = sa;
-                sa = sb;
-                sb = sc;
-                sc = sd;
-                sd = t;
+                k_step<DUAL, false, F16>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                TP_ROTATE1();
             }
         } else {
             i32x8 a[4], b0[4], b1[4];
@@ -903,36 +936,25 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
             // step's weight fragments into b0 (32 register moves).
             int kt = 0;
             for (; kt + 1 < nk - 5; kt += 2) {   // steady steps in pairs: the weight buffers swap by name
-                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                k_step_f8<DUAL, true>(acc, a, b1, b0, sb, sc, kt + 1, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                unsigned char* t0 = sa;
-                unsigned char* t1 = sb;
-                sa = sc;
-                sb = sd;
-                sc = t0;
-                sd = t1;
+                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step_f8<DUAL, true>(acc, a, b1, b0, sb, sc, la, kt + 1, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                TP_ROTATE1();
+                TP_ROTATE1();
             }
             for (; kt < nk - 5; ++kt) {   // steady steps, as in the bf16 loop
-                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                unsigned char* t = sa;
-                sa = sb;
-                sb = sc;
-                sc = sd;
-                sd = t;
+                k_step_f8<DUAL, true>(acc, a, b0, b1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                TP_ROTATE1();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) b0[j] = b1[j];
             }
             for (; kt < nk; ++kt) {
-                k_step_f8<DUAL, false>(acc, a, b0, b1, sa, sb, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
-                unsigned char* t = sa;
-                sa = sb;
-                sb = sc;
-                sc = sd;
-                sd = t;
+                k_step_f8<DUAL, false>(acc, a, b0, b1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                TP_ROTATE1();
 #pragma unroll
                 for (int j = 0; j < 4; ++j) b0[j] = b1[j];
             }
         }
+#undef TP_ROTATE1
     }
     if (q < 0) {
         __syncthreads();   // every wave is done with the stages; each now uses one as its tile
