@@ -50,7 +50,7 @@ def parse():
                     help="seconds of untimed back-to-back headline steps before the first leg (clock settling)")
     ap.add_argument("--no-parity", action="store_true", help="skip the element-wise oracle comparison")
     ap.add_argument("--legs", default="all",
-                    help="comma-separated subset of c0,c1,c2,c3,c4,fp8,merge,backward,moe (profiling runs); "
+                    help="comma-separated subset of c0,c1,c2,c3,c4,fp8,merge,backward,moe,ceiling (profiling runs); "
                          "the headline needs c1")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
@@ -155,11 +155,14 @@ def clock_power(step, seconds: float = 2.5):
         step()
         e1.record(s)
         torch.cuda.synchronize()
-        n = max(1, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+        step_ms = e0.elapsed_time(e1)
+        n = max(1, int(seconds * 1e3 / max(step_ms, 1e-3)))
         seen, fresh = {stamp0}, []
         t0 = tlast = time.perf_counter()
-        for _ in range(n):   # launches block once the queue is full, so the reads interleave
+        for i in range(n):   # launches block once the queue is full, so the reads interleave
             step()
+            if step_ms > 2.0 and i % max(1, int(20.0 / step_ms)) == 0:
+                torch.cuda.synchronize()   # long steps: keep the host in step with the GPU
             now = time.perf_counter()
             if now - tlast > 0.05:
                 tlast = now
@@ -408,13 +411,26 @@ def decode_bench(args):
         cur.wait_stream(s_attn)
         cur.wait_stream(s_mlp)
 
+    ws_f = torch.empty(tp.decode_step_workspace_size(B, H, hq, hkv, inp.theta, kc, vc, inp.cache_len, I, V),
+                       dtype=torch.uint8, device="cuda")
+
+    def step_fused():   # tp_decode_step: the same three parts in five launches on one stream
+        tp.decode_step(X, Wqkv, Wo, hq, hkv, inp.theta, kc, vc, inp.cache_len, Wg, Wu, Wd, Wlm,
+                       Y_attn=Ya, Y_mlp=Ym, logits=logits, workspace=ws_f)
+
     outs = (Ya, Ym, logits)
-    ms_eager = timed(step, args.warmup, args.steps)       # per-kernel HIP-event timing
+    ms_sep_eager = timed(step, args.warmup, args.steps)
+    ms_sep_graph, _ = graph_timed(step_branches, args.warmup, args.steps)
+    ms_eager = timed(step_fused, args.warmup, args.steps)       # per-kernel HIP-event timing
+    att_ms, att_n = kernel_avg("decode_attn")
+    sk_ms, sk_n = kernel_avg("skinny_gemm")
+    rd_ms, rd_n = kernel_avg("skinny_reduce")
+    x_ms, _ = kernel_avg("skinny_gemm_x")
+    od_ms, _ = kernel_avg("skinny_gemm_od")
     eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
-    ms_serial, _ = graph_timed(step, args.warmup, args.steps)
     for t in outs:
         t.fill_(float("nan"))
-    ms, _ = graph_timed(step_branches, args.warmup, args.steps, "decode")   # the step as one HIP graph
+    ms, _ = graph_timed(step_fused, args.warmup, args.steps, "decode")   # the step as one HIP graph
     torch.cuda.synchronize()
     # the outputs left by the last timed replay must equal the eager step's, bit for bit
     replay = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
@@ -425,22 +441,22 @@ def decode_bench(args):
     new_kv = 2 * 2 * B * hkv * d                       # the new key/value written (and read back)
     act = 2 * B * H + 4 * (2 * B * H + B * V)          # X in; two fp32 partials and the logits out
     total = w_bytes + kv_bytes + 2 * new_kv + act
-    att_ms, att_n = kernel_avg("decode_attn")
-    sk_ms, sk_n = kernel_avg("skinny_gemm")
-    rd_ms, rd_n = kernel_avg("skinny_reduce")
     nsamp = sampled_steps(args.steps)
     return {
         "ms_per_step": ms,
         "ms_per_step_eager": ms_eager,
-        "ms_per_step_graph_serial": ms_serial,
+        "ms_per_step_separate_calls_eager": ms_sep_eager,
+        "ms_per_step_separate_calls_graph": ms_sep_graph,
         "step_stats": STEP_STATS.get("decode"),
-        "graph": "one HIP graph per step: attention, MLP and LM-head branches on separate streams",
+        "graph": "tp_decode_step (5 launches) captured as one HIP graph; separate_calls: tp_attn_shard, "
+                 "tp_mlp_shard, tp_column_linear as three graph branches on their own streams",
         "graph_outputs_equal_eager": same,
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
         "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
-                    "skinny_gemm*(avg_us)": sk_ms * 1e3 if sk_ms else None,
+                    "skinny_gemm_x: QKV + gate/up + head (avg_us)": x_ms * 1e3 if x_ms else None,
+                    "skinny_gemm_od: O + down (avg_us)": od_ms * 1e3 if od_ms else None,
                     "skinny_gemm*(launches/step)": sk_n / nsamp,
                     "skinny_reduce*(avg_us)": rd_ms * 1e3 if rd_ms else None,
                     "skinny_reduce*(launches/step)": rd_n / nsamp},
@@ -600,6 +616,48 @@ def moe_bench(args):
         "step_stats": STEP_STATS.get("moe"),
         "kernels": kern,
     }
+
+
+def ceiling_bench(args):
+    """The matrix pipe's sustained bf16 rate with operands in registers (tp_mfma_rate_probe), for
+    random N(0,1) operands and for low-entropy ones, with the clock and socket power meanwhile:
+    the power-limited roof that any bf16 GEMM on real data sits under."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(9)
+    pats = {"random_normal": torch.randn(8 * 256 * 8, device="cuda", generator=g).to(torch.bfloat16),
+            "ones": torch.ones(8 * 256 * 8, device="cuda", dtype=torch.bfloat16),
+            "zeros": torch.zeros(8 * 256 * 8, device="cuda", dtype=torch.bfloat16)}
+    res = {}
+    for name, ops in pats.items():
+        def run(iters):
+            tp.mfma_rate_probe(ops, out, n_wg, iters)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        run(2000)
+        torch.cuda.synchronize()
+        e0.record()
+        run(2000)
+        e1.record()
+        torch.cuda.synchronize()
+        iters = max(1000, int(2000 * 20.0 / max(e0.elapsed_time(e1), 1e-3)))   # ~20 ms per launch
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.5:   # settle the clock at the power limit first
+            run(iters)
+            torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            run(iters)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        flops = n_wg * 4 * 16 * iters * 32768.0
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "ms_per_launch": ms,
+                     "clock_power": None if args.no_clock else clock_power(lambda: run(iters), 2.0)}
+    return {"what": "v_mfma_f32_32x32x16_bf16 back to back, operands in registers, 16 accumulators per wave, "
+                    "one 4-wave workgroup per compute unit (tp_mfma_rate_probe)", "patterns": res}
 
 
 def traffic_probe():
@@ -770,7 +828,7 @@ def main():
     torch.cuda.set_device(0)
     tp.load()
     legs = set(args.legs.split(",")) if args.legs != "all" else \
-        {"c0", "c1", "c2", "c3", "c4", "fp8", "merge", "backward", "moe"}
+        {"c0", "c1", "c2", "c3", "c4", "fp8", "merge", "backward", "moe", "ceiling"}
     keep = {}
     mlp = c0 = c2 = c3 = dec = fp8 = merge = bwd = moe = None
     if "c1" in legs:
@@ -787,13 +845,15 @@ def main():
     merge = merge_bench(args) if "merge" in legs else None
     bwd = backward_bench(args) if "backward" in legs else None
     moe = moe_bench(args) if "moe" in legs else None
+    ceiling = ceiling_bench(args) if "ceiling" in legs else None
     if args.traffic_probe:
         traffic_probe()
     torch.cuda.synchronize()
     par = None if args.no_parity else cpu_oracle_leg(keep)
     if mlp is None:
         print(json.dumps({"legs": sorted(legs), "c0": c0, "c2": c2, "c3": c3, "decode": dec, "fp8_mlp": fp8,
-                          "merge_rmsnorm": merge, "backward": bwd, "moe": moe, "parity": par}))
+                          "merge_rmsnorm": merge, "backward": bwd, "moe": moe, "mfma_ceiling": ceiling,
+                          "parity": par}))
         return
     cpu = None if args.no_cpu else cpu_baseline(keep["c1"]["inp"], args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
@@ -838,6 +898,7 @@ def main():
         "merge_rmsnorm": merge,
         "backward": bwd,
         "moe": moe,
+        "mfma_ceiling": ceiling,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},
     }

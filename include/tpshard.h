@@ -224,6 +224,29 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
 size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt);
 
 /*
+ * tp_decode_step — one rank's whole decode step (one new token for each of B sequences) in five
+ *   launches: its attention shard with the KV cache kept on the rank ("TensorRT LLM 中的并行策略",
+ *   注意力模块), its MLP shard, and its slice of the vocabulary-split output layer ("张量并行：切分
+ *   Transformer 层的分布式训练", 输入与输出层), all on the same input X. The projections that read X
+ *   (QKV, gate/up, output layer) stream their weights in one launch and O / down in another, so
+ *   the step pays the start and end of a launch five times instead of once per layer.
+ *   X [B, H] bf16, B <= 64; desc: a decode step (S == 1, k_cache / v_cache, cache_len <
+ *   cache_capacity; the call appends the new token's rotated key and value at slot cache_len, as
+ *   tp_attn_shard does); W_qkv, W_o as for tp_attn_shard; W_gate, W_up [H, I_shard] and W_down
+ *   [I_shard, H] bf16 (SwiGLU); W_lm [H, V_shard] bf16, or NULL with V_shard = 0 (no output layer).
+ *   Y_attn, Y_mlp [B, H] fp32 partials (overwritten); logits [B, V_shard] fp32.
+ *   The results are those of tp_attn_shard, tp_mlp_shard and tp_column_linear (fp32 output) on the
+ *   same arguments, up to the order of their fp32 split sums. H, I_shard, V_shard multiples of 8;
+ *   tensors 16-byte aligned; workspace >= tp_decode_step_workspace_size(desc, I_shard, V_shard)
+ *   bytes, 16-byte aligned (contents on return unspecified). Deterministic.
+ */
+tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
+                         const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
+                         const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
+                         void* workspace, size_t ws_bytes, void* stream);
+size_t tp_decode_step_workspace_size(const tp_attn_desc* desc, int64_t I_shard, int64_t V_shard);
+
+/*
  * tp_partial_sum — out = ((P_0 + P_1) + P_2) + ... + P_{k-1}, element-wise, in that
  *   order, fp32 ("CUDA tensor parallel computations", 第三类 Row Parallel: partial
  *   contributions are summed; 第四类: the all-reduce result). All buffers are on the
@@ -340,6 +363,17 @@ int tp_abi_version(void);
  * Off by default; at most 65536 launches are recorded between resets.
  */
 tp_status tp_profile_enable(int on);
+/*
+ * Measurement aid (not part of the shard computation): the matrix pipe's sustained bf16 rate
+ * under the board's power limit. Launches n_workgroups workgroups of 4 waves; every wave issues
+ * 16 * iters back-to-back v_mfma_f32_32x32x16_bf16 (32768 flop each) on register operands
+ * loaded once from `operands` (device, 8 fragments x 256 lanes x 16 bytes of bf16: fragments
+ * 0..3 feed the A side, 4..7 the B side), so no memory traffic occurs inside the loop. out
+ * (device) receives n_workgroups * 256 fp32 checksums. Total work: n_workgroups * 4 * 16 *
+ * iters * 32768 flop. 1 <= n_workgroups <= 2^20, 1 <= iters <= 2^30.
+ */
+tp_status tp_mfma_rate_probe(const void* operands, float* out, int64_t n_workgroups, int64_t iters,
+                             void* stream);
 tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches);
 tp_status tp_profile_reset(void);
 

@@ -38,7 +38,8 @@ EXPORTS = [
     "tp_status_string", "tp_last_error", "tp_abi_version", "tp_profile_enable",
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
     "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size", "tp_moe_mlp_shard",
-    "tp_moe_workspace_size", "tp_column_linear_noalloc",
+    "tp_moe_workspace_size", "tp_column_linear_noalloc", "tp_mfma_rate_probe", "tp_decode_step",
+    "tp_decode_step_workspace_size",
 ]
 
 
@@ -108,6 +109,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
                               _P, _SZ, _P], _I32),
         "tp_moe_workspace_size": ([_I64, _I64, _I64, _I32, ctypes.POINTER(_I64)], _SZ),
         "tp_column_linear_noalloc": ([_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P], _I32),
+        "tp_mfma_rate_probe": ([_P, _P, _I64, _I64, _P], _I32),
+        "tp_decode_step": ([_P, _P, _P, ctypes.POINTER(AttnDesc), _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ,
+                            _P], _I32),
+        "tp_decode_step_workspace_size": ([ctypes.POINTER(AttnDesc), _I64, _I64], _SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -312,6 +317,33 @@ def attn_shard(X, W_qkv, W_o, B: int, S: int, hq: int, hkv: int, theta: float = 
     return Y
 
 
+def decode_step_workspace_size(B, H, hq, hkv, theta, k_cache, v_cache, cache_len, I, V) -> int:
+    d = _desc(B, 1, H, hq, hkv, theta, k_cache, v_cache, cache_len)
+    return int(lib().tp_decode_step_workspace_size(ctypes.byref(d), I, V))
+
+
+def decode_step(X, W_qkv, W_o, hq: int, hkv: int, theta: float, k_cache, v_cache, cache_len: int,
+                W_gate, W_up, W_down, W_lm=None, Y_attn=None, Y_mlp=None, logits=None, workspace=None,
+                stream=None):
+    """One rank's decode step (attention shard with KV-cache append, MLP shard and the vocabulary-
+    split head on the same X) through tp_decode_step; returns (Y_attn, Y_mlp, logits or None)."""
+    import torch
+    B, H = X.shape
+    I = W_gate.shape[1]
+    V = W_lm.shape[1] if W_lm is not None else 0
+    Y_attn = Y_attn if Y_attn is not None else torch.empty((B, H), dtype=torch.float32, device=X.device)
+    Y_mlp = Y_mlp if Y_mlp is not None else torch.empty((B, H), dtype=torch.float32, device=X.device)
+    if V and logits is None:
+        logits = torch.empty((B, V), dtype=torch.float32, device=X.device)
+    d = _desc(B, 1, H, hq, hkv, theta, k_cache, v_cache, cache_len)
+    nb = int(lib().tp_decode_step_workspace_size(ctypes.byref(d), I, V))
+    ws, wsb = _workspace(nb, X.device, workspace)
+    _check(lib().tp_decode_step(_ptr(X), _ptr(W_qkv), _ptr(W_o), ctypes.byref(d), _ptr(W_gate), _ptr(W_up),
+                                _ptr(W_down), I, _ptr(W_lm), V, _ptr(Y_attn), _ptr(Y_mlp),
+                                _ptr(logits) if V else None, _ptr(ws), wsb, _stream(stream)))
+    return Y_attn, Y_mlp, logits
+
+
 def partial_sum(partials, out=None, stream=None):
     """((P0 + P1) + P2) + ... for fp32 GPU tensors of equal size."""
     import torch
@@ -401,6 +433,12 @@ def moe_mlp_shard(X, W_gate, W_up, W_down, expert_offsets, row_token, token_rows
 
 
 # --- kernel timing ------------------------------------------------------------------------------
+
+def mfma_rate_probe(operands, out, n_workgroups: int, iters: int, stream=None):
+    """Matrix-pipe rate microbenchmark (measurement aid): see tp_mfma_rate_probe."""
+    _check(lib().tp_mfma_rate_probe(_ptr(operands), _ptr(out), int(n_workgroups), int(iters), _stream(stream)))
+    return out
+
 
 def profile_enable(on: bool = True):
     _check(lib().tp_profile_enable(int(on)))

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libtpshard.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "gemm_f32.hip", "gemm_mfma.hip", "attn.hip", "decode.hip", "norm.hip", "backward.hip", "moe.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "probe.hip"]
 
 
 def hipcc() -> str:

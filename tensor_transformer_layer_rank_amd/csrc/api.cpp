@@ -146,6 +146,15 @@ tp_status tp_profile_reset(void) {
     return TP_OK;
 }
 
+tp_status tp_mfma_rate_probe(const void* operands, float* out, int64_t n_workgroups, int64_t iters, void* stream) {
+    const char* fn = "tp_mfma_rate_probe";
+    if (!operands || !out) return fail(TP_ERR_NULL_POINTER, "%s: operands and out must be non-NULL", fn);
+    if (!aligned(operands, 16) || !aligned(out, 4)) return fail(TP_ERR_MISALIGNED, "%s: operands 16-byte, out 4-byte aligned", fn);
+    if (n_workgroups < 1 || n_workgroups > (1 << 20) || iters < 1 || iters > ((int64_t)1 << 30))
+        return fail(TP_ERR_BAD_SHAPE, "%s: need 1 <= n_workgroups <= 2^20 and 1 <= iters <= 2^30", fn);
+    return from_hip(tpk::mfma_rate(operands, out, n_workgroups, iters, as_stream(stream)), fn);
+}
+
 tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches) {
     if (!prefix || !total_ms || !launches) return fail(TP_ERR_NULL_POINTER, "tp_profile_read: NULL argument");
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -648,6 +657,51 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
     if (e != hipSuccess) return from_hip(e, "tp_attn_shard");
     return from_hip(tpk::skinny_linear(att, W_o, static_cast<float*>(part), B, H, dq, dq, Y_partial, H, 0, s),
                     "tp_attn_shard");
+}
+
+// ---- the whole decode step -------------------------------------------------------------------
+
+static tp_status check_decode_step(const tp_attn_desc* d, int64_t I, int64_t V, bool has_lm) {
+    const char* fn = "tp_decode_step";
+    bool decode = false;
+    tp_status st = check_attn_desc(d, &decode);
+    if (st != TP_OK) return st;
+    if (!decode) return fail(TP_ERR_BAD_SHAPE, "%s: desc must describe a decode step (S == 1 with k_cache and v_cache)", fn);
+    if (I <= 0 || V < 0) return fail(TP_ERR_BAD_SHAPE, "%s: need I_shard > 0 and V_shard >= 0", fn);
+    if ((V > 0) != has_lm) return fail(TP_ERR_BAD_SHAPE, "%s: W_lm and V_shard > 0 go together", fn);
+    if (I % 8 || V % 8) return fail(TP_ERR_MISALIGNED, "%s: I_shard and V_shard must be multiples of 8", fn);
+    if (check_ld(fn, "I_shard", I) != TP_OK) return TP_ERR_UNSUPPORTED;
+    return TP_OK;
+}
+
+size_t tp_decode_step_workspace_size(const tp_attn_desc* desc, int64_t I_shard, int64_t V_shard) {
+    if (!desc || check_decode_step(desc, I_shard, V_shard, V_shard > 0) != TP_OK) return 0;
+    return round_up(tpk::decode_step_ws_bytes(desc->B, desc->H, desc->n_q_heads, desc->n_kv_heads, I_shard, V_shard),
+                    WS_ALIGN);
+}
+
+tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
+                         const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
+                         const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    const char* fn = "tp_decode_step";
+    if (!X || !W_qkv || !W_o || !W_gate || !W_up || !W_down || !Y_attn || !Y_mlp)
+        return fail(TP_ERR_NULL_POINTER, "%s: X, the attention and MLP weights, Y_attn and Y_mlp must be non-NULL", fn);
+    if (V_shard > 0 && !logits) return fail(TP_ERR_NULL_POINTER, "%s: logits must be non-NULL when V_shard > 0", fn);
+    tp_status st = check_decode_step(desc, I_shard, V_shard, W_lm != nullptr);
+    if (st != TP_OK) return st;
+    const void* ptrs[] = {X, W_qkv, W_o, W_gate, W_up, W_down, Y_attn, Y_mlp};
+    for (const void* q : ptrs)
+        if (!aligned(q, 16)) return fail(TP_ERR_MISALIGNED, "%s: tensors must be 16-byte aligned", fn);
+    if (V_shard > 0 && (!aligned(W_lm, 16) || !aligned(logits, 16)))
+        return fail(TP_ERR_MISALIGNED, "%s: W_lm and logits must be 16-byte aligned", fn);
+    st = check_ws(fn, workspace, ws_bytes, tp_decode_step_workspace_size(desc, I_shard, V_shard));
+    if (st != TP_OK) return st;
+    return from_hip(tpk::decode_step(X, W_qkv, W_o, W_gate, W_up, W_down, W_lm, desc->B, desc->H, desc->n_q_heads,
+                                     desc->n_kv_heads, I_shard, V_shard, desc->cache_len, desc->rope_theta,
+                                     desc->k_cache, desc->v_cache, desc->cache_capacity, Y_attn, Y_mlp,
+                                     V_shard > 0 ? logits : nullptr, workspace, as_stream(stream)),
+                    fn);
 }
 
 // ---- merges ------------------------------------------------------------------------------------

@@ -64,6 +64,30 @@ SkinnyPlan plan_skinny(int64_t N, int64_t K, int nb) {
     return p;
 }
 
+// Plans for GEMMs that share one launch: a common K chunk (a multiple of 4 steps) chosen so
+// that the launch has about `target` workgroups in all. n GEMMs: N[i] columns (nb[i] = 2 for
+// the dual gate/up form), K[i] rows.
+void plan_multi(const int64_t* N, const int64_t* K, const int* nb, int n, int64_t target, SkinnyPlan* out) {
+    int64_t best_kc = 4 * STEP, best_err = -1;
+    for (int64_t kc = 4 * STEP; kc <= 16384; kc += 4 * STEP) {
+        int64_t wgs = 0;
+        for (int i = 0; i < n; ++i) wgs += (N[i] + STRIP - 1) / STRIP * nb[i] * ((K[i] + kc - 1) / kc);
+        const int64_t err = wgs > target ? wgs - target : target - wgs;
+        if (best_err < 0 || err < best_err) {
+            best_err = err;
+            best_kc = kc;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        SkinnyPlan& p = out[i];
+        p.strips_per_b = (N[i] + STRIP - 1) / STRIP;
+        p.strips = p.strips_per_b * nb[i];
+        p.ncols = p.strips * STRIP;
+        p.kchunk = best_kc;
+        p.splits = (K[i] + best_kc - 1) / best_kc;
+    }
+}
+
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -77,6 +101,8 @@ struct SkinnyArgs {
     const uint16_t* B2;      // second weight of the dual (gate/up) form
     int64_t M, N, K, kchunk, strips_per_b, ncols;
     int splits;
+    int strips;              // strips per K chunk (dual: gate strips then up strips)
+    int wg0;                 // first workgroup of this GEMM in a launch over several
     float* part;             // [splits][M][ncols]
 };
 
@@ -142,12 +168,12 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[MB][8], const StepRegs<MB>
     }
 }
 
+// One workgroup's strip and K chunk of GEMM g.
 template <int MB, bool F16>
-__global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs g) {
-    __shared__ f32x4 red[4][MB * 16][STRIP / 4];
+__device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, int64_t split,
+                                            f32x4 (&red)[4][MB * 16][STRIP / 4]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, l16 = lane & 15;
-    const int64_t strip = blockIdx.x, split = blockIdx.y;
     const bool second = strip >= g.strips_per_b;
     const uint16_t* Bp = second ? g.B2 : g.B1;
     const int64_t cgroup = strip % g.strips_per_b;
@@ -223,6 +249,37 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
     }
 }
 
+// Up to three GEMMs that share M in one launch (a one-dimensional grid): workgroups g1.wg0..
+// belong to g1, g2.wg0.. to g2, the rest to g0; within a GEMM, workgroup w takes strip
+// w % strips of K chunk w / strips. The GEMM is picked by scalar selects over the three
+// argument slots (the argument block is never indexed dynamically).
+template <int MB, bool F16>
+__global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs g0, SkinnyArgs g1, SkinnyArgs g2,
+                                                                     int n) {
+    __shared__ f32x4 red[4][MB * 16][STRIP / 4];
+    const int bid = (int)blockIdx.x;
+    const bool s2 = n > 2 && bid >= g2.wg0, s1 = !s2 && n > 1 && bid >= g1.wg0;
+    SkinnyArgs g;
+#define TP_SEL(f) g.f = s2 ? g2.f : (s1 ? g1.f : g0.f)
+    TP_SEL(A);
+    TP_SEL(lda);
+    TP_SEL(B1);
+    TP_SEL(B2);
+    TP_SEL(M);
+    TP_SEL(N);
+    TP_SEL(K);
+    TP_SEL(kchunk);
+    TP_SEL(strips_per_b);
+    TP_SEL(ncols);
+    TP_SEL(splits);
+    TP_SEL(strips);
+    TP_SEL(wg0);
+    TP_SEL(part);
+#undef TP_SEL
+    const int local = bid - g.wg0;
+    skinny_body<MB, F16>(g, local % g.strips, local / g.strips, red);
+}
+
 // v[i] = sum over chunks (in order) of part[s][m][c[i]] for NC columns of row m. The chunks'
 // values are loaded 8 at a time for all NC columns together, unconditionally (chunk indexes
 // past the last one re-read the last), so that a thread waits for one memory round trip per
@@ -282,6 +339,62 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
     h[idx] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
 }
 
+// One output of a reduce launch over several: the chunk partials of a skinny GEMM summed in
+// chunk order, then kind 0 fp32 store, 1 fp32 +=, 2 bf16, 3 bf16 ReLU, 4 bf16 SiLU(gate) * up
+// (gate column c and up column up_off + c of the partials; N = I).
+struct ReduceOut {
+    const float* part;
+    int splits;
+    int kind;
+    int64_t N, ncols, up_off, ldc;
+    void* C;
+    int64_t e0;   // first element of this output in the launch
+};
+
+// element idx (< total) of the outputs r0 .. r(n-1) of a reduce over M rows
+__device__ __forceinline__ void reduce_element(const ReduceOut& r0, const ReduceOut& r1, const ReduceOut& r2, int n,
+                                               int64_t M, int64_t idx) {
+    // field-wise selects (no copy of the argument structs to scratch memory)
+    const bool s2 = n > 2 && idx >= r2.e0, s1 = !s2 && n > 1 && idx >= r1.e0;
+    ReduceOut r;
+#define TP_SEL(f) r.f = s2 ? r2.f : (s1 ? r1.f : r0.f)
+    TP_SEL(part);
+    TP_SEL(splits);
+    TP_SEL(kind);
+    TP_SEL(N);
+    TP_SEL(ncols);
+    TP_SEL(up_off);
+    TP_SEL(ldc);
+    TP_SEL(C);
+    TP_SEL(e0);
+#undef TP_SEL
+    const int64_t e = idx - r.e0;
+    const int64_t m = e / r.N, c = e - m * r.N;
+    const int64_t off = m * r.ldc + c;
+    if (r.kind == 4) {
+        const int64_t cols[2] = {c, r.up_off + c};
+        float sum[2];
+        sum_splits<2>(r.part, r.splits, M, r.ncols, m, cols, sum);
+        const float gt = sum[0], up = sum[1];
+        static_cast<uint16_t*>(r.C)[off] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
+        return;
+    }
+    const int64_t cols[1] = {c};
+    float sum[1];
+    sum_splits<1>(r.part, r.splits, M, r.ncols, m, cols, sum);
+    const float v = sum[0];
+    if (r.kind == 0) static_cast<float*>(r.C)[off] = v;
+    else if (r.kind == 1) static_cast<float*>(r.C)[off] += v;
+    else if (r.kind == 2) static_cast<uint16_t*>(r.C)[off] = f32_to_bf16(v);
+    else static_cast<uint16_t*>(r.C)[off] = f32_to_bf16(v > 0.f ? v : 0.f);
+}
+
+__global__ __launch_bounds__(256) void reduce_multi_kernel(ReduceOut r0, ReduceOut r1, ReduceOut r2, int n,
+                                                           int64_t M, int64_t total) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx < total) reduce_element(r0, r1, r2, n, M, idx);
+}
+
 // cos / sin of the 64 rotary angles pos * theta^(-2i/128) of one position (formed in fp64
 // on the host and passed by value)
 struct RopeRow {
@@ -324,18 +437,37 @@ struct QkvPartials {
     int64_t ncols;
 };
 
+// Extra work a decode attention launch may carry: the first n_wg workgroups reduce other
+// split-K partials (RED_PER_THREAD elements per thread) while the attention workgroups stream
+// the cache, so those reductions need no launch of their own.
+constexpr int RED_PER_THREAD = 4;
+struct AttnReduce {
+    ReduceOut r0, r1;
+    int n;           // outputs (0: no reduce workgroups)
+    int n_wg;
+    int64_t M, total;
+};
+
 __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, RopeRow rope,
-                                                                int hq, int hkv, int64_t pos,
+                                                                int hq, int hkv, int64_t B, int64_t pos,
                                                                 int64_t cap, uint16_t* __restrict__ kc,
                                                                 uint16_t* __restrict__ vc,
-                                                                uint16_t* __restrict__ out) {
+                                                                uint16_t* __restrict__ out, AttnReduce xr) {
     __shared__ float red_o[NGRP][128];
     __shared__ float red_m[NGRP], red_l[NGRP];
     __shared__ float qs[128], kn[128], vn[128];
     const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
-    const int h = blockIdx.x;
-    const int64_t b = blockIdx.y;
-    const int64_t B = gridDim.y;
+    if ((int)blockIdx.x < xr.n_wg) {
+        const int64_t e0 = ((int64_t)blockIdx.x * (NGRP * 16) + tid) * RED_PER_THREAD;
+        const ReduceOut r0 = xr.r0, r1 = xr.r1;   // local copies: selecting through the argument block spills
+#pragma unroll
+        for (int u = 0; u < RED_PER_THREAD; ++u)
+            if (e0 + u < xr.total) reduce_element(r0, r1, r0, xr.n, xr.M, e0 + u);
+        return;
+    }
+    const int ab = (int)blockIdx.x - xr.n_wg;   // attention workgroup: (sequence, q head)
+    const int h = ab % hq;
+    const int64_t b = ab / hq;
     const int g = (h * hkv) / hq;
     const uint16_t* kb = kc + ((b * hkv + g) * cap) * 128 + 8 * l16;
     const uint16_t* vb = vc + ((b * hkv + g) * cap) * 128 + 8 * l16;
@@ -470,25 +602,38 @@ __global__ __launch_bounds__(NGRP * 16) void decode_attn_kernel(QkvPartials qp, 
     }
 }
 
-hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name, bool f16 = false) {
+// Launch up to three prepared GEMMs (plan fields and wg0 filled in) as one grid of `wgs` workgroups.
+hipError_t skinny_launch(const SkinnyArgs* a, int n, int wgs, int64_t M, hipStream_t s, const char* name, bool f16) {
+    const SkinnyArgs g0 = a[0], g1 = n > 1 ? a[1] : a[0], g2 = n > 2 ? a[2] : a[0];
+    ProfScope ps(name, s);
+    if (f16) {
+        if (M <= 32)
+            skinny_kernel<2, true><<<(unsigned)wgs, 256, 0, s>>>(g0, g1, g2, n);
+        else
+            skinny_kernel<4, true><<<(unsigned)wgs, 256, 0, s>>>(g0, g1, g2, n);
+    } else {
+        if (M <= 32)
+            skinny_kernel<2, false><<<(unsigned)wgs, 256, 0, s>>>(g0, g1, g2, n);
+        else
+            skinny_kernel<4, false><<<(unsigned)wgs, 256, 0, s>>>(g0, g1, g2, n);
+    }
+    return hipGetLastError();
+}
+
+// fill the plan fields of a (nb = 2 for the dual gate/up form) and place it at workgroup wg0
+int skinny_place(SkinnyArgs& a, const SkinnyPlan& p, int wg0) {
     a.kchunk = p.kchunk;
     a.strips_per_b = p.strips_per_b;
     a.ncols = p.ncols;
     a.splits = (int)p.splits;
-    dim3 grid((unsigned)p.strips, (unsigned)p.splits);
-    ProfScope ps(name, s);
-    if (f16) {
-        if (a.M <= 32)
-            skinny_kernel<2, true><<<grid, 256, 0, s>>>(a);
-        else
-            skinny_kernel<4, true><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (a.M <= 32)
-            skinny_kernel<2, false><<<grid, 256, 0, s>>>(a);
-        else
-            skinny_kernel<4, false><<<grid, 256, 0, s>>>(a);
-    }
-    return hipGetLastError();
+    a.strips = (int)p.strips;
+    a.wg0 = wg0;
+    return wg0 + (int)(p.strips * p.splits);
+}
+
+hipError_t skinny_run(SkinnyArgs& a, const SkinnyPlan& p, hipStream_t s, const char* name, bool f16 = false) {
+    const int wgs = skinny_place(a, p, 0);
+    return skinny_launch(&a, 1, wgs, a.M, s, name, f16);
 }
 
 SkinnyArgs skinny_args(const void* A, const void* B1, const void* B2, float* part, int64_t M,
@@ -541,6 +686,118 @@ hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* p
     return hipGetLastError();
 }
 
+// ---- the whole decode step of a rank in four launches ------------------------------------
+// K1: every projection of X (QKV, gate/up, vocabulary-split head) as one split-K launch;
+// K2: decode attention (sums the QKV partials, RoPE, cache append, attention over the cache),
+//     whose leading workgroups meanwhile sum the gate/up partials through SiLU(gate) * up into h
+//     and the head's partials into the logits;
+// K4: O and down projections as one split-K launch; K5: their partials into the two fp32 outputs.
+namespace {
+
+constexpr int64_t K1_TARGET = 1024, K4_TARGET = 512;
+
+struct DecodePlan {
+    SkinnyPlan p1[3], p4[2];
+    int n1;
+    size_t off[7];   // qkv, gate/up, head partials, attention out, h, O, down partials
+    size_t bytes;
+};
+
+DecodePlan plan_decode(int64_t B, int64_t H, int hq, int hkv, int64_t I, int64_t V) {
+    DecodePlan d{};
+    const int64_t nqkv = (int64_t)(hq + 2 * hkv) * 128, dq = (int64_t)hq * 128;
+    const int64_t N1[3] = {nqkv, I, V}, K1[3] = {H, H, H};
+    const int nb1[3] = {1, 2, 1};
+    d.n1 = V > 0 ? 3 : 2;
+    plan_multi(N1, K1, nb1, d.n1, K1_TARGET, d.p1);
+    const int64_t N4[2] = {H, H}, K4[2] = {dq, I};
+    const int nb4[2] = {1, 1};
+    plan_multi(N4, K4, nb4, 2, K4_TARGET, d.p4);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o = 0;
+    auto take = [&](int i, size_t bytes) { d.off[i] = o; o += up(bytes); };
+    take(0, (size_t)(d.p1[0].splits * B * d.p1[0].ncols) * 4);
+    take(1, (size_t)(d.p1[1].splits * B * d.p1[1].ncols) * 4);
+    take(2, d.n1 > 2 ? (size_t)(d.p1[2].splits * B * d.p1[2].ncols) * 4 : 0);
+    take(3, (size_t)(B * dq) * 2);
+    take(4, (size_t)(B * I) * 2);
+    take(5, (size_t)(d.p4[0].splits * B * d.p4[0].ncols) * 4);
+    take(6, (size_t)(d.p4[1].splits * B * d.p4[1].ncols) * 4);
+    d.bytes = o;
+    return d;
+}
+
+}  // namespace
+
+size_t decode_step_ws_bytes(int64_t B, int64_t H, int hq, int hkv, int64_t I, int64_t V) {
+    return plan_decode(B, H, hq, hkv, I, V).bytes;
+}
+
+hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const void* Wg, const void* Wu,
+                       const void* Wd, const void* Wlm, int64_t B, int64_t H, int hq, int hkv, int64_t I,
+                       int64_t V, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap, float* Ya,
+                       float* Ym, float* logits, void* ws, hipStream_t s) {
+    const DecodePlan d = plan_decode(B, H, hq, hkv, I, V);
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    float* part_qkv = reinterpret_cast<float*>(base + d.off[0]);
+    float* part_gu = reinterpret_cast<float*>(base + d.off[1]);
+    float* part_lm = reinterpret_cast<float*>(base + d.off[2]);
+    void* att = base + d.off[3];
+    void* h = base + d.off[4];
+    float* part_o = reinterpret_cast<float*>(base + d.off[5]);
+    float* part_d = reinterpret_cast<float*>(base + d.off[6]);
+    const int64_t nqkv = (int64_t)(hq + 2 * hkv) * 128, dq = (int64_t)hq * 128;
+    // K1
+    SkinnyArgs a1[3] = {skinny_args(X, Wqkv, nullptr, part_qkv, B, nqkv, H, H),
+                        skinny_args(X, Wg, Wu, part_gu, B, I, H, H),
+                        skinny_args(X, Wlm, nullptr, part_lm, B, V, H, H)};
+    int w = 0;
+    for (int i = 0; i < d.n1; ++i) w = skinny_place(a1[i], d.p1[i], w);
+    hipError_t e = skinny_launch(a1, d.n1, w, B, s, "skinny_gemm_x", false);
+    if (e != hipSuccess) return e;
+    // K2
+    RopeRow rope;
+    for (int i = 0; i < 64; ++i) {
+        const double ang = (double)pos * std::pow((double)theta, -2.0 * (double)i / 128.0);
+        rope.c[i] = (float)std::cos(ang);
+        rope.s[i] = (float)std::sin(ang);
+    }
+    // K2 + K3: attention, with the gate/up and head reductions in leading workgroups
+    {
+        const QkvPartials qp{part_qkv, (int)d.p1[0].splits, d.p1[0].ncols};
+        AttnReduce xr{};
+        xr.r0 = ReduceOut{part_gu, (int)d.p1[1].splits, 4, I, d.p1[1].ncols, d.p1[1].ncols / 2, I, h, 0};
+        xr.n = 1;
+        xr.M = B;
+        xr.total = B * I;
+        if (d.n1 > 2) {
+            xr.r1 = ReduceOut{part_lm, (int)d.p1[2].splits, 0, V, d.p1[2].ncols, 0, V, logits, xr.total};
+            xr.total += B * V;
+            xr.n = 2;
+        }
+        constexpr int64_t per_wg = (int64_t)NGRP * 16 * RED_PER_THREAD;
+        xr.n_wg = (int)((xr.total + per_wg - 1) / per_wg);
+        ProfScope ps("decode_attn", s);
+        decode_attn_kernel<<<(unsigned)(xr.n_wg + hq * B), NGRP * 16, 0, s>>>(
+            qp, rope, hq, hkv, B, pos, cap, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+            static_cast<uint16_t*>(att), xr);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // K4
+    SkinnyArgs a4[2] = {skinny_args(att, Wo, nullptr, part_o, B, H, dq, dq),
+                        skinny_args(h, Wd, nullptr, part_d, B, H, I, I)};
+    w = 0;
+    for (int i = 0; i < 2; ++i) w = skinny_place(a4[i], d.p4[i], w);
+    e = skinny_launch(a4, 2, w, B, s, "skinny_gemm_od", false);
+    if (e != hipSuccess) return e;
+    // K5
+    const ReduceOut r0{part_o, (int)d.p4[0].splits, 0, H, d.p4[0].ncols, 0, H, Ya, 0};
+    const ReduceOut r1{part_d, (int)d.p4[1].splits, 0, H, d.p4[1].ncols, 0, H, Ym, B * H};
+    ProfScope ps("skinny_reduce_od", s);
+    reduce_multi_kernel<<<(unsigned)((2 * B * H + 255) / 256), 256, 0, s>>>(r0, r1, r0, 2, B, 2 * B * H);
+    return hipGetLastError();
+}
+
 hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H, int hq,
                             int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
                             void* out, hipStream_t s) {
@@ -557,9 +814,9 @@ hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_
     }
     const QkvPartials qp{part, (int)p.splits, p.ncols};
     ProfScope ps("decode_attn", s);
-    decode_attn_kernel<<<dim3((unsigned)hq, (unsigned)B), NGRP * 16, 0, s>>>(
-        qp, rope, hq, hkv, pos, cap, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-        static_cast<uint16_t*>(out));
+    decode_attn_kernel<<<(unsigned)(hq * B), NGRP * 16, 0, s>>>(
+        qp, rope, hq, hkv, B, pos, cap, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+        static_cast<uint16_t*>(out), AttnReduce{});
     return hipGetLastError();
 }
 

@@ -22,6 +22,11 @@ struct ProfScope {
     ~ProfScope() { prof_end(s); }
 };
 
+// ---- matrix-pipe rate microbenchmark (measurement aid) --------------------------------
+// n_wg workgroups of 4 waves, each wave 16 * iters v_mfma_f32_32x32x16_bf16 on register
+// operands loaded from ops (8 x 256 x 16 bytes); out: n_wg * 256 fp32 checksums
+hipError_t mfma_rate(const void* ops, float* out, int64_t n_wg, int64_t iters, hipStream_t s);
+
 // ---- the allocation-free column linear call ------------------------------------------
 // Device address of the library's static scratch array (TP_NOALLOC_SCRATCH_BYTES) on the
 // device of stream s; looked up once per device.
@@ -120,6 +125,15 @@ hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* p
 hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_t B, int64_t H, int hq,
                             int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
                             void* out, hipStream_t s);
+
+// The whole decode step of a rank in five launches: attention shard (QKV + RoPE + cache append
+// + attention + O partial Ya), MLP shard on the same X (Ym), and the vocabulary-split head
+// (logits [B, V]; V = 0: none). B <= 64; cap, pos as for decode_attn_step.
+size_t decode_step_ws_bytes(int64_t B, int64_t H, int hq, int hkv, int64_t I, int64_t V);
+hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const void* Wg, const void* Wu,
+                       const void* Wd, const void* Wlm, int64_t B, int64_t H, int hq, int hkv, int64_t I,
+                       int64_t V, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap, float* Ya,
+                       float* Ym, float* logits, void* ws, hipStream_t s);
 
 // ---- backward of a linear shard ---------------------------------------------------------
 // dX [T, K] fp32 = dY [T, N] . W^T, dW [K, N] fp32 = X^T [K, T] . dY (bf16 operands; T, K, N

@@ -349,3 +349,38 @@ def test_noalloc_column_linear_validation(L):
     assert L.tp_linear_workspace_size(64, 512, 131072, tp.TP_BF16) > 16 << 20
     assert _st(f(FAKE, FAKE, FAKE, 64, 512, 131072, 131072, tp.TP_BF16, tp.TP_F32, 0, None, None)) == "TP_ERR_UNSUPPORTED"
     assert "scratch" in L.tp_last_error().decode()
+
+
+def test_mfma_rate_probe_validation(L):
+    f = L.tp_mfma_rate_probe
+    assert _st(f(None, FAKE, 256, 100, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE_ODD, FAKE, 256, 100, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE, FAKE, 0, 100, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, FAKE, 256, 0, None)) == "TP_ERR_BAD_SHAPE"
+
+
+def test_decode_step_validation(L):
+    f = L.tp_decode_step
+    d = tp._desc(4, 8, 256, 2, 2)          # no cache: a prefill, not a decode step
+    args = [FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, 136, FAKE, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert _st(f(*args)) == "TP_ERR_BAD_SHAPE"
+    d = tp.AttnDesc()
+    d.B, d.S, d.H, d.n_q_heads, d.n_kv_heads, d.head_dim, d.rope_theta, d.causal = 4, 1, 256, 2, 2, 128, 1e4, 1
+    d.k_cache, d.v_cache, d.cache_len, d.cache_capacity = 0x1000, 0x2000, 37, 40
+    args[3] = ctypes.byref(d)
+    assert L.tp_decode_step_workspace_size(ctypes.byref(d), 136, 1000) > 0
+    assert L.tp_decode_step_workspace_size(ctypes.byref(d), 136, 0) > 0
+    bad = list(args); bad[0] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"
+    bad = list(args); bad[12] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"                      # logits needed for V_shard > 0
+    bad = list(args); bad[8] = None
+    assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"                         # V_shard > 0 without W_lm
+    bad = list(args); bad[7] = 132
+    assert _st(f(*bad)) == "TP_ERR_MISALIGNED"                        # I_shard not a multiple of 8
+    bad = list(args); bad[14] = 16
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
+    bad = list(args); bad[6] = FAKE_ODD
+    assert _st(f(*bad)) == "TP_ERR_MISALIGNED"
+    d.B = 65
+    assert _st(f(*args)) == "TP_ERR_UNSUPPORTED"                      # at most 64 sequences

@@ -724,3 +724,56 @@ def test_error_is_raised_not_launched(tp):
         tp.column_linear(X, W)
     assert ei.value.name == "TP_ERR_MISALIGNED"
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- the fused decode step
+
+def _decode_step(tp, inp, with_lm=True):
+    import torch
+    kc, vc = dev(inp.k_cache), dev(inp.v_cache)
+    Ya, Ym, lg = tp.decode_step(dev(inp.X), dev(inp.W_qkv), dev(inp.W_o), inp.hq, inp.hkv, inp.theta, kc, vc,
+                                inp.cache_len, dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down),
+                                dev(inp.W_lm) if with_lm else None,
+                                Y_attn=_nan((inp.B, inp.H), torch.float32), Y_mlp=_nan((inp.B, inp.H), torch.float32))
+    torch.cuda.synchronize()
+    return host(Ya), host(Ym), (host(lg) if with_lm else None), host(kc), host(vc)
+
+
+def _check_decode_step(tp, inp, what, with_lm=True):
+    ya, ym, lg, kc, vc = _decode_step(tp, inp, with_lm)
+    L = inp.cache_len
+    ref, knew, vnew = O.decode_attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.k_cache, inp.v_cache, L, inp.hq, inp.hkv,
+                                          inp.d, inp.theta)
+    assert_close_bf16(ya, ref, what + ": attention partial")
+    assert_close_bf16(ym, O.mlp_swiglu_shard(inp.X, inp.W_gate, inp.W_up, inp.W_down), what + ": mlp partial")
+    if with_lm:
+        assert_close_bf16(lg, O.lm_head_shard(inp.X, inp.W_lm), what + ": logits")
+    assert_close_bf16(kc[:, :, L], knew, what + ": appended keys", out="bf16")
+    assert_close_bf16(vc[:, :, L], vnew, what + ": appended values", out="bf16")
+    assert np.array_equal(kc[:, :, :L], inp.k_cache[:, :, :L]), "cache prefix modified"
+    assert np.array_equal(vc[:, :, :L], inp.v_cache[:, :, :L]), "cache prefix modified"
+
+
+@pytest.mark.parametrize("B,H,hq,hkv,I,V,L,cap", [(4, 256, 2, 2, 136, 1000, 37, 40), (3, 512, 4, 1, 264, 520, 300, 301),
+                                                  (32, 256, 2, 2, 64, 128, 1, 8), (1, 1024, 8, 2, 2048, 4000, 0, 4),
+                                                  (64, 512, 4, 4, 1000, 2056, 129, 130)])
+def test_decode_step_small(tp, B, H, hq, hkv, I, V, L, cap):
+    """tp_decode_step: attention (with cache append), MLP and vocabulary-split head in one call."""
+    inp = wl.random_decode(B * 7 + L, B, H, hq, hkv, I, V, L, cap)
+    _check_decode_step(tp, inp, f"decode step B{B} H{H} hq{hq} hkv{hkv} I{I} V{V} L{L}")
+
+
+def test_decode_step_without_head(tp):
+    inp = wl.random_decode(5, 8, 512, 4, 2, 264, 64, 100, 104)
+    _check_decode_step(tp, inp, "decode step, no output layer", with_lm=False)
+
+
+def test_decode7b_tp2_fused_step_full_size(tp):
+    """The 7B TP=2 decode step through tp_decode_step: 32 sequences, 16 heads, 1024 cached tokens,
+    I_shard 5504, vocabulary shard 16000; every output element, and two calls bitwise equal."""
+    inp = wl.decode7b_tp2()
+    _check_decode_step(tp, inp, "decode7b_tp2 fused step")
+    a = _decode_step(tp, inp)
+    b = _decode_step(tp, inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y), "two calls differ bitwise"
