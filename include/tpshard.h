@@ -337,7 +337,9 @@ size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E,
  *   runs on until the process ends:
  *     - T <= 64 needs tp_linear_workspace_size(T, K, N, in_dt) bytes of it; a call that needs more
  *       returns TP_ERR_UNSUPPORTED before any HIP call;
- *     - larger T uses the split only when it fits (otherwise every tile runs whole; same result).
+ *     - larger T uses the tail split only when its partials fit (otherwise every tile runs whole:
+ *       the same products summed in another order, so the result can differ from
+ *       tp_column_linear's in the last bits of fp32 rounding; bitwise equal when the split fits).
  *   The first call on a device looks the array's address up on that device (a HIP call that can
  *   fail with TP_ERR_HIP). All calls on one GPU share the array: calls that overlap on one GPU
  *   (other streams, other host threads) race and must be ordered by the caller. Nothing in it
