@@ -414,7 +414,7 @@ def decode_bench(args):
     ws_f = torch.empty(tp.decode_step_workspace_size(B, H, hq, hkv, inp.theta, kc, vc, inp.cache_len, I, V),
                        dtype=torch.uint8, device="cuda")
 
-    def step_fused():   # tp_decode_step: the same three parts in five launches on one stream
+    def step_fused():   # tp_decode_step: the same three parts in four launches on one stream
         tp.decode_step(X, Wqkv, Wo, hq, hkv, inp.theta, kc, vc, inp.cache_len, Wg, Wu, Wd, Wlm,
                        Y_attn=Ya, Y_mlp=Ym, logits=logits, workspace=ws_f)
 
@@ -426,7 +426,7 @@ def decode_bench(args):
     sk_ms, sk_n = kernel_avg("skinny_gemm")
     rd_ms, rd_n = kernel_avg("skinny_reduce")
     x_ms, _ = kernel_avg("skinny_gemm_x")
-    od_ms, _ = kernel_avg("skinny_gemm_od")
+    out_ms, _ = kernel_avg("skinny_gemm_out")
     eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
     for t in outs:
         t.fill_(float("nan"))
@@ -448,15 +448,15 @@ def decode_bench(args):
         "ms_per_step_separate_calls_eager": ms_sep_eager,
         "ms_per_step_separate_calls_graph": ms_sep_graph,
         "step_stats": STEP_STATS.get("decode"),
-        "graph": "tp_decode_step (5 launches) captured as one HIP graph; separate_calls: tp_attn_shard, "
+        "graph": "tp_decode_step (4 launches) captured as one HIP graph; separate_calls: tp_attn_shard, "
                  "tp_mlp_shard, tp_column_linear as three graph branches on their own streams",
         "graph_outputs_equal_eager": same,
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
         "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
-                    "skinny_gemm_x: QKV + gate/up + head (avg_us)": x_ms * 1e3 if x_ms else None,
-                    "skinny_gemm_od: O + down (avg_us)": od_ms * 1e3 if od_ms else None,
+                    "skinny_gemm_x: QKV + gate/up (avg_us)": x_ms * 1e3 if x_ms else None,
+                    "skinny_gemm_out: O + down + head (avg_us)": out_ms * 1e3 if out_ms else None,
                     "skinny_gemm*(launches/step)": sk_n / nsamp,
                     "skinny_reduce*(avg_us)": rd_ms * 1e3 if rd_ms else None,
                     "skinny_reduce*(launches/step)": rd_n / nsamp},

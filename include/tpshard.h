@@ -224,12 +224,13 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv, const void* W_o, float
 size_t tp_attn_workspace_size(const tp_attn_desc* desc, tp_dtype in_dt);
 
 /*
- * tp_decode_step — one rank's whole decode step (one new token for each of B sequences) in five
+ * tp_decode_step — one rank's whole decode step (one new token for each of B sequences) in four
  *   launches: its attention shard with the KV cache kept on the rank ("TensorRT LLM 中的并行策略",
  *   注意力模块), its MLP shard, and its slice of the vocabulary-split output layer ("张量并行：切分
- *   Transformer 层的分布式训练", 输入与输出层), all on the same input X. The projections that read X
- *   (QKV, gate/up, output layer) stream their weights in one launch and O / down in another, so
- *   the step pays the start and end of a launch five times instead of once per layer.
+ *   Transformer 层的分布式训练", 输入与输出层), all on the same input X. QKV and gate/up stream their
+ *   weights in one launch, the attention launch also forms h, and O, down and the output layer
+ *   share one more launch before a final reduction, so the step pays the start and end of a
+ *   launch four times instead of once per layer.
  *   X [B, H] bf16, B <= 64; desc: a decode step (S == 1, k_cache / v_cache, cache_len <
  *   cache_capacity; the call appends the new token's rotated key and value at slot cache_len, as
  *   tp_attn_shard does); W_qkv, W_o as for tp_attn_shard; W_gate, W_up [H, I_shard] and W_down
