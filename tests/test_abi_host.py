@@ -384,3 +384,29 @@ def test_decode_step_validation(L):
     assert _st(f(*bad)) == "TP_ERR_MISALIGNED"
     d.B = 65
     assert _st(f(*args)) == "TP_ERR_UNSUPPORTED"                      # at most 64 sequences
+
+
+def test_workspace_size_arithmetic_at_large_shapes(L):
+    """Every size query at large valid shapes: positive, in range, and growing with the token
+    count (run under the host-sanitizer build, this also checks the size arithmetic for
+    signed overflow and out-of-bounds host accesses)."""
+    big = 1 << 62
+    for T in (64, 1 << 16, 1 << 22):
+        assert 0 < L.tp_linear_workspace_size(32, (1 << 23) - 8, 1 << 16, tp.TP_BF16) < big
+        assert L.tp_linear_workspace_size(T, 16384, 53248, tp.TP_BF16) < big
+        m1 = L.tp_mlp_workspace_size(T, 16384, 53248, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16)
+        m2 = L.tp_mlp_workspace_size(2 * T, 16384, 53248, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_BF16)
+        assert 0 < m1 < m2 < big
+        if T > 64:
+            assert m1 < L.tp_mlp_workspace_size(T, 16384, 53248, tp.TP_MLP_SWIGLU, tp.TP_BF16, tp.TP_F16) < big
+        assert 0 < L.tp_mlp_fp8_workspace_size(T, 16384, 53248, tp.TP_MLP_SWIGLU) < big
+        assert 0 < L.tp_linear_backward_workspace_size(T, 8192, 8192) < big
+    for B, S in ((1, 1 << 20), (64, 1 << 14), (1 << 12, 1 << 8)):
+        d = _desc(B=B, S=S, H=16384, n_q_heads=64, n_kv_heads=8)
+        assert 0 < L.tp_attn_workspace_size(ctypes.byref(d), tp.TP_BF16) < big
+    d = _desc(B=64, S=1, H=16384, n_q_heads=128, n_kv_heads=16, k_cache=0x1000, v_cache=0x2000,
+              cache_len=(1 << 20) - 1, cache_capacity=1 << 20)
+    assert 0 < L.tp_decode_step_workspace_size(ctypes.byref(d), 53248, 128000) < big
+    E = 64
+    offs = (ctypes.c_int64 * (E + 1))(*[i * (1 << 14) for i in range(E + 1)])
+    assert 0 < L.tp_moe_workspace_size(1 << 19, 8192, 16384, E, offs) < big
