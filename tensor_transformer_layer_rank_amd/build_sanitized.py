@@ -5,7 +5,7 @@
 The C-ABI front end (csrc/api.cpp: argument validation, shape limits, size and workspace
 arithmetic, dispatch) is compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer
 (host code only: api.cpp holds no device code) and linked with the unchanged kernel objects
-of the regular build into _build/libtpshard_san.so. The sanitizer runtimes are not linked in:
+of the regular build into _build/sanitized/libtpshard_san.so. The sanitizer runtimes are not linked in:
 they are preloaded into the Python process that loads the library (sanitized_env()), and
 TPSHARD_LIB points the package at it. --run-tests runs tests/test_abi_host.py that way; any
 sanitizer report aborts the run.
@@ -20,7 +20,8 @@ import sys
 
 from . import build as _build
 
-SAN_LIB = os.path.join(_build.BUILD, "libtpshard_san.so")
+SAN_DIR = os.path.join(_build.BUILD, "sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libtpshard_san.so")
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 
 
@@ -58,7 +59,8 @@ def build() -> str:
     objs = [os.path.join(_build.BUILD, os.path.splitext(s)[0] + ".o") for s in _build.SOURCES if s != "api.cpp"]
     if not all(os.path.exists(o) for o in objs):
         _build.build()
-    api_o = os.path.join(_build.BUILD, "api_san.o")
+    os.makedirs(SAN_DIR, exist_ok=True)
+    api_o = os.path.join(SAN_DIR, "api.o")
     cmd = [_gxx(), "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
            f"-I{_build.INCLUDE}", f"-I{_build.CSRC}", *SAN_FLAGS, "-c", os.path.join(_build.CSRC, "api.cpp"),
            "-o", api_o]
@@ -66,7 +68,7 @@ def build() -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     # the kernel objects carry gfx950 code, so the device link stays the regular one; the
-    # sanitizer symbols of api_san.o resolve against the preloaded runtimes
+    # sanitizer symbols of the rebuilt api.o resolve against the preloaded runtimes
     tmp = SAN_LIB + ".tmp"
     cmd = [_build.hipcc(), f"--offload-arch={_build.ARCH}", "-shared", "-fPIC", api_o, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
