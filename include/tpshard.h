@@ -289,8 +289,10 @@ tp_status tp_merge_rmsnorm(const float* const* partials, int32_t k, const void* 
  *   dW_r is local in both.
  *   X [T, K], W_shard [K, N], dY [T, N]: in_dt (BF16) row-major; dX [T, K] and dW [K, N] fp32
  *   (overwritten). T, K, N multiples of 8 and below 2^23; all pointers 16-byte aligned;
- *   workspace >= tp_linear_backward_workspace_size(T, K, N) bytes, 16-byte aligned (holds
- *   W^T and X^T in bf16). fp32 accumulation; deterministic.
+ *   workspace >= tp_linear_backward_workspace_size(T, K, N) bytes, 16-byte aligned (the
+ *   split-K partials of the GEMMs' last round; 0 bytes, and workspace may be NULL, when both
+ *   grids fill whole rounds). W and X are read in place (no transposed copies). At most 2^22
+ *   output tiles of 256 x 256 in dX and dW together. fp32 accumulation; deterministic.
  */
 tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY, float* dX, float* dW,
                              int64_t T, int64_t K, int64_t N, tp_dtype in_dt, void* workspace,

@@ -842,10 +842,10 @@ tp_status tp_linear_backward(const void* X, const void* W_shard, const void* dY,
                     (long long)T, (long long)K, (long long)N);
     if (T >= ((int64_t)1 << 23) || K >= ((int64_t)1 << 23) || N >= ((int64_t)1 << 23))
         return fail(TP_ERR_UNSUPPORTED, "%s: T, K and N must be below 2^23", fn);
-    // the transposes of W [K, N] and X [T, K] launch one 256-thread workgroup per 64 x 64 tile;
-    // a grid holds fewer than 2^32 threads, i.e. fewer than 2^24 tiles
-    if (((K + 63) / 64) * ((N + 63) / 64) >= ((int64_t)1 << 24) || ((T + 63) / 64) * ((K + 63) / 64) >= ((int64_t)1 << 24))
-        return fail(TP_ERR_UNSUPPORTED, "%s: the transposes of W and X need fewer than 2^24 tiles of 64 x 64", fn);
+    // the two GEMMs launch one 256-thread workgroup per 256 x 256 output tile (up to 4 per tile
+    // with the tail split); a grid holds fewer than 2^32 threads, so the tiles stay below 2^22
+    if (((T + 255) / 256) * ((K + 255) / 256) + ((K + 255) / 256) * ((N + 255) / 256) >= ((int64_t)1 << 22))
+        return fail(TP_ERR_UNSUPPORTED, "%s: dX and dW need fewer than 2^22 tiles of 256 x 256", fn);
     if (!aligned(X, 16) || !aligned(W_shard, 16) || !aligned(dY, 16) || !aligned(dX, 16) || !aligned(dW, 16))
         return fail(TP_ERR_MISALIGNED, "%s: X, W_shard, dY, dX and dW must be 16-byte aligned", fn);
     tp_status st = check_ws(fn, workspace, ws_bytes, tp_linear_backward_workspace_size(T, K, N));

@@ -59,6 +59,19 @@ constexpr int A_PER_WAVE = BM * 4 / 4;    // 256 granules of 16 B = 4 DMA instru
 constexpr int B_PER_WAVE = B_BYTES / 16 / 4;
 constexpr int DMA_A = 4, DMA_B = 4;
 
+// Operand layouts of the bf16 tiles. LAY_NN: A [M, K] with K contiguous, B [K, N] with N
+// contiguous. LAY_NT: B is given as B^T [N, K] (K contiguous): its tile holds 256 columns x one
+// K step of 64 bytes each, i.e. the activation tile's shape, so it is staged and read like one.
+// LAY_TN: A is given as A^T [K, M] (M contiguous): its tile holds one K step of 512-byte rows,
+// the weight tile's shape, and is staged and read (with the transposing LDS reads) like one.
+// The backward products use them to read W and X in place instead of transposed copies.
+constexpr int LAY_NN = 0, LAY_NT = 1, LAY_TN = 2;
+// element offsets of K step k0 from the tile's first element of A and of B
+template <int LAY>
+__device__ __forceinline__ int64_t a_kstep(int64_t k0, int64_t lda) { return LAY == LAY_TN ? k0 * lda : k0; }
+template <int LAY>
+__device__ __forceinline__ int64_t b_kstep(int64_t k0, int64_t ldb) { return LAY == LAY_NT ? k0 : k0 * ldb; }
+
 // Operand format: element type, K per step, elements per 16-byte granule, weight row bytes
 template <bool F8>
 struct Fmt;
@@ -150,20 +163,31 @@ __device__ __forceinline__ int64_t b_offset(const Geom<F8>& g, int64_t n0, int r
     return extra + (int64_t)row * g.ldb + col;
 }
 
-template <bool DUAL, bool F8>
+template <bool DUAL, bool F8, int LAY = LAY_NN>
 __device__ __forceinline__ void make_plan(DmaPlan& p, const Geom<F8>& g, int64_t m0, int64_t n0,
                                           int wave, int lane) {
+    static_assert(LAY == LAY_NN || (!DUAL && !F8), "transposed operands: single bf16/fp16 weight only");
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
-        a_granule(wave, i, lane, row, c);
-        p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + Fmt<F8>::EPG * c);
+        if constexpr (LAY == LAY_TN) {   // row = k, c = granule of 8 rows m (columns past M: the first)
+            b_granule<false>(wave, i, lane, row, c);
+            p.a_off[i] = (int32_t)(row * g.lda + (m0 + 8 * c < g.M ? 8 * c : 0));
+        } else {
+            a_granule(wave, i, lane, row, c);
+            p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + Fmt<F8>::EPG * c);
+        }
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule<F8>(wave, i, lane, row, gr);
-        p.b_off[i] = b_offset<DUAL, F8>(g, n0, row, gr);
+        if constexpr (LAY == LAY_NT) {   // row = output column n, gr = chunk of 8 k
+            a_granule(wave, i, lane, row, gr);
+            p.b_off[i] = (n0 + row < g.N ? row : 0) * g.ldb + 8 * gr;
+        } else {
+            b_granule<F8>(wave, i, lane, row, gr);
+            p.b_off[i] = b_offset<DUAL, F8>(g, n0, row, gr);
+        }
     }
 }
 
@@ -183,17 +207,19 @@ __device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
     return (unsigned)(uintptr_t)((const __attribute__((address_space(3))) unsigned char*)(p));
 }
 
-// Issue this wave's DMA_A + DMA_B loads for the K step starting at k0 into `stage`.
-template <bool DUAL, bool F8>
+// Issue this wave's DMA_A + DMA_B loads for the K step starting at k0 into `stage`. a_base and
+// b_base are the tile's first elements of A and B in their layout.
+template <bool DUAL, bool F8, int LAY = LAY_NN>
 __device__ __forceinline__ void issue_stage(unsigned stage, const DmaPlan& p, const Geom<F8>& g,
-                                            const typename Fmt<F8>::E* a_base, int64_t m0, int64_t n0,
+                                            const typename Fmt<F8>::E* a_base,
+                                            const typename Fmt<F8>::E* b_base, int64_t m0, int64_t n0,
                                             int64_t k0, int wave, int lane) {
     constexpr int BK = Fmt<F8>::BK, EPG = Fmt<F8>::EPG;
     const unsigned a_dst = stage + wave * A_PER_WAVE * 16;
     const unsigned b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
     if (k0 + BK <= g.K) {
-        const auto* a_k = a_base + k0;
-        const auto* b_k = g.B1 + k0 * g.ldb;
+        const auto* a_k = a_base + a_kstep<LAY>(k0, g.lda);
+        const auto* b_k = b_base + b_kstep<LAY>(k0, g.ldb);
 #pragma unroll
         for (int i = 0; i < DMA_A; ++i) dma16(a_k + p.a_off[i], a_dst + i * 1024);
 #pragma unroll
@@ -204,39 +230,65 @@ __device__ __forceinline__ void issue_stage(unsigned stage, const DmaPlan& p, co
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
-        a_granule(wave, i, lane, row, c);
-        if (k0 + EPG * c >= g.K) c = 0;
-        if (m0 + row >= g.M) row = 0;
-        dma16(a_base + k0 + (int64_t)row * g.lda + EPG * c, a_dst + i * 1024);
+        if constexpr (LAY == LAY_TN) {
+            b_granule<false>(wave, i, lane, row, c);
+            if (k0 + row >= g.K) row = 0;
+            if (m0 + 8 * c >= g.M) c = 0;
+            dma16(a_base + (k0 + row) * g.lda + 8 * c, a_dst + i * 1024);
+        } else {
+            a_granule(wave, i, lane, row, c);
+            if (k0 + EPG * c >= g.K) c = 0;
+            if (m0 + row >= g.M) row = 0;
+            dma16(a_base + k0 + (int64_t)row * g.lda + EPG * c, a_dst + i * 1024);
+        }
     }
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule<F8>(wave, i, lane, row, gr);
-        if (k0 + row >= g.K) row = 0;
-        dma16(g.B1 + k0 * g.ldb + b_offset<DUAL, F8>(g, n0, row, gr), b_dst + i * 1024);
+        if constexpr (LAY == LAY_NT) {
+            a_granule(wave, i, lane, row, gr);
+            if (k0 + 8 * gr >= g.K) gr = 0;
+            if (n0 + row >= g.N) row = 0;
+            dma16(b_base + k0 + (int64_t)row * g.ldb + 8 * gr, b_dst + i * 1024);
+        } else {
+            b_granule<F8>(wave, i, lane, row, gr);
+            if (k0 + row >= g.K) row = 0;
+            dma16(b_base + k0 * g.ldb + b_offset<DUAL, F8>(g, n0, row, gr), b_dst + i * 1024);
+        }
     }
 }
 
 // After a partial final K step has landed: zero this wave's granules that lie past K.
-template <bool F8>
+template <bool F8, int LAY = LAY_NN>
 __device__ __forceinline__ void zero_tail(unsigned char* stage, const Geom<F8>& g, int64_t k0,
                                           int wave, int lane) {
     unsigned char* a_dst = stage + wave * A_PER_WAVE * 16;
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
         int row, c;
-        a_granule(wave, i, lane, row, c);
-        if (k0 + Fmt<F8>::EPG * c >= g.K)
-            *reinterpret_cast<u32x4*>(a_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+        bool past;
+        if constexpr (LAY == LAY_TN) {
+            b_granule<false>(wave, i, lane, row, c);
+            past = k0 + row >= g.K;
+        } else {
+            a_granule(wave, i, lane, row, c);
+            past = k0 + Fmt<F8>::EPG * c >= g.K;
+        }
+        if (past) *reinterpret_cast<u32x4*>(a_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
     unsigned char* b_dst = stage + A_BYTES + wave * B_PER_WAVE * 16;
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
         int row, gr;
-        b_granule<F8>(wave, i, lane, row, gr);
-        if (k0 + row >= g.K)
-            *reinterpret_cast<u32x4*>(b_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+        bool past;
+        if constexpr (LAY == LAY_NT) {
+            a_granule(wave, i, lane, row, gr);
+            past = k0 + 8 * gr >= g.K;
+        } else {
+            b_granule<F8>(wave, i, lane, row, gr);
+            past = k0 + row >= g.K;
+        }
+        if (past) *reinterpret_cast<u32x4*>(b_dst + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -279,23 +331,33 @@ struct Frags {
 // Pieces of the operand fragments of 16-deep K slice ks for wave (wm, wn), so that they can
 // be interleaved one by one with MFMAs: piece 0..3 = activation block i (ds_read_b128),
 // piece 4..7 = weight block j (two ds_read_b64_tr_b16).
-template <bool DUAL>
+// (LAY_NT: the weight block is read like an activation block; LAY_TN: the activation block is
+// read with the weight tile's transposing reads.)
+template <bool DUAL, int LAY = LAY_NN>
 __device__ __forceinline__ void read_piece(Frags& f, int piece, const unsigned char* stage, int ks,
                                            int wm, int wn, int lane) {
+    const int r32 = lane & 31, hi = lane >> 5;
     if (piece < 4) {
-        const int r32 = lane & 31, hi = lane >> 5;
-        f.a[piece] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(stage + a_lds(wm * 128 + piece * 32 + r32, ks * 2 + hi)));
+        if constexpr (LAY == LAY_TN)
+            f.a[piece] = read_b_frag(stage, ks, wm * 128 + piece * 32, lane);
+        else
+            f.a[piece] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(stage + a_lds(wm * 128 + piece * 32 + r32, ks * 2 + hi)));
     } else {
-        f.b[piece - 4] = read_b_frag(stage + A_BYTES, ks, b_col_of<DUAL>(piece - 4, wn), lane);
+        if constexpr (LAY == LAY_NT)
+            f.b[piece - 4] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(stage + A_BYTES +
+                                                        a_lds(b_col_of<DUAL>(piece - 4, wn) + r32, ks * 2 + hi)));
+        else
+            f.b[piece - 4] = read_b_frag(stage + A_BYTES, ks, b_col_of<DUAL>(piece - 4, wn), lane);
     }
 }
 
-template <bool DUAL>
+template <bool DUAL, int LAY = LAY_NN>
 __device__ __forceinline__ void read_frags(Frags& f, const unsigned char* stage, int ks, int wm,
                                            int wn, int lane) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) read_piece<DUAL>(f, q, stage, ks, wm, wn, lane);
+    for (int q = 0; q < 8; ++q) read_piece<DUAL, LAY>(f, q, stage, ks, wm, wn, lane);
 }
 
 // F16: the 16-bit operands are IEEE half values (same LDS layout and fragments as bf16)
@@ -597,7 +659,7 @@ __device__ __forceinline__ bool k0_full(const Geom<F8>& g, int64_t k0) { return 
 // Wait until this wave's DMA for a stage has landed while the `ops` DMA instructions it issued
 // after that stage's may still be in flight, zero its granules past K if it is the partial
 // final step, then barrier: after it the stage is readable by every wave.
-template <bool F8>
+template <bool F8, int LAY = LAY_NN>
 __device__ __forceinline__ void publish(unsigned char* stage, int ops, const Geom<F8>& g,
                                         int64_t k0, int wave, int lane) {
     constexpr int GRP = DMA_A + DMA_B;
@@ -610,7 +672,7 @@ __device__ __forceinline__ void publish(unsigned char* stage, int ops, const Geo
     else wait_vm<0>();
     if (k0 + Fmt<F8>::BK > g.K) {
         wait_vm<0>();
-        zero_tail<F8>(stage, g, k0, wave, lane);
+        zero_tail<F8, LAY>(stage, g, k0, wave, lane);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS traffic done
     __builtin_amdgcn_s_barrier();
@@ -637,12 +699,12 @@ __device__ __forceinline__ int ops_after_next(int kt, int nk, int refill_ops) {
 // STEADY steps (every step but the last five of a tile) know at compile time that a next step
 // exists, that the refill is a whole step and that two later stages are in flight, so their
 // instruction stream has no branches.
-template <bool DUAL, bool STEADY, bool F16>
+template <bool DUAL, bool STEADY, bool F16, int LAY>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
                                        unsigned char* cur, unsigned char* nxt, unsigned ref_lds, int kt, int nk,
                                        int64_t kbase, const DmaPlan& p, const Geom<false>& g,
-                                       const uint16_t* a_base, int64_t m0, int64_t n0, int wm, int wn,
-                                       int wave, int lane) {
+                                       const uint16_t* a_base, const uint16_t* b_base, int64_t m0, int64_t n0,
+                                       int wm, int wn, int wave, int lane) {
     constexpr int BK = Fmt<false>::BK;
     constexpr int GRP = DMA_A + DMA_B;
     const bool has_next = STEADY || kt + 1 < nk;
@@ -651,16 +713,16 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
     // whole refill steps interleave their DMA with the MFMAs; a partial final step takes the
     // general path up front
     const bool inline_dma = STEADY || (refill && k0_full<false>(g, k_ref));
-    if (refill && !inline_dma) issue_stage<DUAL, false>(ref_lds, p, g, a_base, m0, n0, k_ref, wave, lane);
-    const uint16_t* a_k = a_base + k_ref;
-    const uint16_t* b_k = g.B1 + k_ref * g.ldb;
+    if (refill && !inline_dma) issue_stage<DUAL, false, LAY>(ref_lds, p, g, a_base, b_base, m0, n0, k_ref, wave, lane);
+    const uint16_t* a_k = a_base + a_kstep<LAY>(k_ref, g.lda);
+    const uint16_t* b_k = b_base + b_kstep<LAY>(k_ref, g.ldb);
     const unsigned a_dst = ref_lds + wave * A_PER_WAVE * 16;
     const unsigned b_dst = ref_lds + A_BYTES + wave * B_PER_WAVE * 16;
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         mfma1<F16>(acc, f0, n);
-        if (n < 8) read_piece<DUAL>(f1, n, cur, 1, wm, wn, lane);
+        if (n < 8) read_piece<DUAL, LAY>(f1, n, cur, 1, wm, wn, lane);
         if (inline_dma && (n & 3) == 2) dma16(a_k + p.a_off[n >> 2], a_dst + (n >> 2) * 1024);
         TP_FENCE();
     }
@@ -670,14 +732,14 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], Frags& f0, Frags& f1
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     } else if (has_next) {
-        publish<false>(nxt, ops_after_next(kt, nk, refill ? (inline_dma ? DMA_A : GRP) : 0), g,
+        publish<false, LAY>(nxt, ops_after_next(kt, nk, refill ? (inline_dma ? DMA_A : GRP) : 0), g,
                        kbase + (int64_t)(kt + 1) * BK, wave, lane);
     }
     TP_FENCE();
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         mfma1<F16>(acc, f1, n);
-        if (has_next && n < 8) read_piece<DUAL>(f0, n, nxt, 0, wm, wn, lane);
+        if (has_next && n < 8) read_piece<DUAL, LAY>(f0, n, nxt, 0, wm, wn, lane);
         if (inline_dma && (n & 3) == 2) dma16(b_k + p.b_off[n >> 2], b_dst + (n >> 2) * 1024);
         TP_FENCE();
     }
@@ -719,7 +781,7 @@ __device__ __forceinline__ void k_step_f8(f32x16 (&acc)[4][4], i32x8 (&a)[4], i3
     // step kt+4 goes to the stage of step kt-1 (free since the previous step's barrier)
     const int64_t k_ref = kbase + (int64_t)(kt + 4) * BK;
     const bool inline_dma = STEADY || (refill && k0_full<true>(g, k_ref));
-    if (refill && !inline_dma) issue_stage<DUAL, true>(ref_lds, p, g, a_base, m0, n0, k_ref, wave, lane);
+    if (refill && !inline_dma) issue_stage<DUAL, true>(ref_lds, p, g, a_base, g.B1, m0, n0, k_ref, wave, lane);
     const uint8_t* a_k = a_base + k_ref;
     const uint8_t* b_k = g.B1 + k_ref * g.ldb;
     const unsigned a_dst = ref_lds + wave * A_PER_WAVE * 16;
@@ -810,49 +872,21 @@ struct Pair {
     }
 };
 
-// F16 (with F8 false): fp16 operands instead of bf16
-template <bool F8, bool DUAL, class Epi, class Grp, bool F16 = false>
-__global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
-                                                            int tiles_n, SplitArgs sp, Grp gr) {
+// One tile (or one K piece of a split tile) of the kernel below, with operand layout LAY.
+template <bool F8, bool DUAL, class Epi, bool F16, int LAY>
+__device__ __forceinline__ void tile_body(const Geom<F8>& g, const Epi& epi, int tiles_m, int tiles_n,
+                                          const SplitArgs& sp, int L, int q, unsigned char* st0, unsigned char* st1,
+                                          unsigned char* st2, unsigned char* st3, unsigned char* st4) {
     constexpr int BK = Fmt<F8>::BK;
-    __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char st4[STAGE_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const int bid = (int)blockIdx.x;
-    int L, q = -1;
-    if (bid < sp.g_full) {
-        L = xcd_remap(bid, sp.g_full);
-    } else {
-        q = bid - sp.g_full;
-        L = sp.g_full + q / sp.pieces;
-    }
-    if constexpr (Grp::MODE == 2) {
-        if (gr.second(L)) {
-            g = gr.g1;
-            epi = gr.e1;
-            tiles_m = gr.tiles_m1;
-            tiles_n = gr.tiles_n1;
-        }
-    }
-    if constexpr (Grp::MODE == 1) {
-        int64_t r0, m;
-        const int e = gr.locate(L, tiles_n, tiles_m, r0, m);
-        g.A += r0 * g.lda;
-        g.B1 += e * gr.b_stride;
-        if constexpr (DUAL) g.B2 += e * gr.b_stride;
-        g.M = m;
-        epi.shift_rows(r0, m);
-    }
     int tm, tn;
     tile_of(L, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * (DUAL ? BN / 2 : BN);
-    const auto* a_base = g.A + m0 * g.lda;
+    const auto* a_base = LAY == LAY_TN ? g.A + m0 : g.A + m0 * g.lda;
+    const auto* b_base = LAY == LAY_NT ? g.B1 + n0 * g.ldb : g.B1;
     const int nk_total = (int)((g.K + BK - 1) / BK);
     int64_t kbase = 0;
     int nk = nk_total;
@@ -863,7 +897,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
     }
 
     DmaPlan p;
-    make_plan<DUAL, F8>(p, g, m0, n0, wave, lane);
+    make_plan<DUAL, F8, LAY>(p, g, m0, n0, wave, lane);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -877,11 +911,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         // prologue: steps 0..3 in flight, publish step 0; step 4 is loaded during step 0
         const unsigned l0 = lds_addr(st0), l1 = lds_addr(st1), l2 = lds_addr(st2), l3 = lds_addr(st3),
                        l4 = lds_addr(st4);
-        issue_stage<DUAL, F8>(l0, p, g, a_base, m0, n0, kbase, wave, lane);
-        if (nk > 1) issue_stage<DUAL, F8>(l1, p, g, a_base, m0, n0, kbase + BK, wave, lane);
-        if (nk > 2) issue_stage<DUAL, F8>(l2, p, g, a_base, m0, n0, kbase + 2 * BK, wave, lane);
-        if (nk > 3) issue_stage<DUAL, F8>(l3, p, g, a_base, m0, n0, kbase + 3 * BK, wave, lane);
-        publish<F8>(st0, (DMA_A + DMA_B) * ((nk - 1 < 3) ? nk - 1 : 3), g, kbase, wave, lane);
+        issue_stage<DUAL, F8, LAY>(l0, p, g, a_base, b_base, m0, n0, kbase, wave, lane);
+        if (nk > 1) issue_stage<DUAL, F8, LAY>(l1, p, g, a_base, b_base, m0, n0, kbase + BK, wave, lane);
+        if (nk > 2) issue_stage<DUAL, F8, LAY>(l2, p, g, a_base, b_base, m0, n0, kbase + 2 * BK, wave, lane);
+        if (nk > 3) issue_stage<DUAL, F8, LAY>(l3, p, g, a_base, b_base, m0, n0, kbase + 3 * BK, wave, lane);
+        publish<F8, LAY>(st0, (DMA_A + DMA_B) * ((nk - 1 < 3) ? nk - 1 : 3), g, kbase, wave, lane);
 
         // stage of step kt (and its LDS address); sb, sc, sd hold steps kt+1, kt+2, kt+3 and se
         // (the stage of step kt-1) receives step kt+4
@@ -908,16 +942,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
     } while (0)
         if constexpr (!F8) {
             Frags f0, f1;
-            read_frags<DUAL>(f0, st0, 0, wm, wn, lane);
+            read_frags<DUAL, LAY>(f0, st0, 0, wm, wn, lane);
             // steady steps: kt + 4 <= nk - 2, so step kt+1 exists, the refill (step kt+4) is
             // whole and not the tile's last step, and two stages after kt+1 are in flight
             int kt = 0;
             for (; kt < nk - 5; ++kt) {
-                k_step<DUAL, true, F16>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step<DUAL, true, F16, LAY>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, b_base, m0, n0, wm, wn, wave, lane);
                 TP_ROTATE1();
             }
             for (; kt < nk; ++kt) {
-                k_step<DUAL, false, F16>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, m0, n0, wm, wn, wave, lane);
+                k_step<DUAL, false, F16, LAY>(acc, f0, f1, sa, sb, le, kt, nk, kbase, p, g, a_base, b_base, m0, n0, wm, wn, wave, lane);
                 TP_ROTATE1();
             }
         } else {
@@ -969,6 +1003,53 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dst[((i * 4 + j) * 16 + r) * 64] = acc[i][j][r];
+}
+
+
+// F16 (with F8 false): fp16 operands instead of bf16. LAY: operand layout of the tiles; a Pair
+// launch's second GEMM uses LAY1.
+template <bool F8, bool DUAL, class Epi, class Grp, bool F16 = false, int LAY = LAY_NN, int LAY1 = LAY_NN>
+__global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi, int tiles_m,
+                                                            int tiles_n, SplitArgs sp, Grp gr) {
+    __shared__ __attribute__((aligned(16))) unsigned char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st3[STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char st4[STAGE_BYTES];
+    const int bid = (int)blockIdx.x;
+    int L, q = -1;
+    if (bid < sp.g_full) {
+        L = xcd_remap(bid, sp.g_full);
+    } else {
+        q = bid - sp.g_full;
+        L = sp.g_full + q / sp.pieces;
+    }
+    bool second = false;
+    if constexpr (Grp::MODE == 2) {
+        if (gr.second(L)) {
+            second = true;
+            g = gr.g1;
+            epi = gr.e1;
+            tiles_m = gr.tiles_m1;
+            tiles_n = gr.tiles_n1;
+        }
+    }
+    if constexpr (Grp::MODE == 1) {
+        int64_t r0, m;
+        const int e = gr.locate(L, tiles_n, tiles_m, r0, m);
+        g.A += r0 * g.lda;
+        g.B1 += e * gr.b_stride;
+        if constexpr (DUAL) g.B2 += e * gr.b_stride;
+        g.M = m;
+        epi.shift_rows(r0, m);
+    }
+    if constexpr (LAY1 != LAY) {
+        if (second) {
+            tile_body<F8, DUAL, Epi, F16, LAY1>(g, epi, tiles_m, tiles_n, sp, L, q, st0, st1, st2, st3, st4);
+            return;
+        }
+    }
+    tile_body<F8, DUAL, Epi, F16, LAY>(g, epi, tiles_m, tiles_n, sp, L, q, st0, st1, st2, st3, st4);
 }
 
 // One wave per (split tile, wave of the tile, accumulator row block i): sum the tile's
@@ -1087,7 +1168,8 @@ size_t split_bytes_of(int64_t M, int64_t N, int64_t K, bool dual, int bk) {
 
 // ws may be NULL (or too small): the tiles then all run whole. A grouped launch takes its
 // tile count from the groups (g.M then only bounds nothing: each group sets its own).
-template <bool F8, bool DUAL, class Epi, class Grp = NoGroups, bool F16 = false>
+template <bool F8, bool DUAL, class Epi, class Grp = NoGroups, bool F16 = false, int LAY = LAY_NN,
+          int LAY1 = LAY_NN>
 hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, hipStream_t s,
                   const char* name, const Grp& gr = Grp{}) {
     constexpr int BK = Fmt<F8>::BK;
@@ -1105,7 +1187,8 @@ hipError_t launch(const Geom<F8>& g, const Epi& epi, void* ws, size_t ws_bytes, 
     const int64_t blocks = sp.pieces >= 2 ? sp.g_full + (G - sp.g_full) * sp.pieces : G;
     {
         ProfScope ps(name, s);
-        gemm_mfma_kernel<F8, DUAL, Epi, Grp, F16><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m, (int)tiles_n, sp, gr);
+        gemm_mfma_kernel<F8, DUAL, Epi, Grp, F16, LAY, LAY1><<<(unsigned)blocks, NTHR, 0, s>>>(g, epi, (int)tiles_m,
+                                                                                          (int)tiles_n, sp, gr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || sp.pieces < 2) return e;
     }
@@ -1281,6 +1364,33 @@ hipError_t gemm_bf16_f32out_pair(const void* A0, const void* B0, float* C0, int6
                                     M1, N1, K, lda1, ldb1},
                         Epi{C1, ldc1, M1, N1, 1.0f, 1.0f}, (int)tm1, (int)tn1, (int)(tm0 * tn0)};
     return launch<false, false>(g0, Epi{C0, ldc0, M0, N0, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_f32out", pr);
+}
+
+hipError_t gemm_bf16_f32out_t(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                              int64_t ldb, int64_t ldc, int b_trans, void* ws, size_t ws_bytes, hipStream_t s) {
+    using Epi = EpiStore<2, false>;
+    const Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), nullptr, M, N, K, lda, ldb};
+    if (b_trans)
+        return launch<false, false, Epi, NoGroups, false, LAY_NT>(g, Epi{C, ldc, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
+                                                                   "gemm_bf16_f32out_nt");
+    return launch<false, false, Epi, NoGroups, false, LAY_TN>(g, Epi{C, ldc, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
+                                                               "gemm_bf16_f32out_tn");
+}
+
+hipError_t gemm_bf16_f32out_pair_nt_tn(const void* A0, const void* B0t, float* C0, int64_t M0, int64_t N0,
+                                       int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1t, const void* B1,
+                                       float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
+                                       int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+    using Epi = EpiStore<2, false>;
+    Geom<false> g0{static_cast<const uint16_t*>(A0), static_cast<const uint16_t*>(B0t), nullptr, M0, N0, K, lda0, ldb0};
+    int64_t tm0, tn0, tm1, tn1;
+    tiles_of<false>(M0, N0, tm0, tn0);
+    tiles_of<false>(M1, N1, tm1, tn1);
+    Pair<false, Epi> pr{Geom<false>{static_cast<const uint16_t*>(A1t), static_cast<const uint16_t*>(B1), nullptr,
+                                    M1, N1, K, lda1, ldb1},
+                        Epi{C1, ldc1, M1, N1, 1.0f, 1.0f}, (int)tm1, (int)tn1, (int)(tm0 * tn0)};
+    return launch<false, false, Epi, Pair<false, Epi>, false, LAY_NT, LAY_TN>(
+        g0, Epi{C0, ldc0, M0, N0, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_f32out_nt_tn", pr);
 }
 
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
