@@ -430,11 +430,26 @@ def decode_bench(args):
     eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
     for t in outs:
         t.fill_(float("nan"))
-    ms, _ = graph_timed(step_fused, args.warmup, args.steps, "decode")   # the step as one HIP graph
+    ms, g = graph_timed(step_fused, args.warmup, args.steps, "decode")   # the step as one HIP graph
     torch.cuda.synchronize()
     # the outputs left by the last timed replay must equal the eager step's, bit for bit
     replay = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
     same = all(a.tobytes() == b.tobytes() for a, b in zip(eager, replay))
+    # The same replays with the 256 MB Infinity Cache flushed first: a 512 MiB buffer is read and
+    # rewritten before each one (outside its events), so no step finds weights or cache rows that
+    # the previous step left in the cache. Back-to-back steps re-read a 606 MB working set.
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    n_cold = min(args.steps, 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    for e0, e1 in ev:
+        flush.add_(1.0)
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    cold = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    ms_cold = sum(cold) / len(cold)
+    del flush
     d = 128
     w_bytes = 2 * (H * (hq + 2 * hkv) * d + hq * d * H + 2 * H * I + I * H + H * V)
     kv_bytes = 2 * 2 * B * hkv * (L - 1) * d          # cached keys and values read once
@@ -445,6 +460,8 @@ def decode_bench(args):
     return {
         "ms_per_step": ms,
         "ms_per_step_eager": ms_eager,
+        "ms_per_step_cache_flushed": ms_cold,
+        "median_ms_cache_flushed": cold[len(cold) // 2],
         "ms_per_step_separate_calls_eager": ms_sep_eager,
         "ms_per_step_separate_calls_graph": ms_sep_graph,
         "step_stats": STEP_STATS.get("decode"),
@@ -453,6 +470,7 @@ def decode_bench(args):
         "graph_outputs_equal_eager": same,
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
+        "gbs_cache_flushed": total / (ms_cold * 1e-3) / 1e9,
         "frac_hbm": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "kernels": {"decode_attn(avg_us)": att_ms * 1e3 if att_ms else None,
                     "skinny_gemm_x: QKV + gate/up (avg_us)": x_ms * 1e3 if x_ms else None,
