@@ -823,8 +823,9 @@ def cpu_baseline(inp, target_s: float):
 
 
 def _round(x, nd=5):
+    """nd decimals, or 4 significant digits for magnitudes below 1e-3 (error norms stay readable)."""
     if isinstance(x, float):
-        return round(x, nd)
+        return float(f"{x:.4g}") if x != 0.0 and abs(x) < 1e-3 else round(x, nd)
     if isinstance(x, dict):
         return {k: _round(v, nd) for k, v in x.items()}
     if isinstance(x, list):
