@@ -2,13 +2,16 @@
 // The work is bound by streaming the weight shards and the KV cache from HBM once.
 //
 //   skinny_kernel        split-K GEMM A[M, K] . W[K, N] for small M. A workgroup owns a
-//                        128-column strip and one K chunk; its 4 waves take interleaved 32-row
-//                        steps, each streaming a 32 x 128 weight block with 128-bit loads
-//                        (every weight byte read once, the next step's block already in
-//                        flight), transposing it in registers (v_perm) and feeding
-//                        v_mfma_f32_16x16x32_bf16 with the activations as the A operand. The
-//                        waves' partials meet in LDS; each wave then sums a quarter of the rows
-//                        in wave order and writes it to the chunk's fp32 partial buffer.
+//                        128-column strip and one K chunk; its 4 waves take 32-row steps, each
+//                        streaming a 32 x 128 weight block with 128-bit loads (every weight byte
+//                        read once, the next step's block already in flight), transposing it in
+//                        registers (v_perm) and feeding v_mfma_f32_16x16x32_bf16 with the
+//                        activations as the A operand. For M <= 32 each wave streams its own
+//                        contiguous quarter of the chunk and stages the activation rows through
+//                        LDS (whole 256-byte rows per load); for larger M the waves interleave
+//                        steps and load the fragments directly. The waves' partials meet in LDS;
+//                        each wave then sums a quarter of the rows in wave order and writes it to
+//                        the chunk's fp32 partial buffer.
 //   reduce kernels       sum the chunk partials in chunk order and apply the layer's
 //                        epilogue: fp32/bf16 store (O and down partials, vocabulary-split
 //                        logits) or SiLU(gate)*up.
@@ -232,6 +235,137 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, 
     }
 }
 
+// The same for M <= 32 (MB = 2), with the activations staged through LDS: wave w streams the
+// contiguous K sub-range w of the chunk (kchunk / 4 rows), 4 steps (128 rows) per group. For each
+// group it loads the activation block A[0..31][128 k] with whole 256-byte rows (16 lanes per
+// row, 4 rows per instruction: 1 KB of contiguous bytes each, instead of 16 rows x 64 bytes per
+// MFMA fragment load), writes it to its own LDS region (16-byte chunk c of row r at chunk
+// position c ^ (r & 15)) and reads the MFMA fragments from there. The next group's block is in
+// flight in registers meanwhile. No barrier: each wave reads only what it wrote. Measured on the
+// 7B decode step: 0.131 -> 0.128 ms (the fragment loads' scattered cache lines cost ~8 us in all;
+// whole-row loads recover part of it).
+template <bool F16>
+__device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t strip, int64_t split,
+                                                f32x4 (&red)[4][32][STRIP / 4]) {
+    constexpr int MB = 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane >> 4, l16 = lane & 15;
+    const bool second = strip >= g.strips_per_b;
+    const uint16_t* Bp = second ? g.B2 : g.B1;
+    const int64_t cgroup = strip % g.strips_per_b;
+    const int64_t c0 = cgroup * STRIP;
+    const int64_t col = c0 + 8 * l16;
+    const bool col_ok = col < g.N;
+    const int64_t kbeg = split * g.kchunk;
+    const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+    const int64_t kw = g.kchunk / 4;                  // rows per wave (a multiple of 32)
+    const int64_t wbeg = kbeg + wave * kw;
+    int64_t wend = wbeg + kw;
+    if (wend > kend) wend = kend;
+    const int nst = wend > wbeg ? (int)((wend - wbeg + STEP - 1) / STEP) : 0;
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    unsigned char* stg = reinterpret_cast<unsigned char*>(&red[wave][0][0]);   // 16 KB: two 8 KB blocks
+    const uint16_t* wsafe = Bp + kbeg * g.N + (col_ok ? col : c0);
+    const uint16_t* asafe = g.A + kbeg;
+    // this lane's weight rows of step i: wbeg + 32 i + 8 grp .. + 7
+    auto load_w = [&](StepRegs<MB>& s, int i) {
+        const int64_t kr = wbeg + (int64_t)i * STEP + 8 * grp;
+        s.k_ok = kr < wend;
+        const bool ok = s.k_ok && col_ok;
+        const uint16_t* wp = Bp + kr * g.N + col;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) s.w[r] = ld_stream(ok ? wp + r * g.N : wsafe);
+    };
+    // activation block of group G: row 4 j + (lane >> 4), 16-byte chunk lane & 15 of its 128 k
+    u32x4 areg[8];
+    auto load_a = [&](int G) {
+        const int64_t k = wbeg + (int64_t)G * 4 * STEP + 8 * (lane & 15);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            const bool ok = row < g.M && k < wend;
+            areg[j] = *reinterpret_cast<const u32x4*>(ok ? g.A + (int64_t)row * g.lda + k : asafe);
+        }
+    };
+    auto store_a = [&](int G) {
+        unsigned char* base = stg + (G & 1) * 8192;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            *reinterpret_cast<u32x4*>(base + row * 256 + (((lane & 15) ^ (row & 15)) << 4)) = areg[j];
+        }
+    };
+    // fragments of step t (0..3) of group G: row l16 + 16 mb, k chunk 4 t + grp
+    auto frag_a = [&](StepRegs<MB>& s, int G, int t) {
+        const unsigned char* base = stg + (G & 1) * 8192;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = l16 + 16 * mb;
+            s.a[mb] = *reinterpret_cast<const u32x4*>(base + row * 256 + (((4 * t + grp) ^ (row & 15)) << 4));
+        }
+    };
+    StepRegs<MB> s0, s1;
+    if (nst > 0) {
+        load_a(0);
+        load_w(s0, 0);
+    }
+    for (int G = 0; 4 * G < nst; ++G) {
+        // every load below is issued whether or not its step exists (stand-in addresses, masked
+        // by k_ok), so each wave's loop body is branch-free and the load counts stay exact
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(G);
+        load_a(G + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(s1, 4 * G + 1);
+        frag_a(s0, G, 0);
+        mma_step<MB, F16>(acc, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(s0, 4 * G + 2);
+        frag_a(s1, G, 1);
+        mma_step<MB, F16>(acc, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(s1, 4 * G + 3);
+        frag_a(s0, G, 2);
+        mma_step<MB, F16>(acc, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(s0, 4 * G + 4);
+        frag_a(s1, G, 3);
+        mma_step<MB, F16>(acc, s1);
+    }
+
+    // every wave's partial goes to LDS (its own staging region: the slot it owns in `red`)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = mb * 16 + 4 * grp + r;
+            red[wave][m][2 * l16] = f32x4{acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            red[wave][m][2 * l16 + 1] = f32x4{acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+        }
+    __syncthreads();
+    constexpr int ROWS = MB * 16 / 4;
+    float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
+#pragma unroll
+    for (int rr = lane >> 3; rr < ROWS; rr += 8) {
+        const int m = wave * ROWS + rr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = (lane & 7) + 8 * q;
+            f32x4 v = red[0][m][c];
+            v += red[1][m][c];
+            v += red[2][m][c];
+            v += red[3][m][c];
+            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * g.ncols + 4 * c) = v;
+        }
+    }
+}
+
 // Up to three GEMMs that share M in one launch (a one-dimensional grid): workgroups g1.wg0..
 // belong to g1, g2.wg0.. to g2, the rest to g0; within a GEMM, workgroup w takes strip
 // w % strips of K chunk w / strips. The GEMM is picked by scalar selects over the three
@@ -260,7 +394,10 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
     TP_SEL(part);
 #undef TP_SEL
     const int local = bid - g.wg0;
-    skinny_body<MB, F16>(g, local % g.strips, local / g.strips, red);
+    if constexpr (MB == 2)
+        skinny_body_lds<F16>(g, local % g.strips, local / g.strips, red);
+    else
+        skinny_body<MB, F16>(g, local % g.strips, local / g.strips, red);
 }
 
 // v[i] = sum over chunks (in order) of part[s][m][c[i]] for NC columns of row m. The chunks'
