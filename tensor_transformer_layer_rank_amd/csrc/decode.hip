@@ -6,10 +6,10 @@
 //                        streaming a 32 x 128 weight block with 128-bit loads (every weight byte
 //                        read once, the next step's block already in flight), transposing it in
 //                        registers (v_perm) and feeding v_mfma_f32_16x16x32_bf16 with the
-//                        activations as the A operand. For M <= 32 each wave streams its own
-//                        contiguous quarter of the chunk and stages the activation rows through
-//                        LDS (whole 256-byte rows per load); for larger M the waves interleave
-//                        steps and load the fragments directly. The waves' partials meet in LDS;
+//                        activations as the A operand. For M <= 32 the waves take interleaved
+//                        128-row groups and stage the activation rows through LDS (whole 256-byte
+//                        rows per load); for larger M they interleave 32-row steps and load the
+//                        fragments directly. The waves' partials meet in LDS;
 //                        each wave then sums a quarter of the rows in wave order and writes it to
 //                        the chunk's fp32 partial buffer.
 //   reduce kernels       sum the chunk partials in chunk order and apply the layer's
@@ -235,14 +235,15 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, 
     }
 }
 
-// The same for M <= 32 (MB = 2), with the activations staged through LDS: wave w streams the
-// contiguous K sub-range w of the chunk (kchunk / 4 rows), 4 steps (128 rows) per group. For each
+// The same for M <= 32 (MB = 2), with the activations staged through LDS: wave w takes the
+// 128-row groups w, w + 4, ... of the chunk (4 steps each; 128-row interleaving keeps the four
+// waves on neighbouring weight rows, which streamed faster than contiguous quarters). For each
 // group it loads the activation block A[0..31][128 k] with whole 256-byte rows (16 lanes per
 // row, 4 rows per instruction: 1 KB of contiguous bytes each, instead of 16 rows x 64 bytes per
 // MFMA fragment load), writes it to its own LDS region (16-byte chunk c of row r at chunk
 // position c ^ (r & 15)) and reads the MFMA fragments from there. The next group's block is in
 // flight in registers meanwhile. No barrier: each wave reads only what it wrote. Measured on the
-// 7B decode step: 0.131 -> 0.128 ms (the fragment loads' scattered cache lines cost ~8 us in all;
+// 7B decode step: 0.131 -> 0.127 ms (the fragment loads' scattered cache lines cost ~8 us in all;
 // whole-row loads recover part of it).
 template <bool F16>
 __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t strip, int64_t split,
@@ -258,11 +259,11 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
     const bool col_ok = col < g.N;
     const int64_t kbeg = split * g.kchunk;
     const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
-    const int64_t kw = g.kchunk / 4;                  // rows per wave (a multiple of 32)
-    const int64_t wbeg = kbeg + wave * kw;
-    int64_t wend = wbeg + kw;
-    if (wend > kend) wend = kend;
-    const int nst = wend > wbeg ? (int)((wend - wbeg + STEP - 1) / STEP) : 0;
+    // wave w takes 128-row groups w, w + 4, ... of the chunk
+    const int64_t wbeg = kbeg + wave * 4 * STEP;
+    const int64_t wend = kend;
+    const int ngw = wend > wbeg ? (int)((wend - wbeg + 16 * STEP - 1) / (16 * STEP)) : 0;
+    const int nst = 4 * ngw;
 
     f32x4 acc[MB][8];
 #pragma unroll
@@ -273,9 +274,9 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
     unsigned char* stg = reinterpret_cast<unsigned char*>(&red[wave][0][0]);   // 16 KB: two 8 KB blocks
     const uint16_t* wsafe = Bp + kbeg * g.N + (col_ok ? col : c0);
     const uint16_t* asafe = g.A + kbeg;
-    // this lane's weight rows of step i: wbeg + 32 i + 8 grp .. + 7
+    // this lane's weight rows of step i (step i & 3 of group i >> 2): 8 grp .. + 7 of it
     auto load_w = [&](StepRegs<MB>& s, int i) {
-        const int64_t kr = wbeg + (int64_t)i * STEP + 8 * grp;
+        const int64_t kr = wbeg + (int64_t)(i >> 2) * 16 * STEP + (i & 3) * STEP + 8 * grp;
         s.k_ok = kr < wend;
         const bool ok = s.k_ok && col_ok;
         const uint16_t* wp = Bp + kr * g.N + col;
@@ -285,7 +286,7 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
     // activation block of group G: row 4 j + (lane >> 4), 16-byte chunk lane & 15 of its 128 k
     u32x4 areg[8];
     auto load_a = [&](int G) {
-        const int64_t k = wbeg + (int64_t)G * 4 * STEP + 8 * (lane & 15);
+        const int64_t k = wbeg + (int64_t)G * 16 * STEP + 8 * (lane & 15);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = 4 * j + (lane >> 4);
