@@ -850,31 +850,56 @@ def main():
         {"c0", "c1", "c2", "c3", "c4", "fp8", "merge", "backward", "moe", "ceiling"}
     keep = {}
     mlp = c0 = c2 = c3 = dec = fp8 = merge = bwd = moe = None
+    t_start = time.perf_counter()
+
+    def done(leg):   # one progress line per finished leg, on stderr (stdout carries the JSON line)
+        print(f"bench: {leg} done at {time.perf_counter() - t_start:.1f} s", file=sys.stderr, flush=True)
+
     if "c1" in legs:
         mlp, keep["c1"] = mlp_bench(args)        # headline first, after the clock-settling prewarm
+        done("c1")
     if "c0" in legs:
         c0, keep["c0"] = int_mlp_bench(args)
+        done("c0")
     if "c2" in legs:
         c2, keep["c2"] = attn_bench(args, "attn7b_tp4")
+        done("c2")
     if "c3" in legs:
         c3, keep["c3"] = attn_bench(args, "layer70b_tp8")
+        done("c3")
     if "c4" in legs:
         dec, keep["c4"] = decode_bench(args)
-    fp8 = fp8_mlp_bench(args) if "fp8" in legs else None
-    merge = merge_bench(args) if "merge" in legs else None
-    bwd = backward_bench(args) if "backward" in legs else None
-    moe = moe_bench(args) if "moe" in legs else None
-    ceiling = ceiling_bench(args) if "ceiling" in legs else None
+        done("c4")
+    if "fp8" in legs:
+        fp8 = fp8_mlp_bench(args)
+        done("fp8")
+    if "merge" in legs:
+        merge = merge_bench(args)
+        done("merge")
+    if "backward" in legs:
+        bwd = backward_bench(args)
+        done("backward")
+    if "moe" in legs:
+        moe = moe_bench(args)
+        done("moe")
+    ceiling = None
+    if "ceiling" in legs:
+        ceiling = ceiling_bench(args)
+        done("ceiling")
     if args.traffic_probe:
         traffic_probe()
     torch.cuda.synchronize()
     par = None if args.no_parity else cpu_oracle_leg(keep)
+    if par is not None:
+        done("parity (fp64 oracle over every output element)")
     if mlp is None:
         print(json.dumps({"legs": sorted(legs), "c0": c0, "c2": c2, "c3": c3, "decode": dec, "fp8_mlp": fp8,
                           "merge_rmsnorm": merge, "backward": bwd, "moe": moe, "mfma_ceiling": ceiling,
                           "parity": par}))
         return
     cpu = None if args.no_cpu else cpu_baseline(keep["c1"]["inp"], args.cpu_seconds)
+    if cpu is not None:
+        done("cpu baseline")
     props = torch.cuda.get_device_properties(0)
     c1 = {"workload": "mlp7b_tp4", "ms_per_step": mlp["ms_per_step"], "tflops": mlp["tflops"],
           "frac_bf16_peak": mlp["tflops"] / PEAK_BF16_TFLOPS}
