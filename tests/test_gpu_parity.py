@@ -359,6 +359,26 @@ def test_column_linear_bf16(tp, T, K, N, out):
     assert_close_bf16(host(Y), O.linear(X, W), f"column {T}x{K}x{N} -> {out}", out=out)
 
 
+@pytest.mark.parametrize("T,K,N", [(5, 1032, 200), (17, 3000, 136), (31, 8, 72), (32, 264, 4104), (33, 776, 520)])
+def test_few_row_linear_ragged(tp, T, K, N):
+    """The weight-streaming kernels (T <= 64) on odd row counts, K off the 32-row step and the
+    128-row staging group (K = 8 included) and N off the 128-column strip: column output in bf16
+    and fp32, and the row partial with accumulation."""
+    import torch
+    rng = np.random.default_rng(11 * T + K + N)
+    X = wl.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    ref = O.linear(X, W)
+    for out, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        Y = tp.column_linear(dev(X), dev(W), Y=_nan((T, N), dt))
+        torch.cuda.synchronize()
+        assert_close_bf16(host(Y), ref, f"few-row column {T}x{K}x{N} -> {out}", out=out)
+    P = tp.row_linear_partial(dev(X), dev(W), Y=_nan((T, N), torch.float32))
+    tp.row_linear_partial(dev(X), dev(W), Y=P, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(P), 2 * ref, f"few-row row partial {T}x{K}x{N} accumulate")
+
+
 def test_column_linear_relu_and_ldy(tp):
     import torch
     rng = np.random.default_rng(3)
