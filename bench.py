@@ -225,10 +225,15 @@ def int_mlp_bench(args):
         tp.partial_sum(P, out=Y)
 
     ms = timed(step, args.warmup, args.steps, "c0")
+    # the same five calls captured as one HIP graph: the GPU-side latency without the per-call
+    # host cost (Python, ctypes, argument checks, launch)
+    g_ms, _ = graph_timed(step, args.warmup, args.steps, "c0_graph")
     return {"workload": "mlp_relu_tp2: integer fp32 MLP, X[16,64], W1[64,256] column-split into 2x[64,128] + ReLU, "
                         "W2[256,64] row-split into 2x[128,64]; both ranks in turn, then tp_partial_sum (5 launches)",
-            "us_per_step": ms * 1e3, "flops_per_step": 2.0 * 16 * 64 * 256 * 2,
-            "step_stats": STEP_STATS.get("c0")}, {"inp": inp, "Y": Y}
+            "us_per_step": ms * 1e3, "us_per_step_graph": g_ms * 1e3, "flops_per_step": 2.0 * 16 * 64 * 256 * 2,
+            "step_stats": STEP_STATS.get("c0"), "step_stats_graph": STEP_STATS.get("c0_graph"),
+            "graph": "the five calls of a step captured as one HIP graph (torch.cuda.CUDAGraph), replays timed"}, \
+        {"inp": inp, "Y": Y}
 
 
 # ---------------------------------------------------------------------------- c1

@@ -11,54 +11,67 @@
 namespace tpk {
 namespace {
 
-constexpr int TM = 64, TN = 64, TK = 16;   // block tile; 256 threads, 4x4 outputs each
+// Block tile of 16R x 16R outputs: 256 threads (16 x 16), R x R outputs each; R = 4 for
+// larger products, R = 1 for small ones (more workgroups, a quarter of the FMA chain length
+// per thread on the critical path). The 64-deep K tile fetches A and B of a K <= 64 product in
+// one memory round trip (this path serves small, latency-bound layers).
+constexpr int TK = 64;
 
-template <bool RELU, bool ACCUM>
+template <int R, bool RELU, bool ACCUM>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A,
                                                        const float* __restrict__ B,
                                                        float* __restrict__ C, int64_t M,
                                                        int64_t N, int64_t K, int64_t lda,
                                                        int64_t ldb, int64_t ldc) {
+    constexpr int TM = 16 * R, TN = 16 * R;
+    constexpr int PER = TM * TK / 256;   // A (and B) values each thread loads per K tile
+    static_assert(TM * TK % 256 == 0, "whole loads per thread");
     __shared__ float As[TK][TM + 4];   // As[k][m]
     __shared__ float Bs[TK][TN + 4];   // Bs[k][n]
     const int tid = threadIdx.x;
-    const int tx = tid % 16, ty = tid / 16;              // 16 x 16 threads, 4x4 outputs each
+    const int tx = tid % 16, ty = tid / 16;
     const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
-    float acc[4][4] = {};
+    float acc[R][R] = {};
     for (int64_t k0 = 0; k0 < K; k0 += TK) {
-        // A tile TM x TK: 1024 values, 4 per thread
-        for (int i = tid; i < TM * TK; i += 256) {
-            const int mm = i / TK, kk = i % TK;
-            const int64_t gm = m0 + mm, gk = k0 + kk;
-            As[kk][mm] = (gm < M && gk < K) ? A[gm * lda + gk] : 0.0f;
+        // A and B tiles, TM x TK and TK x TN: all of a thread's loads are issued before the
+        // first is stored
+        float av[PER], bv[PER];
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int i = tid + r * 256;
+            const int64_t gm = m0 + i / TK, gk = k0 + i % TK;
+            av[r] = (gm < M && gk < K) ? A[gm * lda + gk] : 0.0f;
+            const int64_t hk = k0 + i / TN, hn = n0 + i % TN;
+            bv[r] = (hk < K && hn < N) ? B[hk * ldb + hn] : 0.0f;
         }
-        for (int i = tid; i < TK * TN; i += 256) {
-            const int kk = i / TN, nn = i % TN;
-            const int64_t gk = k0 + kk, gn = n0 + nn;
-            Bs[kk][nn] = (gk < K && gn < N) ? B[gk * ldb + gn] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const int i = tid + r * 256;
+            As[i % TK][i / TK] = av[r];
+            Bs[i / TN][i % TN] = bv[r];
         }
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < TK; ++kk) {
-            float a[4], b[4];
+            float a[R], b[R];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+            for (int i = 0; i < R; ++i) a[i] = As[kk][ty * R + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+            for (int j = 0; j < R; ++j) b[j] = Bs[kk][tx * R + j];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < R; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < R; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gm = m0 + ty * 4 + i;
+    for (int i = 0; i < R; ++i) {
+        const int64_t gm = m0 + ty * R + i;
         if (gm >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t gn = n0 + tx * 4 + j;
+        for (int j = 0; j < R; ++j) {
+            const int64_t gn = n0 + tx * R + j;
             if (gn >= N) continue;
             float v = acc[i][j];
             if (RELU) v = v > 0.0f ? v : 0.0f;
@@ -94,20 +107,35 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(PartialPtrs pk, int k,
 
 }  // namespace
 
+namespace {
+
+template <int R>
+hipError_t launch_f32(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                      int64_t ldb, int64_t ldc, int relu, int accumulate, hipStream_t s) {
+    constexpr int T = 16 * R;
+    dim3 grid((unsigned)((N + T - 1) / T), (unsigned)((M + T - 1) / T));
+    if (relu && accumulate)
+        gemm_f32_kernel<R, true, true><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    else if (relu)
+        gemm_f32_kernel<R, true, false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    else if (accumulate)
+        gemm_f32_kernel<R, false, true><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    else
+        gemm_f32_kernel<R, false, false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// 64 x 64 tiles once they give the machine at least one workgroup per compute unit, 16 x 16
+// tiles below that
 hipError_t gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K,
                     int64_t lda, int64_t ldb, int64_t ldc, int relu, int accumulate,
                     hipStream_t s) {
-    dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM));
     ProfScope ps("gemm_f32", s);
-    if (relu && accumulate)
-        gemm_f32_kernel<true, true><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
-    else if (relu)
-        gemm_f32_kernel<true, false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
-    else if (accumulate)
-        gemm_f32_kernel<false, true><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
-    else
-        gemm_f32_kernel<false, false><<<grid, 256, 0, s>>>(A, B, C, M, N, K, lda, ldb, ldc);
-    return hipGetLastError();
+    if (((M + 63) / 64) * ((N + 63) / 64) >= 256)
+        return launch_f32<4>(A, B, C, M, N, K, lda, ldb, ldc, relu, accumulate, s);
+    return launch_f32<1>(A, B, C, M, N, K, lda, ldb, ldc, relu, accumulate, s);
 }
 
 hipError_t partial_sum(const float* const* parts, int k, float* out, int64_t n, hipStream_t s) {

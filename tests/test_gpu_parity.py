@@ -78,8 +78,10 @@ def test_config0_two_ranks_bit_exact(tp):
     assert np.array_equal(host(Y), O.partial_sum(parts_ref))
 
 
-@pytest.mark.parametrize("T,K,N", [(1, 1, 1), (70, 33, 130), (129, 200, 65)])
+@pytest.mark.parametrize("T,K,N", [(1, 1, 1), (70, 33, 130), (129, 200, 65), (1030, 72, 1032)])
 def test_fp32_linear_ragged_exact(tp, T, K, N):
+    """Bit-exact on integer inputs: the 16 x 16 tiles of small products and (1030 x 1032: 289
+    tiles of 64 x 64) the large-product tiles, ragged in every dimension, K over one 64-deep tile."""
     import torch
     rng = np.random.default_rng(T + K + N)
     X = wl.int_matrix(rng, (T, K))
