@@ -841,7 +841,7 @@ def _round(x, nd=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU: one rank's shard; "
+        print(json.dumps({"error": "bench.py measures one GPU: one rank's shard; "
                                    "run with --gpus 1 (multi-GPU sharding is described, not built)"}))
         sys.exit(2)
     import torch
