@@ -1021,7 +1021,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
     if (bid < sp.g_full) {
         L = xcd_remap(bid, sp.g_full);
     } else {
+        // tail pieces, dealt piece-major so that each XCD takes one K piece of a contiguous run
+        // of tail tiles (rows and columns its L2 shares) instead of one piece of tiles spread
+        // over every column; q = tile * pieces + piece indexes the partial buffer either way
         q = bid - sp.g_full;
+        if ((sp.g_full & 7) == 0) {
+            const int n = (int)gridDim.x - sp.g_full, tail = n / sp.pieces;
+            const int v = xcd_remap(q, n);
+            q = (v % tail) * sp.pieces + v / tail;
+        }
         L = sp.g_full + q / sp.pieces;
     }
     bool second = false;
