@@ -433,8 +433,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Store ROWS x CHUNKS 16-byte chunks of the tile (row pitch PITCH) to dest(r, c) (nullptr =
-// skip); RMW adds the fp32 chunk to what is in memory (accumulating fp32 epilogue).
-template <int ROWS, int CHUNKS, int PITCH, bool RMW = false, class Dest>
+// skip); RMW adds the fp32 chunk to what is in memory (accumulating fp32 epilogue); NT stores
+// nontemporally (the fp32 partial outputs, which nothing in the kernel reads back: they then
+// displace fewer operand lines from the L2; attn7b_tp4's O GEMM 90 -> 84 us).
+template <int ROWS, int CHUNKS, int PITCH, bool RMW = false, class Dest, bool NT = false>
 __device__ __forceinline__ void flush_tile(const unsigned char* lds, Dest dest, int lane) {
     wave_lds_sync();
 #pragma unroll
@@ -446,6 +448,8 @@ __device__ __forceinline__ void flush_tile(const unsigned char* lds, Dest dest, 
         if (RMW) {
             const f32x4 old = *reinterpret_cast<const f32x4*>(d);
             *reinterpret_cast<f32x4*>(d) = old + __builtin_bit_cast(f32x4, v);
+        } else if constexpr (NT) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(d));
         } else {
             *reinterpret_cast<u32x4*>(d) = v;
         }
@@ -486,10 +490,10 @@ struct EpiStore {
         const int64_t row0 = m0 + wm * 128 + i * 32, col0 = n0 + wn * 128;
         const int64_t rows_ok = M - row0, chunks_ok = (N - col0) * ES / 16;   // N is a multiple of 16 / ES
         unsigned char* base = static_cast<unsigned char*>(C) + (row0 * ldc + col0) * ES;
-        flush_tile<32, CHUNKS, PITCH, KIND == 3>(
-            lds, [&](int r, int c) -> unsigned char* {
-                return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * ldc) * ES + 16 * c : nullptr;
-            }, lane);
+        auto dest = [&](int r, int c) -> unsigned char* {
+            return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * ldc) * ES + 16 * c : nullptr;
+        };
+        flush_tile<32, CHUNKS, PITCH, KIND == 3, decltype(dest), KIND == 2>(lds, dest, lane);
     }
     // grouped launches: this group's output rows r0 .. r0+m-1
     __device__ void shift_rows(int64_t r0, int64_t m) {
