@@ -743,7 +743,9 @@ size_t tp_moe_workspace_size(int64_t T, int64_t H, int64_t I_shard, int32_t E, c
     if (moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
         const size_t gu = tpk::gemm_bf16_grouped_split_bytes(expert_offsets, E, I_shard, H, 1);
         const size_t dn = tpk::gemm_bf16_grouped_split_bytes(expert_offsets, E, H, I_shard, 0);
-        return rows + round_up((size_t)(R * I_shard) * 2, WS_ALIGN) + round_up(gu > dn ? gu : dn, WS_ALIGN);
+        // Xg and h each get one more row, of zeros (moe_zero_rows)
+        return rows + round_up((size_t)H * 2, WS_ALIGN) + round_up((size_t)((R + 1) * I_shard) * 2, WS_ALIGN) +
+               round_up(gu > dn ? gu : dn, WS_ALIGN);
     }
     size_t mlp = 0;
     for (int32_t e = 0; e < E; ++e) {
@@ -795,19 +797,31 @@ tp_status tp_moe_mlp_shard(const void* X, int64_t T, int64_t H, int64_t I_shard,
     if (st != TP_OK) return st;
     hipStream_t s = as_stream(stream);
     Carver c(workspace);
-    void* Xg = c.take((size_t)(R * H) * 2);
-    float* Yg = static_cast<float*>(c.take((size_t)(R * H) * 4));
-    hipError_t e = tpk::moe_gather(X, row_token, Xg, R, T, H, s);
-    if (e == hipSuccess && moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
-        void* h = c.take((size_t)(R * I_shard) * 2);
+    if (moe_max_rows(expert_offsets, E) > SKINNY_MAX_T) {
+        // grouped launches: the rows of an expert's last tile past its end read a row of zeros
+        // (row R of Xg, row R of h) rather than a copy of a real row; zero operands draw less
+        // power at the same speed. The DMA offsets of those rows (up to (R + 1) rows) are 32-bit.
+        void* Xg = c.take((size_t)((R + 1) * H) * 2);
+        float* Yg = static_cast<float*>(c.take((size_t)(R * H) * 4));
+        void* h = c.take((size_t)((R + 1) * I_shard) * 2);
         void* split = c.take(0);
         const size_t split_bytes = need - c.off;
-        e = tpk::gemm_bf16_swiglu_grouped(Xg, W_gate, W_up, h, expert_offsets, E, I_shard, H, split, split_bytes, s);
+        const bool zr = (R + 1) * (H > I_shard ? H : I_shard) < ((int64_t)1 << 31);
+        unsigned char* xz = static_cast<unsigned char*>(Xg) + (size_t)(R * H) * 2;
+        unsigned char* hz = static_cast<unsigned char*>(h) + (size_t)(R * I_shard) * 2;
+        hipError_t e = tpk::moe_gather(X, row_token, Xg, R, T, H, s, zr ? xz : nullptr, H, zr ? hz : nullptr, I_shard);
         if (e == hipSuccess)
-            e = tpk::gemm_bf16_f32out_grouped(h, W_down, Yg, expert_offsets, E, H, I_shard, split, split_bytes, s);
+            e = tpk::gemm_bf16_swiglu_grouped(Xg, W_gate, W_up, h, expert_offsets, E, I_shard, H, split, split_bytes, s,
+                                              zr ? R : -1);
+        if (e == hipSuccess)
+            e = tpk::gemm_bf16_f32out_grouped(h, W_down, Yg, expert_offsets, E, H, I_shard, split, split_bytes, s,
+                                              zr ? R : -1);
         if (e == hipSuccess) e = tpk::moe_combine(Yg, token_rows, gates, k, Y_partial, T, R, H, s);
         return from_hip(e, fn);
     }
+    void* Xg = c.take((size_t)(R * H) * 2);
+    float* Yg = static_cast<float*>(c.take((size_t)(R * H) * 4));
+    hipError_t e = tpk::moe_gather(X, row_token, Xg, R, T, H, s);
     void* mlp_ws = c.take(0);   // the largest expert's MLP workspace, reused expert after expert
     for (int32_t x = 0; x < E && e == hipSuccess; ++x) {
         const int64_t a = expert_offsets[x], n = expert_offsets[x + 1] - a;

@@ -116,6 +116,7 @@ struct Geom {
     const E* B1;   // [K, N] row-major, ldb
     const E* B2;   // second weight of the dual (gate/up) form, else unused
     int64_t M, N, K, lda, ldb;
+    int64_t zrow = -1;   // a row of A past M whose K elements are zero (LAY_NN), or -1
 };
 
 // Per-lane source offsets of one wave's share of a stage (fixed for the whole K loop; only
@@ -175,7 +176,10 @@ __device__ __forceinline__ void make_plan(DmaPlan& p, const Geom<F8>& g, int64_t
             p.a_off[i] = (int32_t)(row * g.lda + (m0 + 8 * c < g.M ? 8 * c : 0));
         } else {
             a_granule(wave, i, lane, row, c);
-            p.a_off[i] = (int32_t)((m0 + row < g.M ? row : 0) * g.lda + Fmt<F8>::EPG * c);
+            // rows past M load the zero row when there is one (zero operands draw less power than
+            // a copy of a real row), else the tile's first row
+            const int64_t stand_in = g.zrow >= 0 ? g.zrow - m0 : 0;
+            p.a_off[i] = (int32_t)((m0 + row < g.M ? row : stand_in) * g.lda + Fmt<F8>::EPG * c);
         }
     }
 #pragma unroll
@@ -1050,6 +1054,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(Geom<F8> g, Epi epi,
         int64_t r0, m;
         const int e = gr.locate(L, tiles_n, tiles_m, r0, m);
         g.A += r0 * g.lda;
+        if (g.zrow >= 0) g.zrow -= r0;
         g.B1 += e * gr.b_stride;
         if constexpr (DUAL) g.B2 += e * gr.b_stride;
         g.M = m;
@@ -1407,13 +1412,13 @@ hipError_t gemm_bf16_f32out_pair_nt_tn(const void* A0, const void* B0t, float* C
 
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
                                     const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, void* ws,
-                                    size_t ws_bytes, hipStream_t s) {
+                                    size_t ws_bytes, hipStream_t s, int64_t zero_row) {
     const int64_t M = row_offsets[n_groups], tn = tiles_n_of(N, true);
     for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
         const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
         const int64_t wo = (int64_t)x0 * K * N;
         Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg) + wo,
-                      static_cast<const uint16_t*>(Bu) + wo, M, N, K, K, N};
+                      static_cast<const uint16_t*>(Bu) + wo, M, N, K, K, N, zero_row};
         hipError_t e = launch<false, true>(g, EpiSwiGLU<0>{h, M, N, 1.0f, 1.0f, 1.0f}, ws, ws_bytes, s,
                                            "gemm_bf16_swiglu", make_groups(row_offsets + x0, n, tn, K * N));
         if (e != hipSuccess) return e;
@@ -1422,12 +1427,13 @@ hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* B
 }
 
 hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, const int64_t* row_offsets,
-                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s,
+                                    int64_t zero_row) {
     const int64_t M = row_offsets[n_groups], tn = tiles_n_of(N, false);
     for (int x0 = 0; x0 < n_groups; x0 += MAX_GROUPS) {
         const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
         Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B) + (int64_t)x0 * K * N,
-                      nullptr, M, N, K, K, N};
+                      nullptr, M, N, K, K, N, zero_row};
         hipError_t e = launch<false, false>(g, EpiStore<2, false>{C, N, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
                                             "gemm_bf16_f32out", make_groups(row_offsets + x0, n, tn, K * N));
         if (e != hipSuccess) return e;

@@ -17,11 +17,27 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-// Xg[r, :] = X[row_token[r], :] (bf16, 16-byte chunks); one workgroup per row
+// Xg[r, :] = X[row_token[r], :] (bf16, 16-byte chunks); one workgroup per row. Workgroups R and
+// R + 1 (if launched) instead zero z.p[0] and z.p[1] (z.n[i] elements, multiples of 8): the zero
+// rows that the grouped GEMMs' padding rows read.
+struct ZeroRows {
+    uint16_t* p[2];
+    int64_t n[2];
+};
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ X,
                                                           const int32_t* __restrict__ row_token,
-                                                          uint16_t* __restrict__ Xg, int64_t T, int64_t H) {
+                                                          uint16_t* __restrict__ Xg, int64_t R, int64_t T, int64_t H,
+                                                          ZeroRows z) {
     const int64_t r = blockIdx.x;
+    if (r >= R) {
+        const int i = (int)(r - R);
+        uint16_t* zp = i == 0 ? z.p[0] : z.p[1];
+        const int64_t zn = i == 0 ? z.n[0] : z.n[1];
+        for (int64_t c = threadIdx.x; c < (zn >> 3); c += 256)
+            *reinterpret_cast<u32x4*>(zp + 8 * c) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
     const int32_t t = row_token[r];
     const bool ok = t >= 0 && t < T;
     const int64_t nch = H >> 3;
@@ -54,11 +70,13 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
 }  // namespace
 
 hipError_t moe_gather(const void* X, const int32_t* row_token, void* Xg, int64_t R, int64_t T, int64_t H,
-                      hipStream_t s) {
-    if (R == 0) return hipSuccess;
+                      hipStream_t s, void* z0, int64_t n0, void* z1, int64_t n1) {
+    const ZeroRows z{{static_cast<uint16_t*>(z0), static_cast<uint16_t*>(z1)}, {z0 ? n0 : 0, z1 ? n1 : 0}};
+    const int64_t blocks = R + (z0 || z1 ? 2 : 0);
+    if (blocks == 0) return hipSuccess;
     ProfScope ps("moe_gather", s);
-    gather_rows_kernel<<<(unsigned)R, 256, 0, s>>>(static_cast<const uint16_t*>(X), row_token,
-                                                   static_cast<uint16_t*>(Xg), T, H);
+    gather_rows_kernel<<<(unsigned)blocks, 256, 0, s>>>(static_cast<const uint16_t*>(X), row_token,
+                                                        static_cast<uint16_t*>(Xg), R, T, H, z);
     return hipGetLastError();
 }
 

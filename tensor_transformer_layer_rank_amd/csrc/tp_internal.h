@@ -73,11 +73,15 @@ hipError_t gemm_bf16_f32out_pair_nt_tn(const void* A0, const void* B0t, float* C
                                        float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
                                        int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, int dual);
+// zero_row: a row of A (index from A's first row, lda = K) whose K elements are zero and which
+// no group covers, or -1; the rows of a group's last tile past the group's end then load it
+// (zero operands) instead of a copy of a real row. (zero_row + 1) * K must stay below 2^31.
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,
                                     const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, void* ws,
-                                    size_t ws_bytes, hipStream_t s);
+                                    size_t ws_bytes, hipStream_t s, int64_t zero_row = -1);
 hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, const int64_t* row_offsets,
-                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
+                                    int n_groups, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s,
+                                    int64_t zero_row = -1);
 // h_f16: h stored as fp16 instead of bf16
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
                             int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s, int h_f16 = 0);
@@ -148,16 +152,18 @@ hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const vo
 
 // ---- backward of a linear shard ---------------------------------------------------------
 // dX [T, K] fp32 = dY [T, N] . W^T, dW [K, N] fp32 = X^T [K, T] . dY (bf16 operands; T, K, N
-// multiples of 8). Workspace: W^T and X^T (bf16) and the GEMMs' tail-split partials.
+// multiples of 8; W and X read in place as transposed operands). Workspace: the GEMMs' tail-split
+// partials.
 size_t linear_backward_ws_bytes(int64_t T, int64_t K, int64_t N);
 hipError_t linear_backward(const void* X, const void* W, const void* dY, float* dX, float* dW, int64_t T,
                            int64_t K, int64_t N, void* ws, hipStream_t s);
 
 // ---- mixture of experts ------------------------------------------------------------------
-// Xg[r] = X[row_token[r]] (bf16 [R, H]; out-of-range tokens give a zero row);
+// Xg[r] = X[row_token[r]] (bf16 [R, H]; out-of-range tokens give a zero row); z0[0 .. n0-1] and
+// z1[0 .. n1-1] (bf16, n multiples of 8; NULL = none) are set to zero as well;
 // Y[t] = sum_j gates[t, j] * Yg[token_rows[t, j]] (fp32 [T, H]; out-of-range rows skipped).
 hipError_t moe_gather(const void* X, const int32_t* row_token, void* Xg, int64_t R, int64_t T, int64_t H,
-                      hipStream_t s);
+                      hipStream_t s, void* z0 = nullptr, int64_t n0 = 0, void* z1 = nullptr, int64_t n1 = 0);
 hipError_t moe_combine(const float* Yg, const int32_t* token_rows, const float* gates, int k, float* Y, int64_t T,
                        int64_t R, int64_t H, hipStream_t s);
 
