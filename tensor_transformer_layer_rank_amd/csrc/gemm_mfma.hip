@@ -464,7 +464,10 @@ __device__ __forceinline__ void flush_tile(const unsigned char* lds, Dest dest, 
 // KIND: 0 bf16, 1 fp16, 2 fp32 overwrite, 3 fp32 +=, 4 OCP E4M3 code of v * (1 / out_div).
 // Every accumulator is first multiplied by `scale` (the product of the per-tensor operand
 // scales of fp8 operands; 1 for bf16).
-template <int KIND, bool RELU>
+// NT: fp32 partials stored nontemporally (outputs nothing in the step reads back soon); an output
+// that the next kernel consumes right away (the MoE experts' rows, which the combine reads) keeps
+// cached stores.
+template <int KIND, bool RELU, bool NT = (KIND == 2)>
 struct EpiStore {
     void* C;
     int64_t ldc, M, N;
@@ -497,7 +500,7 @@ struct EpiStore {
         auto dest = [&](int r, int c) -> unsigned char* {
             return (r < rows_ok && c < chunks_ok) ? base + ((int64_t)r * ldc) * ES + 16 * c : nullptr;
         };
-        flush_tile<32, CHUNKS, PITCH, KIND == 3, decltype(dest), KIND == 2>(lds, dest, lane);
+        flush_tile<32, CHUNKS, PITCH, KIND == 3, decltype(dest), NT>(lds, dest, lane);
     }
     // grouped launches: this group's output rows r0 .. r0+m-1
     __device__ void shift_rows(int64_t r0, int64_t m) {
@@ -1434,7 +1437,7 @@ hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, cons
         const int n = n_groups - x0 < MAX_GROUPS ? n_groups - x0 : MAX_GROUPS;
         Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B) + (int64_t)x0 * K * N,
                       nullptr, M, N, K, K, N, zero_row};
-        hipError_t e = launch<false, false>(g, EpiStore<2, false>{C, N, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
+        hipError_t e = launch<false, false>(g, EpiStore<2, false, false>{C, N, M, N, 1.0f, 1.0f}, ws, ws_bytes, s,
                                             "gemm_bf16_f32out", make_groups(row_offsets + x0, n, tn, K * N));
         if (e != hipSuccess) return e;
     }
