@@ -316,7 +316,8 @@ size_t tp_linear_backward_workspace_size(int64_t T, int64_t K, int64_t N);
  *   1 <= E <= 1024; 1 <= k <= 16; X, weights, Y_partial 16-byte aligned; the int32/fp32
  *   routing arrays 4-byte aligned; workspace >= tp_moe_workspace_size(...) bytes, 16-byte
  *   aligned (the gathered rows, their fp32 outputs, and either h for all rows plus the GEMM
- *   split partials or one expert's MLP workspace). Broken rules return TP_ERR_NULL_POINTER /
+ *   split partials, with one zero row appended to the gathered rows and to h for the grouped
+ *   GEMMs' padding rows, or one expert's MLP workspace). Broken rules return TP_ERR_NULL_POINTER /
  *   TP_ERR_BAD_SHAPE / TP_ERR_UNSUPPORTED / TP_ERR_MISALIGNED / TP_ERR_WORKSPACE before any
  *   launch. When an expert has more than 64 rows all experts share one grouped gate/up and one
  *   grouped down GEMM launch (per 32 experts); otherwise the experts run one after another
