@@ -141,7 +141,7 @@ hipError_t decode_attn_step(const void* X, const void* Wqkv, float* part, int64_
                             int hkv, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap,
                             void* out, hipStream_t s);
 
-// The whole decode step of a rank in five launches: attention shard (QKV + RoPE + cache append
+// The whole decode step of a rank in four launches: attention shard (QKV + RoPE + cache append
 // + attention + O partial Ya), MLP shard on the same X (Ym), and the vocabulary-split head
 // (logits [B, V]; V = 0: none). B <= 64; cap, pos as for decode_attn_step.
 size_t decode_step_ws_bytes(int64_t B, int64_t H, int hq, int hkv, int64_t I, int64_t V);
