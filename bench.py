@@ -679,8 +679,41 @@ def ceiling_bench(args):
         tf = flops / (ms * 1e-3) / 1e12
         res[name] = {"tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "ms_per_launch": ms,
                      "clock_power": None if args.no_clock else clock_power(lambda: run(iters), 2.0)}
+    # The headline MLP step itself (same shapes, same kernels and instruction stream) on operands that
+    # draw little power: zero activations with the random weights, and everything zero. Its rate
+    # then shows what the kernels' schedule reaches when the board's power limit does not set the
+    # clock (the outputs are zero; nothing here is a parity case).
+    import workloads as wl
+    inp = wl.mlp7b_tp4()
+    T, H, I = inp.T, inp.H, inp.I
+    Wg, Wu, Wd = _dev(inp.W_gate), _dev(inp.W_up), _dev(inp.W_down)
+    X0 = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tp.mlp_workspace_size(T, H, I, tp.TP_MLP_SWIGLU, tp.TP_BF16), dtype=torch.uint8, device="cuda")
+    flops = 2.0 * T * H * 2 * I + 2.0 * T * I * H
+    mlp = {}
+    for name, (x, wg, wu, wd) in {"zero_activations": (X0, Wg, Wu, Wd),
+                                  "all_zero": (X0, torch.zeros_like(Wg), torch.zeros_like(Wu), torch.zeros_like(Wd))}.items():
+        def step():
+            tp.mlp_shard(x, wg, wu, wd, Y=Y, workspace=ws)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.5:   # let the clock settle on this load
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 50
+        mlp[name] = {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                     "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "clock_power": None if args.no_clock else clock_power(step, 2.0)}
     return {"what": "v_mfma_f32_32x32x16_bf16 back to back, operands in registers, 16 accumulators per wave, "
-                    "one 4-wave workgroup per compute unit (tp_mfma_rate_probe)", "patterns": res}
+                    "one 4-wave workgroup per compute unit (tp_mfma_rate_probe)", "patterns": res,
+            "mlp7b_tp4_low_power_operands": mlp}
 
 
 def traffic_probe():
