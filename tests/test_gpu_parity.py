@@ -427,8 +427,8 @@ def test_row_partials_sum_to_unsharded_layer(tp):
 # 2, 3 or 4 pieces whose fp32 partials a fix-up pass sums, when the shorter tail outweighs the
 # fix-up (272 tiles: 2 pieces at 10 K steps, 4 at 32; 336 tiles: 3 at 96); grids smaller than
 # the machine are cut too (32 tiles: 3 pieces at 32 steps, 4 at 64; 160 tiles: 3 at 202).
-# Ragged M, N and K so that the last piece holds the K tail; the two largest grids are
-# compared with the oracle on sampled rows.
+# Ragged M, N and K so that the last piece holds the K tail; every output element is compared
+# with the oracle, and the split launch with a second launch bitwise.
 @pytest.mark.parametrize("T,K,N,out", [(4200, 296, 4096, "bf16"), (4100, 1000, 4000, "f32"),
                                        (5376, 3072, 4096, "f32"), (1000, 1024, 2000, "bf16"),
                                        (1000, 2048, 2000, "f32"), (2048, 6464, 5120, "bf16")])
