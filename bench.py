@@ -13,7 +13,9 @@ this host's cores:
   c2 the 7B TP=4 attention shard (B=4, S=2048, 8 heads: QKV + RoPE, flash attention, O);
   c3 the 70B TP=8 GQA layer shard (attention with 8 q heads / 1 kv head, plus the MLP shard);
   c4 the 7B TP=2 decode step (attention over a 1024-token KV cache + MLP at 32 tokens +
-     vocabulary-split LM head, one HIP graph) in GB/s of compulsory HBM bytes.
+     vocabulary-split LM head, one HIP graph) in GB/s of compulsory HBM bytes, with the
+     weights packed once into 128-column strips (tp_pack_strips, outside the timed region);
+     the step on the weights in place is timed beside it.
 Beside them: the MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8), the step after the
 merge (tp_merge_rmsnorm), the backward of the MLP down shard (tp_linear_backward) and a
 top-2 MoE MLP over 8 local experts (tp_moe_mlp_shard). Inputs are seeded synthetic tensors
@@ -102,7 +104,7 @@ def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 1
     each step, so the per-step times come from the timed pass itself (STEP_STATS[name]; the whole
     list when keep_steps). libtpshard's per-kernel HIP events (a few microseconds per kernel) are
     switched on for every `sample_every`-th timed step only, starting with the step after the
-    first, so the kernel averages come from inside the timed region."""
+    first, so the kernel averages come from inside the timed region (sample_every = 0: never)."""
     import torch
     import tensor_transformer_layer_rank_amd as tp
     for _ in range(warmup):
@@ -113,7 +115,8 @@ def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 1
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(s)
     for i in range(steps):
-        sampled = i % sample_every == sample_every - 1 or (steps < sample_every and i == steps - 1)
+        sampled = sample_every > 0 and (i % sample_every == sample_every - 1 or
+                                        (steps < sample_every and i == steps - 1))
         if sampled:
             tp.profile_enable(True)
         step()
@@ -423,24 +426,44 @@ def decode_bench(args):
         tp.decode_step(X, Wqkv, Wo, hq, hkv, inp.theta, kc, vc, inp.cache_len, Wg, Wu, Wd, Wlm,
                        Y_attn=Ya, Y_mlp=Ym, logits=logits, workspace=ws_f)
 
+    # the same weights packed once into 128-column strips (load-time layout, not timed): every
+    # workgroup of the step's GEMM launches then streams one contiguous block per K chunk
+    packed = [tp.pack_strips(w) for w in (Wqkv, Wo, Wg, Wu, Wd, Wlm)]
+
+    def step_packed():   # tp_decode_step_packed: the same step on the packed weights
+        tp.decode_step(X, packed[0], packed[1], hq, hkv, inp.theta, kc, vc, inp.cache_len, packed[2], packed[3],
+                       packed[4], packed[5], Y_attn=Ya, Y_mlp=Ym, logits=logits, workspace=ws_f, packed=True,
+                       I=I, V=V)
+
     outs = (Ya, Ym, logits)
     ms_sep_eager = timed(step, args.warmup, args.steps)
     ms_sep_graph, _ = graph_timed(step_branches, args.warmup, args.steps)
-    ms_eager = timed(step_fused, args.warmup, args.steps)       # per-kernel HIP-event timing
+    ms_inplace_eager = timed(step_fused, args.warmup, args.steps, "decode_inplace", sample_every=0)
+    eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
+    ms_inplace_graph, _ = graph_timed(step_fused, args.warmup, args.steps)
+    timed(step_packed, args.warmup, args.steps)                 # per-kernel HIP-event timing
     att_ms, att_n = kernel_avg("decode_attn")
     sk_ms, sk_n = kernel_avg("skinny_gemm")
     rd_ms, rd_n = kernel_avg("skinny_reduce")
     x_ms, _ = kernel_avg("skinny_gemm_x")
     out_ms, _ = kernel_avg("skinny_gemm_out")
-    eager = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
     for t in outs:
         t.fill_(float("nan"))
-    ms, g = graph_timed(step_fused, args.warmup, args.steps, "decode")   # the step as one HIP graph
+    # the headline: the packed step issued on one stream, no per-kernel events
+    ms = timed(step_packed, args.warmup, args.steps, "decode", sample_every=0)
+    torch.cuda.synchronize()
+    # its outputs must equal the eager in-place step's, bit for bit (the packed step runs the same
+    # kernels and sums; only the weight addresses differ)
+    packed_out = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
+    same_packed = all(a.tobytes() == b.tobytes() for a, b in zip(eager, packed_out))
+    for t in outs:
+        t.fill_(float("nan"))
+    ms_graph, g = graph_timed(step_packed, args.warmup, args.steps, "decode_graph")   # as one HIP graph
     torch.cuda.synchronize()
     # the outputs left by the last timed replay must equal the eager step's, bit for bit
     replay = [_host(t) for t in outs] + [_host(kc[:, :, inp.cache_len])]
     same = all(a.tobytes() == b.tobytes() for a, b in zip(eager, replay))
-    # The same replays with the 256 MB Infinity Cache flushed first: a 512 MiB buffer is read and
+    # The same steps with the 256 MB Infinity Cache flushed first: a 512 MiB buffer is read and
     # rewritten before each one (outside its events), so no step finds weights or cache rows that
     # the previous step left in the cache. Back-to-back steps re-read a 606 MB working set.
     flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
@@ -449,7 +472,7 @@ def decode_bench(args):
     for e0, e1 in ev:
         flush.add_(1.0)
         e0.record()
-        g.replay()
+        step_packed()
         e1.record()
     torch.cuda.synchronize()
     cold = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
@@ -464,14 +487,23 @@ def decode_bench(args):
     nsamp = sampled_steps(args.steps)
     return {
         "ms_per_step": ms,
-        "ms_per_step_eager": ms_eager,
+        "ms_per_step_graph": ms_graph,
+        "step_stats_graph": STEP_STATS.get("decode_graph"),
+        "ms_per_step_weights_in_place": ms_inplace_eager,
+        "ms_per_step_weights_in_place_graph": ms_inplace_graph,
+        "gbs_weights_in_place": total / (ms_inplace_eager * 1e-3) / 1e9,
+        "step_stats_weights_in_place": STEP_STATS.get("decode_inplace"),
         "ms_per_step_cache_flushed": ms_cold,
         "median_ms_cache_flushed": cold[len(cold) // 2],
         "ms_per_step_separate_calls_eager": ms_sep_eager,
         "ms_per_step_separate_calls_graph": ms_sep_graph,
         "step_stats": STEP_STATS.get("decode"),
-        "graph": "tp_decode_step (4 launches) captured as one HIP graph; separate_calls: tp_attn_shard, "
-                 "tp_mlp_shard, tp_column_linear as three graph branches on their own streams",
+        "step": "tp_decode_step_packed (4 launches on one stream; the weights packed once into 128-column "
+                "strips by tp_pack_strips, outside the timed region), no per-kernel events; graph: the same "
+                "step captured as one HIP graph and replayed; weights_in_place: tp_decode_step on the [K, N] "
+                "weights; separate_calls: tp_attn_shard, tp_mlp_shard, tp_column_linear as three graph "
+                "branches on their own streams; kernels: per-kernel events on every 10th step of another pass",
+        "packed_outputs_equal_in_place": same_packed,
         "graph_outputs_equal_eager": same,
         "bytes_per_step": total,
         "gbs": total / (ms * 1e-3) / 1e9,
@@ -943,6 +975,8 @@ def main():
           "frac_bf16_peak": mlp["tflops"] / PEAK_BF16_TFLOPS}
     configs = {"c0_mlp_relu_tp2": c0, "c1_mlp7b_tp4": c1, "c2_attn7b_tp4": c2, "c3_layer70b_tp8": c3,
                "c4_decode7b_tp2": dec and {k: dec[k] for k in ("ms_per_step", "gbs", "frac_hbm",
+                                                              "ms_per_step_graph", "ms_per_step_weights_in_place",
+                                                              "gbs_weights_in_place", "packed_outputs_equal_in_place",
                                                               "graph_outputs_equal_eager")}}
     if par:
         for key, c in (("c0_mlp_relu_tp2", "c0"), ("c1_mlp7b_tp4", "c1"), ("c2_attn7b_tp4", "c2"),

@@ -248,6 +248,25 @@ tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, cons
 size_t tp_decode_step_workspace_size(const tp_attn_desc* desc, int64_t I_shard, int64_t V_shard);
 
 /*
+ * tp_decode_step_packed — tp_decode_step with every weight (W_qkv, W_o, W_gate, W_up, W_down,
+ *   W_lm) in the strip layout that tp_pack_strips writes; the other arguments, the workspace size
+ *   (tp_decode_step_workspace_size), the results and the errors are those of tp_decode_step.
+ *
+ * tp_pack_strips — W [K, N] (bf16 or fp16, row-major) rearranged into 128-column strips:
+ *   W_packed [ceil(N / 128)][K][128], strip s holding columns 128 s .. 128 s + 127 of every row,
+ *   columns past N zero. A weight is packed once (at load time); a decode step then streams each
+ *   strip as one contiguous block. W_packed: tp_packed_strips_bytes(K, N) bytes, caller-owned,
+ *   must not overlap W. N a multiple of 8; K, N < 2^40; pointers 16-byte aligned. Asynchronous on
+ *   the stream. tp_packed_strips_bytes returns 0 for shapes tp_pack_strips rejects.
+ */
+tp_status tp_decode_step_packed(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
+                                const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
+                                const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
+                                void* workspace, size_t ws_bytes, void* stream);
+tp_status tp_pack_strips(const void* W, int64_t K, int64_t N, void* W_packed, void* stream);
+size_t tp_packed_strips_bytes(int64_t K, int64_t N);
+
+/*
  * tp_partial_sum — out = ((P_0 + P_1) + P_2) + ... + P_{k-1}, element-wise, in that
  *   order, fp32 ("CUDA tensor parallel computations", 第三类 Row Parallel: partial
  *   contributions are summed; 第四类: the all-reduce result). All buffers are on the

@@ -39,7 +39,7 @@ EXPORTS = [
     "tp_profile_read", "tp_profile_reset", "tp_mlp_shard_fp8", "tp_mlp_fp8_workspace_size",
     "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size", "tp_moe_mlp_shard",
     "tp_moe_workspace_size", "tp_column_linear_noalloc", "tp_mfma_rate_probe", "tp_decode_step",
-    "tp_decode_step_workspace_size",
+    "tp_decode_step_workspace_size", "tp_decode_step_packed", "tp_pack_strips", "tp_packed_strips_bytes",
 ]
 
 
@@ -113,6 +113,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tp_decode_step": ([_P, _P, _P, ctypes.POINTER(AttnDesc), _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P, _SZ,
                             _P], _I32),
         "tp_decode_step_workspace_size": ([ctypes.POINTER(AttnDesc), _I64, _I64], _SZ),
+        "tp_decode_step_packed": ([_P, _P, _P, ctypes.POINTER(AttnDesc), _P, _P, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                                   _SZ, _P], _I32),
+        "tp_pack_strips": ([_P, _I64, _I64, _P, _P], _I32),
+        "tp_packed_strips_bytes": ([_I64, _I64], _SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -322,15 +326,30 @@ def decode_step_workspace_size(B, H, hq, hkv, theta, k_cache, v_cache, cache_len
     return int(lib().tp_decode_step_workspace_size(ctypes.byref(d), I, V))
 
 
+def pack_strips(W, out=None, stream=None):
+    """W [K, N] (bf16/fp16) -> its 128-column strips [ceil(N/128), K, 128] through tp_pack_strips."""
+    import torch
+    K, N = W.shape
+    if out is None:
+        out = torch.empty(((N + 127) // 128, K, 128), dtype=W.dtype, device=W.device)
+    _check(lib().tp_pack_strips(_ptr(W), K, N, _ptr(out), _stream(stream)))
+    return out
+
+
 def decode_step(X, W_qkv, W_o, hq: int, hkv: int, theta: float, k_cache, v_cache, cache_len: int,
                 W_gate, W_up, W_down, W_lm=None, Y_attn=None, Y_mlp=None, logits=None, workspace=None,
-                stream=None):
+                stream=None, packed: bool = False, I: int = None, V: int = None):
     """One rank's decode step (attention shard with KV-cache append, MLP shard and the vocabulary-
-    split head on the same X) through tp_decode_step; returns (Y_attn, Y_mlp, logits or None)."""
+    split head on the same X) through tp_decode_step; returns (Y_attn, Y_mlp, logits or None).
+    packed=True: tp_decode_step_packed, every weight from pack_strips ([strips, K, 128]), with
+    I (= I_shard) and V (= V_shard, 0 without W_lm) given."""
     import torch
     B, H = X.shape
-    I = W_gate.shape[1]
-    V = W_lm.shape[1] if W_lm is not None else 0
+    if not packed:
+        I = W_gate.shape[1]
+        V = W_lm.shape[1] if W_lm is not None else 0
+    elif I is None or V is None:
+        raise ValueError("decode_step(packed=True) needs I and V")
     Y_attn = Y_attn if Y_attn is not None else torch.empty((B, H), dtype=torch.float32, device=X.device)
     Y_mlp = Y_mlp if Y_mlp is not None else torch.empty((B, H), dtype=torch.float32, device=X.device)
     if V and logits is None:
@@ -338,9 +357,10 @@ def decode_step(X, W_qkv, W_o, hq: int, hkv: int, theta: float, k_cache, v_cache
     d = _desc(B, 1, H, hq, hkv, theta, k_cache, v_cache, cache_len)
     nb = int(lib().tp_decode_step_workspace_size(ctypes.byref(d), I, V))
     ws, wsb = _workspace(nb, X.device, workspace)
-    _check(lib().tp_decode_step(_ptr(X), _ptr(W_qkv), _ptr(W_o), ctypes.byref(d), _ptr(W_gate), _ptr(W_up),
-                                _ptr(W_down), I, _ptr(W_lm), V, _ptr(Y_attn), _ptr(Y_mlp),
-                                _ptr(logits) if V else None, _ptr(ws), wsb, _stream(stream)))
+    fn = lib().tp_decode_step_packed if packed else lib().tp_decode_step
+    _check(fn(_ptr(X), _ptr(W_qkv), _ptr(W_o), ctypes.byref(d), _ptr(W_gate), _ptr(W_up), _ptr(W_down), I,
+              _ptr(W_lm), V, _ptr(Y_attn), _ptr(Y_mlp), _ptr(logits) if V else None, _ptr(ws), wsb,
+              _stream(stream)))
     return Y_attn, Y_mlp, logits
 
 

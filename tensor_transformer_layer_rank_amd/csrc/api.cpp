@@ -680,11 +680,10 @@ size_t tp_decode_step_workspace_size(const tp_attn_desc* desc, int64_t I_shard, 
                     WS_ALIGN);
 }
 
-tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
-                         const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
-                         const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
-                         void* workspace, size_t ws_bytes, void* stream) {
-    const char* fn = "tp_decode_step";
+static tp_status decode_step_impl(const char* fn, bool packed, const void* X, const void* W_qkv, const void* W_o,
+                                  const tp_attn_desc* desc, const void* W_gate, const void* W_up, const void* W_down,
+                                  int64_t I_shard, const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp,
+                                  float* logits, void* workspace, size_t ws_bytes, void* stream) {
     if (!X || !W_qkv || !W_o || !W_gate || !W_up || !W_down || !Y_attn || !Y_mlp)
         return fail(TP_ERR_NULL_POINTER, "%s: X, the attention and MLP weights, Y_attn and Y_mlp must be non-NULL", fn);
     if (V_shard > 0 && !logits) return fail(TP_ERR_NULL_POINTER, "%s: logits must be non-NULL when V_shard > 0", fn);
@@ -700,8 +699,41 @@ tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, cons
     return from_hip(tpk::decode_step(X, W_qkv, W_o, W_gate, W_up, W_down, W_lm, desc->B, desc->H, desc->n_q_heads,
                                      desc->n_kv_heads, I_shard, V_shard, desc->cache_len, desc->rope_theta,
                                      desc->k_cache, desc->v_cache, desc->cache_capacity, Y_attn, Y_mlp,
-                                     V_shard > 0 ? logits : nullptr, workspace, as_stream(stream)),
+                                     V_shard > 0 ? logits : nullptr, workspace, as_stream(stream), packed),
                     fn);
+}
+
+tp_status tp_decode_step(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
+                         const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
+                         const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    return decode_step_impl("tp_decode_step", false, X, W_qkv, W_o, desc, W_gate, W_up, W_down, I_shard, W_lm,
+                            V_shard, Y_attn, Y_mlp, logits, workspace, ws_bytes, stream);
+}
+
+tp_status tp_decode_step_packed(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,
+                                const void* W_gate, const void* W_up, const void* W_down, int64_t I_shard,
+                                const void* W_lm, int64_t V_shard, float* Y_attn, float* Y_mlp, float* logits,
+                                void* workspace, size_t ws_bytes, void* stream) {
+    return decode_step_impl("tp_decode_step_packed", true, X, W_qkv, W_o, desc, W_gate, W_up, W_down, I_shard,
+                            W_lm, V_shard, Y_attn, Y_mlp, logits, workspace, ws_bytes, stream);
+}
+
+size_t tp_packed_strips_bytes(int64_t K, int64_t N) {
+    if (K <= 0 || N <= 0 || N % 8 || K >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40)) return 0;
+    return tpk::packed_strips_bytes(K, N);
+}
+
+tp_status tp_pack_strips(const void* W, int64_t K, int64_t N, void* W_packed, void* stream) {
+    const char* fn = "tp_pack_strips";
+    if (!W || !W_packed) return fail(TP_ERR_NULL_POINTER, "%s: W and W_packed must be non-NULL", fn);
+    if (K <= 0 || N <= 0) return fail(TP_ERR_BAD_SHAPE, "%s: need K > 0 and N > 0", fn);
+    if (N % 8) return fail(TP_ERR_MISALIGNED, "%s: N must be a multiple of 8", fn);
+    if (K >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40))
+        return fail(TP_ERR_UNSUPPORTED, "%s: K and N must be below 2^40", fn);
+    if (!aligned(W, 16) || !aligned(W_packed, 16))
+        return fail(TP_ERR_MISALIGNED, "%s: W and W_packed must be 16-byte aligned", fn);
+    return from_hip(tpk::pack_strips(W, K, N, W_packed, as_stream(stream)), fn);
 }
 
 // ---- merges ------------------------------------------------------------------------------------

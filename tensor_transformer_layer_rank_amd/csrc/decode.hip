@@ -90,6 +90,7 @@ struct SkinnyArgs {
     int strips;              // strips per K chunk (dual: gate strips then up strips)
     int wg0;                 // first workgroup of this GEMM in a launch over several
     float* part;             // [splits][M][ncols]
+    int packed;              // weights in 128-column strips: [strip][K][128] (else [K][N])
 };
 
 template <int MB>
@@ -180,25 +181,29 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) m_ok |= (mb * 16 + l16 < g.M) ? (1u << mb) : 0u;
     const int64_t kfirst = kbeg + wave * STEP + 8 * grp;
-    const uint16_t* wp = Bp + kfirst * g.N + col;          // advances 4 steps at a time
+    // weight rows: [K][N] in place, or the strip's own [K][128] block when packed
+    const int64_t ldw = g.packed ? STRIP : g.N;
+    const uint16_t* Bs = g.packed ? Bp + cgroup * g.K * STRIP : Bp;
+    const int64_t colw = g.packed ? 8 * l16 : col;
+    const uint16_t* wp = Bs + kfirst * ldw + colw;         // advances 4 steps at a time
     const uint16_t* ap = g.A + (int64_t)l16 * g.lda + kfirst;
-    const int64_t wstep = 4 * STEP * g.N, astep = 4 * STEP;
+    const int64_t wstep = 4 * STEP * ldw, astep = 4 * STEP;
     // in-bounds stand-ins: row kbeg of this lane's column group (or of the strip's first
     // group), and token row 0 at column kbeg
-    const uint16_t* wsafe = Bp + kbeg * g.N + (col_ok ? col : c0);
+    const uint16_t* wsafe = Bs + kbeg * ldw + (col_ok ? colw : colw - 8 * l16);
     const uint16_t* asafe = g.A + kbeg;
     StepRegs<MB> s0, s1;
     int64_t kr = kfirst;
-    if (kr - 8 * grp < kend) load_step<MB>(s0, wp, ap, wsafe, asafe, g.N, g.lda, kr, kend, col_ok, m_ok);
+    if (kr - 8 * grp < kend) load_step<MB>(s0, wp, ap, wsafe, asafe, ldw, g.lda, kr, kend, col_ok, m_ok);
     for (; kr - 8 * grp < kend; kr += 8 * STEP) {
         // the next two steps are loaded whether or not they exist (see load_step); the
         // scheduling barriers keep each step's loads issued before the previous step's MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        load_step<MB>(s1, wp + wstep, ap + astep, wsafe, asafe, g.N, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
+        load_step<MB>(s1, wp + wstep, ap + astep, wsafe, asafe, ldw, g.lda, kr + 4 * STEP, kend, col_ok, m_ok);
         __builtin_amdgcn_sched_barrier(0);
         mma_step<MB, F16>(acc, s0);
         __builtin_amdgcn_sched_barrier(0);
-        load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, wsafe, asafe, g.N, g.lda, kr + 8 * STEP, kend, col_ok,
+        load_step<MB>(s0, wp + 2 * wstep, ap + 2 * astep, wsafe, asafe, ldw, g.lda, kr + 8 * STEP, kend, col_ok,
                       m_ok);
         __builtin_amdgcn_sched_barrier(0);
         if (kr + 4 * STEP - 8 * grp < kend) mma_step<MB, F16>(acc, s1);
@@ -272,16 +277,20 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
         for (int t = 0; t < 8; ++t) acc[mb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     unsigned char* stg = reinterpret_cast<unsigned char*>(&red[wave][0][0]);   // 16 KB: two 8 KB blocks
-    const uint16_t* wsafe = Bp + kbeg * g.N + (col_ok ? col : c0);
+    // weight rows: [K][N] in place, or the strip's own [K][128] block when packed
+    const int64_t ldw = g.packed ? STRIP : g.N;
+    const uint16_t* Bs = g.packed ? Bp + cgroup * g.K * STRIP : Bp;
+    const int64_t colw = g.packed ? 8 * l16 : col;
+    const uint16_t* wsafe = Bs + kbeg * ldw + (col_ok ? colw : colw - 8 * l16);
     const uint16_t* asafe = g.A + kbeg;
     // this lane's weight rows of step i (step i & 3 of group i >> 2): 8 grp .. + 7 of it
     auto load_w = [&](StepRegs<MB>& s, int i) {
         const int64_t kr = wbeg + (int64_t)(i >> 2) * 16 * STEP + (i & 3) * STEP + 8 * grp;
         s.k_ok = kr < wend;
         const bool ok = s.k_ok && col_ok;
-        const uint16_t* wp = Bp + kr * g.N + col;
+        const uint16_t* wp = Bs + kr * ldw + colw;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) s.w[r] = ld_stream(ok ? wp + r * g.N : wsafe);
+        for (int r = 0; r < 8; ++r) s.w[r] = ld_stream(ok ? wp + r * ldw : wsafe);
     };
     // activation block of group G: row 4 j + (lane >> 4), 16-byte chunk lane & 15 of its 128 k
     u32x4 areg[8];
@@ -393,6 +402,7 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
     TP_SEL(strips);
     TP_SEL(wg0);
     TP_SEL(part);
+    TP_SEL(packed);
 #undef TP_SEL
     const int local = bid - g.wg0;
     if constexpr (MB == 2)
@@ -815,6 +825,30 @@ hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* p
     return hipGetLastError();
 }
 
+// W [K, N] (16-bit elements, row-major) -> P [ceil(N / 128)][K][128]: each 128-column strip of
+// W as one contiguous block, columns past N zero. One thread copies 16 bytes.
+__global__ __launch_bounds__(256) void pack_strips_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ P,
+                                                          int64_t K, int64_t N, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 16-byte chunk of P
+    if (i >= total) return;
+    const int64_t j = i & 15, row = i >> 4;                              // row = strip * K + k
+    const int64_t strip = row / K, k = row - strip * K;
+    const int64_t col = strip * STRIP + 8 * j;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (col < N) v = *reinterpret_cast<const u32x4*>(W + k * N + col);
+    *reinterpret_cast<u32x4*>(P + i * 8) = v;
+}
+
+size_t packed_strips_bytes(int64_t K, int64_t N) { return (size_t)((N + STRIP - 1) / STRIP) * K * STRIP * 2; }
+
+hipError_t pack_strips(const void* W, int64_t K, int64_t N, void* P, hipStream_t s) {
+    const int64_t total = (N + STRIP - 1) / STRIP * K * 16;
+    ProfScope ps("pack_strips", s);
+    pack_strips_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(W),
+                                                                        static_cast<uint16_t*>(P), K, N, total);
+    return hipGetLastError();
+}
+
 // ---- the whole decode step of a rank in four launches ------------------------------------
 // K1: the projections that feed the attention and the MLP (QKV and gate/up) as one split-K launch;
 // K2: decode attention (sums the QKV partials, RoPE, cache append, attention over the cache),
@@ -904,7 +938,7 @@ size_t decode_step_ws_bytes(int64_t B, int64_t H, int hq, int hkv, int64_t I, in
 hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const void* Wg, const void* Wu,
                        const void* Wd, const void* Wlm, int64_t B, int64_t H, int hq, int hkv, int64_t I,
                        int64_t V, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap, float* Ya,
-                       float* Ym, float* logits, void* ws, hipStream_t s) {
+                       float* Ym, float* logits, void* ws, hipStream_t s, bool packed) {
     const DecodePlan d = plan_decode(B, H, hq, hkv, I, V);
     unsigned char* base = static_cast<unsigned char*>(ws);
     float* part_qkv = reinterpret_cast<float*>(base + d.off[0]);
@@ -919,7 +953,10 @@ hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const vo
     SkinnyArgs a1[2] = {skinny_args(X, Wqkv, nullptr, part_qkv, B, nqkv, H, H),
                         skinny_args(X, Wg, Wu, part_gu, B, I, H, H)};
     int w = 0;
-    for (int i = 0; i < 2; ++i) w = skinny_place(a1[i], d.p1[i], w);
+    for (int i = 0; i < 2; ++i) {
+        w = skinny_place(a1[i], d.p1[i], w);
+        a1[i].packed = packed;
+    }
     hipError_t e = skinny_launch(a1, 2, w, B, s, "skinny_gemm_x", false);
     if (e != hipSuccess) return e;
     // K2: attention, with the gate/up reduction in the attention workgroups' spare threads
@@ -948,7 +985,10 @@ hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const vo
                         skinny_args(h, Wd, nullptr, part_d, B, H, I, I),
                         skinny_args(X, Wlm, nullptr, part_lm, B, V, H, H)};
     w = 0;
-    for (int i = 0; i < d.n3; ++i) w = skinny_place(a3[i], d.p3[i], w);
+    for (int i = 0; i < d.n3; ++i) {
+        w = skinny_place(a3[i], d.p3[i], w);
+        a3[i].packed = packed;
+    }
     e = skinny_launch(a3, d.n3, w, B, s, "skinny_gemm_out", false);
     if (e != hipSuccess) return e;
     // K4

@@ -148,7 +148,10 @@ size_t decode_step_ws_bytes(int64_t B, int64_t H, int hq, int hkv, int64_t I, in
 hipError_t decode_step(const void* X, const void* Wqkv, const void* Wo, const void* Wg, const void* Wu,
                        const void* Wd, const void* Wlm, int64_t B, int64_t H, int hq, int hkv, int64_t I,
                        int64_t V, int64_t pos, float theta, void* k_cache, void* v_cache, int64_t cap, float* Ya,
-                       float* Ym, float* logits, void* ws, hipStream_t s);
+                       float* Ym, float* logits, void* ws, hipStream_t s, bool packed = false);
+// W [K, N] 16-bit -> [ceil(N / 128)][K][128] (the decode kernels' strip layout)
+size_t packed_strips_bytes(int64_t K, int64_t N);
+hipError_t pack_strips(const void* W, int64_t K, int64_t N, void* P, hipStream_t s);
 
 // ---- backward of a linear shard ---------------------------------------------------------
 // dX [T, K] fp32 = dY [T, N] . W^T, dW [K, N] fp32 = X^T [K, T] . dY (bf16 operands; T, K, N

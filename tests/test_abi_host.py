@@ -388,6 +388,35 @@ def test_decode_step_validation(L):
     assert _st(f(*args)) == "TP_ERR_UNSUPPORTED"                      # at most 64 sequences
 
 
+def test_packed_decode_validation(L):
+    """tp_decode_step_packed validates like tp_decode_step; tp_pack_strips and its size query
+    reject NULL, misaligned and unpackable arguments before any HIP call."""
+    f = L.tp_decode_step_packed
+    d = tp.AttnDesc()
+    d.B, d.S, d.H, d.n_q_heads, d.n_kv_heads, d.head_dim, d.rope_theta, d.causal = 4, 1, 256, 2, 2, 128, 1e4, 1
+    d.k_cache, d.v_cache, d.cache_len, d.cache_capacity = 0x1000, 0x2000, 37, 40
+    args = [FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, FAKE, FAKE, 136, FAKE, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    bad = list(args); bad[1] = None
+    assert _st(f(*bad)) == "TP_ERR_NULL_POINTER"
+    assert "tp_decode_step_packed" in L.tp_last_error().decode()
+    bad = list(args); bad[14] = 16
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
+    bad = list(args); bad[7] = 132
+    assert _st(f(*bad)) == "TP_ERR_MISALIGNED"
+    g = L.tp_pack_strips
+    assert _st(g(None, 64, 256, FAKE, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(g(FAKE, 64, 256, None, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(g(FAKE, 0, 256, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(g(FAKE, 64, 0, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(g(FAKE, 64, 252, FAKE, None)) == "TP_ERR_MISALIGNED"
+    assert _st(g(FAKE_ODD, 64, 256, FAKE, None)) == "TP_ERR_MISALIGNED"
+    assert _st(g(FAKE, 1 << 40, 256, FAKE, None)) == "TP_ERR_UNSUPPORTED"
+    assert L.tp_packed_strips_bytes(4096, 16000) == 125 * 4096 * 128 * 2
+    assert L.tp_packed_strips_bytes(40, 136) == 2 * 40 * 128 * 2
+    assert L.tp_packed_strips_bytes(40, 132) == 0
+    assert L.tp_packed_strips_bytes(0, 128) == 0
+
+
 def test_workspace_size_arithmetic_at_large_shapes(L):
     """Every size query at large valid shapes: positive, in range, and growing with the token
     count (run under the host-sanitizer build, this also checks the size arithmetic for

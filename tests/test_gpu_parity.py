@@ -750,19 +750,22 @@ def test_error_is_raised_not_launched(tp):
 
 # ---------------------------------------------------------------- the fused decode step
 
-def _decode_step(tp, inp, with_lm=True):
+def _decode_step(tp, inp, with_lm=True, packed=False):
     import torch
     kc, vc = dev(inp.k_cache), dev(inp.v_cache)
-    Ya, Ym, lg = tp.decode_step(dev(inp.X), dev(inp.W_qkv), dev(inp.W_o), inp.hq, inp.hkv, inp.theta, kc, vc,
-                                inp.cache_len, dev(inp.W_gate), dev(inp.W_up), dev(inp.W_down),
-                                dev(inp.W_lm) if with_lm else None,
-                                Y_attn=_nan((inp.B, inp.H), torch.float32), Y_mlp=_nan((inp.B, inp.H), torch.float32))
+    W = (lambda w: tp.pack_strips(dev(w))) if packed else dev
+    I, V = inp.W_gate.shape[1], (inp.W_lm.shape[1] if with_lm else 0)
+    Ya, Ym, lg = tp.decode_step(dev(inp.X), W(inp.W_qkv), W(inp.W_o), inp.hq, inp.hkv, inp.theta, kc, vc,
+                                inp.cache_len, W(inp.W_gate), W(inp.W_up), W(inp.W_down),
+                                W(inp.W_lm) if with_lm else None,
+                                Y_attn=_nan((inp.B, inp.H), torch.float32), Y_mlp=_nan((inp.B, inp.H), torch.float32),
+                                packed=packed, I=I, V=V)
     torch.cuda.synchronize()
     return host(Ya), host(Ym), (host(lg) if with_lm else None), host(kc), host(vc)
 
 
-def _check_decode_step(tp, inp, what, with_lm=True):
-    ya, ym, lg, kc, vc = _decode_step(tp, inp, with_lm)
+def _check_decode_step(tp, inp, what, with_lm=True, packed=False):
+    ya, ym, lg, kc, vc = _decode_step(tp, inp, with_lm, packed)
     L = inp.cache_len
     ref, knew, vnew = O.decode_attn_shard(inp.X, inp.W_qkv, inp.W_o, inp.k_cache, inp.v_cache, L, inp.hq, inp.hkv,
                                           inp.d, inp.theta)
@@ -799,3 +802,42 @@ def test_decode7b_tp2_fused_step_full_size(tp):
     b = _decode_step(tp, inp)
     for x, y in zip(a, b):
         assert np.array_equal(x, y), "two calls differ bitwise"
+
+
+# ---------------------------------------------------------------- packed strips
+
+@pytest.mark.parametrize("K,N", [(8, 8), (40, 136), (4096, 16000), (264, 1000), (1, 128)])
+def test_pack_strips_layout(tp, K, N):
+    """tp_pack_strips moves every element, bit for bit, to [strip][k][column in strip], and zeroes
+    the columns past N in the last strip."""
+    import torch
+    W = np.random.default_rng(K * 7 + N).standard_normal((K, N)).astype(np.float32)
+    Wd = dev(W)
+    P = host(tp.pack_strips(Wd))
+    torch.cuda.synchronize()
+    ns = (N + 127) // 128
+    ref = np.zeros((K, ns * 128), np.float32)
+    ref[:, :N] = host(Wd)
+    ref = ref.reshape(K, ns, 128).transpose(1, 0, 2)
+    assert P.shape == (ns, K, 128)
+    assert np.array_equal(P, ref)
+
+
+@pytest.mark.parametrize("B,H,hq,hkv,I,V,L,cap", [(4, 256, 2, 2, 136, 1000, 37, 40), (3, 512, 4, 1, 264, 520, 300, 301),
+                                                  (64, 512, 4, 4, 1000, 2056, 129, 130)])
+def test_decode_step_packed_small(tp, B, H, hq, hkv, I, V, L, cap):
+    """tp_decode_step_packed: the decode step with every weight in 128-column strips (ragged last
+    strips, both activation-row paths)."""
+    inp = wl.random_decode(B * 11 + L, B, H, hq, hkv, I, V, L, cap)
+    _check_decode_step(tp, inp, f"packed decode step B{B} H{H} hq{hq} hkv{hkv} I{I} V{V} L{L}", packed=True)
+
+
+def test_decode7b_tp2_packed_step_full_size(tp):
+    """The 7B TP=2 decode step with packed weights: every output element against the oracle, and
+    equal bit for bit to the step on the weights in place (same kernels, same sums)."""
+    inp = wl.decode7b_tp2()
+    _check_decode_step(tp, inp, "decode7b_tp2 packed step", packed=True)
+    a = _decode_step(tp, inp, packed=True)
+    b = _decode_step(tp, inp)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y), "packed and in-place steps differ bitwise"
