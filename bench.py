@@ -97,6 +97,48 @@ def prewarm(step, seconds: float):
     return n
 
 
+class TimingEvent:
+    """A HIP event for timing only, recorded on a torch stream (the current one by default).
+    Created with hipEventDisableSystemFence: recording it does not write back and invalidate the
+    caches at system scope, which a default event does (torch.cuda.Event), costing microseconds
+    per record and slowing the kernels after it. Same interface as torch.cuda.Event for timing."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            import torch  # noqa: F401  (loads the HIP runtime that torch and libtpshard share)
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = h
+        self._ct = ctypes
+        self.e = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.e), 0x20000000)   # hipEventDisableSystemFence
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = TimingEvent._hip.hipEventRecord(self.e, self._ct.c_void_p(s.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, other) -> float:
+        ms = self._ct.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.e, other.e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.e:
+            TimingEvent._hip.hipEventDestroy(self.e)
+
+
 def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 10, keep_steps: bool = False):
     """Run `warmup` untimed steps, then time exactly `steps` steps; returns ms per step.
 
@@ -112,7 +154,7 @@ def timed(step, warmup: int, steps: int, name: str = None, sample_every: int = 1
     torch.cuda.synchronize()
     tp.profile_reset()
     s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev = [TimingEvent() for _ in range(steps + 1)]
     ev[0].record(s)
     for i in range(steps):
         sampled = sample_every > 0 and (i % sample_every == sample_every - 1 or
@@ -153,7 +195,7 @@ def clock_power(step, seconds: float = 2.5):
         h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
         stamp0 = amdsmi.amdsmi_get_gpu_metrics_info(h).get("system_clock_counter")
         s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record(s)
         step()
         e1.record(s)
@@ -366,7 +408,7 @@ def graph_timed(step, warmup: int, steps: int, name: str = None):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev = [TimingEvent() for _ in range(steps + 1)]
     ev[0].record()
     for i in range(steps):
         g.replay()
@@ -468,7 +510,7 @@ def decode_bench(args):
     # the previous step left in the cache. Back-to-back steps re-read a 606 MB working set.
     flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
     n_cold = min(args.steps, 20)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(n_cold)]
     for e0, e1 in ev:
         flush.add_(1.0)
         e0.record()
@@ -689,7 +731,7 @@ def ceiling_bench(args):
     for name, ops in pats.items():
         def run(iters):
             tp.mfma_rate_probe(ops, out, n_wg, iters)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         run(2000)
         torch.cuda.synchronize()
         e0.record()
@@ -733,7 +775,7 @@ def ceiling_bench(args):
             for _ in range(20):
                 step()
             torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         e0.record()
         for _ in range(50):
             step()

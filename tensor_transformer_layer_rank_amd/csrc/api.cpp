@@ -79,7 +79,9 @@ constexpr size_t PROF_MAX = 65536;
 hipEvent_t pool_event() {
     if (g_pool_used == g_pool.size()) {
         hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        // timing only: no system-scope cache write-back and invalidate when the event is
+        // recorded (that fence costs microseconds and slows the kernels that follow)
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         g_pool.push_back(e);
     }
     return g_pool[g_pool_used++];
