@@ -249,14 +249,22 @@ size_t tp_decode_step_workspace_size(const tp_attn_desc* desc, int64_t I_shard, 
 
 /*
  * tp_decode_step_packed — tp_decode_step with every weight (W_qkv, W_o, W_gate, W_up, W_down,
- *   W_lm) in the strip layout that tp_pack_strips writes; the other arguments, the workspace size
- *   (tp_decode_step_workspace_size), the results and the errors are those of tp_decode_step.
+ *   W_lm) in the strip layout that tp_pack_strips writes, each packed from the [K, N] weight that
+ *   tp_decode_step would take (W_qkv from [H, (n_q_heads + 2 n_kv_heads) 128], W_o from
+ *   [n_q_heads 128, H], W_gate / W_up from [H, I_shard], W_down from [I_shard, H], W_lm from
+ *   [H, V_shard]); the library cannot check the packed buffers' sizes. The other arguments, the
+ *   workspace size (tp_decode_step_workspace_size), the errors and the results are those of
+ *   tp_decode_step, bit for bit (same kernels and sums; only the weight addresses differ). The
+ *   rank's weights are streamed once per step in both forms: packed, a workgroup's K chunk of a
+ *   strip is one contiguous block ("TensorRT LLM 中的并行策略", 注意力模块 and "张量并行：切分
+ *   Transformer 层的分布式训练", 输入与输出层, as for tp_decode_step).
  *
  * tp_pack_strips — W [K, N] (bf16 or fp16, row-major) rearranged into 128-column strips:
  *   W_packed [ceil(N / 128)][K][128], strip s holding columns 128 s .. 128 s + 127 of every row,
  *   columns past N zero. A weight is packed once (at load time); a decode step then streams each
  *   strip as one contiguous block. W_packed: tp_packed_strips_bytes(K, N) bytes, caller-owned,
- *   must not overlap W. N a multiple of 8; K, N < 2^40; pointers 16-byte aligned. Asynchronous on
+ *   must not overlap W. N a multiple of 8; K x (N rounded up to 128) at most 2^36 elements
+ *   (TP_ERR_UNSUPPORTED otherwise); pointers 16-byte aligned. Asynchronous on
  *   the stream. tp_packed_strips_bytes returns 0 for shapes tp_pack_strips rejects.
  */
 tp_status tp_decode_step_packed(const void* X, const void* W_qkv, const void* W_o, const tp_attn_desc* desc,

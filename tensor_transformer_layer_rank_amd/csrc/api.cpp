@@ -721,8 +721,16 @@ tp_status tp_decode_step_packed(const void* X, const void* W_qkv, const void* W_
                             W_lm, V_shard, Y_attn, Y_mlp, logits, workspace, ws_bytes, stream);
 }
 
+// packed weights are limited to 2^36 elements (padded), which keeps the copy's grid below 2^25
+// workgroups and every index in 64 bits
+static bool packable(int64_t K, int64_t N) {
+    if (K <= 0 || N <= 0 || K >= ((int64_t)1 << 36) || N >= ((int64_t)1 << 36)) return false;
+    const int64_t strips = (N + 127) / 128;
+    return strips <= (((int64_t)1 << 36) / 128) / K;
+}
+
 size_t tp_packed_strips_bytes(int64_t K, int64_t N) {
-    if (K <= 0 || N <= 0 || N % 8 || K >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40)) return 0;
+    if (N % 8 || !packable(K, N)) return 0;
     return tpk::packed_strips_bytes(K, N);
 }
 
@@ -731,8 +739,8 @@ tp_status tp_pack_strips(const void* W, int64_t K, int64_t N, void* W_packed, vo
     if (!W || !W_packed) return fail(TP_ERR_NULL_POINTER, "%s: W and W_packed must be non-NULL", fn);
     if (K <= 0 || N <= 0) return fail(TP_ERR_BAD_SHAPE, "%s: need K > 0 and N > 0", fn);
     if (N % 8) return fail(TP_ERR_MISALIGNED, "%s: N must be a multiple of 8", fn);
-    if (K >= ((int64_t)1 << 40) || N >= ((int64_t)1 << 40))
-        return fail(TP_ERR_UNSUPPORTED, "%s: K and N must be below 2^40", fn);
+    if (!packable(K, N))
+        return fail(TP_ERR_UNSUPPORTED, "%s: K x N (N rounded up to 128) must be at most 2^36 elements", fn);
     if (!aligned(W, 16) || !aligned(W_packed, 16))
         return fail(TP_ERR_MISALIGNED, "%s: W and W_packed must be 16-byte aligned", fn);
     return from_hip(tpk::pack_strips(W, K, N, W_packed, as_stream(stream)), fn);

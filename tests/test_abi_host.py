@@ -411,6 +411,9 @@ def test_packed_decode_validation(L):
     assert _st(g(FAKE, 64, 252, FAKE, None)) == "TP_ERR_MISALIGNED"
     assert _st(g(FAKE_ODD, 64, 256, FAKE, None)) == "TP_ERR_MISALIGNED"
     assert _st(g(FAKE, 1 << 40, 256, FAKE, None)) == "TP_ERR_UNSUPPORTED"
+    assert _st(g(FAKE, 1 << 20, 1 << 20, FAKE, None)) == "TP_ERR_UNSUPPORTED"   # 2^40 elements
+    assert L.tp_packed_strips_bytes(1 << 20, 1 << 20) == 0
+    assert L.tp_packed_strips_bytes(1 << 20, 1 << 16) == (1 << 36) * 2       # exactly 2^36 elements
     assert L.tp_packed_strips_bytes(4096, 16000) == 125 * 4096 * 128 * 2
     assert L.tp_packed_strips_bytes(40, 136) == 2 * 40 * 128 * 2
     assert L.tp_packed_strips_bytes(40, 132) == 0
