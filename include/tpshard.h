@@ -83,7 +83,7 @@ typedef struct { float x_scale; float w_scale; } tp_fp8_scales;
  *                                   rank write its slice of a full [T, N*tp] buffer
  *                                   (the concatenation happens in place).
  *   in_dt/out_dt: (F32, F32) — exact fp32 path; (BF16 or F16, BF16|F16|F32) with fp32
- *                 accumulation (T <= 64: BF16|F32 output only);
+ *                 accumulation;
  *                 (FP8_E4M3, BF16|F16|F32) with scales q: Y = act(x_scale * w_scale *
  *                 (codes(X) . codes(W))), accumulated in fp32.
  *   16-bit and fp8 operands: K < 2^23 (else TP_ERR_UNSUPPORTED).

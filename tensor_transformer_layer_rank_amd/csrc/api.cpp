@@ -225,7 +225,7 @@ static tp_status check_bf16_gemm(const char* fn, const void* X, const void* W, c
 struct ColumnPlan {
     enum { F32, FP8, SKINNY, MFMA16 } path;
     int kind;       // store kind of the prefill tiles (0 bf16, 1 fp16, 2 fp32)
-    int rk;         // epilogue of the few-row reduce (0 fp32, 2 bf16, 3 bf16 ReLU)
+    int rk;         // epilogue of the few-row reduce (0 fp32, 2 bf16, 3 bf16 ReLU, 5 fp16, 6 fp16 ReLU, 7 fp32 ReLU)
     int f16;        // fp16 operands (else bf16)
     size_t need;    // tp_linear_workspace_size of the call
 };
@@ -269,9 +269,8 @@ static tp_status column_linear_check(const char* fn, const void* X, const void* 
     p->f16 = in_dt == TP_F16;
     p->need = tp_linear_workspace_size(T, K, N, in_dt);
     if (T <= SKINNY_MAX_T) {
-        if (out_dt == TP_F16) return fail(TP_ERR_UNSUPPORTED, "%s: fp16 output is not offered for T <= %d", fn, (int)SKINNY_MAX_T);
-        p->rk = out_dt == TP_F32 ? (act == TP_ACT_RELU ? -1 : 0) : (act == TP_ACT_RELU ? 3 : 2);
-        if (p->rk < 0) return fail(TP_ERR_UNSUPPORTED, "%s: ReLU with fp32 output is not offered for T <= %d", fn, (int)SKINNY_MAX_T);
+        const bool relu = act == TP_ACT_RELU;
+        p->rk = out_dt == TP_F32 ? (relu ? 7 : 0) : out_dt == TP_BF16 ? (relu ? 3 : 2) : (relu ? 6 : 5);
         p->path = ColumnPlan::SKINNY;
         return TP_OK;
     }

@@ -439,7 +439,11 @@ __device__ __forceinline__ void sum_splits(const float* part, int splits, int64_
     }
 }
 
-// kind: 0 fp32 store, 1 fp32 +=, 2 bf16, 3 bf16 ReLU
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// kind: 0 fp32 store, 1 fp32 +=, 2 bf16, 3 bf16 ReLU, 5 fp16, 6 fp16 ReLU, 7 fp32 ReLU
 __global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restrict__ part, int splits,
                                                            int64_t M, int64_t N, int64_t ncols, void* C,
                                                            int64_t ldc, int kind) {
@@ -454,7 +458,10 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restri
     if (kind == 0) static_cast<float*>(C)[off] = v;
     else if (kind == 1) static_cast<float*>(C)[off] += v;
     else if (kind == 2) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v);
-    else static_cast<uint16_t*>(C)[off] = f32_to_bf16(v > 0.f ? v : 0.f);
+    else if (kind == 3) static_cast<uint16_t*>(C)[off] = f32_to_bf16(v > 0.f ? v : 0.f);
+    else if (kind == 5) static_cast<uint16_t*>(C)[off] = f32_to_f16(v);
+    else if (kind == 6) static_cast<uint16_t*>(C)[off] = f32_to_f16(v > 0.f ? v : 0.f);
+    else static_cast<float*>(C)[off] = v > 0.f ? v : 0.f;
 }
 
 __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restrict__ part, int splits,

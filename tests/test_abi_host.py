@@ -301,8 +301,10 @@ def test_fp16_operands_follow_the_bf16_rules(L):
     assert L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_F16) == L.tp_linear_workspace_size(32, 4096, 16000, tp.TP_BF16)
     assert _st(col(FAKE, FAKE, FAKE, 100, 12, 8, 8, tp.TP_F16, tp.TP_F32, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
     assert _st(col(FAKE_ODD, FAKE, FAKE, 100, 8, 8, 8, tp.TP_F16, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
-    # the weight-streaming kernels of the few-row regime store fp32 or bf16 only
-    assert _st(col(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_F16, tp.TP_F16, 0, None, FAKE, 1 << 20, None)) == "TP_ERR_UNSUPPORTED"
+    # the few-row regime offers every output type too: an fp16-output call passes the dtype checks
+    # and stops at the workspace size (no launch with these fake pointers)
+    assert _st(col(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_F16, tp.TP_F16, 0, None, FAKE, 16, None)) == "TP_ERR_WORKSPACE"
+    assert _st(col(FAKE, FAKE, FAKE, 4, 64, 64, 64, tp.TP_BF16, tp.TP_F32, 1, None, FAKE, 16, None)) == "TP_ERR_WORKSPACE"
     assert _st(row(FAKE, FAKE, FAKE, 100, 12, 8, tp.TP_F16, 0, None, None, 0, None)) == "TP_ERR_MISALIGNED"
 
 

@@ -381,6 +381,21 @@ def test_few_row_linear_ragged(tp, T, K, N):
     assert_close_bf16(host(P), 2 * ref, f"few-row row partial {T}x{K}x{N} accumulate")
 
 
+@pytest.mark.parametrize("T", [1, 17, 64])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_column_linear_relu_few_rows(tp, T, out):
+    """ReLU on the few-row (weight-streaming) path with each output type, K off the chunk step and
+    N off the 128-column strip."""
+    import torch
+    rng = np.random.default_rng(T * 3 + len(out))
+    X = wl.bf16_round(rng.standard_normal((T, 1000)).astype(np.float32))
+    W = wl.bf16_round((rng.standard_normal((1000, 392)) * 0.05).astype(np.float32))
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[out]
+    Y = tp.column_linear(dev(X), dev(W), Y=_nan((T, 392), dt), act=tp.TP_ACT_RELU)
+    torch.cuda.synchronize()
+    assert_close_bf16(host(Y), O.relu(O.linear(X, W)), f"few-row relu {T} out {out}", out=out)
+
+
 def test_column_linear_relu_and_ldy(tp):
     import torch
     rng = np.random.default_rng(3)
@@ -484,10 +499,8 @@ def _f16(a):
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 def test_column_linear_fp16_operands(tp, T, K, N, out):
     """fp16 X and W (fp32 accumulation): the prefill tiles (ragged, and a grid split past the first
-    round) and the few-row weight-streaming kernels (which store fp32 or bf16 only)."""
+    round) and the few-row weight-streaming kernels."""
     import torch
-    if T <= 64 and out == "f16":
-        pytest.skip("the few-row kernels offer fp32 and bf16 outputs")
     rng = np.random.default_rng(T + K + N)
     X = _f16(rng.standard_normal((T, K)))
     W = _f16(rng.standard_normal((K, N)) * 0.05)
