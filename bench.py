@@ -18,7 +18,9 @@ this host's cores:
      the step on the weights in place is timed beside it.
 Beside them: the MLP shard on OCP E4M3 operands (tp_mlp_shard_fp8), the step after the
 merge (tp_merge_rmsnorm), the backward of the MLP down shard (tp_linear_backward) and a
-top-2 MoE MLP over 8 local experts (tp_moe_mlp_shard). Inputs are seeded synthetic tensors
+top-2 MoE MLP over 8 local experts (tp_moe_mlp_shard); and two ceilings measured on the box:
+the matrix pipes' rate under the power limit (tp_mfma_rate_probe) and the HBM read rate of
+the decode GEMMs' access pattern (tp_hbm_read_probe). Inputs are seeded synthetic tensors
 already resident in HBM when timing starts.
 
 Prints ONE JSON line. Each leg's timed steps are bracketed by events recorded after every
@@ -52,7 +54,7 @@ def parse():
                     help="seconds of untimed back-to-back headline steps before the first leg (clock settling)")
     ap.add_argument("--no-parity", action="store_true", help="skip the element-wise oracle comparison")
     ap.add_argument("--legs", default="all",
-                    help="comma-separated subset of c0,c1,c2,c3,c4,fp8,merge,backward,moe,ceiling (profiling runs); "
+                    help="comma-separated subset of c0,c1,c2,c3,c4,fp8,merge,backward,moe,ceiling,hbm (profiling runs); "
                          "the headline needs c1")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
@@ -790,6 +792,39 @@ def ceiling_bench(args):
             "mlp7b_tp4_low_power_operands": mlp}
 
 
+def hbm_read_bench(args):
+    """The HBM read rate the decode GEMMs' access pattern can reach without their arithmetic
+    (tp_hbm_read_probe): the grids of the decode step's two weight-streaming launches, each
+    workgroup reading a contiguous run in 8 KB blocks. Five buffers of the launch's size are read
+    in turn, so no launch finds its bytes in the 256 MB Infinity Cache; back-to-back launches."""
+    import torch
+    import tensor_transformer_layer_rank_amd as tp
+    res = {}
+    out = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
+    for name, n_wg, nbytes in (("decode_K1_grid", 402, 140509184), ("decode_K3_grid", 378, 192937984),
+                               ("512_workgroups", 512, 140509184)):
+        per = nbytes // n_wg // 8192 * 8192
+        stride = (per * n_wg + (1 << 20)) // 256 * 256
+        buf = torch.ones(stride * 5, dtype=torch.uint8, device="cuda")
+        for i in range(10):
+            tp.hbm_read_probe(buf[(i % 5) * stride:], per, n_wg, out)
+        torch.cuda.synchronize()
+        reps = 100
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record()
+        for i in range(reps):
+            tp.hbm_read_probe(buf[(i % 5) * stride:], per, n_wg, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"workgroups": n_wg, "bytes": per * n_wg, "us_per_launch": ms * 1e3,
+                     "gbs": per * n_wg / (ms * 1e-3) / 1e9, "frac_hbm": per * n_wg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del buf
+    return {"what": "contiguous run per workgroup, 4 waves, 16-byte nontemporal loads in 8 KB blocks, one block "
+                    "ahead, two workgroups per compute unit; five buffers read in turn (tp_hbm_read_probe)",
+            "grids": res}
+
+
 def traffic_probe():
     """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
     import torch
@@ -959,7 +994,7 @@ def main():
     torch.cuda.set_device(0)
     tp.load()
     legs = set(args.legs.split(",")) if args.legs != "all" else \
-        {"c0", "c1", "c2", "c3", "c4", "fp8", "merge", "backward", "moe", "ceiling"}
+        {"c0", "c1", "c2", "c3", "c4", "fp8", "merge", "backward", "moe", "ceiling", "hbm"}
     keep = {}
     mlp = c0 = c2 = c3 = dec = fp8 = merge = bwd = moe = None
     t_start = time.perf_counter()
@@ -998,6 +1033,10 @@ def main():
     if "ceiling" in legs:
         ceiling = ceiling_bench(args)
         done("ceiling")
+    hbm = None
+    if "hbm" in legs:
+        hbm = hbm_read_bench(args)
+        done("hbm read ceiling")
     if args.traffic_probe:
         traffic_probe()
     torch.cuda.synchronize()
@@ -1006,7 +1045,7 @@ def main():
         done("parity (fp64 oracle over every output element)")
     if mlp is None:
         print(json.dumps({"legs": sorted(legs), "c0": c0, "c2": c2, "c3": c3, "decode": dec, "fp8_mlp": fp8,
-                          "merge_rmsnorm": merge, "backward": bwd, "moe": moe, "mfma_ceiling": ceiling,
+                          "merge_rmsnorm": merge, "backward": bwd, "moe": moe, "mfma_ceiling": ceiling, "hbm_read_ceiling": hbm,
                           "parity": par}))
         return
     cpu = None if args.no_cpu else cpu_baseline(keep["c1"]["inp"], args.cpu_seconds)
@@ -1057,6 +1096,7 @@ def main():
         "backward": bwd,
         "moe": moe,
         "mfma_ceiling": ceiling,
+        "hbm_read_ceiling": hbm,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", None)},
     }

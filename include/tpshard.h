@@ -407,6 +407,17 @@ tp_status tp_profile_enable(int on);
  */
 tp_status tp_mfma_rate_probe(const void* operands, float* out, int64_t n_workgroups, int64_t iters,
                              void* stream);
+/*
+ * Measurement aid (not part of the shard computation): the HBM read rate that a decode GEMM's
+ * access pattern can reach, without its arithmetic. n_workgroups workgroups of 4 waves (two per
+ * compute unit, as in the decode GEMMs) each read bytes_per_workgroup contiguous bytes of buf
+ * (device; n_workgroups * bytes_per_workgroup bytes) in 8 KB blocks of 16-byte nontemporal loads,
+ * the next block in flight while the current one is consumed. out (device) receives
+ * n_workgroups * 256 checksums. bytes_per_workgroup a multiple of 8192 in [8192, 2^34];
+ * 1 <= n_workgroups <= 2^20; buf 16-byte aligned.
+ */
+tp_status tp_hbm_read_probe(const void* buf, int64_t bytes_per_workgroup, int64_t n_workgroups, unsigned* out,
+                            void* stream);
 tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches);
 tp_status tp_profile_reset(void);
 

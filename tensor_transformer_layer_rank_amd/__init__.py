@@ -20,7 +20,8 @@ __all__ = [
     "profile_enable", "profile_reset", "profile_read", "merge_rmsnorm", "linear_backward",
     "linear_backward_workspace_size", "moe_mlp_shard", "moe_workspace_size",
     "TP_F32", "TP_BF16", "TP_F16", "TP_FP8_E4M3", "TP_ACT_NONE", "TP_ACT_RELU",
-    "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS",
+    "TP_MLP_RELU", "TP_MLP_SWIGLU", "STATUS", "decode_step", "decode_step_workspace_size", "pack_strips",
+    "column_linear_noalloc", "mfma_rate_probe", "hbm_read_probe",
 ]
 
 # TPSHARD_LIB names another build of the same library (e.g. the host-checked one)
@@ -40,6 +41,7 @@ EXPORTS = [
     "tp_merge_rmsnorm", "tp_linear_backward", "tp_linear_backward_workspace_size", "tp_moe_mlp_shard",
     "tp_moe_workspace_size", "tp_column_linear_noalloc", "tp_mfma_rate_probe", "tp_decode_step",
     "tp_decode_step_workspace_size", "tp_decode_step_packed", "tp_pack_strips", "tp_packed_strips_bytes",
+    "tp_hbm_read_probe",
 ]
 
 
@@ -117,6 +119,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                    _SZ, _P], _I32),
         "tp_pack_strips": ([_P, _I64, _I64, _P, _P], _I32),
         "tp_packed_strips_bytes": ([_I64, _I64], _SZ),
+        "tp_hbm_read_probe": ([_P, _I64, _I64, _P, _P], _I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -453,6 +456,12 @@ def moe_mlp_shard(X, W_gate, W_up, W_down, expert_offsets, row_token, token_rows
 
 
 # --- kernel timing ------------------------------------------------------------------------------
+
+def hbm_read_probe(buf, bytes_per_workgroup: int, n_workgroups: int, out, stream=None):
+    """HBM read-rate microbenchmark (measurement aid): see tp_hbm_read_probe."""
+    _check(lib().tp_hbm_read_probe(_ptr(buf), int(bytes_per_workgroup), int(n_workgroups), _ptr(out),
+                                   _stream(stream)))
+
 
 def mfma_rate_probe(operands, out, n_workgroups: int, iters: int, stream=None):
     """Matrix-pipe rate microbenchmark (measurement aid): see tp_mfma_rate_probe."""

@@ -157,6 +157,18 @@ tp_status tp_mfma_rate_probe(const void* operands, float* out, int64_t n_workgro
     return from_hip(tpk::mfma_rate(operands, out, n_workgroups, iters, as_stream(stream)), fn);
 }
 
+tp_status tp_hbm_read_probe(const void* buf, int64_t bytes_per_workgroup, int64_t n_workgroups, unsigned* out,
+                            void* stream) {
+    const char* fn = "tp_hbm_read_probe";
+    if (!buf || !out) return fail(TP_ERR_NULL_POINTER, "%s: buf and out must be non-NULL", fn);
+    if (!aligned(buf, 16) || !aligned(out, 4)) return fail(TP_ERR_MISALIGNED, "%s: buf 16-byte, out 4-byte aligned", fn);
+    if (n_workgroups < 1 || n_workgroups > (1 << 20) || bytes_per_workgroup < 8192 ||
+        bytes_per_workgroup > ((int64_t)1 << 34) || bytes_per_workgroup % 8192)
+        return fail(TP_ERR_BAD_SHAPE, "%s: need 1 <= n_workgroups <= 2^20 and bytes_per_workgroup a multiple of 8192 "
+                    "in [8192, 2^34]", fn);
+    return from_hip(tpk::hbm_read(buf, bytes_per_workgroup, n_workgroups, out, as_stream(stream)), fn);
+}
+
 tp_status tp_profile_read(const char* prefix, double* total_ms, int64_t* launches) {
     if (!prefix || !total_ms || !launches) return fail(TP_ERR_NULL_POINTER, "tp_profile_read: NULL argument");
     std::lock_guard<std::mutex> lk(g_prof_mu);

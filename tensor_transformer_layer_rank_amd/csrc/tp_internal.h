@@ -26,6 +26,8 @@ struct ProfScope {
 // n_wg workgroups of 4 waves, each wave 16 * iters v_mfma_f32_32x32x16_bf16 on register
 // operands loaded from ops (8 x 256 x 16 bytes); out: n_wg * 256 fp32 checksums
 hipError_t mfma_rate(const void* ops, float* out, int64_t n_wg, int64_t iters, hipStream_t s);
+// n_wg workgroups each reading per_wg bytes (a multiple of 8192) of buf; out: n_wg * 256 checksums
+hipError_t hbm_read(const void* buf, int64_t per_wg, int64_t n_wg, unsigned* out, hipStream_t s);
 
 // ---- the allocation-free column linear call ------------------------------------------
 // Device address of the library's static scratch array (TP_NOALLOC_SCRATCH_BYTES) on the

@@ -363,6 +363,17 @@ def test_mfma_rate_probe_validation(L):
     assert _st(f(FAKE, FAKE, 256, 0, None)) == "TP_ERR_BAD_SHAPE"
 
 
+def test_hbm_read_probe_validation(L):
+    f = L.tp_hbm_read_probe
+    assert _st(f(None, 8192, 4, FAKE, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE, 8192, 4, None, None)) == "TP_ERR_NULL_POINTER"
+    assert _st(f(FAKE_ODD, 8192, 4, FAKE, None)) == "TP_ERR_MISALIGNED"
+    assert _st(f(FAKE, 8192 + 16, 4, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, 4096, 4, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, 8192, 0, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+    assert _st(f(FAKE, 8192, (1 << 20) + 1, FAKE, None)) == "TP_ERR_BAD_SHAPE"
+
+
 def test_decode_step_validation(L):
     f = L.tp_decode_step
     d = tp._desc(4, 8, 256, 2, 2)          # no cache: a prefill, not a decode step
