@@ -89,7 +89,7 @@ struct SkinnyArgs {
     int splits;
     int strips;              // strips per K chunk (dual: gate strips then up strips)
     int wg0;                 // first workgroup of this GEMM in a launch over several
-    float* part;             // [splits][M][ncols]
+    float* part;             // [splits][strips][M][128]: one contiguous block per workgroup
     int packed;              // weights in 128-column strips: [strip][K][128] (else [K][N])
 };
 
@@ -224,7 +224,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, 
         }
     __syncthreads();
     constexpr int ROWS = MB * 16 / 4;   // rows per wave
-    float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
+    float* dst = g.part + (split * g.M) * g.ncols + strip * g.M * STRIP;
 #pragma unroll
     for (int rr = lane >> 3; rr < ROWS; rr += 8) {   // lane: row rr, 16-byte chunks lane%8 + 8q
         const int m = wave * ROWS + rr;
@@ -235,7 +235,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs& g, int64_t strip, 
             v += red[1][m][c];
             v += red[2][m][c];
             v += red[3][m][c];
-            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * g.ncols + 4 * c) = v;
+            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * STRIP + 4 * c) = v;
         }
     }
 }
@@ -360,7 +360,7 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
         }
     __syncthreads();
     constexpr int ROWS = MB * 16 / 4;
-    float* dst = g.part + (split * g.M) * g.ncols + strip * STRIP;
+    float* dst = g.part + (split * g.M) * g.ncols + strip * g.M * STRIP;
 #pragma unroll
     for (int rr = lane >> 3; rr < ROWS; rr += 8) {
         const int m = wave * ROWS + rr;
@@ -371,7 +371,7 @@ __device__ __forceinline__ void skinny_body_lds(const SkinnyArgs& g, int64_t str
             v += red[1][m][c];
             v += red[2][m][c];
             v += red[3][m][c];
-            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * g.ncols + 4 * c) = v;
+            if (m < g.M) *reinterpret_cast<f32x4*>(dst + m * STRIP + 4 * c) = v;
         }
     }
 }
@@ -415,11 +415,15 @@ __global__ __launch_bounds__(256, MB <= 2 ? 2 : 1) void skinny_kernel(SkinnyArgs
 // values are loaded 8 at a time for all NC columns together, unconditionally (chunk indexes
 // past the last one re-read the last), so that a thread waits for one memory round trip per
 // 8 chunks rather than one per chunk and column.
+// offset of element (row m, column c) inside one chunk's partials [strips][M][128]
+__device__ __forceinline__ int64_t part_ofs(int64_t m, int64_t c, int64_t M) {
+    return (c >> 7) * M * STRIP + m * STRIP + (c & (STRIP - 1));
+}
+
 template <int NC>
 __device__ __forceinline__ void sum_splits(const float* part, int splits, int64_t M, int64_t ncols,
                                            int64_t m, const int64_t (&c)[NC], float (&v)[NC]) {
     constexpr int U = 8;
-    const float* p = part + m * ncols;
     const int64_t stride = M * ncols;
 #pragma unroll
     for (int i = 0; i < NC; ++i) v[i] = 0.f;
@@ -427,9 +431,9 @@ __device__ __forceinline__ void sum_splits(const float* part, int splits, int64_
         float t[U][NC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float* ps = p + (int64_t)(s0 + u < splits ? s0 + u : splits - 1) * stride;
+            const float* ps = part + (int64_t)(s0 + u < splits ? s0 + u : splits - 1) * stride;
 #pragma unroll
-            for (int i = 0; i < NC; ++i) t[u][i] = ps[c[i]];
+            for (int i = 0; i < NC; ++i) t[u][i] = ps[part_ofs(m, c[i], M)];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(256) void reduce4_store_kernel(ReduceOut r0, Reduce
     const int64_t e = e4 - (s2 ? r2.e0 : (s1 ? r1.e0 : r0.e0));
     const int64_t m = e / N, c = e - m * N;
     constexpr int U = 8;
-    const float* p = part + m * ncols + c;
+    const float* p = part + part_ofs(m, c, M);
     const int64_t stride = M * ncols;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < splits; s0 += U) {
@@ -581,7 +585,7 @@ constexpr int DU = 4;     // keys per group per iteration
 constexpr int NGRP = 32;  // 16-lane groups per workgroup
 
 struct QkvPartials {
-    const float* part;   // [splits][B][ncols]: columns [q heads | k heads | v heads] x 128
+    const float* part;   // [splits][strips][B][128]: columns [q heads | k heads | v heads] x 128
     int splits;
     int64_t ncols;
 };
