@@ -134,10 +134,11 @@ size_t tp_linear_workspace_size(int64_t T, int64_t K, int64_t N, tp_dtype in_dt)
  *   kind TP_MLP_RELU:   P = relu(X . W_gate) . W_down          (W_up must be NULL)
  *   kind TP_MLP_SWIGLU: P = (SiLU(X . W_gate) * (X . W_up)) . W_down,
  *                       SiLU(z) = z / (1 + exp(-z)), evaluated in fp32.
- *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: in_dt (F32 or BF16)
+ *   X [T, H], W_gate/W_up [H, I_shard], W_down [I_shard, H]: in_dt (F32, BF16 or F16)
  *   Y_partial [T, H] fp32 (overwritten).
  *   h_dt: storage type of the activated intermediate h [T, I_shard], which lives
- *   only in the workspace: F32 for the F32 path; BF16 or F16 for the BF16 path. F16 (T > 64
+ *   only in the workspace: F32 for the F32 path; F16 for the F16 path (fp16 operands
+ *   throughout, fp32 accumulation, any T); BF16 or F16 for the BF16 path. There, F16 (T > 64
  *   only, else TP_ERR_UNSUPPORTED) keeps 3 more bits of h for wide shards (h's rounding is the
  *   largest error term of the block): the down projection then runs on fp16 operands, with
  *   W_down converted to fp16 into the workspace first (exact for |w| >= 2^-14; smaller

@@ -404,10 +404,12 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
     (void)kind;
     if (T <= 0 || H <= 0 || I_shard <= 0) return 0;
     if (in_dt == TP_F32) return round_up((size_t)(T * I_shard) * 4, WS_ALIGN);
-    if (in_dt != TP_BF16 || (h_dt != TP_BF16 && h_dt != TP_F16)) return 0;
-    if (h_dt == TP_F16 && T <= SKINNY_MAX_T) return 0;
+    if (in_dt == TP_F16 && h_dt != TP_F16) return 0;                 // fp16 operands keep h in fp16
+    if (in_dt != TP_BF16 && in_dt != TP_F16) return 0;
+    if (h_dt != TP_BF16 && h_dt != TP_F16) return 0;
+    if (in_dt == TP_BF16 && h_dt == TP_F16 && T <= SKINNY_MAX_T) return 0;
     size_t bytes = round_up((size_t)(T * I_shard) * 2, WS_ALIGN);   // h
-    if (h_dt == TP_F16) bytes += round_up((size_t)(I_shard * H) * 2, WS_ALIGN);   // W_down in fp16
+    if (in_dt == TP_BF16 && h_dt == TP_F16) bytes += round_up((size_t)(I_shard * H) * 2, WS_ALIGN);   // W_down in fp16
     if (T <= SKINNY_MAX_T) {
         const size_t first = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu_partials_bytes(T, I_shard, H)
                                                    : tpk::skinny_partials_bytes(T, I_shard, H);
@@ -425,11 +427,28 @@ size_t tp_mlp_workspace_size(int64_t T, int64_t H, int64_t I_shard, tp_mlp_kind 
 // into h in the workspace, then the down projection's fp32 partial. `need` is
 // tp_mlp_workspace_size of the same arguments. h_f16 (T > 64 only): h is stored in fp16, W_down
 // is converted to fp16 into the workspace, and the down projection runs on fp16 operands.
+// in_f16: every operand is fp16 already, and so is h (no conversion).
 static hipError_t mlp_bf16(const void* X, const void* W_gate, const void* W_up, const void* W_down, float* Y,
                            int64_t T, int64_t H, int64_t I, tp_mlp_kind kind, void* workspace, size_t need,
-                           hipStream_t s, bool h_f16 = false) {
+                           hipStream_t s, bool h_f16 = false, bool in_f16 = false) {
     Carver c(workspace);
     void* h = c.take((size_t)(T * I) * 2);
+    if (in_f16) {
+        if (T <= SKINNY_MAX_T) {
+            float* part = static_cast<float*>(c.take(0));
+            hipError_t e = kind == TP_MLP_SWIGLU ? tpk::skinny_swiglu(X, W_gate, W_up, part, h, T, I, H, s, 1)
+                                                 : tpk::skinny_linear(X, W_gate, part, T, I, H, H, h, I, 6, s, 1);
+            if (e != hipSuccess) return e;
+            return tpk::skinny_linear(h, W_down, part, T, H, I, I, Y, H, 0, s, 1);
+        }
+        void* split = c.take(0);
+        const size_t split_bytes = need - c.off;
+        hipError_t e = kind == TP_MLP_SWIGLU
+                           ? tpk::gemm_f16_swiglu(X, W_gate, W_up, h, T, I, H, split, split_bytes, s)
+                           : tpk::gemm_f16_store(X, W_gate, h, T, I, H, H, I, I, 1, 1, split, split_bytes, s);
+        if (e != hipSuccess) return e;
+        return tpk::gemm_f16_store(h, W_down, Y, T, H, I, I, H, H, 2, 0, split, split_bytes, s);
+    }
     if (h_f16) {
         void* wd16 = c.take((size_t)(I * H) * 2);
         void* split = c.take(0);
@@ -474,7 +493,9 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
         return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: bf16 input keeps h in bf16 or fp16");
     if (in_dt == TP_BF16 && h_dt == TP_F16 && T <= SKINNY_MAX_T)
         return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: an fp16 h is offered for T > %d", (int)SKINNY_MAX_T);
-    if (in_dt != TP_F32 && in_dt != TP_BF16) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: input dtype %d not offered", (int)in_dt);
+    if (in_dt == TP_F16 && h_dt != TP_F16) return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: fp16 input keeps h in fp16");
+    if (in_dt != TP_F32 && in_dt != TP_BF16 && in_dt != TP_F16)
+        return fail(TP_ERR_BAD_DTYPE, "tp_mlp_shard: input dtype %d not offered", (int)in_dt);
     if (in_dt == TP_F32 && kind == TP_MLP_SWIGLU) return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard: the fp32 path offers the ReLU form");
     const size_t need = tp_mlp_workspace_size(T, H, I_shard, kind, in_dt, h_dt);
     if (!workspace || ws_bytes < need)
@@ -494,14 +515,14 @@ tp_status tp_mlp_shard(const void* X, const void* W_gate, const void* W_up, cons
     }
     if (!aligned(X, 16) || !aligned(W_gate, 16) || (W_up && !aligned(W_up, 16)) || !aligned(W_down, 16) ||
         !aligned(Y_partial, 16))
-        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs 16-byte aligned pointers");
+        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: 16-bit operands need 16-byte aligned pointers");
     if (H % 8 || I_shard % 8)
-        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: bf16 path needs H and I_shard multiples of 8");
+        return fail(TP_ERR_MISALIGNED, "tp_mlp_shard: 16-bit operands need H and I_shard multiples of 8");
     tp_status st = check_ld("tp_mlp_shard", "H", H);
     if (st == TP_OK) st = check_ld("tp_mlp_shard", "I_shard", I_shard);
     if (st != TP_OK) return st;
     return from_hip(mlp_bf16(X, W_gate, W_up, W_down, Y_partial, T, H, I_shard, kind, workspace, need, s,
-                             h_dt == TP_F16),
+                             in_dt == TP_BF16 && h_dt == TP_F16, in_dt == TP_F16),
                     "tp_mlp_shard");
 }
 

@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restri
 
 __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restrict__ part, int splits,
                                                             int64_t M, int64_t I, int64_t ncols,
-                                                            int64_t up_off, uint16_t* __restrict__ h) {
+                                                            int64_t up_off, uint16_t* __restrict__ h, int h16) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= M * I) return;
     const int64_t m = idx / I, c = idx - m * I;
@@ -478,7 +478,8 @@ __global__ __launch_bounds__(256) void reduce_swiglu_kernel(const float* __restr
     float sum[2];
     sum_splits<2>(part, splits, M, ncols, m, cols, sum);
     const float gt = sum[0], up = sum[1];
-    h[idx] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
+    const float v = gt / (1.0f + __expf(-gt)) * up;
+    h[idx] = h16 ? f32_to_f16(v) : f32_to_bf16(v);
 }
 
 // One output of a reduce launch over several: the chunk partials of a skinny GEMM summed in
@@ -824,15 +825,15 @@ hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, i
 }
 
 hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
-                         int64_t M, int64_t I, int64_t H, hipStream_t s) {
+                         int64_t M, int64_t I, int64_t H, hipStream_t s, int f16) {
     SkinnyArgs a = skinny_args(X, Wg, Wu, part, M, I, H, H);
     const SkinnyPlan p = plan_skinny(I, H, 2);
-    hipError_t e = skinny_run(a, p, s, "skinny_gemm_gateup");
+    hipError_t e = skinny_run(a, p, s, "skinny_gemm_gateup", f16 != 0);
     if (e != hipSuccess) return e;
     const int64_t n = M * I;
     ProfScope ps("skinny_reduce_swiglu", s);
     reduce_swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, (int)p.splits, M, I, p.ncols,
-                                                                     p.ncols / 2, static_cast<uint16_t*>(h));
+                                                                     p.ncols / 2, static_cast<uint16_t*>(h), f16);
     return hipGetLastError();
 }
 

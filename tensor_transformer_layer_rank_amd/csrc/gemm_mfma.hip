@@ -1326,6 +1326,14 @@ hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void*
                                "gemm_bf16_swiglu");
 }
 
+hipError_t gemm_f16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
+                           int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
+    Geom<false> g{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(Bg),
+                  static_cast<const uint16_t*>(Bu), M, N, K, K, N};
+    return launch<false, true, EpiSwiGLU<1>, NoGroups, true>(g, EpiSwiGLU<1>{h, M, N, 1.0f, 1.0f, 1.0f}, ws,
+                                                             ws_bytes, s, "gemm_f16_swiglu");
+}
+
 namespace {
 
 // groups 0..n-1 from their row offsets (n+1 entries, relative to the launch's A and output)

@@ -87,6 +87,9 @@ hipError_t gemm_bf16_f32out_grouped(const void* A, const void* B, float* C, cons
 // h_f16: h stored as fp16 instead of bf16
 hipError_t gemm_bf16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
                             int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s, int h_f16 = 0);
+// the same on fp16 operands, h stored as fp16
+hipError_t gemm_f16_swiglu(const void* A, const void* Bg, const void* Bu, void* h, int64_t M,
+                           int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 // out[i] = fp16(in[i]) for n bf16 values (n a multiple of 8, 16-byte aligned buffers)
 hipError_t bf16_to_f16(const void* in, void* out, int64_t n, hipStream_t s);
 
@@ -128,13 +131,13 @@ hipError_t flash_attn_fwd(const void* q, const void* k, const void* vt, void* ou
 // in chunk order and applies the epilogue.
 size_t skinny_partials_bytes(int64_t M, int64_t N, int64_t K);
 size_t skinny_swiglu_partials_bytes(int64_t M, int64_t I, int64_t H);
-// kind: 0 = fp32 store (ldc), 1 = fp32 +=, 2 = bf16 store, 3 = bf16 ReLU; f16_in: the operands
-// are fp16 instead of bf16
+// kind: 0 = fp32 store (ldc), 1 = fp32 +=, 2 = bf16 store, 3 = bf16 ReLU, 5 = fp16 store,
+// 6 = fp16 ReLU, 7 = fp32 ReLU; f16_in: the operands are fp16 instead of bf16
 hipError_t skinny_linear(const void* A, const void* B, float* part, int64_t M, int64_t N, int64_t K,
                          int64_t lda, void* C, int64_t ldc, int kind, hipStream_t s, int f16_in = 0);
-// h bf16 [M, I] = SiLU(X . Wg) * (X . Wu)
+// h [M, I] = SiLU(X . Wg) * (X . Wu), bf16 operands and h, or (f16) fp16 operands and h
 hipError_t skinny_swiglu(const void* X, const void* Wg, const void* Wu, float* part, void* h,
-                         int64_t M, int64_t I, int64_t H, hipStream_t s);
+                         int64_t M, int64_t I, int64_t H, hipStream_t s, int f16 = 0);
 // decode attention step of an attention shard: QKV split-K partials (workspace `part`,
 // skinny_partials_bytes(B, (hq + 2 hkv) * 128, H)), then one fused kernel that reduces them,
 // rotates q and k by position pos, appends k and v (bf16) at cache slot pos and attends over

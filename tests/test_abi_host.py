@@ -158,6 +158,15 @@ def test_mlp_validation(L):
     assert _st(f(*bad)) == "TP_ERR_MISALIGNED"              # I_shard not a multiple of 8
     bad = list(args); bad[5] = 0
     assert _st(f(*bad)) == "TP_ERR_BAD_SHAPE"
+    # fp16 operands keep h in fp16 (any T); their workspace holds no converted W_down
+    bad = list(args); bad[9] = tp.TP_F16
+    assert _st(f(*bad)) == "TP_ERR_BAD_DTYPE"                       # fp16 input with a bf16 h
+    assert L.tp_mlp_workspace_size(512, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_F16, tp.TP_BF16) == 0
+    w16 = L.tp_mlp_workspace_size(512, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_F16, tp.TP_F16)
+    assert w16 == ws
+    assert L.tp_mlp_workspace_size(32, 256, 128, tp.TP_MLP_SWIGLU, tp.TP_F16, tp.TP_F16) > 0
+    bad = list(args); bad[9] = tp.TP_F16; bad[10] = tp.TP_F16; bad[12] = w16 - 1
+    assert _st(f(*bad)) == "TP_ERR_WORKSPACE"
 
 
 def _desc(**kw):

@@ -495,6 +495,26 @@ def _f16(a):
     return np.asarray(a, np.float32).astype(np.float16).astype(np.float32)
 
 
+@pytest.mark.parametrize("T,H,I,kind", [(300, 256, 200, "swiglu"), (520, 512, 264, "relu"), (17, 1024, 1000, "swiglu"),
+                                         (64, 512, 264, "relu"), (4100, 1024, 2752, "swiglu")])
+def test_mlp_fp16_operands(tp, T, H, I, kind):
+    """tp_mlp_shard on fp16 X and weights (h in fp16, fp32 accumulation): the prefill tiles (ragged,
+    one grid split past the first round) and the few-row weight-streaming kernels."""
+    import torch
+    rng = np.random.default_rng(T * 5 + H + I)
+    X = _f16(rng.standard_normal((T, H)))
+    Wg = _f16(rng.standard_normal((H, I)) * 0.02)
+    Wu = _f16(rng.standard_normal((H, I)) * 0.02) if kind == "swiglu" else None
+    Wd = _f16(rng.standard_normal((I, H)) * 0.02)
+    k = tp.TP_MLP_SWIGLU if kind == "swiglu" else tp.TP_MLP_RELU
+    Y = tp.mlp_shard(dev(X, "f16"), dev(Wg, "f16"), dev(Wu, "f16") if Wu is not None else None, dev(Wd, "f16"),
+                     Y=_nan((T, H), torch.float32), kind=k)
+    torch.cuda.synchronize()
+    ref = O.mlp_swiglu_shard(X, Wg, Wu, Wd) if kind == "swiglu" else O.mlp_relu_shard(X, Wg, Wd)
+    rf, _ = assert_close_bf16(host(Y), ref, f"mlp fp16 operands {kind} {T}x{H}x{I}")
+    assert rf < 1e-3, "fp16 operands and h should leave far less error than bf16 ones"
+
+
 @pytest.mark.parametrize("T,K,N", [(300, 520, 264), (16, 1024, 392), (64, 4096, 512), (4100, 1000, 4000)])
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 def test_column_linear_fp16_operands(tp, T, K, N, out):
