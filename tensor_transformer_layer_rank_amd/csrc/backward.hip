@@ -20,12 +20,15 @@ size_t linear_backward_ws_bytes(int64_t T, int64_t K, int64_t N) {
 
 // dX [T, K] = dY [T, N] . W^T and dW [K, N] = X^T . dY [T, N]. When the two products share
 // their inner size (N == T) they run as one launch, so the tail split fills the machine across
-// both grids (two 176-tile grids on 256 units would each leave 80 idle).
+// both grids (two 176-tile grids on 256 units would each leave 80 idle). dW's tiles come first:
+// the tail round (the launch's last tiles, cut into K pieces) then holds dX tiles, whose
+// operands stage without the transposing reads, and the step is ~1% shorter than in the
+// other order (backward7b_tp4 on one GPU: 189.8 -> 187.5 us).
 hipError_t linear_backward(const void* X, const void* W, const void* dY, float* dX, float* dW, int64_t T,
                            int64_t K, int64_t N, void* ws, hipStream_t s) {
     const size_t ws_bytes = linear_backward_ws_bytes(T, K, N);
     if (N == T)
-        return gemm_bf16_f32out_pair_nt_tn(dY, W, dX, T, K, N, N, K, X, dY, dW, K, N, K, N, N, N, ws, ws_bytes, s);
+        return gemm_bf16_f32out_pair_tn_nt(X, dY, dW, K, N, K, N, N, dY, W, dX, T, K, N, N, K, N, ws, ws_bytes, s);
     hipError_t e = gemm_bf16_f32out_t(dY, W, dX, T, K, N, N, N, K, 1, ws, ws_bytes, s);
     if (e != hipSuccess) return e;
     return gemm_bf16_f32out_t(X, dY, dW, K, N, T, K, N, N, 0, ws, ws_bytes, s);

@@ -1405,20 +1405,20 @@ hipError_t gemm_bf16_f32out_t(const void* A, const void* B, float* C, int64_t M,
                                                                "gemm_bf16_f32out_tn");
 }
 
-hipError_t gemm_bf16_f32out_pair_nt_tn(const void* A0, const void* B0t, float* C0, int64_t M0, int64_t N0,
-                                       int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1t, const void* B1,
+hipError_t gemm_bf16_f32out_pair_tn_nt(const void* A0t, const void* B0, float* C0, int64_t M0, int64_t N0,
+                                       int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1, const void* B1t,
                                        float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
                                        int64_t K, void* ws, size_t ws_bytes, hipStream_t s) {
     using Epi = EpiStore<2, false>;
-    Geom<false> g0{static_cast<const uint16_t*>(A0), static_cast<const uint16_t*>(B0t), nullptr, M0, N0, K, lda0, ldb0};
+    Geom<false> g0{static_cast<const uint16_t*>(A0t), static_cast<const uint16_t*>(B0), nullptr, M0, N0, K, lda0, ldb0};
     int64_t tm0, tn0, tm1, tn1;
     tiles_of<false>(M0, N0, tm0, tn0);
     tiles_of<false>(M1, N1, tm1, tn1);
-    Pair<false, Epi> pr{Geom<false>{static_cast<const uint16_t*>(A1t), static_cast<const uint16_t*>(B1), nullptr,
+    Pair<false, Epi> pr{Geom<false>{static_cast<const uint16_t*>(A1), static_cast<const uint16_t*>(B1t), nullptr,
                                     M1, N1, K, lda1, ldb1},
                         Epi{C1, ldc1, M1, N1, 1.0f, 1.0f}, (int)tm1, (int)tn1, (int)(tm0 * tn0)};
-    return launch<false, false, Epi, Pair<false, Epi>, false, LAY_NT, LAY_TN>(
-        g0, Epi{C0, ldc0, M0, N0, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_f32out_nt_tn", pr);
+    return launch<false, false, Epi, Pair<false, Epi>, false, LAY_TN, LAY_NT>(
+        g0, Epi{C0, ldc0, M0, N0, 1.0f, 1.0f}, ws, ws_bytes, s, "gemm_bf16_f32out_tn_nt", pr);
 }
 
 hipError_t gemm_bf16_swiglu_grouped(const void* A, const void* Bg, const void* Bu, void* h,

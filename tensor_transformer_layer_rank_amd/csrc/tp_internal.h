@@ -68,10 +68,10 @@ hipError_t gemm_bf16_f32out_pair(const void* A0, const void* B0, float* C0, int6
 // C = At^T . B. M, N, K multiples of 8. Workspace as gemm_bf16_split_bytes(M, N, K, 0).
 hipError_t gemm_bf16_f32out_t(const void* A, const void* B, float* C, int64_t M, int64_t N, int64_t K, int64_t lda,
                               int64_t ldb, int64_t ldc, int b_trans, void* ws, size_t ws_bytes, hipStream_t s);
-// Both in one launch (same K): C0 = A0 . B0t^T and C1 = A1t^T . B1 (the backward's dX and dW).
+// Both in one launch (same K): C0 = A0t^T . B0 and C1 = A1 . B1t^T (the backward's dW and dX).
 // Workspace as gemm_bf16_pair_split_bytes.
-hipError_t gemm_bf16_f32out_pair_nt_tn(const void* A0, const void* B0t, float* C0, int64_t M0, int64_t N0,
-                                       int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1t, const void* B1,
+hipError_t gemm_bf16_f32out_pair_tn_nt(const void* A0t, const void* B0, float* C0, int64_t M0, int64_t N0,
+                                       int64_t lda0, int64_t ldb0, int64_t ldc0, const void* A1, const void* B1t,
                                        float* C1, int64_t M1, int64_t N1, int64_t lda1, int64_t ldb1, int64_t ldc1,
                                        int64_t K, void* ws, size_t ws_bytes, hipStream_t s);
 size_t gemm_bf16_grouped_split_bytes(const int64_t* row_offsets, int n_groups, int64_t N, int64_t K, int dual);

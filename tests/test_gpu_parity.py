@@ -857,12 +857,18 @@ def test_pack_strips_layout(tp, K, N):
 
 
 @pytest.mark.parametrize("B,H,hq,hkv,I,V,L,cap", [(4, 256, 2, 2, 136, 1000, 37, 40), (3, 512, 4, 1, 264, 520, 300, 301),
+                                                  (32, 256, 2, 2, 64, 128, 1, 8), (1, 1024, 8, 2, 2048, 4000, 0, 4),
                                                   (64, 512, 4, 4, 1000, 2056, 129, 130)])
 def test_decode_step_packed_small(tp, B, H, hq, hkv, I, V, L, cap):
     """tp_decode_step_packed: the decode step with every weight in 128-column strips (ragged last
-    strips, both activation-row paths)."""
+    strips, one token, an empty cache, both activation-row paths)."""
     inp = wl.random_decode(B * 11 + L, B, H, hq, hkv, I, V, L, cap)
     _check_decode_step(tp, inp, f"packed decode step B{B} H{H} hq{hq} hkv{hkv} I{I} V{V} L{L}", packed=True)
+
+
+def test_decode_step_packed_without_head(tp):
+    inp = wl.random_decode(6, 8, 512, 4, 2, 264, 64, 100, 104)
+    _check_decode_step(tp, inp, "packed decode step, no output layer", with_lm=False, packed=True)
 
 
 def test_decode7b_tp2_packed_step_full_size(tp):
